@@ -115,17 +115,17 @@ def frexp_exponent(A: np.float32) -> int:
 
 
 def channel_scores(r, A) -> np.ndarray:
-    """score_j = sum over rows of floor(|r_ij| * 2**(32 - E_A)), an exact
+    """score_j = sum over rows of floor(|r_ij| * 2**(31 - E_A)), an exact
     integer sum (uint64).  This is the 'residual magnitude' ranking statistic:
     the mean |r| over all rows, up to a positive factor, truncated below
-    2**-32 * 2**E_A per element so that any summation order gives the same
-    bits."""
+    2**-31 * 2**E_A per element so that any summation order gives the same
+    bits.  |r| <= 2**E_A, so each term fits in 32 bits."""
     r = np.asarray(r, dtype=np.float64)
     if A == 0:
         return np.zeros(r.shape[1], dtype=np.uint64)
     E = frexp_exponent(A)
-    t = np.floor(np.ldexp(np.abs(r), 32 - E))
-    assert np.all(t < 2.0 ** 34)
+    t = np.floor(np.ldexp(np.abs(r), 31 - E))
+    assert np.all(t <= 2.0 ** 31)
     return t.astype(np.uint64).sum(axis=0, dtype=np.uint64)
 
 

@@ -153,7 +153,7 @@ def test_scores_exact_and_order_free():
     m, E = np.frexp(float(A))
     assert 0.5 <= m < 1
     for j in (0, 7, 33, 63):
-        want = sum(int((abs(Fraction(float(r[i, j]))) * Fraction(2) ** (32 - E)).__floor__())
+        want = sum(int((abs(Fraction(float(r[i, j]))) * Fraction(2) ** (31 - E)).__floor__())
                    for i in range(40))
         assert int(sc[j]) == want
     p = rng.permutation(40)
