@@ -1,0 +1,220 @@
+"""NVFP4 W4A4 MoE expert GEMM with Residual Activation Compensation for
+AMD MI355X (gfx950): Python binding of libnvfp4rac.so.
+
+The binding only marshals arguments: it allocates outputs and workspaces as
+torch tensors on the current device, passes raw device pointers and the
+current HIP stream to the C ABI declared in include/nvfp4rac.h, and raises on
+a non-OK status.  Every step of the path runs in the library's HIP kernels;
+there is no fallback: importing the library fails loudly if it is missing.
+
+Calls (same names as the C ABI):
+    nvfp4_qdq_weights, nvfp4_quantize_act, select_residual_channels,
+    moe_permute, grouped_w4a4_gemm_rac, moe_unpermute_combine
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import LIB as LIB_PATH
+
+__all__ = ["lib", "nvfp4_qdq_weights", "nvfp4_quantize_act", "select_residual_channels",
+           "moe_permute", "grouped_w4a4_gemm_rac", "moe_unpermute_combine", "NvfpError",
+           "EXPORTED_SYMBOLS"]
+
+EXPORTED_SYMBOLS = [
+    "nvfp4_version", "nvfp4_status_str", "nvfp4_last_error",
+    "nvfp4_qdq_weights_workspace_size", "nvfp4_qdq_weights",
+    "nvfp4_quantize_act_workspace_size", "nvfp4_quantize_act",
+    "select_residual_channels_workspace_size", "select_residual_channels",
+    "moe_permute_workspace_size", "moe_permute",
+    "grouped_w4a4_gemm_rac_workspace_size", "grouped_w4a4_gemm_rac",
+    "moe_unpermute_combine",
+]
+
+
+class NvfpError(RuntimeError):
+    pass
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise NvfpError(f"{LIB_PATH} is not built; run python -m fp4_quantized_gemm_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    L.nvfp4_version.restype = ctypes.c_int
+    L.nvfp4_status_str.restype = ctypes.c_char_p
+    L.nvfp4_status_str.argtypes = [ctypes.c_int]
+    L.nvfp4_last_error.restype = ctypes.c_char_p
+    for name, args in {
+        "nvfp4_qdq_weights_workspace_size": [_I64],
+        "nvfp4_quantize_act_workspace_size": [_I64, _I64],
+        "select_residual_channels_workspace_size": [_I64, _I64, _I64],
+        "moe_permute_workspace_size": [_I64, _I64],
+        "grouped_w4a4_gemm_rac_workspace_size": [_I64, _I64, _I64, _I64, _I64],
+    }.items():
+        f = getattr(L, name)
+        f.restype = _SZ
+        f.argtypes = args
+    sigs = {
+        "nvfp4_qdq_weights": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P],
+        "nvfp4_quantize_act": [_P, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P, _P, _P, _P, _SZ, _P],
+        "select_residual_channels": [_P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _SZ, _P],
+        "moe_permute": [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P],
+        "grouped_w4a4_gemm_rac": [_P, _P, _P, _P, _I64, _P, _P, _I64, _P, _P, _P, _P, _I64, _I64,
+                                  _I64, _I64, _P, _P, _SZ, _P],
+        "moe_unpermute_combine": [_P, _P, _P, _I64, _I64, _I64, _P, _P],
+    }
+    for name, args in sigs.items():
+        f = getattr(L, name)
+        f.restype = ctypes.c_int
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def lib():
+    return _load()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _check(status, name):
+    if status != 0:
+        L = _load()
+        raise NvfpError(f"{name}: {L.nvfp4_status_str(status).decode()}: "
+                        f"{L.nvfp4_last_error().decode()}")
+
+
+def _ws(nbytes, device):
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def _need(t, dtype, name):
+    if not t.is_cuda:
+        raise NvfpError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise NvfpError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise NvfpError(f"{name} must be contiguous")
+
+
+def nvfp4_qdq_weights(w, want_qdq=True):
+    """w [E][N][K] bf16 -> (codes [E][N][K/2] u8, scales [E][N][K/16] u8,
+    g_w [E] f32, w_qdq [E][N][K] bf16 or None)."""
+    L = _load()
+    _need(w, torch.bfloat16, "w")
+    E, N, K = w.shape
+    dev = w.device
+    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((E, N, K // 16), dtype=torch.uint8, device=dev)
+    g_w = torch.empty(E, dtype=torch.float32, device=dev)
+    w_qdq = torch.empty_like(w) if want_qdq else None
+    ws = _ws(L.nvfp4_qdq_weights_workspace_size(E), dev)
+    _check(L.nvfp4_qdq_weights(_ptr(w), E, N, K, _ptr(codes), _ptr(scales), _ptr(g_w),
+                               _ptr(w_qdq), _ptr(ws), ws.numel(), _stream(dev)),
+           "nvfp4_qdq_weights")
+    return codes, scales, g_w, w_qdq
+
+
+def nvfp4_quantize_act(x, glu=False, want_score=True):
+    """x [M][K] bf16 (glu: [M][2K] = [gate | up]) -> dict(codes, scales, g,
+    score, x_used).  x_used is x itself for glu=False, else h."""
+    L = _load()
+    _need(x, torch.bfloat16, "x")
+    M, C = x.shape
+    K = C // 2 if glu else C
+    dev = x.device
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+    g = torch.empty(1, dtype=torch.float32, device=dev)
+    score = torch.empty(K, dtype=torch.uint64, device=dev) if want_score else None
+    h = torch.empty((M, K), dtype=torch.bfloat16, device=dev) if glu else None
+    ws = _ws(L.nvfp4_quantize_act_workspace_size(M, K), dev)
+    _check(L.nvfp4_quantize_act(_ptr(x), M, K, C, int(bool(glu)), _ptr(codes), _ptr(scales),
+                                _ptr(g), _ptr(score), _ptr(h), _ptr(ws), ws.numel(), _stream(dev)),
+           "nvfp4_quantize_act")
+    return dict(codes=codes, scales=scales, g=g, score=score, x_used=h if glu else x)
+
+
+def select_residual_channels(x_used, codes, scales, g, score, k):
+    """-> (S [k] int32 ascending, R_S [M][k] bf16)."""
+    L = _load()
+    M, K = x_used.shape
+    dev = x_used.device
+    S = torch.empty(k, dtype=torch.int32, device=dev)
+    R = torch.empty((M, k), dtype=torch.bfloat16, device=dev)
+    ws = _ws(L.select_residual_channels_workspace_size(M, K, k), dev)
+    _check(L.select_residual_channels(_ptr(x_used), x_used.stride(0), _ptr(codes), _ptr(scales),
+                                      _ptr(g), _ptr(score), M, K, k, _ptr(S), _ptr(R), _ptr(ws),
+                                      ws.numel(), _stream(dev)),
+           "select_residual_channels")
+    return S, R
+
+
+def moe_permute(logits, topk, bias=None):
+    """logits [T][E] f32 -> (topk_ids [T][tk] i32, topk_w [T][tk] f32,
+    expert_offsets [E+1] i32, perm_token [T*tk] i32, inv_perm [T][tk] i32)."""
+    L = _load()
+    _need(logits, torch.float32, "logits")
+    T, E = logits.shape
+    dev = logits.device
+    ids = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    w = torch.empty((T, topk), dtype=torch.float32, device=dev)
+    offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * topk, dtype=torch.int32, device=dev)
+    inv = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    ws = _ws(L.moe_permute_workspace_size(T, E), dev)
+    _check(L.moe_permute(_ptr(logits), _ptr(bias), T, E, topk, _ptr(ids), _ptr(w), _ptr(offs),
+                         _ptr(perm), _ptr(inv), _ptr(ws), ws.numel(), _stream(dev)),
+           "moe_permute")
+    return ids, w, offs, perm, inv
+
+
+def grouped_w4a4_gemm_rac(a_codes, a_scales, g_x, a_rows, R_S, S, w_codes, w_scales, g_w,
+                          expert_offsets, M_total=None, out=None):
+    """Y [M_total][N] bf16 for the expert-grouped W4A4 GEMM plus the residual
+    correction on the channels S (k = len(S), 0 disables it)."""
+    L = _load()
+    M_src, Kh = a_codes.shape
+    K = Kh * 2
+    E, N, _ = w_codes.shape
+    k = 0 if S is None else int(S.numel())
+    if M_total is None:
+        M_total = int(a_rows.numel()) if a_rows is not None else M_src
+    dev = a_codes.device
+    y = out if out is not None else torch.empty((M_total, N), dtype=torch.bfloat16, device=dev)
+    ws = _ws(L.grouped_w4a4_gemm_rac_workspace_size(E, M_total, N, K, k), dev)
+    _check(L.grouped_w4a4_gemm_rac(_ptr(a_codes), _ptr(a_scales), _ptr(g_x), _ptr(a_rows), M_src,
+                                   _ptr(R_S) if k else None, _ptr(S) if k else None, k,
+                                   _ptr(w_codes), _ptr(w_scales), _ptr(g_w), _ptr(expert_offsets),
+                                   E, M_total, N, K, _ptr(y), _ptr(ws), ws.numel(), _stream(dev)),
+           "grouped_w4a4_gemm_rac")
+    return y
+
+
+def moe_unpermute_combine(y, inv_perm, topk_w, out=None):
+    L = _load()
+    T, tk = inv_perm.shape
+    N = y.shape[1]
+    o = out if out is not None else torch.empty((T, N), dtype=torch.bfloat16, device=y.device)
+    _check(L.moe_unpermute_combine(_ptr(y), _ptr(inv_perm), _ptr(topk_w), T, tk, N, _ptr(o),
+                                   _stream(y.device)),
+           "moe_unpermute_combine")
+    return o

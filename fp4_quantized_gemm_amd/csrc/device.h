@@ -1,0 +1,105 @@
+// Device helpers for the NVFP4 kernels (gfx950 only).
+//
+// Number formats: E2M1 element codes (sign | 3-bit magnitude index into
+// {0, .5, 1, 1.5, 2, 3, 4, 6}), OCP FP8 E4M3 block scales over 16 elements,
+// one float32 tensor scale.  The QUADS pages name only the E2M1 grid and
+// "fine-grained scaling" (gist.science technical summary §1; arXiv
+// abstract); the block layout is the public NVFP4 definition.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kE4M3Max = 448.0f;
+constexpr float kScaleDen = 2688.0f;   // 6 * 448: largest E2M1 magnitude x largest E4M3
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
+// float32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Non-negative float32 -> E4M3 byte, round to nearest even, saturate at 448.
+// Subnormal range (u < 2^-6): the code is the nearest multiple of 2^-9,
+// which rintf (ties to even) gives exactly after an exact power-of-two
+// scaling; a result of 8 is the smallest normal's code, as it should be.
+__device__ __forceinline__ uint32_t e4m3_encode_nonneg(float u) {
+  if (!(u < kE4M3Max)) return 0x7Eu;
+  if (u < 0.015625f) return (uint32_t)__builtin_rintf(u * 512.0f);
+  uint32_t b = __float_as_uint(u);
+  uint32_t e = (b >> 23) - 127u + 7u;        // biased E4M3 exponent, 1..15
+  uint32_t m = b & 0x7FFFFFu;
+  uint32_t f = m >> 20, rem = m & 0xFFFFFu;
+  f += (rem > 0x80000u || (rem == 0x80000u && (f & 1u))) ? 1u : 0u;
+  uint32_t code = (e << 3) + f;              // a mantissa carry bumps the exponent
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t byte) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
+}
+
+// Two float32 values -> one byte of two E2M1 codes (a in bits 3:0, b in
+// bits 7:4): round to nearest, ties to the even code, saturating at 6, sign
+// kept for values that round to zero (the hardware conversion with unit
+// scale does exactly this).
+__device__ __forceinline__ uint32_t e2m1_pack2(float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xFFu;
+}
+
+// Byte `sel` (0..3) of w, two E2M1 codes -> their two values as float32.
+// The conversion's own scale only applies a power of two, so an E4M3 block
+// scale is multiplied in separately by the callers.
+template <int SEL>
+__device__ __forceinline__ f32x2 e2m1_unpack2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
+// Pack the (exact) bf16 images of two float32 values whose low 16 bits are
+// zero: the upper halves, a low, b high.
+__device__ __forceinline__ uint32_t pack_hi16(float a, float b) {
+  return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+
+// 8 E2M1 codes (one dword) times one block scale -> 8 bf16 values, exact
+// (a code value has 2 significant bits, an E4M3 value 4, bf16 holds 8).
+__device__ __forceinline__ u32x4 decode8_bf16(uint32_t w, float s) {
+  f32x2 v0 = e2m1_unpack2<0>(w), v1 = e2m1_unpack2<1>(w);
+  f32x2 v2 = e2m1_unpack2<2>(w), v3 = e2m1_unpack2<3>(w);
+  u32x4 r;
+  r.x = pack_hi16(v0.x * s, v0.y * s);
+  r.y = pack_hi16(v1.x * s, v1.y * s);
+  r.z = pack_hi16(v2.x * s, v2.y * s);
+  r.w = pack_hi16(v3.x * s, v3.y * s);
+  return r;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t w = __shfl_xor(v, o);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int frexp_exponent(float a) {
+  return (int)((__float_as_uint(a) >> 23) & 0xFFu) - 126;   // a normal and > 0
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,250 @@
+// MoE routing, expert-major permutation and the weighted un-permute/combine
+// around the grouped expert GEMM (the MoE model of the QUADS pages,
+// gist.science technical summary §4; the router is not described there:
+// top-k of logit + bias, ties to the lower expert, softmax over the chosen k).
+//
+// Permutation without host synchronisation or float atomics:
+//   1. k_route: one wave per token -> topk_ids, topk_w (softmax in float64).
+//   2. k_route_masks: one wave per chunk of 64 tokens; per expert a 64-bit
+//      mask of the chunk's tokens that chose it (LDS atomic OR), plus counts.
+//   3. k_chunk_scan: one workgroup; per expert an exclusive scan over chunks,
+//      then over experts -> expert_offsets and each chunk's base per expert.
+//   4. k_scatter: row = base[chunk][e] + popcount(mask below the token), so
+//      tokens stay ascending inside an expert.
+#include "device.h"
+#include "runtime.h"
+
+namespace nvfp4 {
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopk = 32;
+
+__global__ void __launch_bounds__(256)
+k_route(const float* __restrict__ logits, const float* __restrict__ bias, int64_t T, int E,
+        int tk, int32_t* __restrict__ ids, float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = blockIdx.x * 4LL + (threadIdx.x >> 6);
+  if (t >= T) return;
+  constexpr int kPer = kMaxExperts / 64;
+  float v[kPer];
+  uint32_t taken = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    int e = lane + 64 * i;
+    float l = -INFINITY;
+    if (e < E) {
+      l = logits[t * E + e];
+      if (bias) l = l + bias[e];
+    }
+    v[i] = l;
+    if (e >= E) taken |= 1u << i;
+  }
+  double sel[kMaxTopk];
+  int sel_e[kMaxTopk];
+  for (int r = 0; r < tk; ++r) {
+    // lane-local best among untaken (value desc, index asc)
+    float bv = -INFINITY;
+    int be = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      int e = lane + 64 * i;
+      if (!(taken & (1u << i)) && (v[i] > bv || (v[i] == bv && e < be))) {
+        bv = v[i];
+        be = e;
+      }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      float ov = __shfl_xor(bv, o);
+      int oe = __shfl_xor(be, o);
+      if (ov > bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if ((be & 63) == lane) taken |= 1u << (be >> 6);
+    sel[r] = (double)bv;
+    sel_e[r] = be;
+  }
+  if (lane == 0) {
+    double mx = sel[0], sum = 0.0;
+    double z[kMaxTopk];
+    for (int r = 0; r < tk; ++r) {
+      z[r] = exp(sel[r] - mx);
+      sum += z[r];
+    }
+    for (int r = 0; r < tk; ++r) {
+      ids[t * tk + r] = sel_e[r];
+      w[t * tk + r] = (float)(z[r] / sum);
+    }
+  }
+}
+
+// masks [nchunks][E] uint64, counts [nchunks][E] int32
+__global__ void __launch_bounds__(64)
+k_route_masks(const int32_t* __restrict__ ids, int64_t T, int E, int tk,
+              uint64_t* __restrict__ masks, int32_t* __restrict__ counts) {
+  __shared__ unsigned long long m[kMaxExperts];
+  const int lane = threadIdx.x;
+  const int64_t c = blockIdx.x;
+  for (int e = lane; e < E; e += 64) m[e] = 0ull;
+  __syncthreads();
+  const int64_t t = c * 64 + lane;
+  if (t < T)
+    for (int j = 0; j < tk; ++j) atomicOr(&m[ids[t * tk + j]], 1ull << lane);
+  __syncthreads();
+  for (int e = lane; e < E; e += 64) {
+    masks[c * E + e] = m[e];
+    counts[c * E + e] = __popcll(m[e]);
+  }
+}
+
+// One workgroup of 1024 threads.  base[c][e] = offsets[e] + sum_{c' < c} counts[c'][e].
+__global__ void __launch_bounds__(1024)
+k_chunk_scan(int32_t* __restrict__ counts_to_base, int64_t nchunks, int E,
+             int32_t* __restrict__ offsets) {
+  __shared__ int tot[kMaxExperts];
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 1024) {
+    int run = 0;
+    for (int64_t c = 0; c < nchunks; ++c) {
+      int v = counts_to_base[c * E + e];
+      counts_to_base[c * E + e] = run;
+      run += v;
+    }
+    tot[e] = run;
+  }
+  __syncthreads();
+  // exclusive scan of tot over experts (E <= 1024: one value per thread)
+  int v = tid < E ? tot[tid] : 0;
+  int incl = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    int u = __shfl_up(incl, o);
+    if ((tid & 63) >= o) incl += u;
+  }
+  if ((tid & 63) == 63) wsum[tid >> 6] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < (tid >> 6); ++w) base += wsum[w];
+  const int excl = base + incl - v;
+  if (tid < E) offsets[tid] = excl;
+  if (tid == E - 1) offsets[E] = excl + v;
+  __syncthreads();
+  if (tid < E) tot[tid] = excl;
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024)
+    for (int64_t c = 0; c < nchunks; ++c) counts_to_base[c * E + e] += tot[e];
+}
+
+__global__ void __launch_bounds__(64)
+k_scatter(const int32_t* __restrict__ ids, int64_t T, int E, int tk,
+          const uint64_t* __restrict__ masks, const int32_t* __restrict__ base,
+          int32_t* __restrict__ perm_token, int32_t* __restrict__ inv_perm) {
+  const int lane = threadIdx.x;
+  const int64_t c = blockIdx.x;
+  const int64_t t = c * 64 + lane;
+  if (t >= T) return;
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  for (int j = 0; j < tk; ++j) {
+    const int e = ids[t * tk + j];
+    const int p = base[c * E + e] + __popcll(masks[c * E + e] & below);
+    perm_token[p] = (int32_t)t;
+    inv_perm[t * tk + j] = p;
+  }
+}
+
+// out[t][n..n+8) = bf16(sum_j w[t][j] * y[inv_perm[t][j]][n..n+8)), float32 in slot order
+__global__ void __launch_bounds__(256)
+k_combine(const uint16_t* __restrict__ y, const int32_t* __restrict__ inv_perm,
+          const float* __restrict__ tw, int64_t T, int tk, int64_t N, uint16_t* __restrict__ out) {
+  const int64_t chunks = N / 8;
+  const int64_t total = T * chunks;
+  for (int64_t e = blockIdx.x * 256LL + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int64_t t = e / chunks;
+    const int64_t n = (e - t * chunks) * 8;
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int j = 0; j < tk; ++j) {
+      const int64_t p = inv_perm[t * tk + j];
+      const float wj = tw[t * tk + j];
+      uint4 v = *reinterpret_cast<const uint4*>(y + p * N + n);
+      uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = __builtin_fmaf(wj, bf16_bits_to_f32(u[i] & 0xFFFFu), acc[2 * i]);
+        acc[2 * i + 1] = __builtin_fmaf(wj, bf16_bits_to_f32(u[i] >> 16), acc[2 * i + 1]);
+      }
+    }
+    uint4 o;
+    o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+    o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+    o.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
+    o.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
+    *reinterpret_cast<uint4*>(out + t * N + n) = o;
+  }
+}
+
+}  // namespace nvfp4
+
+using namespace nvfp4;
+
+extern "C" {
+
+size_t moe_permute_workspace_size(int64_t T, int64_t E) {
+  int64_t nchunks = (T + 63) / 64;
+  if (nchunks < 1) nchunks = 1;
+  return round_up((size_t)nchunks * (size_t)E * sizeof(uint64_t), 256) +
+         round_up((size_t)nchunks * (size_t)E * sizeof(int32_t), 256);
+}
+
+int moe_permute(const float* logits, const float* bias, int64_t T, int64_t E, int64_t tk,
+                int32_t* topk_ids, float* topk_w, int32_t* expert_offsets, int32_t* perm_token,
+                int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
+  NV_REQUIRE(T >= 0 && E >= 1 && E <= kMaxExperts && tk >= 1 && tk <= E && tk <= kMaxTopk &&
+                 T * tk < (1LL << 31),
+             NVFP4_ERR_SHAPE, "moe_permute: need T >= 0, 1 <= tk <= min(E, %d), E <= %d",
+             kMaxTopk, kMaxExperts);
+  NV_REQUIRE(expert_offsets && ws && (T == 0 || (logits && topk_ids && topk_w && perm_token &&
+                                                 inv_perm)),
+             NVFP4_ERR_NULL, "moe_permute: missing pointer");
+  NV_REQUIRE(aligned(ws, 16) && aligned(logits, 4) && aligned(topk_ids, 4), NVFP4_ERR_ALIGN,
+             "moe_permute: misaligned pointer");
+  NV_REQUIRE(ws_bytes >= moe_permute_workspace_size(T, E), NVFP4_ERR_WORKSPACE,
+             "moe_permute: workspace too small");
+  hipStream_t s = as_stream(stream);
+  int64_t nchunks = (T + 63) / 64;
+  uint64_t* masks = static_cast<uint64_t*>(ws);
+  int32_t* counts = reinterpret_cast<int32_t*>(
+      static_cast<char*>(ws) +
+      round_up((size_t)(nchunks > 0 ? nchunks : 1) * (size_t)E * sizeof(uint64_t), 256));
+  if (T == 0) {
+    fill_u32(reinterpret_cast<uint32_t*>(expert_offsets), E + 1, 0u, s);
+    return check_launch("moe_permute");
+  }
+  k_route<<<(unsigned)((T + 3) / 4), 256, 0, s>>>(logits, bias, T, (int)E, (int)tk, topk_ids,
+                                                  topk_w);
+  k_route_masks<<<(unsigned)nchunks, 64, 0, s>>>(topk_ids, T, (int)E, (int)tk, masks, counts);
+  k_chunk_scan<<<1, 1024, 0, s>>>(counts, nchunks, (int)E, expert_offsets);
+  k_scatter<<<(unsigned)nchunks, 64, 0, s>>>(topk_ids, T, (int)E, (int)tk, masks, counts,
+                                             perm_token, inv_perm);
+  return check_launch("moe_permute");
+}
+
+int moe_unpermute_combine(const void* y, const int32_t* inv_perm, const float* topk_w, int64_t T,
+                          int64_t tk, int64_t N, void* out, void* stream) {
+  NV_REQUIRE(T >= 0 && tk >= 1 && N >= 8 && N % 8 == 0, NVFP4_ERR_SHAPE,
+             "moe_unpermute_combine: need T >= 0, tk >= 1, N %% 8 == 0");
+  if (T == 0) return ok();
+  NV_REQUIRE(y && inv_perm && topk_w && out, NVFP4_ERR_NULL, "moe_unpermute_combine: missing pointer");
+  NV_REQUIRE(aligned(y, 16) && aligned(out, 16), NVFP4_ERR_ALIGN,
+             "moe_unpermute_combine: misaligned pointer");
+  hipStream_t s = as_stream(stream);
+  int64_t total = T * (N / 8);
+  int64_t blocks = (total + 255) / 256;
+  int64_t cap = 16LL * num_cus();
+  k_combine<<<(unsigned)(blocks < cap ? blocks : cap), 256, 0, s>>>(
+      static_cast<const uint16_t*>(y), inv_perm, topk_w, T, (int)tk, N,
+      static_cast<uint16_t*>(out));
+  return check_launch("moe_unpermute_combine");
+}
+
+}  // extern "C"

@@ -1,0 +1,363 @@
+// NVFP4 quantizers: online activation quantization (with the per-channel
+// residual statistic used to pick compensation channels) and the weight QDQ
+// path shared by trainer and rollout.
+//
+// QUADS (arXiv abstract; gist.science technical summary §2.1, §2.2 A-B):
+// activations are recomputed and quantized to E2M1 every forward; weights go
+// through one quantize-dequantize path on both sides; the channels with the
+// largest activation residual get compensated.
+//
+// Pass structure (both HBM-bound):
+//   1. amax: per-tensor max |x| (integer max over bf16 bit patterns, so the
+//      result is exact and order-free); for the SwiGLU input it also forms
+//      h = bf16(silu(gate) * up) and writes h once.
+//   2. quantize: one thread per 16-element block; block max -> E4M3 scale,
+//      codes via the hardware E2M1 conversion, residual and fixed-point
+//      channel score in the same pass.
+#include "device.h"
+#include "runtime.h"
+
+namespace nvfp4 {
+
+// Thread -> (row sub-index, column chunk) mapping used by both passes: a
+// workgroup of 256 threads covers `rows_per_iter` rows of `chunks` chunks.
+struct RowTiling {
+  int chunks;          // chunks per row
+  int rows_per_iter;   // rows a workgroup covers per step
+  int col_groups;      // gridDim.y when a row has more than 256 chunks
+};
+
+static RowTiling row_tiling(int64_t chunks) {
+  RowTiling t;
+  if (chunks >= 256) {
+    t.chunks = (int)chunks;
+    t.rows_per_iter = 1;
+    t.col_groups = (int)((chunks + 255) / 256);
+  } else {
+    t.chunks = (int)chunks;
+    t.rows_per_iter = 256 / (int)chunks;
+    t.col_groups = 1;
+  }
+  return t;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1a: amax over one or more [rows][K] bf16 tensors stacked by row
+// (tensor id = blockIdx.z).  Chunks of 8 elements (one 16-byte load).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+k_amax(const uint16_t* __restrict__ x, int64_t rows, int64_t ldx, int64_t tensor_stride,
+       int chunks, int rows_per_iter, uint32_t* __restrict__ amax) {
+  const int tid = threadIdx.x;
+  const int cw = chunks < 256 ? chunks : 256;
+  const int rsub = tid / cw;
+  const int c = blockIdx.y * 256 + tid % cw;
+  const uint16_t* xt = x + (int64_t)blockIdx.z * tensor_stride;
+  uint32_t m = 0;
+  if (rsub < rows_per_iter && c < chunks) {
+    for (int64_t r = (int64_t)blockIdx.x * rows_per_iter + rsub; r < rows;
+         r += (int64_t)gridDim.x * rows_per_iter) {
+      uint4 v = *reinterpret_cast<const uint4*>(xt + r * ldx + (int64_t)c * 8);
+      uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu, d = v.z & 0x7FFF7FFFu,
+               e = v.w & 0x7FFF7FFFu;
+      uint32_t hi = max(max(a >> 16, b >> 16), max(d >> 16, e >> 16));
+      uint32_t lo = max(max(a & 0xFFFFu, b & 0xFFFFu), max(d & 0xFFFFu, e & 0xFFFFu));
+      m = max(m, max(hi, lo));
+    }
+  }
+  m = wave_max_u32(m);
+  if ((tid & 63) == 0 && m) atomicMax(amax + blockIdx.z, m);
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1b: h = bf16(silu(gate) * up) from y = [gate | up] ([M][2I], row stride
+// ldy); writes h [M][I] and its amax.  silu(g) = g / (1 + exp(-g)), float32.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t swiglu_pair(uint32_t g2, uint32_t u2) {
+  float g0 = bf16_bits_to_f32(g2 & 0xFFFFu), g1 = bf16_bits_to_f32(g2 >> 16);
+  float u0 = bf16_bits_to_f32(u2 & 0xFFFFu), u1 = bf16_bits_to_f32(u2 >> 16);
+  float h0 = g0 / (1.0f + expf(-g0)) * u0;
+  float h1 = g1 / (1.0f + expf(-g1)) * u1;
+  return f32_to_bf16_rne(h0) | (f32_to_bf16_rne(h1) << 16);
+}
+
+__global__ void __launch_bounds__(256)
+k_swiglu_amax(const uint16_t* __restrict__ y, int64_t rows, int64_t ldy, int64_t inter,
+              int chunks, int rows_per_iter, uint16_t* __restrict__ h,
+              uint32_t* __restrict__ amax) {
+  const int tid = threadIdx.x;
+  const int cw = chunks < 256 ? chunks : 256;
+  const int rsub = tid / cw;
+  const int c = blockIdx.y * 256 + tid % cw;
+  uint32_t m = 0;
+  if (rsub < rows_per_iter && c < chunks) {
+    for (int64_t r = (int64_t)blockIdx.x * rows_per_iter + rsub; r < rows;
+         r += (int64_t)gridDim.x * rows_per_iter) {
+      const uint16_t* yr = y + r * ldy + (int64_t)c * 8;
+      uint4 g = *reinterpret_cast<const uint4*>(yr);
+      uint4 u = *reinterpret_cast<const uint4*>(yr + inter);
+      uint4 o;
+      o.x = swiglu_pair(g.x, u.x);
+      o.y = swiglu_pair(g.y, u.y);
+      o.z = swiglu_pair(g.z, u.z);
+      o.w = swiglu_pair(g.w, u.w);
+      *reinterpret_cast<uint4*>(h + r * inter + (int64_t)c * 8) = o;
+      uint32_t a = o.x & 0x7FFF7FFFu, b = o.y & 0x7FFF7FFFu, d = o.z & 0x7FFF7FFFu,
+               e = o.w & 0x7FFF7FFFu;
+      uint32_t hi = max(max(a >> 16, b >> 16), max(d >> 16, e >> 16));
+      uint32_t lo = max(max(a & 0xFFFFu, b & 0xFFFFu), max(d & 0xFFFFu, e & 0xFFFFu));
+      m = max(m, max(hi, lo));
+    }
+  }
+  m = wave_max_u32(m);
+  if ((tid & 63) == 0 && m) atomicMax(amax, m);
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: block quantizer.  One thread per 16-element block; tensors stacked
+// by row (blockIdx.z), each with its own amax (bf16 bits) and tensor scale.
+//
+//   A = amax, g = fp32(A / 2688)
+//   s = e4m3( fp32(blockmax * 448) / A )            (fp32 divide, RNE)
+//   rho = fp32(2688 / fp32(s * A)),  v = fp32(x * rho),  code = e2m1(v)
+//   s == 0: every magnitude 0.   Sign of a code = sign of x.
+//   residual r = bf16(fma(-(q*s), g, x))            (one rounding to fp32)
+//   score[j] += floor(|r| * 2^(31 - E_A))           (exact, <= 2^31)
+//   w_qdq = bf16(fp32(q*s) * g)                     (trainer fake-quant)
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+k_quantize(const uint16_t* __restrict__ x, int64_t rows, int64_t ldx, int64_t K,
+           int64_t tensor_stride, int ntensors, int blocks, int rows_per_iter,
+           const uint32_t* __restrict__ amax, uint8_t* __restrict__ codes,
+           uint8_t* __restrict__ scales, float* __restrict__ g_out,
+           uint64_t* __restrict__ partial, uint16_t* __restrict__ w_qdq) {
+  // partial: [gridDim.x][K] per-workgroup channel sums (or NULL: no scores)
+  __shared__ uint64_t red[256 * 16];
+  uint64_t* score = partial;
+  const int tid = threadIdx.x;
+  const int t = blockIdx.z;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0)
+    g_out[t] = bf16_bits_to_f32(amax[t]) / kScaleDen;
+  const int cw = blocks < 256 ? blocks : 256;
+  const int rsub = tid / cw;
+  const int c = blockIdx.y * 256 + tid % cw;
+  const bool active = rsub < rows_per_iter && c < blocks;
+
+  const float A = bf16_bits_to_f32(amax[t]);
+  const float g = A / kScaleDen;
+  const int ea = A > 0.0f ? frexp_exponent(A) : 0;
+  const uint16_t* xt = x + (int64_t)t * tensor_stride;
+  const int64_t row0 = (int64_t)t * rows;     // output row offset of this tensor
+  uint64_t acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0;
+
+  for (int64_t r = (int64_t)blockIdx.x * rows_per_iter + rsub; active && r < rows;
+       r += (int64_t)gridDim.x * rows_per_iter) {
+    const uint16_t* xr = xt + r * ldx + (int64_t)c * 16;
+    uint4 v0 = *reinterpret_cast<const uint4*>(xr);
+    uint4 v1 = *reinterpret_cast<const uint4*>(xr + 8);
+    uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    float xf[16];
+    uint32_t bmax = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      xf[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+      xf[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+      bmax = max(bmax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+    }
+    uint32_t sbyte = 0;
+    float s = 0.0f;
+    uint32_t pk[2] = {0u, 0u};
+    if (A > 0.0f) {
+      float u = (bf16_bits_to_f32(bmax) * kE4M3Max) / A;
+      sbyte = e4m3_encode_nonneg(u);
+      s = e4m3_decode(sbyte);
+    }
+    if (s > 0.0f) {
+      const float rho = kScaleDen / (s * A);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t b = e2m1_pack2(xf[2 * i] * rho, xf[2 * i + 1] * rho);
+        pk[i >> 2] |= b << (8 * (i & 3));
+      }
+    } else {
+      // magnitude 0 everywhere; keep the signs
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t b = ((w[i] >> 12) & 0x8u) | ((w[i] >> 24) & 0x80u);
+        pk[i >> 2] |= b << (8 * (i & 3));
+      }
+    }
+    const int64_t orow = row0 + r;
+    *reinterpret_cast<uint2*>(codes + orow * (K / 2) + (int64_t)c * 8) = make_uint2(pk[0], pk[1]);
+    scales[orow * (K / 16) + c] = (uint8_t)sbyte;
+
+    if (score != nullptr || w_qdq != nullptr) {
+      float qs[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x2 a0 = e2m1_unpack2<0>(pk[i >> 1] >> (16 * (i & 1)));
+        f32x2 a1 = e2m1_unpack2<1>(pk[i >> 1] >> (16 * (i & 1)));
+        qs[4 * i + 0] = a0.x * s;
+        qs[4 * i + 1] = a0.y * s;
+        qs[4 * i + 2] = a1.x * s;
+        qs[4 * i + 3] = a1.y * s;
+      }
+      if (score != nullptr && A > 0.0f) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float rr = __builtin_fmaf(-qs[i], g, xf[i]);
+          float rb = bf16_bits_to_f32(f32_to_bf16_rne(rr));
+          acc[i] += (uint64_t)(uint32_t)__builtin_ldexpf(__builtin_fabsf(rb), 31 - ea);
+        }
+      }
+      if (w_qdq != nullptr) {
+        uint32_t o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint32_t c0 = (pk[i >> 2] >> (8 * (i & 3))) & 0xFu;
+          uint32_t c1 = (pk[i >> 2] >> (8 * (i & 3) + 4)) & 0xFu;
+          uint32_t h0 = f32_to_bf16_rne(__builtin_fabsf(qs[2 * i]) * g) | ((c0 & 8u) << 12);
+          uint32_t h1 = f32_to_bf16_rne(__builtin_fabsf(qs[2 * i + 1]) * g) | ((c1 & 8u) << 12);
+          o[i] = h0 | (h1 << 16);
+        }
+        uint16_t* wo = w_qdq + orow * K + (int64_t)c * 16;
+        *reinterpret_cast<uint4*>(wo) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4*>(wo + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+      }
+    }
+  }
+  if (partial == nullptr) return;
+  // sum the rows_per_iter row groups of this workgroup, then one write per
+  // channel: exact integer sums, so any grouping gives the same bits
+  if (rows_per_iter > 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[tid * 16 + i] = acc[i];
+    __syncthreads();
+    if (rsub == 0 && active) {
+      for (int q = 1; q < rows_per_iter; ++q)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] += red[(q * cw + tid) * 16 + i];
+    }
+  }
+  if (rsub == 0 && active) {
+    uint64_t* dst = partial + (int64_t)blockIdx.x * K + (int64_t)c * 16;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2)
+      *reinterpret_cast<ulonglong2*>(dst + i) = make_ulonglong2(acc[i], acc[i + 1]);
+  }
+}
+
+// score[j] = sum over workgroups of partial[w][j]
+__global__ void __launch_bounds__(256)
+k_score_reduce(const uint64_t* __restrict__ partial, int nparts, int64_t K,
+               uint64_t* __restrict__ score) {
+  int64_t j = blockIdx.x * 256LL + threadIdx.x;
+  if (j >= K) return;
+  uint64_t s = 0;
+  for (int w = 0; w < nparts; ++w) s += partial[(int64_t)w * K + j];
+  score[j] = s;
+}
+
+static unsigned grid_rows(int64_t rows, int rows_per_iter, int64_t cap) {
+  int64_t need = (rows + rows_per_iter - 1) / rows_per_iter;
+  if (need < 1) need = 1;
+  return (unsigned)(need < cap ? need : cap);
+}
+
+}  // namespace nvfp4
+
+using namespace nvfp4;
+
+extern "C" {
+
+static int quant_grid(int64_t M, int64_t K) {
+  RowTiling t16 = row_tiling(K / 16);
+  return (int)grid_rows(M, t16.rows_per_iter, 4LL * num_cus());
+}
+
+size_t nvfp4_quantize_act_workspace_size(int64_t M, int64_t K) {
+  if (M < 0 || K < 32) return 256;
+  return 256 + round_up((size_t)quant_grid(M, K) * (size_t)K * sizeof(uint64_t), 256);
+}
+
+size_t nvfp4_qdq_weights_workspace_size(int64_t E) {
+  return round_up((size_t)(E > 0 ? E : 1) * sizeof(uint32_t), 256);
+}
+
+int nvfp4_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, int glu,
+                       uint8_t* codes, uint8_t* scales, float* g_x, uint64_t* score,
+                       void* x_used, void* ws, size_t ws_bytes, void* stream) {
+  NV_REQUIRE(g_x && ws, NVFP4_ERR_NULL, "nvfp4_quantize_act: g_x and ws are required");
+  NV_REQUIRE(M >= 0 && K >= 32 && K % 32 == 0, NVFP4_ERR_SHAPE,
+             "nvfp4_quantize_act: need M >= 0, K >= 32, K %% 32 == 0 (M=%lld K=%lld)",
+             (long long)M, (long long)K);
+  NV_REQUIRE(glu == 0 || glu == 1, NVFP4_ERR_SHAPE, "nvfp4_quantize_act: glu must be 0 or 1");
+  NV_REQUIRE(ldx >= (glu ? 2 * K : K) && ldx % 8 == 0, NVFP4_ERR_SHAPE,
+             "nvfp4_quantize_act: bad ldx %lld", (long long)ldx);
+  NV_REQUIRE(M == 0 || (x && codes && scales), NVFP4_ERR_NULL,
+             "nvfp4_quantize_act: x, codes and scales are required");
+  NV_REQUIRE(!glu || x_used, NVFP4_ERR_NULL, "nvfp4_quantize_act: glu=1 needs x_used for h");
+  NV_REQUIRE(aligned(x, 16) && aligned(codes, 8) && aligned(x_used, 16) && aligned(score, 8) &&
+                 aligned(ws, 16),
+             NVFP4_ERR_ALIGN, "nvfp4_quantize_act: misaligned pointer");
+  NV_REQUIRE(ws_bytes >= nvfp4_quantize_act_workspace_size(M, K), NVFP4_ERR_WORKSPACE,
+             "nvfp4_quantize_act: workspace too small");
+  hipStream_t s = as_stream(stream);
+  uint32_t* amax = static_cast<uint32_t*>(ws);
+  uint64_t* partial = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + 256);
+  fill_u32(amax, 1, 0u, s);
+  const int cus = num_cus();
+  const uint16_t* src = static_cast<const uint16_t*>(x);
+  int64_t ld = ldx;
+  if (M > 0) {
+    RowTiling t8 = row_tiling(K / 8);
+    dim3 grid(grid_rows(M, t8.rows_per_iter, 8LL * cus), t8.col_groups, 1);
+    if (glu) {
+      k_swiglu_amax<<<grid, 256, 0, s>>>(src, M, ldx, K, t8.chunks, t8.rows_per_iter,
+                                         static_cast<uint16_t*>(x_used), amax);
+      src = static_cast<const uint16_t*>(x_used);
+      ld = K;
+    } else {
+      k_amax<<<grid, 256, 0, s>>>(src, M, ldx, 0, t8.chunks, t8.rows_per_iter, amax);
+    }
+  }
+  RowTiling t16 = row_tiling(K / 16);
+  const int nq = quant_grid(M, K);
+  dim3 grid(nq, t16.col_groups, 1);
+  k_quantize<<<grid, 256, 0, s>>>(src, M, ld, K, 0, 1, t16.chunks, t16.rows_per_iter, amax,
+                                  codes, scales, g_x, score ? partial : nullptr, nullptr);
+  if (score) k_score_reduce<<<(unsigned)((K + 255) / 256), 256, 0, s>>>(partial, nq, K, score);
+  return check_launch("nvfp4_quantize_act");
+}
+
+int nvfp4_qdq_weights(const void* w, int64_t E, int64_t N, int64_t K, uint8_t* codes,
+                      uint8_t* scales, float* g_w, void* w_qdq, void* ws, size_t ws_bytes,
+                      void* stream) {
+  NV_REQUIRE(w && codes && scales && g_w && ws, NVFP4_ERR_NULL,
+             "nvfp4_qdq_weights: w, codes, scales, g_w and ws are required");
+  NV_REQUIRE(E >= 1 && E <= 65535 && N >= 1 && K >= 32 && K % 32 == 0, NVFP4_ERR_SHAPE,
+             "nvfp4_qdq_weights: need 1 <= E <= 65535, N >= 1, K %% 32 == 0");
+  NV_REQUIRE(aligned(w, 16) && aligned(codes, 8) && aligned(w_qdq, 16) && aligned(ws, 16),
+             NVFP4_ERR_ALIGN, "nvfp4_qdq_weights: misaligned pointer");
+  NV_REQUIRE(ws_bytes >= nvfp4_qdq_weights_workspace_size(E), NVFP4_ERR_WORKSPACE,
+             "nvfp4_qdq_weights: workspace too small");
+  hipStream_t s = as_stream(stream);
+  uint32_t* amax = static_cast<uint32_t*>(ws);
+  fill_u32(amax, E, 0u, s);
+  const int cus = num_cus();
+  const int64_t per_e = (8LL * cus + E - 1) / E;
+  RowTiling t8 = row_tiling(K / 8);
+  dim3 g1(grid_rows(N, t8.rows_per_iter, per_e > 1 ? per_e : 1), t8.col_groups, (unsigned)E);
+  k_amax<<<g1, 256, 0, s>>>(static_cast<const uint16_t*>(w), N, K, N * K, t8.chunks,
+                            t8.rows_per_iter, amax);
+  RowTiling t16 = row_tiling(K / 16);
+  dim3 g2(grid_rows(N, t16.rows_per_iter, per_e > 1 ? per_e : 1), t16.col_groups, (unsigned)E);
+  k_quantize<<<g2, 256, 0, s>>>(static_cast<const uint16_t*>(w), N, K, K, N * K, (int)E,
+                                t16.chunks, t16.rows_per_iter, amax, codes, scales, g_w,
+                                nullptr, static_cast<uint16_t*>(w_qdq));
+  return check_launch("nvfp4_qdq_weights");
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+"""The rollout-side MoE expert block as a chain of library calls.
+
+Weights go through the shared QDQ path once (per weight sync); each forward
+routes and permutes tokens, quantizes the activation online, selects the
+high-residual channels, runs the grouped W4A4 GEMM with the residual added
+back, forms and quantizes the SwiGLU activation for the down projection the
+same way, and combines the expert outputs (QUADS: arXiv abstract;
+gist.science technical summary §2.1-§2.2).  Nothing here computes: every
+step is one call into libnvfp4rac.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import (grouped_w4a4_gemm_rac, moe_permute, moe_unpermute_combine, nvfp4_qdq_weights,
+               nvfp4_quantize_act, select_residual_channels)
+
+
+@dataclass
+class QuantWeights:
+    codes: torch.Tensor      # [E][N][K/2] u8
+    scales: torch.Tensor     # [E][N][K/16] u8
+    g: torch.Tensor          # [E] f32
+    qdq: torch.Tensor        # [E][N][K] bf16 or None
+
+
+def prepare_weights(w, want_qdq=False) -> QuantWeights:
+    return QuantWeights(*nvfp4_qdq_weights(w, want_qdq=want_qdq))
+
+
+def quantized_linear_rac(x, wq: QuantWeights, k, a_rows=None, offsets=None, M_total=None,
+                         glu=False):
+    """Quantize x (or SwiGLU of x), select k channels, grouped GEMM.
+    Returns (y, stage dict)."""
+    q = nvfp4_quantize_act(x, glu=glu, want_score=k > 0)
+    S = R = None
+    if k > 0:
+        S, R = select_residual_channels(q["x_used"], q["codes"], q["scales"], q["g"], q["score"], k)
+    if offsets is None:
+        offsets = torch.tensor([0, x.shape[0]], dtype=torch.int32, device=x.device)
+    y = grouped_w4a4_gemm_rac(q["codes"], q["scales"], q["g"], a_rows, R, S, wq.codes, wq.scales,
+                              wq.g, offsets, M_total=M_total)
+    return y, dict(q=q, S=S, R=R)
+
+
+def moe_forward(x, logits, topk, w_first: QuantWeights, w_down: QuantWeights, k_first, k_down,
+                bias=None, keep=False):
+    """x [T][H] bf16, logits [T][E] f32.  w_first [E][N1][H] (N1 = 2I for
+    gate+up, I for an up-only block); w_down [E][H][I] or None.  Returns the
+    combined output [T][H] (or the first GEMM's permuted output when there is
+    no down projection) and, with keep=True, every intermediate."""
+    ids, tw, offs, perm, inv = moe_permute(logits, topk, bias)
+    rows = perm.numel()
+    y1, st1 = quantized_linear_rac(x, w_first, k_first, a_rows=perm, offsets=offs, M_total=rows)
+    out = dict(topk_ids=ids, topk_w=tw, offsets=offs, perm_token=perm, inv_perm=inv, y1=y1,
+               st1=st1) if keep else {}
+    if w_down is None:
+        return y1, out
+    y2, st2 = quantized_linear_rac(y1, w_down, k_down, a_rows=None, offsets=offs, M_total=rows,
+                                   glu=True)
+    o = moe_unpermute_combine(y2, inv, tw)
+    if keep:
+        out.update(y2=y2, st2=st2, out=o)
+    return o, out

@@ -1,0 +1,190 @@
+/*
+ * nvfp4rac.h - NVFP4 W4A4 MoE expert GEMM with Residual Activation
+ * Compensation, for AMD Instinct MI355X (CDNA4, gfx950).
+ *
+ * The method is QUADS (arXiv 2607.15810).  Its rollout side quantizes
+ * activations online to FP4 every forward, runs the W4A4 GEMM against
+ * weights that came through the same quantize-dequantize (QDQ) path the
+ * trainer fake-quantizes with, and adds back the quantization residual of
+ * the few activation channels where it is largest (arXiv abstract; the
+ * gist.science technical summary, sections 2.1 and 2.2, in Italian and
+ * Korean).  This library is that hot path, one call per step.
+ *
+ * Formats (the public NVFP4 definition; the pages only name the E2M1 grid
+ * and "fine-grained scaling"):
+ *   - element: E2M1 code, 4 bits = sign | 3-bit magnitude index into
+ *     {0, 0.5, 1, 1.5, 2, 3, 4, 6}.  Two codes per byte, element 2j in bits
+ *     3:0 and element 2j+1 in bits 7:4.  Row-major [rows][K/2].
+ *   - block scale: one OCP FP8 E4M3 byte per 16 consecutive elements along
+ *     K, row-major [rows][K/16].
+ *   - tensor scale: one float32 g per tensor (per expert for weights).
+ *   - value = e2m1(code) * e4m3(scale) * g.
+ *
+ * Conventions for every call:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *     library never allocates, frees or synchronises; it keeps no pointer
+ *     after returning.  Device pointers must be 16-byte aligned unless noted.
+ *   - bf16 tensors are passed as void* holding IEEE bfloat16 bit patterns.
+ *   - `stream` is a hipStream_t (NULL: the legacy default stream).  All work
+ *     is enqueued on it in order.
+ *   - `ws` is caller-owned device scratch of at least the size returned by
+ *     the matching *_workspace_size query; its contents need not be
+ *     initialised and are clobbered.  Calls that share a ws must not
+ *     overlap in time.
+ *   - Return: NVFP4_OK, or an error status for bad arguments (nothing is
+ *     enqueued) or for a failed launch.  nvfp4_last_error() then holds a
+ *     message (per thread).  Device faults surface at the caller's next
+ *     synchronisation, as usual in HIP.
+ *   - Value contract: finite inputs whose tensor absolute maximum is 0 or lies
+ *     in [2^-100, 2^100].  NaN/Inf inputs give unspecified outputs.
+ */
+#ifndef NVFP4RAC_H
+#define NVFP4RAC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  NVFP4_ERR_SHAPE = 2,       /* a size is out of range (K % 16, k > K, ...)    */
+  NVFP4_ERR_ALIGN = 3,       /* a device pointer or stride is misaligned       */
+  NVFP4_ERR_WORKSPACE = 4,   /* ws_bytes smaller than the workspace query      */
+  NVFP4_ERR_UNSUPPORTED = 5, /* valid, but outside what the kernels implement  */
+  NVFP4_ERR_HIP = 6          /* a HIP runtime or launch call failed            */
+} nvfp4_status;
+
+/* Library version, major*10000 + minor*100 + patch. */
+int nvfp4_version(void);
+/* Static name of a status code. */
+const char* nvfp4_status_str(int status);
+/* Detail message of the last failing call on this thread ("" if none). */
+const char* nvfp4_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Weight QDQ (shared quantize-dequantize path).
+ * Weights are synchronised from trainer to rollout through one QDQ path, so
+ * the rollout's FP4 weights and the trainer's fake-quantized weights are the
+ * same numbers (arXiv abstract; gist.science summary §2.1 "weights" and
+ * §2.2 A, asymmetric W4A16 QAT).
+ *
+ * w      [E][N][K] bf16, K contiguous (each expert's weight, out x in).
+ * codes  [E][N][K/2] packed E2M1.        scales [E][N][K/16] E4M3.
+ * g_w    [E] float32: per-expert tensor scale g = fp32(amax_e / 2688).
+ * w_qdq  [E][N][K] bf16 or NULL: bf16(fp32(e2m1 * e4m3) * g), the weight the
+ *        trainer's forward sees.
+ * Scale recipe per 16-block (all float32, round to nearest even):
+ *   s = e4m3((blockmax * 448) / amax);  code = e2m1(x * (2688 / (s * amax)))
+ *   (s == 0 gives magnitude 0); the sign bit of a code is the sign of x.
+ * Requires 1 <= E <= 65535, N >= 1, K >= 32, K % 32 == 0.
+ * ---------------------------------------------------------------------- */
+size_t nvfp4_qdq_weights_workspace_size(int64_t E);
+int nvfp4_qdq_weights(const void* w, int64_t E, int64_t N, int64_t K,
+                      uint8_t* codes, uint8_t* scales, float* g_w, void* w_qdq,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Online activation quantization (activations are recomputed and quantized
+ * every forward: arXiv abstract; gist.science summary §2.1), with the
+ * per-channel residual statistic that Residual Activation Compensation ranks
+ * channels by (summary §2.2 B).
+ *
+ * x      glu == 0: [M][K] bf16, row stride ldx elements (ldx >= K).
+ *        glu == 1: [M][2K] bf16 = [gate | up], row stride ldx (>= 2K); the
+ *        tensor quantized is h = bf16(silu(gate) * up), evaluated in float32.
+ * codes  [M][K/2], scales [M][K/16], g_x [1] float32 (dynamic, per call).
+ * score  [K] uint64 or NULL: score_j = sum over rows of
+ *        floor(|r_ij| * 2^(31 - E_A)), r = bf16(fp32(x - dequant(x))), E_A the
+ *        binary exponent of the tensor amax A (A = m 2^E_A, m in [0.5, 1)).
+ *        An exact integer sum: bitwise reproducible in any order.
+ * x_used [M][K] bf16 or NULL: the tensor that was quantized (required for
+ *        glu == 1, where it receives h; for glu == 0 it is not written).
+ * Requires M >= 0, K >= 32, K % 32 == 0, ldx % 8 == 0.  M == 0 writes
+ * g_x = 0 and zero scores.
+ * ---------------------------------------------------------------------- */
+size_t nvfp4_quantize_act_workspace_size(int64_t M, int64_t K);
+int nvfp4_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, int glu,
+                       uint8_t* codes, uint8_t* scales, float* g_x,
+                       uint64_t* score, void* x_used,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * High-residual channel selection (the binary channel mask of Residual
+ * Activation Compensation, gist.science summary §2.2 B, both languages).
+ *
+ * Picks the k channels with the largest score (ties: lower index), returns
+ * them ascending in S [k] int32, and gathers the residual of those channels,
+ * R_S [M][k] bf16 = bf16(fp32(x - dequant(x))), from x_used (row stride ldx),
+ * codes, scales and g_x as produced by nvfp4_quantize_act.
+ * k == 0 enqueues nothing.  Requires 0 <= k <= K <= 4096, K % 32 == 0.
+ * ---------------------------------------------------------------------- */
+size_t select_residual_channels_workspace_size(int64_t M, int64_t K, int64_t k);
+int select_residual_channels(const void* x_used, int64_t ldx, const uint8_t* codes,
+                             const uint8_t* scales, const float* g_x,
+                             const uint64_t* score, int64_t M, int64_t K, int64_t k,
+                             int32_t* S, void* R_S, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* ------------------------------------------------------------------------
+ * MoE routing and expert-major permutation (the MoE model of the pages,
+ * gist.science summary §4; the router itself is not described there).
+ *
+ * logits [T][E] float32, bias [E] float32 or NULL.  Per token: the tk experts
+ * of largest l = fp32(logit + bias) (ties: lower expert index), weights =
+ * softmax over those tk values (float64, rounded to float32).
+ * topk_ids [T][tk] int32, topk_w [T][tk] float32,
+ * expert_offsets [E+1] int32 (rows of expert e are [off[e], off[e+1])),
+ * perm_token [T*tk] int32 (token of each permuted row; tokens ascending within
+ * an expert), inv_perm [T][tk] int32 (row of each (token, slot)).
+ * Requires T >= 0, 1 <= tk <= E <= 1024, tk <= 32, T*tk < 2^31.
+ * ---------------------------------------------------------------------- */
+size_t moe_permute_workspace_size(int64_t T, int64_t E);
+int moe_permute(const float* logits, const float* bias, int64_t T, int64_t E, int64_t tk,
+                int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                int32_t* perm_token, int32_t* inv_perm,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Expert-grouped W4A4 GEMM with Residual Activation Compensation: the native
+ * FP4 product over all of K plus the residual of the selected channels
+ * multiplied by the same FP4 weights (gist.science summary §2.2 B; arXiv
+ * abstract).  For permuted row p of expert e (off[e] <= p < off[e+1]) and
+ * activation row t = a_rows ? a_rows[p] : p:
+ *
+ *   y[p][n] = bf16( g_w[e] * ( g_x * sum_k x~[t][k] w~e[n][k]
+ *                              + sum_{j<k} R_S[t][j] w~e[n][S[j]] ) )
+ *
+ * with x~ = e2m1 * e4m3 of the activation, w~ likewise of the weight (exact
+ * in the bf16/fp16 operands of the matrix cores), float32 accumulation.
+ * a_codes [M_src][K/2], a_scales [M_src][K/16], g_x [1]; a_rows [M_total] or
+ * NULL (then M_src >= M_total); R_S [M_src][k] bf16 (NULL iff k == 0);
+ * S [k] int32 ascending; w_codes [E][N][K/2], w_scales [E][N][K/16], g_w [E];
+ * expert_offsets [E+1] (device; off[0] = 0, off[E] = M_total); y [M_total][N]
+ * bf16.  Requires K % 128 == 0, N % 16 == 0, 0 <= k <= K.
+ * ---------------------------------------------------------------------- */
+size_t grouped_w4a4_gemm_rac_workspace_size(int64_t E, int64_t M_total, int64_t N,
+                                            int64_t K, int64_t k);
+int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
+                          const int32_t* a_rows, int64_t M_src,
+                          const void* R_S, const int32_t* S, int64_t k,
+                          const uint8_t* w_codes, const uint8_t* w_scales, const float* g_w,
+                          const int32_t* expert_offsets, int64_t E, int64_t M_total,
+                          int64_t N, int64_t K, void* y,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Un-permute and combine: out[t][n] = bf16( sum_j topk_w[t][j] *
+ * y[inv_perm[t][j]][n] ), float32 accumulation in slot order j = 0..tk-1.
+ * y [T*tk][N] bf16, out [T][N] bf16.  Requires N % 8 == 0.  No workspace.
+ * ---------------------------------------------------------------------- */
+int moe_unpermute_combine(const void* y, const int32_t* inv_perm, const float* topk_w,
+                          int64_t T, int64_t tk, int64_t N, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4RAC_H */

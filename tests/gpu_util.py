@@ -1,0 +1,59 @@
+"""Host <-> device helpers for the GPU parity tests (no method arithmetic)."""
+import numpy as np
+import torch
+
+from oracle import formats as OF
+
+
+def to_dev_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def host_vals(t: torch.Tensor) -> np.ndarray:
+    return OF.bf16_bits_to_f64(host_bits(t))
+
+
+def bits_of(vals: np.ndarray) -> np.ndarray:
+    return OF.f64_to_bf16_bits(vals)
+
+
+def f32_bits(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float32).view(np.uint32)
+
+
+def heavy_bf16(rng, shape, df=3.0, ch_sigma=1.0):
+    x = rng.standard_t(df, size=shape) * rng.lognormal(0, ch_sigma, size=shape[-1])
+    return OF.round_to_bf16(x)
+
+
+def rownorm_err(y, ref):
+    num = np.linalg.norm(y - ref, axis=1)
+    den = np.linalg.norm(ref, axis=1)
+    ok = den > 0
+    worst = np.max(num[ok] / den[ok]) if ok.any() else 0.0
+    return max(worst, np.max(num[~ok]) if (~ok).any() else 0.0)
+
+
+def maxabs_err(y, ref):
+    m = np.max(np.abs(ref))
+    return np.max(np.abs(y - ref)) / m if m > 0 else np.max(np.abs(y))
+
+
+def assert_gemm_close(y, ref, tol=2e-3, min_exact=0.98):
+    """The output tolerance: row-normwise and max-abs-over-max relative error
+    both <= tol against the oracle's bf16-rounded float64 result, and most
+    elements bit-identical (float32 vs float64 accumulation differs by at most
+    one bf16 rounding step on a few elements)."""
+    assert y.shape == ref.shape
+    assert np.all(np.isfinite(y))
+    e1, e2 = rownorm_err(y, ref), maxabs_err(y, ref)
+    exact = np.mean(y == ref)
+    assert e1 <= tol, f"row-normwise error {e1:.3e}"
+    assert e2 <= tol, f"max-abs error {e2:.3e}"
+    assert exact >= min_exact, f"only {exact:.4f} of elements bit-identical"
+    return e1, e2, exact

@@ -1,0 +1,127 @@
+"""C-ABI library checks that need no GPU: it loads, exports every function
+the header declares, and rejects bad arguments with the documented status
+before enqueueing anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp4_quantized_gemm_amd as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4rac.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WS = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_six_calls():
+    names = declared_functions()
+    for n in ["nvfp4_qdq_weights", "nvfp4_quantize_act", "select_residual_channels",
+              "moe_permute", "grouped_w4a4_gemm_rac", "moe_unpermute_combine"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = F.lib()
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(F.EXPORTED_SYMBOLS) == names
+
+
+def test_version_and_status_strings():
+    L = F.lib()
+    assert L.nvfp4_version() >= 100
+    assert L.nvfp4_status_str(0) == b"NVFP4_OK"
+    assert L.nvfp4_status_str(2) == b"NVFP4_ERR_SHAPE"
+    assert L.nvfp4_status_str(99) == b"NVFP4_ERR_UNKNOWN"
+
+
+# Fake, 256-aligned, never-dereferenced addresses: every call below must fail
+# validation before it touches memory or launches anything.
+FAKE = ctypes.c_void_p(0x10000)
+FAKE_MIS = ctypes.c_void_p(0x10001)
+
+
+def test_quantize_act_validation():
+    L = F.lib()
+    st = L.nvfp4_quantize_act(FAKE, 4, 48, 48, 0, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 20, None)
+    assert st == ERR_SHAPE and b"K" in L.nvfp4_last_error()
+    st = L.nvfp4_quantize_act(FAKE, 4, 64, 64, 0, FAKE, FAKE, None, None, None, FAKE, 1 << 20, None)
+    assert st == ERR_NULL
+    st = L.nvfp4_quantize_act(FAKE, 4, 64, 64, 1, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 20, None)
+    assert st == ERR_SHAPE                       # glu needs ldx >= 2K
+    st = L.nvfp4_quantize_act(FAKE, 4, 64, 128, 1, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 20, None)
+    assert st == ERR_NULL                        # glu needs x_used
+    st = L.nvfp4_quantize_act(FAKE_MIS, 4, 64, 64, 0, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 20, None)
+    assert st == ERR_ALIGN
+    st = L.nvfp4_quantize_act(FAKE, 4, 64, 64, 0, FAKE, FAKE, FAKE, None, None, FAKE, 8, None)
+    assert st == ERR_WS
+
+
+def test_qdq_weights_validation():
+    L = F.lib()
+    assert L.nvfp4_qdq_weights(FAKE, 0, 8, 64, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == ERR_SHAPE
+    assert L.nvfp4_qdq_weights(FAKE, 2, 8, 40, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == ERR_SHAPE
+    assert L.nvfp4_qdq_weights(None, 2, 8, 64, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == ERR_NULL
+    assert L.nvfp4_qdq_weights(FAKE, 2, 8, 64, FAKE, FAKE, FAKE, None, FAKE, 4, None) == ERR_WS
+
+
+def test_select_validation():
+    L = F.lib()
+    assert L.select_residual_channels(FAKE, 64, FAKE, FAKE, FAKE, FAKE, 4, 64, 65, FAKE, FAKE,
+                                      None, 0, None) == ERR_SHAPE
+    assert L.select_residual_channels(FAKE, 8192, FAKE, FAKE, FAKE, FAKE, 4, 8192, 8, FAKE, FAKE,
+                                      None, 0, None) == ERR_SHAPE
+    # k == 0 is a no-op and needs no pointers at all
+    assert L.select_residual_channels(None, 64, None, None, None, None, 4, 64, 0, None, None,
+                                      None, 0, None) == OK
+    assert L.select_residual_channels(FAKE, 64, FAKE, FAKE, FAKE, None, 4, 64, 3, FAKE, FAKE,
+                                      None, 0, None) == ERR_NULL
+
+
+def test_permute_validation():
+    L = F.lib()
+    ws = L.moe_permute_workspace_size(10, 8)
+    assert ws > 0
+    assert L.moe_permute(FAKE, None, 10, 8, 9, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == ERR_SHAPE
+    assert L.moe_permute(FAKE, None, 10, 2048, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == ERR_SHAPE
+    assert L.moe_permute(FAKE, None, 10, 8, 2, FAKE, FAKE, None, FAKE, FAKE, FAKE, ws, None) == ERR_NULL
+    assert L.moe_permute(FAKE, None, 10, 8, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == ERR_WS
+
+
+def test_gemm_validation():
+    L = F.lib()
+    ws = L.grouped_w4a4_gemm_rac_workspace_size(4, 64, 128, 256, 8)
+    args = lambda **kw: [kw.get("ac", FAKE), FAKE, FAKE, kw.get("rows", None), kw.get("msrc", 64),
+                         kw.get("R", None), kw.get("S", None), kw.get("k", 0), FAKE, FAKE, FAKE,
+                         FAKE, kw.get("E", 4), 64, kw.get("N", 128), kw.get("K", 256), FAKE, FAKE,
+                         kw.get("ws", ws), None]
+    assert L.grouped_w4a4_gemm_rac(*args(K=192)) == ERR_SHAPE           # K % 128
+    assert L.grouped_w4a4_gemm_rac(*args(N=120)) == ERR_SHAPE           # N % 16
+    assert L.grouped_w4a4_gemm_rac(*args(k=300)) == ERR_SHAPE           # k > K
+    assert L.grouped_w4a4_gemm_rac(*args(msrc=10)) == ERR_SHAPE         # no gather, M_src < M_total
+    assert L.grouped_w4a4_gemm_rac(*args(k=4)) == ERR_NULL              # k > 0 needs R_S and S
+    assert L.grouped_w4a4_gemm_rac(*args(ac=FAKE_MIS)) == ERR_ALIGN
+    assert L.grouped_w4a4_gemm_rac(*args(ws=0)) == ERR_WS
+
+
+def test_combine_validation():
+    L = F.lib()
+    assert L.moe_unpermute_combine(FAKE, FAKE, FAKE, 4, 2, 12, FAKE, None) == ERR_SHAPE
+    assert L.moe_unpermute_combine(None, FAKE, FAKE, 4, 2, 16, FAKE, None) == ERR_NULL
+    assert L.moe_unpermute_combine(None, None, None, 0, 2, 16, None, None) == OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(F.NvfpError):
+        F.nvfp4_quantize_act(torch.zeros(4, 64, dtype=torch.bfloat16))

@@ -1,0 +1,233 @@
+"""GPU parity: every library call against the CPU oracle, stage by stage, on
+seeded inputs that span several tiles, ragged tails and degenerate cases.
+
+Bit-exact: codes, scales, tensor scales, channel scores, S, R_S, routing ids,
+offsets and permutations, w_qdq.  Tolerance: softmax weights (1e-6 rel),
+SwiGLU h (1 bf16 ulp), GEMM and combine outputs (row-normwise and max-abs
+relative error <= 2e-3 against the oracle's bf16-rounded float64 result)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import fp4_quantized_gemm_amd as F
+from oracle import formats as OF
+from oracle import gemm as OG
+from oracle import moe as OM
+from oracle import nvfp4 as OQ
+from tests.gpu_util import (assert_gemm_close, f32_bits, heavy_bf16, host_bits, host_vals,
+                            to_dev_bf16)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_quant(x_vals, glu=False):
+    xd = to_dev_bf16(OF.f64_to_bf16_bits(x_vals))
+    q = F.nvfp4_quantize_act(xd, glu=glu)
+    torch.cuda.synchronize()
+    return q
+
+
+def check_quant_against_oracle(q, x_vals):
+    codes, scales, g, A = OQ.quantize(x_vals)
+    got_codes = OQ.unpack_codes(q["codes"].cpu().numpy())
+    assert np.array_equal(got_codes, codes), f"codes differ at {np.argwhere(got_codes != codes)[:5]}"
+    assert np.array_equal(q["scales"].cpu().numpy(), scales)
+    assert f32_bits(q["g"].cpu().numpy()[0]) == f32_bits(g)
+    r = OQ.residual(x_vals, codes, scales, g)
+    score = OQ.channel_scores(r, A)
+    assert np.array_equal(q["score"].cpu().numpy(), score)
+    return codes, scales, g, A, r, score
+
+
+# ------------------------------------------------------------------ quantizer
+
+@pytest.mark.parametrize("M,K", [(1, 32), (5, 96), (37, 512), (130, 768), (64, 4096), (3, 8192)])
+def test_quantize_act_bitexact(dev, M, K):
+    say(f"quantize M={M} K={K}")
+    rng = np.random.default_rng(M * 1000 + K)
+    x = heavy_bf16(rng, (M, K))
+    check_quant_against_oracle(gpu_quant(x), x)
+
+
+def test_quantize_act_edge_values(dev):
+    say("quantize edge values")
+    # hand-worked ties (A = 6 so rho = 1 in the first block), negative zeros,
+    # an all-zero block, tiny blocks with subnormal E4M3 scales, saturation
+    row = [6, -0.3, 0.25, 0.75, 1.25, 1.75, 2.5, -3.5, 5, 4.9, 0, 1, 2, 3, 4, -6]
+    x = np.zeros((4, 64))
+    x[0, :16] = row
+    x[1, :16] = -0.0
+    x[1, 16:32] = [2.0 ** -12 * (i + 1) for i in range(16)]
+    x[2, 32:48] = 1e-3
+    x[3, 48:64] = np.linspace(-6, 6, 16)
+    x = OF.round_to_bf16(x)
+    x[1, :16] = -0.0
+    check_quant_against_oracle(gpu_quant(x), x)
+
+
+def test_quantize_act_zero_and_empty(dev):
+    say("quantize zeros / empty")
+    x = np.zeros((3, 64))
+    q = gpu_quant(x)
+    assert not q["codes"].cpu().numpy().any() and not q["scales"].cpu().numpy().any()
+    assert q["g"].item() == 0.0 and not q["score"].cpu().numpy().any()
+    xd = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    q = F.nvfp4_quantize_act(xd)
+    torch.cuda.synchronize()
+    assert q["g"].item() == 0.0 and not q["score"].cpu().numpy().any()
+
+
+@pytest.mark.parametrize("M,I", [(7, 32), (100, 768), (33, 1536)])
+def test_quantize_glu(dev, M, I):
+    say(f"quantize glu M={M} I={I}")
+    rng = np.random.default_rng(M + I)
+    y = OF.round_to_bf16(rng.standard_normal((M, 2 * I)) * 2)
+    q = gpu_quant(y, glu=True)
+    h_gpu = host_vals(q["x_used"])
+    h_ref = OM.swiglu(y, I)
+    rel = np.abs(h_gpu - h_ref) / np.maximum(np.abs(h_ref), 1e-30)
+    assert np.all(rel <= 2.0 ** -7)                      # at most one bf16 step
+    assert np.mean(h_gpu == h_ref) > 0.99
+    check_quant_against_oracle(q, h_gpu)                 # teacher-forced on the GPU's h
+
+
+@pytest.mark.parametrize("E,N,K", [(1, 16, 32), (3, 48, 96), (2, 130, 512)])
+def test_qdq_weights_bitexact(dev, E, N, K):
+    say(f"qdq E={E} N={N} K={K}")
+    rng = np.random.default_rng(E * N + K)
+    w = OF.round_to_bf16(rng.standard_normal((E, N, K)) * 0.02)
+    w[0, 0, :16] = 0.0
+    wd = to_dev_bf16(OF.f64_to_bf16_bits(w))
+    codes, scales, g_w, w_qdq = F.nvfp4_qdq_weights(wd, want_qdq=True)
+    torch.cuda.synchronize()
+    rc, rs, rg, rq = OQ.qdq_weights(w)
+    assert np.array_equal(OQ.unpack_codes(codes.cpu().numpy()), rc)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert np.array_equal(f32_bits(g_w.cpu().numpy()), f32_bits(rg))
+    assert np.array_equal(host_bits(w_qdq), OF.f64_to_bf16_bits(rq))
+
+
+# ------------------------------------------------------------------ selection
+
+@pytest.mark.parametrize("M,K,k", [(9, 64, 1), (50, 512, 16), (20, 768, 64), (4, 96, 96), (300, 4096, 128)])
+def test_select_residual_bitexact(dev, M, K, k):
+    say(f"select M={M} K={K} k={k}")
+    rng = np.random.default_rng(M + K + k)
+    x = heavy_bf16(rng, (M, K))
+    q = gpu_quant(x)
+    S, R = F.select_residual_channels(q["x_used"], q["codes"], q["scales"], q["g"], q["score"], k)
+    torch.cuda.synchronize()
+    ref = OQ.quantize_activation(x, k)
+    assert np.array_equal(S.cpu().numpy(), ref["S"])
+    assert np.array_equal(host_bits(R), OF.f64_to_bf16_bits(ref["R_S"]))
+
+
+def test_select_ties_prefer_lower_index(dev):
+    say("select ties")
+    rng = np.random.default_rng(77)
+    x = heavy_bf16(rng, (40, 128))
+    x[:, 64:80] = x[:, 0:16]             # equal residuals -> equal scores
+    q = gpu_quant(x)
+    for k in (1, 5, 17, 40):
+        S, _ = F.select_residual_channels(q["x_used"], q["codes"], q["scales"], q["g"], q["score"], k)
+        ref = OQ.quantize_activation(x, k)
+        assert np.array_equal(S.cpu().numpy(), ref["S"])
+
+
+# ------------------------------------------------------------- route / permute
+
+@pytest.mark.parametrize("T,E,tk,bias", [(1, 8, 2, False), (63, 8, 1, False), (64, 16, 4, True),
+                                         (65, 128, 8, True), (300, 128, 8, False),
+                                         (1000, 1024, 32, True)])
+def test_moe_permute_bitexact(dev, T, E, tk, bias):
+    say(f"permute T={T} E={E} tk={tk} bias={bias}")
+    rng = np.random.default_rng(T + E + tk)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[0, :] = 0.25                       # a fully tied token
+    b = rng.standard_normal(E).astype(np.float32) if bias else None
+    ld = torch.from_numpy(logits).cuda()
+    bd = torch.from_numpy(b).cuda() if bias else None
+    ids, w, offs, perm, inv = F.moe_permute(ld, tk, bd)
+    torch.cuda.synchronize()
+    rid, rw = OM.route(logits, tk, b)
+    roffs, rperm, rinv = OM.permute(rid, E)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    assert np.allclose(w.cpu().numpy(), rw, rtol=1e-6, atol=0)
+    assert np.array_equal(offs.cpu().numpy(), roffs)
+    assert np.array_equal(perm.cpu().numpy(), rperm)
+    assert np.array_equal(inv.cpu().numpy(), rinv)
+
+
+# ---------------------------------------------------------------------- GEMM
+
+def _gemm_case(rng, M_src, counts, N, K, k, gather):
+    E = len(counts)
+    x = heavy_bf16(rng, (M_src, K))
+    qa = OQ.quantize_activation(x, k)
+    w = OF.round_to_bf16(rng.standard_normal((E, N, K)) * 0.02)
+    wc, ws, gw, _ = OQ.qdq_weights(w)
+    offs = np.zeros(E + 1, dtype=np.int32)
+    offs[1:] = np.cumsum(counts)
+    M_total = int(offs[-1])
+    a_rows = rng.integers(0, M_src, M_total).astype(np.int32) if gather else None
+    ref = OG.grouped_gemm_rac(qa["codes"], qa["scales"], qa["g"], a_rows, qa["R_S"], qa["S"],
+                              wc, ws, gw, offs)
+    cu = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    y = F.grouped_w4a4_gemm_rac(
+        cu(OQ.pack_codes(qa["codes"])), cu(qa["scales"]), cu(np.array([qa["g"]], np.float32)),
+        cu(a_rows) if gather else None,
+        to_dev_bf16(OF.f64_to_bf16_bits(qa["R_S"])) if k else None,
+        cu(qa["S"]) if k else None,
+        cu(OQ.pack_codes(wc)), cu(ws), cu(gw), cu(offs), M_total=M_total)
+    torch.cuda.synchronize()
+    return host_vals(y), ref
+
+
+@pytest.mark.parametrize("M_src,counts,N,K,k,gather", [
+    (64, [64], 512, 512, 16, False),                  # the dense 64x512x512 case
+    (200, [0, 130, 1, 257], 144, 256, 37, True),      # empty / single-row experts, N and k tails
+    (300, [300], 256, 384, 0, False),                 # no compensation
+    (96, [50, 46], 128, 256, 256, False),             # every channel compensated
+    (500, [17, 0, 0, 400, 83], 272, 1024, 128, True),
+])
+def test_grouped_gemm_rac(dev, M_src, counts, N, K, k, gather):
+    say(f"gemm counts={counts} N={N} K={K} k={k} gather={gather}")
+    rng = np.random.default_rng(sum(counts) + N + K + k)
+    y, ref = _gemm_case(rng, M_src, counts, N, K, k, gather)
+    e1, e2, ex = assert_gemm_close(y, ref)
+    say(f"   rownorm {e1:.2e} maxabs {e2:.2e} exact {ex:.5f}")
+
+
+def test_grouped_gemm_deterministic(dev):
+    say("gemm determinism")
+    rng = np.random.default_rng(5)
+    y1, _ = _gemm_case(rng, 300, [100, 200], 256, 512, 64, True)
+    rng = np.random.default_rng(5)
+    y2, _ = _gemm_case(rng, 300, [100, 200], 256, 512, 64, True)
+    assert np.array_equal(y1, y2)
+
+
+# ------------------------------------------------------------------- combine
+
+@pytest.mark.parametrize("T,tk,N", [(1, 1, 8), (37, 2, 64), (256, 8, 1024)])
+def test_combine(dev, T, tk, N):
+    say(f"combine T={T} tk={tk} N={N}")
+    rng = np.random.default_rng(T * tk + N)
+    y = OF.round_to_bf16(rng.standard_normal((T * tk, N)))
+    inv = rng.permutation(T * tk).reshape(T, tk).astype(np.int32)
+    w = rng.dirichlet(np.ones(tk), size=T).astype(np.float32)
+    out = F.moe_unpermute_combine(to_dev_bf16(OF.f64_to_bf16_bits(y)), torch.from_numpy(inv).cuda(),
+                                  torch.from_numpy(w).cuda())
+    torch.cuda.synchronize()
+    ref = OM.combine(y, inv, w)
+    got = host_vals(out)
+    assert_gemm_close(got, ref, min_exact=0.99)
+    if tk == 1:
+        assert np.array_equal(got, y[inv[:, 0]])
