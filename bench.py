@@ -1,0 +1,271 @@
+"""Throughput of the NVFP4 W4A4 + residual-compensation MoE hot path on one
+MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 1..5] [--no-cpu-baseline]
+
+One step = one pass of the whole path over one batch, inputs resident in HBM:
+weight QDQ of both expert weight tensors (nvfp4_qdq_weights), route and
+permute (moe_permute), online activation quantization with channel scores,
+channel selection and residual gather, the gate+up grouped GEMM with the
+residual correction, SwiGLU fused into the second quantizer, selection, the
+down grouped GEMM with correction, and the combine.
+
+Prints ONE JSON line.  `value` = algorithmic GEMM flops of a step (2 * rows *
+N * (K + k) summed over both GEMMs) / wall time per step, in TFLOP/s.
+`roofline` covers the grouped GEMM kernel: algorithmic flops / its average
+launch duration, measured with HIP events on the launch stream over the
+timed steps, against the bf16 dense MFMA peak (the exact NVFP4 product runs
+on the bf16 matrix path).  `cpu_baseline` times the CPU oracle on a bounded
+sample of the same block.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP4_TFLOPS = 10100.0      # MI355X dense fp4 MFMA
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=128)
+    ap.add_argument("--cpu-experts", type=int, default=4)
+    return ap.parse_args()
+
+
+def to_dev(bits, dev):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+class Timer:
+    """Average duration of a bracketed region, from HIP events recorded on
+    the current (launch) stream."""
+
+    def __init__(self):
+        self.pairs = []
+
+    def start(self):
+        import torch
+        a = torch.cuda.Event(enable_timing=True)
+        a.record()
+        return a
+
+    def stop(self, a):
+        import torch
+        b = torch.cuda.Event(enable_timing=True)
+        b.record()
+        self.pairs.append((a, b))
+
+    def mean_ms(self):
+        if not self.pairs:
+            return float("nan")
+        return sum(a.elapsed_time(b) for a, b in self.pairs) / len(self.pairs)
+
+
+def run_gpu(cfg, wl, steps, warmup):
+    import torch
+
+    import fp4_quantized_gemm_amd as F
+
+    dev = torch.device("cuda:0")
+    x = to_dev(wl.x, dev)
+    w1 = to_dev(wl.w_first, dev)
+    w2 = to_dev(wl.w_down, dev) if wl.w_down is not None else None
+    if wl.logits is not None:
+        logits = torch.from_numpy(wl.logits).to(dev)
+        bias = torch.from_numpy(wl.bias).to(dev) if wl.bias is not None else None
+    torch.cuda.synchronize()
+
+    timers = {n: Timer() for n in ("qdq", "permute", "quant1", "select1", "gemm1", "quant2",
+                                   "select2", "gemm2", "combine")}
+    record = [False]
+
+    def timed(name, fn, *a, **kw):
+        if not record[0]:
+            return fn(*a, **kw)
+        t0 = timers[name].start()
+        r = fn(*a, **kw)
+        timers[name].stop(t0)
+        return r
+
+    def step():
+        q1w = timed("qdq", lambda: (F.nvfp4_qdq_weights(w1, want_qdq=False),
+                                    F.nvfp4_qdq_weights(w2, want_qdq=False) if w2 is not None else None))
+        (c1, s1, g1, _), wd = q1w
+        if cfg.kind == "dense":
+            offs = torch.tensor([0, cfg.T], dtype=torch.int32, device=dev)
+            perm = None
+            rows = cfg.T
+        else:
+            ids, tw, offs, perm, inv = timed("permute", F.moe_permute, logits, cfg.topk, bias)
+            rows = perm.numel()
+        q = timed("quant1", F.nvfp4_quantize_act, x, False, cfg.k_first > 0)
+        S = R = None
+        if cfg.k_first:
+            S, R = timed("select1", F.select_residual_channels, q["x_used"], q["codes"],
+                         q["scales"], q["g"], q["score"], cfg.k_first)
+        y1 = timed("gemm1", F.grouped_w4a4_gemm_rac, q["codes"], q["scales"], q["g"], perm, R, S,
+                   c1, s1, g1, offs, M_total=rows)
+        if wd is None:
+            return y1
+        c2, s2, g2, _ = wd
+        q2 = timed("quant2", F.nvfp4_quantize_act, y1, True, cfg.k_down > 0)
+        S2 = R2 = None
+        if cfg.k_down:
+            S2, R2 = timed("select2", F.select_residual_channels, q2["x_used"], q2["codes"],
+                           q2["scales"], q2["g"], q2["score"], cfg.k_down)
+        y2 = timed("gemm2", F.grouped_w4a4_gemm_rac, q2["codes"], q2["scales"], q2["g"], None, R2,
+                   S2, c2, s2, g2, offs, M_total=rows)
+        return timed("combine", F.moe_unpermute_combine, y2, inv, tw)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # a second pass with per-call events (kept out of the wall-clock region)
+    record[0] = True
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    stage_ms = {n: t.mean_ms() for n, t in timers.items() if t.pairs}
+
+    # residual-compensation overhead: the same GEMMs with k = 0
+    rac = {}
+    if cfg.k_first:
+        q = F.nvfp4_quantize_act(x, False, True)
+        S, R = F.select_residual_channels(q["x_used"], q["codes"], q["scales"], q["g"], q["score"],
+                                          cfg.k_first)
+        c1, s1, g1, _ = F.nvfp4_qdq_weights(w1, want_qdq=False)
+        if cfg.kind == "dense":
+            offs = torch.tensor([0, cfg.T], dtype=torch.int32, device=dev)
+            perm, rows = None, cfg.T
+        else:
+            _, _, offs, perm, _ = F.moe_permute(logits, cfg.topk, bias)
+            rows = perm.numel()
+        for kk, (RR, SS) in (("k", (R, S)), ("0", (None, None))):
+            tm = Timer()
+            for i in range(steps + 2):
+                a = tm.start()
+                F.grouped_w4a4_gemm_rac(q["codes"], q["scales"], q["g"], perm, RR, SS, c1, s1, g1,
+                                        offs, M_total=rows)
+                tm.stop(a)
+            torch.cuda.synchronize()
+            tm.pairs = tm.pairs[2:]
+            rac[kk] = tm.mean_ms()
+        rac = {"gemm1_ms_k": rac["k"], "gemm1_ms_k0": rac["0"],
+               "overhead": rac["k"] / rac["0"] - 1.0}
+    return wall / steps * 1e3, stage_ms, rac
+
+
+def cpu_baseline(cfg, wl, tokens, experts):
+    """The oracle, as it stands, on a bounded sample of the same block: the
+    first `tokens` tokens routed over the first `experts` experts (top-k
+    capped at experts / 2), every stage of the block."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import formats as OF
+    from oracle import layer
+
+    tk = min(cfg.topk, max(1, experts // 2)) if cfg.kind != "dense" else 1
+    T = min(tokens, cfg.T)
+    x = OF.bf16_bits_to_f64(wl.x[:T])
+    t0 = time.perf_counter()
+    if cfg.kind == "dense":
+        w = OF.bf16_bits_to_f64(wl.w_first[0])
+        layer.dense_forward(x, w, cfg.k_first)
+        flops = 2 * T * w.shape[0] * (cfg.H + cfg.k_first)
+        desc = f"dense {T}x{w.shape[0]}x{cfg.H}"
+    else:
+        E = min(experts, cfg.E)
+        w1 = OF.bf16_bits_to_f64(wl.w_first[:E])
+        w2 = OF.bf16_bits_to_f64(wl.w_down[:E]) if wl.w_down is not None else None
+        logits = wl.logits[:T, :E]
+        bias = wl.bias[:E] if wl.bias is not None else None
+        layer.moe_forward(x, logits, bias, tk, w1, w2, cfg.k_first, cfg.k_down)
+        rows = T * tk
+        flops = 2 * rows * w1.shape[1] * (cfg.H + cfg.k_first)
+        if w2 is not None:
+            flops += 2 * rows * cfg.H * (cfg.inter + cfg.k_down)
+        desc = (f"{T} tokens x top-{tk} of the first {E} experts, every stage incl. weight QDQ "
+                f"of those experts")
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": desc, "seconds": round(dt, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              f"multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import synth
+
+    cfg = synth.get(args.config)
+    wl = synth.make(cfg)
+    ms, stage_ms, rac = run_gpu(cfg, wl, args.steps, args.warmup)
+    shapes = cfg.gemm_shapes()
+    flops_step = cfg.gemm_flops()
+    value = flops_step / (ms * 1e-3) / 1e12
+    gemm_ms = stage_ms.get("gemm1", 0.0) + stage_ms.get("gemm2", 0.0)
+    achieved = flops_step / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else None
+    q_bytes = 2.5625 * cfg.T * cfg.H
+    quant = {"quant1_GBps": q_bytes / (stage_ms["quant1"] * 1e-3) / 1e9}
+    if "quant2" in stage_ms:
+        q2_bytes = 4.5625 * cfg.rows * cfg.inter
+        quant["quant2_GBps"] = q2_bytes / (stage_ms["quant2"] * 1e-3) / 1e9
+    line = {
+        "metric": "grouped W4A4+RAC GEMM TFLOP/s and % of MI355X FP4 MFMA peak; quantizer GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "storage": "nvfp4 (E2M1 + E4M3/16 + f32), decoded exactly to bf16 MFMA operands, f32 acc",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E,
+                   "topk": cfg.topk, "inter": cfg.inter, "rac_k": [s[4] for s in shapes],
+                   "gemms": [f"{n} {m}x{nn}x{k}" for n, m, nn, k, _ in shapes]},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2) if achieved else None,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4) if achieved else None,
+                     "traffic": None, "kernel": "k_gemm_rac",
+                     "frac_of_fp4_peak": round(achieved / PEAK_FP4_TFLOPS, 4) if achieved else None},
+        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "quantizer": {k: round(v, 1) for k, v in quant.items()},
+        "rac_overhead": {k: round(v, 4) for k, v in rac.items()},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, wl, args.cpu_tokens, args.cpu_experts)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

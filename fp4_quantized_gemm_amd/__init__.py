@@ -61,7 +61,7 @@ def _load():
         "nvfp4_quantize_act_workspace_size": [_I64, _I64],
         "select_residual_channels_workspace_size": [_I64, _I64, _I64],
         "moe_permute_workspace_size": [_I64, _I64],
-        "grouped_w4a4_gemm_rac_workspace_size": [_I64, _I64, _I64, _I64, _I64],
+        "grouped_w4a4_gemm_rac_workspace_size": [_I64, _I64, _I64, _I64, _I64, _I64],
     }.items():
         f = getattr(L, name)
         f.restype = _SZ
@@ -200,7 +200,7 @@ def grouped_w4a4_gemm_rac(a_codes, a_scales, g_x, a_rows, R_S, S, w_codes, w_sca
         M_total = int(a_rows.numel()) if a_rows is not None else M_src
     dev = a_codes.device
     y = out if out is not None else torch.empty((M_total, N), dtype=torch.bfloat16, device=dev)
-    ws = _ws(L.grouped_w4a4_gemm_rac_workspace_size(E, M_total, N, K, k), dev)
+    ws = _ws(L.grouped_w4a4_gemm_rac_workspace_size(E, M_src, M_total, N, K, k), dev)
     _check(L.grouped_w4a4_gemm_rac(_ptr(a_codes), _ptr(a_scales), _ptr(g_x), _ptr(a_rows), M_src,
                                    _ptr(R_S) if k else None, _ptr(S) if k else None, k,
                                    _ptr(w_codes), _ptr(w_scales), _ptr(g_w), _ptr(expert_offsets),

@@ -19,6 +19,9 @@
 // k-offset 32*(l/16) of its row and feeds four MFMA k-slices from them; the
 // k order inside an MFMA is permuted identically for A and B, which leaves
 // the dot products unchanged.
+#include <cstdlib>
+#include <cstring>
+
 #include "device.h"
 #include "runtime.h"
 
@@ -80,7 +83,7 @@ __device__ __forceinline__ f32x4_t mfma_bf16(const u32x4& a, const u32x4& b, f32
 }
 
 __global__ void __launch_bounds__(256)
-k_gemm_rac(GemmArgs p) {
+k_gemm_generic(GemmArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smA[kBM * kRowBytes];
   __shared__ __attribute__((aligned(16))) uint8_t smB[kBN * kRowBytes];
   __shared__ int32_t rows_src[kBM];
@@ -248,19 +251,370 @@ k_gemm_rac(GemmArgs p) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Large-tile path (two kernels).
+//
+// 1. k_decode_a: the activation operand, codes and E4M3 block scales, is
+//    decoded once per call into an exact f16 image x~ = q * s (at most 6
+//    significant bits, magnitudes 2^-10 .. 2880, so f16 holds it exactly) in
+//    the workspace.  Inside every 64-wide K block the eight 16-byte chunks
+//    are stored in the order the matrix-core lanes consume them.
+// 2. k_gemm_big: 256x256 per workgroup, four waves of 128x128, K in steps of
+//    64 through double-buffered LDS filled by direct global->LDS loads.  A
+//    tiles arrive as f16; weight tiles arrive packed and each wave decodes
+//    its 128 columns in registers: the hardware FP4 convert applies the block
+//    scale's power of two, one packed f16 multiply its significand
+//    (s = 2^E * mu, mu in [1, 2)).  Products run on v_mfma_f32_32x32x16_f16.
+//    The weights of the selected residual channels are copied out of each
+//    staged K tile into an LDS tile (bf16, exact) as the loop passes them;
+//    after the loop the correction runs on v_mfma_f32_32x32x16_bf16 into
+//    the same accumulators.
+//
+// MFMA 32x32x16 operand layout: lane l supplies row (or column) l % 32 and
+// the 8 k values of group kg = l / 32.  Within a 64-wide K step, lane group
+// kg at k-slice t (0..3) covers k in [32 kg + 8 t, +8) for both operands; the
+// 16 accumulators of a lane hold column l % 32, rows 8 (r/4) + 4 kg + r % 4.
+// ---------------------------------------------------------------------------
+namespace big {
+constexpr int BM = 256, BN = 256, BK = 64, NSTAGE = 2;
+constexpr int A_BYTES = BM * BK * 2;           // f16 [256][64]: 8 chunks/row, chunk c at c ^ (row & 7)
+constexpr int B_CODES = BN * 32;               // [256][32 B]: chunk c at c ^ ((row >> 2) & 1)
+constexpr int B_SCALES = BN * 4;               // [256][4 B]
+constexpr int STAGE = A_BYTES + B_CODES + B_SCALES;   // 41984
+constexpr int KMAX = 128;                      // residual channels held in LDS
+constexpr int KSTEPS_MAX = 1024;               // K <= 65536
+constexpr int WSROW = KMAX * 2 + 16;           // bf16 row of the W_S tile (+pad)
+constexpr int WS_OFF = NSTAGE * STAGE;
+constexpr int OUTROW = BN * 2 + 16;            // bf16 output staging row (+pad)
+constexpr int LDS_MAIN = WS_OFF + BN * WSROW;  // 153600
+constexpr int LDS = LDS_MAIN > BM * OUTROW ? LDS_MAIN : BM * OUTROW;
+}  // namespace big
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+template <int SEL>
+__device__ __forceinline__ uint32_t dec2_f16(uint32_t w, float sc, h2_t mu) {
+  h2_t v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, sc, SEL);
+  return __builtin_bit_cast(uint32_t, v * mu);
+}
+
+// 8 codes (one dword) -> 8 exact f16 values q * s.  `sc` is the block scale
+// as float32 (the convert uses only its exponent), `mu` its significand.
+__device__ __forceinline__ u32x4 decode8_f16(uint32_t w, float sc, h2_t mu) {
+  return u32x4{dec2_f16<0>(w, sc, mu), dec2_f16<1>(w, sc, mu), dec2_f16<2>(w, sc, mu),
+               dec2_f16<3>(w, sc, mu)};
+}
+
+__device__ __forceinline__ void scale_prep(uint32_t byte, float& sc, h2_t& mu) {
+  const float s = __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
+  const float m = __uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
+  mu = __builtin_bit_cast(h2_t, __builtin_amdgcn_cvt_pkrtz(m, m));
+  sc = s;
+}
+
+__device__ __forceinline__ void wait_vmem0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ f32x16_t mfma32_f16(const u32x4& a, const u32x4& b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16_t mfma32_bf16(const u32x4& a, const u32x4& b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// codes [M][K/2] + scales [M][K/16] -> f16 image [M][K]; one thread per 8
+// consecutive k (one code dword, one block scale), written to the chunk slot
+// 2 t + kg of its 64-wide block, where k % 64 = 32 kg + 8 t.
+__global__ void __launch_bounds__(256)
+k_decode_a(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t M,
+           int64_t K, uint16_t* __restrict__ img) {
+  const int64_t per_row = K / 8;
+  const int64_t total = M * per_row;
+  for (int64_t q = blockIdx.x * 256LL + threadIdx.x; q < total; q += (int64_t)gridDim.x * 256) {
+    const int64_t m = q / per_row;
+    const int64_t c8 = q - m * per_row;
+    const int64_t k = c8 * 8;
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + m * (K / 2) + k / 2);
+    float sc;
+    h2_t mu;
+    scale_prep(scales[m * (K / 16) + k / 16], sc, mu);
+    const u32x4 v = decode8_f16(w, sc, mu);
+    const int kk = (int)(k & 63), kg = kk >> 5, t = (kk & 31) >> 3;
+    uint16_t* dst = img + m * K + (k - kk) + (2 * t + kg) * 8;
+    *reinterpret_cast<uint4*>(dst) = make_uint4(v.x, v.y, v.z, v.w);
+  }
+}
+
+// Eight waves (two per SIMD, so one wave's waits are covered by the other's
+// MFMAs): wave w owns rows 128 * (w / 4) .. +128 and columns 64 * (w % 4) .. +64
+// of the 256x256 tile.
+__global__ void __launch_bounds__(512, 1)
+k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_tiles) {
+  using namespace big;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
+  __shared__ int32_t rows_src[BM];
+  __shared__ int32_t s_local[KMAX];
+  __shared__ int32_t j_first[KSTEPS_MAX + 1];     // first selected channel at or after step kt
+  uint8_t* const wsl = smem + WS_OFF;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;                      // 0..7
+  const int wm = wave >> 2, wn = wave & 3;
+  const int kg = lane >> 5, r32 = lane & 31;
+
+  // tile order: groups of 4 row tiles x all column tiles, so the workgroups
+  // in flight share A and weight tiles through L2
+  const int v = (int)blockIdx.x;
+  const int group = 4 * n_tiles;
+  const int gi = v / group, gr = v - gi * group;
+  if (4 * gi >= m_tiles) return;
+  const int gm = m_tiles - 4 * gi < 4 ? m_tiles - 4 * gi : 4;
+  const int gt = 4 * gi + gr % gm;                // row tile
+  const int nt = gr / gm;                         // column tile
+  if (gt >= p.tile_prefix[p.E] || nt >= n_tiles) return;
+  int lo = 0, hi = p.E;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (p.tile_prefix[mid] <= gt) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  int64_t e_lo = p.offsets[e], e_hi = p.offsets[e + 1];
+  e_lo = e_lo < 0 ? 0 : (e_lo > p.M_total ? p.M_total : e_lo);
+  e_hi = e_hi < e_lo ? e_lo : (e_hi > p.M_total ? p.M_total : e_hi);
+  const int64_t p0 = e_lo + (int64_t)(gt - p.tile_prefix[e]) * BM;
+  const int64_t n0 = (int64_t)nt * BN;
+  const uint32_t Kh = (uint32_t)(p.K / 2), Ks = (uint32_t)(p.K / 16), K2 = (uint32_t)(p.K * 2);
+  const int kk = p.k;
+
+  if (tid < BM) {
+    int64_t pr = p0 + tid;
+    if (pr >= e_hi) pr = e_hi - 1;
+    int64_t t = p.a_rows ? (int64_t)p.a_rows[pr] : pr;
+    rows_src[tid] = (int32_t)(t < 0 ? 0 : (t >= p.M_src ? p.M_src - 1 : t));
+    if (tid < kk) {
+      int c = p.S[tid];
+      s_local[tid] = c < 0 ? 0 : (c >= p.K ? (int)p.K - 1 : c);
+    }
+    const int kpad = (kk + 15) & ~15;          // zero slots k .. next multiple of 16
+    for (int j = kk; j < kpad; ++j) *reinterpret_cast<uint16_t*>(wsl + tid * WSROW + 2 * j) = 0;
+  }
+  __syncthreads();
+  const int nk = (int)(p.K / BK);
+  if (kk > 0) {
+    // j_first[kt] = first j with S[j] >= kt * BK (S ascending), by binary search
+    for (int kt = tid; kt <= nk; kt += 512) {
+      int a = 0, b = kk;
+      while (a < b) {
+        const int m = (a + b) >> 1;
+        if (s_local[m] < kt * BK) a = m + 1; else b = m;
+      }
+      j_first[kt] = a;
+    }
+    __syncthreads();
+  }
+
+  const uint8_t* wc = p.w_codes + (int64_t)e * p.N * Kh;
+  const uint8_t* wsc = p.w_scales + (int64_t)e * p.N * Ks;
+
+  // byte offsets of this lane's staging loads (fixed over K): A 2048 chunks
+  // (4 per thread), B codes 512 chunks (1 per thread), B scales 256 dwords
+  // (waves 0..3)
+  uint32_t off_a[4], off_b, off_s = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = (i * 8 + wave) * 64 + lane;
+    const int r = q >> 3, c = (q & 7) ^ (r & 7);
+    off_a[i] = (uint32_t)rows_src[r] * K2 + 16u * c;
+  }
+  {
+    const int q = wave * 64 + lane;
+    const int r = q >> 1, c = (q & 1) ^ ((r >> 2) & 1);
+    int64_t n = n0 + r;
+    if (n >= p.N) n = p.N - 1;
+    off_b = (uint32_t)n * Kh + 16u * c;
+  }
+  if (wave < 4) {
+    int64_t n = n0 + wave * 64 + lane;
+    if (n >= p.N) n = p.N - 1;
+    off_s = (uint32_t)n * Ks;
+  }
+  auto issue_loads = [&](int buf, uint32_t k0) {
+    uint8_t* st = smem + buf * STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds(a_img + off_a[i] + k0 * 2, st + (i * 8 + wave) * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(wc + off_b + k0 / 2, st + A_BYTES + wave * 1024, 16, 0, 0);
+    if (wave < 4)
+      __builtin_amdgcn_global_load_lds(wsc + off_s + k0 / 16, st + A_BYTES + B_CODES + wave * 256, 4,
+                                       0, 0);
+  };
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int swa = r32 & 7;                         // A rows = 32 i + r32 (+ multiples of 32)
+  const int physb = kg ^ ((r32 >> 2) & 1);
+  issue_loads(0, 0);
+  wait_vmem0();
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) issue_loads(buf ^ 1, (uint32_t)(kt + 1) * BK);
+    const uint8_t* ab = smem + buf * STAGE;
+    const uint8_t* bb = ab + A_BYTES;
+    const uint8_t* sb = bb + B_CODES;
+
+    if (kk > 0) {
+      // copy the weights of the selected channels in [k0, k0 + BK) out of
+      // this stage: thread t owns weight row t % 256, channels of parity t / 256
+      const int k0 = kt * BK;
+      const int jhi = j_first[kt + 1];
+      const int row = tid & 255;
+      const uint8_t* rowc = bb + row * 32;
+      const int sw = (row >> 2) & 1;
+      for (int j = j_first[kt] + (tid >> 8); j < jhi; j += 2) {
+        const int c = s_local[j] - k0;
+        const int byte = c >> 1;
+        const uint32_t code = (rowc[(((byte >> 4) ^ sw) << 4) | (byte & 15)] >> (4 * (c & 1))) & 0xFu;
+        const float q = e2m1_unpack2<0>(code).x;
+        const float sc = e4m3_decode(sb[row * 4 + (c >> 4)]);
+        *reinterpret_cast<uint16_t*>(wsl + row * WSROW + 2 * j) =
+            (uint16_t)(__float_as_uint(q * sc) >> 16);
+      }
+    }
+
+    uint4 br[2];
+    uint32_t bs[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int rb = wn * 64 + 32 * j + r32;
+      br[j] = *reinterpret_cast<const uint4*>(bb + rb * 32 + physb * 16);
+      bs[j] = *reinterpret_cast<const uint16_t*>(sb + rb * 4 + 2 * kg);
+    }
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      float sbv[2];
+      h2_t mb[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) scale_prep((bs[j] >> (8 * hb)) & 0xFFu, sbv[j], mb[j]);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int t = 2 * hb + s2;
+        u32x4 A[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ra = wm * 128 + 32 * i + r32;
+          const uint4 v4 = *reinterpret_cast<const uint4*>(ab + ra * 128 + (((2 * t + kg) ^ swa) << 4));
+          A[i] = u32x4{v4.x, v4.y, v4.z, v4.w};
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint32_t w = t == 0 ? br[j].x : t == 1 ? br[j].y : t == 2 ? br[j].z : br[j].w;
+          const u32x4 B = decode8_f16(w, sbv[j], mb[j]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i][j] = mfma32_f16(A[i], B, acc[i][j]);
+        }
+      }
+    }
+
+    wait_vmem0();
+    __syncthreads();
+  }
+
+  // epilogue: x g_x, residual K-extension (16 channels per MFMA), x g_w.
+  // Residual operand loads are issued in batches of four chunks, then consumed.
+  const float gx = *p.g_x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] *= gx;
+
+  for (int cb0 = 0; cb0 < kk; cb0 += 64) {
+    u32x4 A[4][4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int slot = cb0 + 16 * c + 8 * kg;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t t = rows_src[wm * 128 + 32 * i + r32];
+        const uint16_t* rr = p.R + t * kk + slot;
+        if ((kk & 7) == 0 && slot + 8 <= kk) {
+          const uint4 vv = *reinterpret_cast<const uint4*>(rr);
+          A[c][i] = u32x4{vv.x, vv.y, vv.z, vv.w};
+        } else {
+          uint32_t vv[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) vv[q] = (slot + q < kk) ? rr[q] : 0u;
+          A[c][i] = u32x4{vv[0] | (vv[1] << 16), vv[2] | (vv[3] << 16), vv[4] | (vv[5] << 16),
+                          vv[6] | (vv[7] << 16)};
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if (cb0 + 16 * c >= kk) break;
+      const int slot = cb0 + 16 * c + 8 * kg;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint4 vv = *reinterpret_cast<const uint4*>(wsl + (wn * 64 + 32 * j + r32) * WSROW + 2 * slot);
+        const u32x4 B = u32x4{vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][j] = mfma32_bf16(A[c][i], B, acc[i][j]);
+      }
+    }
+  }
+
+  // y = bf16(g_w * acc), staged through LDS for 16-byte row stores
+  const float gw = p.g_w[e];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 128 + 32 * i + 8 * (r >> 2) + 4 * kg + (r & 3);
+        const int col = wn * 64 + 32 * j + r32;
+        *reinterpret_cast<uint16_t*>(smem + row * OUTROW + 2 * col) =
+            (uint16_t)f32_to_bf16_rne(acc[i][j][r] * gw);
+      }
+  __syncthreads();
+  for (int q = tid; q < BM * (BN / 8); q += 512) {
+    const int row = q / (BN / 8), ch = q % (BN / 8);
+    const int64_t prow = p0 + row;
+    const int64_t n = n0 + ch * 8;
+    if (prow < e_hi && n < p.N)
+      *reinterpret_cast<uint4*>(p.y + prow * p.N + n) =
+          *reinterpret_cast<const uint4*>(smem + row * OUTROW + ch * 16);
+  }
+}
+
 }  // namespace nvfp4
 
 using namespace nvfp4;
 
 extern "C" {
 
-size_t grouped_w4a4_gemm_rac_workspace_size(int64_t E, int64_t M_total, int64_t N, int64_t K,
-                                            int64_t k) {
+// prefix [E+1] int32, then (large-tile path) the f16 image of A [M_src][K]
+static size_t img_offset(int64_t E) { return round_up((size_t)(E + 1) * sizeof(int32_t), 256); }
+
+size_t grouped_w4a4_gemm_rac_workspace_size(int64_t E, int64_t M_src, int64_t M_total, int64_t N,
+                                            int64_t K, int64_t k) {
   (void)M_total;
   (void)N;
-  (void)K;
   (void)k;
-  return round_up((size_t)(E + 1) * sizeof(int32_t), 256);
+  if (E < 1 || M_src < 0 || K < 0) return 256;
+  return img_offset(E) + round_up((size_t)M_src * (size_t)K * 2, 256);
 }
 
 int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
@@ -284,12 +638,11 @@ int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const
   NV_REQUIRE(aligned(a_codes, 16) && aligned(w_codes, 16) && aligned(a_scales, 8) &&
                  aligned(w_scales, 8) && aligned(ws, 16) && aligned(y, 2) && aligned(R_S, 2),
              NVFP4_ERR_ALIGN, "grouped_w4a4_gemm_rac: misaligned pointer");
-  NV_REQUIRE(ws_bytes >= grouped_w4a4_gemm_rac_workspace_size(E, M_total, N, K, k),
-             NVFP4_ERR_WORKSPACE, "grouped_w4a4_gemm_rac: workspace too small");
+  NV_REQUIRE(ws_bytes >= img_offset(E), NVFP4_ERR_WORKSPACE,
+             "grouped_w4a4_gemm_rac: workspace too small");
   if (M_total == 0) return ok();
   hipStream_t s = as_stream(stream);
   int32_t* prefix = static_cast<int32_t*>(ws);
-  k_tile_prefix<<<1, 1024, 0, s>>>(expert_offsets, (int)E, M_total, kBM, prefix);
   GemmArgs a;
   a.a_codes = a_codes;
   a.a_scales = a_scales;
@@ -311,7 +664,32 @@ int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const
   a.k = (int)k;
   const int64_t m_tiles = (M_total + kBM - 1) / kBM + E;
   const int64_t n_tiles = (N + kBN - 1) / kBN;
-  k_gemm_rac<<<dim3((unsigned)m_tiles, (unsigned)n_tiles), 256, 0, s>>>(a);
+    const int64_t n_tiles_big = (N + big::BN - 1) / big::BN;
+  const int64_t m_tiles_big = (M_total + big::BM - 1) / big::BM + E;
+  // NVFP4RAC_GEMM=generic|big forces a kernel (tests use it to cover both on
+  // small shapes).  The large-tile path holds at most KMAX residual channels,
+  // needs the f16 image of A in the workspace and 32-bit image offsets.
+  const char* force = getenv("NVFP4RAC_GEMM");
+  bool use_big = (M_total / big::BM) * n_tiles_big >= 2LL * num_cus();
+  if (force && strcmp(force, "big") == 0) use_big = true;
+  if (force && strcmp(force, "generic") == 0) use_big = false;
+  const size_t need_big = grouped_w4a4_gemm_rac_workspace_size(E, M_src, M_total, N, K, k);
+  use_big = use_big && k <= big::KMAX && K / big::BK <= big::KSTEPS_MAX && ws_bytes >= need_big &&
+            (uint64_t)M_src * K * 2 < (1ULL << 32);
+  if (use_big) {
+    uint16_t* img = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + img_offset(E));
+    const int64_t chunks = M_src * (K / 8);
+    int64_t nb = (chunks + 255) / 256;
+    if (nb > 16LL * num_cus()) nb = 16LL * num_cus();
+    k_decode_a<<<(unsigned)nb, 256, 0, s>>>(a_codes, a_scales, M_src, K, img);
+    k_tile_prefix<<<1, 1024, 0, s>>>(expert_offsets, (int)E, M_total, big::BM, prefix);
+    const int64_t nblk = ((m_tiles_big + 3) / 4) * 4 * n_tiles_big;
+    k_gemm_big<<<(unsigned)nblk, 512, 0, s>>>(a, reinterpret_cast<const uint8_t*>(img),
+                                             (int)n_tiles_big, (int)m_tiles_big);
+  } else {
+    k_tile_prefix<<<1, 1024, 0, s>>>(expert_offsets, (int)E, M_total, kBM, prefix);
+    k_gemm_generic<<<dim3((unsigned)m_tiles, (unsigned)n_tiles), 256, 0, s>>>(a);
+  }
   return check_launch("grouped_w4a4_gemm_rac");
 }
 

@@ -166,8 +166,8 @@ int moe_permute(const float* logits, const float* bias, int64_t T, int64_t E, in
  * expert_offsets [E+1] (device; off[0] = 0, off[E] = M_total); y [M_total][N]
  * bf16.  Requires K % 128 == 0, N % 16 == 0, 0 <= k <= K.
  * ---------------------------------------------------------------------- */
-size_t grouped_w4a4_gemm_rac_workspace_size(int64_t E, int64_t M_total, int64_t N,
-                                            int64_t K, int64_t k);
+size_t grouped_w4a4_gemm_rac_workspace_size(int64_t E, int64_t M_src, int64_t M_total,
+                                            int64_t N, int64_t K, int64_t k);
 int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
                           const int32_t* a_rows, int64_t M_src,
                           const void* R_S, const int32_t* S, int64_t k,

@@ -100,7 +100,7 @@ def test_permute_validation():
 
 def test_gemm_validation():
     L = F.lib()
-    ws = L.grouped_w4a4_gemm_rac_workspace_size(4, 64, 128, 256, 8)
+    ws = L.grouped_w4a4_gemm_rac_workspace_size(4, 64, 64, 128, 256, 8)
     args = lambda **kw: [kw.get("ac", FAKE), FAKE, FAKE, kw.get("rows", None), kw.get("msrc", 64),
                          kw.get("R", None), kw.get("S", None), kw.get("k", 0), FAKE, FAKE, FAKE,
                          FAKE, kw.get("E", 4), 64, kw.get("N", 128), kw.get("K", 256), FAKE, FAKE,

@@ -190,22 +190,29 @@ def _gemm_case(rng, M_src, counts, N, K, k, gather):
     return host_vals(y), ref
 
 
+@pytest.fixture(params=["generic", "big"])
+def gemm_kernel(request, monkeypatch):
+    monkeypatch.setenv("NVFP4RAC_GEMM", request.param)
+    return request.param
+
+
 @pytest.mark.parametrize("M_src,counts,N,K,k,gather", [
     (64, [64], 512, 512, 16, False),                  # the dense 64x512x512 case
     (200, [0, 130, 1, 257], 144, 256, 37, True),      # empty / single-row experts, N and k tails
     (300, [300], 256, 384, 0, False),                 # no compensation
     (96, [50, 46], 128, 256, 256, False),             # every channel compensated
     (500, [17, 0, 0, 400, 83], 272, 1024, 128, True),
+    (700, [300, 1, 511, 0, 255], 528, 768, 64, True),  # several 256-row tiles, N tail
 ])
-def test_grouped_gemm_rac(dev, M_src, counts, N, K, k, gather):
-    say(f"gemm counts={counts} N={N} K={K} k={k} gather={gather}")
+def test_grouped_gemm_rac(dev, gemm_kernel, M_src, counts, N, K, k, gather):
+    say(f"gemm[{gemm_kernel}] counts={counts} N={N} K={K} k={k} gather={gather}")
     rng = np.random.default_rng(sum(counts) + N + K + k)
     y, ref = _gemm_case(rng, M_src, counts, N, K, k, gather)
     e1, e2, ex = assert_gemm_close(y, ref)
     say(f"   rownorm {e1:.2e} maxabs {e2:.2e} exact {ex:.5f}")
 
 
-def test_grouped_gemm_deterministic(dev):
+def test_grouped_gemm_deterministic(dev, gemm_kernel):
     say("gemm determinism")
     rng = np.random.default_rng(5)
     y1, _ = _gemm_case(rng, 300, [100, 200], 256, 512, 64, True)
