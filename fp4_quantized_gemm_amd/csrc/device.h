@@ -98,6 +98,22 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+// Block-wide max of non-negative 32-bit values, then one device atomic per
+// block (instead of one per wave, which serialises at the L2 on one address).
+template <int NTHREADS>
+__device__ __forceinline__ void block_atomic_max(uint32_t v, uint32_t* dst) {
+  __shared__ uint32_t wm[NTHREADS / 64];
+  v = wave_max_u32(v);
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < NTHREADS / 64; ++i) m = wm[i] > m ? wm[i] : m;
+    if (m) atomicMax(dst, m);
+  }
+}
+
 __device__ __forceinline__ int frexp_exponent(float a) {
   return (int)((__float_as_uint(a) >> 23) & 0xFFu) - 126;   // a normal and > 0
 }

@@ -7,10 +7,11 @@
 //   1. k_route: one wave per token -> topk_ids, topk_w (softmax in float64).
 //   2. k_route_masks: one wave per chunk of 64 tokens; per expert a 64-bit
 //      mask of the chunk's tokens that chose it (LDS atomic OR), plus counts.
-//   3. k_chunk_scan: one workgroup; per expert an exclusive scan over chunks,
-//      then over experts -> expert_offsets and each chunk's base per expert.
-//   4. k_scatter: row = base[chunk][e] + popcount(mask below the token), so
-//      tokens stay ascending inside an expert.
+//   3. k_chunk_scan: one wave per expert, exclusive scan over chunks -> each
+//      chunk's base inside the expert and the expert's total;
+//      k_expert_offsets: exclusive scan of the totals -> expert_offsets.
+//   4. k_scatter: row = offsets[e] + base[chunk][e] + popcount(mask below the
+//      token), so tokens stay ascending inside an expert.
 #include "device.h"
 #include "runtime.h"
 
@@ -39,8 +40,10 @@ k_route(const float* __restrict__ logits, const float* __restrict__ bias, int64_
     v[i] = l;
     if (e >= E) taken |= 1u << i;
   }
-  double sel[kMaxTopk];
-  int sel_e[kMaxTopk];
+  // lane r keeps the r-th pick; the picks come out in descending order
+  float my_v = -INFINITY;
+  int my_e = 0;
+  float top = 0.0f;
   for (int r = 0; r < tk; ++r) {
     // lane-local best among untaken (value desc, index asc)
     float bv = -INFINITY;
@@ -62,20 +65,16 @@ k_route(const float* __restrict__ logits, const float* __restrict__ bias, int64_
       }
     }
     if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    sel[r] = (double)bv;
-    sel_e[r] = be;
+    if (lane == r) { my_v = bv; my_e = be; }
+    if (r == 0) top = bv;
   }
-  if (lane == 0) {
-    double mx = sel[0], sum = 0.0;
-    double z[kMaxTopk];
-    for (int r = 0; r < tk; ++r) {
-      z[r] = exp(sel[r] - mx);
-      sum += z[r];
-    }
-    for (int r = 0; r < tk; ++r) {
-      ids[t * tk + r] = sel_e[r];
-      w[t * tk + r] = (float)(z[r] / sum);
-    }
+  // softmax over the picks in float64, one pick per lane
+  const double z = lane < tk ? exp((double)my_v - (double)top) : 0.0;
+  double sum = z;
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+  if (lane < tk) {
+    ids[t * tk + lane] = my_e;
+    w[t * tk + lane] = (float)(z / sum);
   }
 }
 
@@ -98,25 +97,38 @@ k_route_masks(const int32_t* __restrict__ ids, int64_t T, int E, int tk,
   }
 }
 
-// One workgroup of 1024 threads.  base[c][e] = offsets[e] + sum_{c' < c} counts[c'][e].
-__global__ void __launch_bounds__(1024)
+// One wave per expert: base[c][e] = sum_{c' < c} counts[c'][e] (exclusive scan
+// over chunks, lane-contiguous runs), totals[e] = the expert's row count.
+__global__ void __launch_bounds__(256)
 k_chunk_scan(int32_t* __restrict__ counts_to_base, int64_t nchunks, int E,
-             int32_t* __restrict__ offsets) {
-  __shared__ int tot[kMaxExperts];
+             int32_t* __restrict__ totals) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;
+  const int64_t per = (nchunks + 63) / 64;
+  const int64_t c0 = lane * per;
+  int run = 0;
+  for (int64_t c = c0; c < c0 + per && c < nchunks; ++c) run += counts_to_base[c * E + e];
+  int incl = run;
+  for (int o = 1; o < 64; o <<= 1) {
+    int u = __shfl_up(incl, o);
+    if (lane >= o) incl += u;
+  }
+  int base = incl - run;
+  for (int64_t c = c0; c < c0 + per && c < nchunks; ++c) {
+    const int v = counts_to_base[c * E + e];
+    counts_to_base[c * E + e] = base;
+    base += v;
+  }
+  if (lane == 63) totals[e] = incl;
+}
+
+// One workgroup: expert_offsets = exclusive scan of totals (E <= 1024).
+__global__ void __launch_bounds__(1024)
+k_expert_offsets(const int32_t* __restrict__ totals, int E, int32_t* __restrict__ offsets) {
   __shared__ int wsum[16];
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += 1024) {
-    int run = 0;
-    for (int64_t c = 0; c < nchunks; ++c) {
-      int v = counts_to_base[c * E + e];
-      counts_to_base[c * E + e] = run;
-      run += v;
-    }
-    tot[e] = run;
-  }
-  __syncthreads();
-  // exclusive scan of tot over experts (E <= 1024: one value per thread)
-  int v = tid < E ? tot[tid] : 0;
+  const int v = tid < E ? totals[tid] : 0;
   int incl = v;
   for (int o = 1; o < 64; o <<= 1) {
     int u = __shfl_up(incl, o);
@@ -126,19 +138,14 @@ k_chunk_scan(int32_t* __restrict__ counts_to_base, int64_t nchunks, int E,
   __syncthreads();
   int base = 0;
   for (int w = 0; w < (tid >> 6); ++w) base += wsum[w];
-  const int excl = base + incl - v;
-  if (tid < E) offsets[tid] = excl;
-  if (tid == E - 1) offsets[E] = excl + v;
-  __syncthreads();
-  if (tid < E) tot[tid] = excl;
-  __syncthreads();
-  for (int e = tid; e < E; e += 1024)
-    for (int64_t c = 0; c < nchunks; ++c) counts_to_base[c * E + e] += tot[e];
+  if (tid < E) offsets[tid] = base + incl - v;
+  if (tid == E - 1) offsets[E] = base + incl;
 }
 
 __global__ void __launch_bounds__(64)
 k_scatter(const int32_t* __restrict__ ids, int64_t T, int E, int tk,
           const uint64_t* __restrict__ masks, const int32_t* __restrict__ base,
+          const int32_t* __restrict__ offsets,
           int32_t* __restrict__ perm_token, int32_t* __restrict__ inv_perm) {
   const int lane = threadIdx.x;
   const int64_t c = blockIdx.x;
@@ -147,27 +154,31 @@ k_scatter(const int32_t* __restrict__ ids, int64_t T, int E, int tk,
   const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
   for (int j = 0; j < tk; ++j) {
     const int e = ids[t * tk + j];
-    const int p = base[c * E + e] + __popcll(masks[c * E + e] & below);
+    const int p = offsets[e] + base[c * E + e] + __popcll(masks[c * E + e] & below);
     perm_token[p] = (int32_t)t;
     inv_perm[t * tk + j] = p;
   }
 }
 
-// out[t][n..n+8) = bf16(sum_j w[t][j] * y[inv_perm[t][j]][n..n+8)), float32 in slot order
+// out[t][n..n+8) = bf16(sum_j w[t][j] * y[inv_perm[t][j]][n..n+8)), float32
+// in slot order.  One block per token; its routing is read once.
 __global__ void __launch_bounds__(256)
 k_combine(const uint16_t* __restrict__ y, const int32_t* __restrict__ inv_perm,
           const float* __restrict__ tw, int64_t T, int tk, int64_t N, uint16_t* __restrict__ out) {
-  const int64_t chunks = N / 8;
-  const int64_t total = T * chunks;
-  for (int64_t e = blockIdx.x * 256LL + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-    const int64_t t = e / chunks;
-    const int64_t n = (e - t * chunks) * 8;
+  __shared__ int64_t rows[kMaxTopk];
+  __shared__ float wts[kMaxTopk];
+  const int64_t t = blockIdx.x;
+  if (threadIdx.x < tk) {
+    rows[threadIdx.x] = inv_perm[t * tk + threadIdx.x];
+    wts[threadIdx.x] = tw[t * tk + threadIdx.x];
+  }
+  __syncthreads();
+  for (int64_t n = threadIdx.x * 8LL; n < N; n += 256 * 8) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int j = 0; j < tk; ++j) {
-      const int64_t p = inv_perm[t * tk + j];
-      const float wj = tw[t * tk + j];
-      uint4 v = *reinterpret_cast<const uint4*>(y + p * N + n);
-      uint32_t u[4] = {v.x, v.y, v.z, v.w};
+      const float wj = wts[j];
+      const uint4 v = *reinterpret_cast<const uint4*>(y + rows[j] * N + n);
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         acc[2 * i] = __builtin_fmaf(wj, bf16_bits_to_f32(u[i] & 0xFFFFu), acc[2 * i]);
@@ -193,7 +204,7 @@ size_t moe_permute_workspace_size(int64_t T, int64_t E) {
   int64_t nchunks = (T + 63) / 64;
   if (nchunks < 1) nchunks = 1;
   return round_up((size_t)nchunks * (size_t)E * sizeof(uint64_t), 256) +
-         round_up((size_t)nchunks * (size_t)E * sizeof(int32_t), 256);
+         round_up((size_t)(nchunks + 1) * (size_t)E * sizeof(int32_t), 256);
 }
 
 int moe_permute(const float* logits, const float* bias, int64_t T, int64_t E, int64_t tk,
@@ -222,10 +233,12 @@ int moe_permute(const float* logits, const float* bias, int64_t T, int64_t E, in
   }
   k_route<<<(unsigned)((T + 3) / 4), 256, 0, s>>>(logits, bias, T, (int)E, (int)tk, topk_ids,
                                                   topk_w);
+  int32_t* totals = counts + (size_t)nchunks * E;
   k_route_masks<<<(unsigned)nchunks, 64, 0, s>>>(topk_ids, T, (int)E, (int)tk, masks, counts);
-  k_chunk_scan<<<1, 1024, 0, s>>>(counts, nchunks, (int)E, expert_offsets);
+  k_chunk_scan<<<(unsigned)((E + 3) / 4), 256, 0, s>>>(counts, nchunks, (int)E, totals);
+  k_expert_offsets<<<1, 1024, 0, s>>>(totals, (int)E, expert_offsets);
   k_scatter<<<(unsigned)nchunks, 64, 0, s>>>(topk_ids, T, (int)E, (int)tk, masks, counts,
-                                             perm_token, inv_perm);
+                                             expert_offsets, perm_token, inv_perm);
   return check_launch("moe_permute");
 }
 
@@ -238,10 +251,9 @@ int moe_unpermute_combine(const void* y, const int32_t* inv_perm, const float* t
   NV_REQUIRE(aligned(y, 16) && aligned(out, 16), NVFP4_ERR_ALIGN,
              "moe_unpermute_combine: misaligned pointer");
   hipStream_t s = as_stream(stream);
-  int64_t total = T * (N / 8);
-  int64_t blocks = (total + 255) / 256;
-  int64_t cap = 16LL * num_cus();
-  k_combine<<<(unsigned)(blocks < cap ? blocks : cap), 256, 0, s>>>(
+  NV_REQUIRE(T < (1LL << 31) && tk <= kMaxTopk, NVFP4_ERR_SHAPE,
+             "moe_unpermute_combine: need T < 2^31 and tk <= %d", kMaxTopk);
+  k_combine<<<(unsigned)T, 256, 0, s>>>(
       static_cast<const uint16_t*>(y), inv_perm, topk_w, T, (int)tk, N,
       static_cast<uint16_t*>(out));
   return check_launch("moe_unpermute_combine");

@@ -65,20 +65,50 @@ k_amax(const uint16_t* __restrict__ x, int64_t rows, int64_t ldx, int64_t tensor
       m = max(m, max(hi, lo));
     }
   }
-  m = wave_max_u32(m);
-  if ((tid & 63) == 0 && m) atomicMax(amax + blockIdx.z, m);
+  block_atomic_max<256>(m, amax + blockIdx.z);
+}
+
+// Contiguous tensors: flat loop, four independent 16-byte loads in flight
+// per thread (tensor t = blockIdx.y, n8 chunks of 8 elements each).
+__device__ __forceinline__ uint32_t absmax8(uint4 v) {
+  uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu, d = v.z & 0x7FFF7FFFu, e = v.w & 0x7FFF7FFFu;
+  uint32_t hi = max(max(a >> 16, b >> 16), max(d >> 16, e >> 16));
+  uint32_t lo = max(max(a & 0xFFFFu, b & 0xFFFFu), max(d & 0xFFFFu, e & 0xFFFFu));
+  return max(hi, lo);
+}
+
+__global__ void __launch_bounds__(256)
+k_amax_flat(const uint16_t* __restrict__ x, int64_t n8, int64_t tensor_stride,
+            uint32_t* __restrict__ amax) {
+  const uint4* xt = reinterpret_cast<const uint4*>(x + (int64_t)blockIdx.y * tensor_stride);
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = blockIdx.x * 256LL + threadIdx.x;
+  uint32_t m = 0;
+  for (; i + 3 * stride < n8; i += 4 * stride) {
+    const uint4 a = xt[i], b = xt[i + stride], c = xt[i + 2 * stride], d = xt[i + 3 * stride];
+    m = max(m, max(max(absmax8(a), absmax8(b)), max(absmax8(c), absmax8(d))));
+  }
+  for (; i < n8; i += stride) m = max(m, absmax8(xt[i]));
+  block_atomic_max<256>(m, amax + blockIdx.y);
 }
 
 // ---------------------------------------------------------------------------
 // Pass 1b: h = bf16(silu(gate) * up) from y = [gate | up] ([M][2I], row stride
 // ldy); writes h [M][I] and its amax.  silu(g) = g / (1 + exp(-g)), float32.
 // ---------------------------------------------------------------------------
+// silu(g) * u in float32 with the hardware exp2 and reciprocal (a few float32
+// ulps), then one rounding to bf16: the result is the correctly rounded bf16
+// value except when the float32 value lies within those ulps of a bf16
+// rounding boundary, i.e. at most one bf16 step away from it.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
 __device__ __forceinline__ uint32_t swiglu_pair(uint32_t g2, uint32_t u2) {
   float g0 = bf16_bits_to_f32(g2 & 0xFFFFu), g1 = bf16_bits_to_f32(g2 >> 16);
   float u0 = bf16_bits_to_f32(u2 & 0xFFFFu), u1 = bf16_bits_to_f32(u2 >> 16);
-  float h0 = g0 / (1.0f + expf(-g0)) * u0;
-  float h1 = g1 / (1.0f + expf(-g1)) * u1;
-  return f32_to_bf16_rne(h0) | (f32_to_bf16_rne(h1) << 16);
+  return f32_to_bf16_rne(silu_mul(g0, u0)) | (f32_to_bf16_rne(silu_mul(g1, u1)) << 16);
 }
 
 __global__ void __launch_bounds__(256)
@@ -109,8 +139,7 @@ k_swiglu_amax(const uint16_t* __restrict__ y, int64_t rows, int64_t ldy, int64_t
       m = max(m, max(hi, lo));
     }
   }
-  m = wave_max_u32(m);
-  if ((tid & 63) == 0 && m) atomicMax(amax, m);
+  block_atomic_max<256>(m, amax);
 }
 
 // ---------------------------------------------------------------------------
@@ -132,7 +161,7 @@ k_quantize(const uint16_t* __restrict__ x, int64_t rows, int64_t ldx, int64_t K,
            uint8_t* __restrict__ scales, float* __restrict__ g_out,
            uint64_t* __restrict__ partial, uint16_t* __restrict__ w_qdq) {
   // partial: [gridDim.x][K] per-workgroup channel sums (or NULL: no scores)
-  __shared__ uint64_t red[256 * 16];
+  extern __shared__ uint64_t red[];               // 256 * 16 entries when rows_per_iter > 1
   uint64_t* score = partial;
   const int tid = threadIdx.x;
   const int t = blockIdx.z;
@@ -152,11 +181,22 @@ k_quantize(const uint16_t* __restrict__ x, int64_t rows, int64_t ldx, int64_t K,
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0;
 
-  for (int64_t r = (int64_t)blockIdx.x * rows_per_iter + rsub; active && r < rows;
-       r += (int64_t)gridDim.x * rows_per_iter) {
+  const int64_t rstep = (int64_t)gridDim.x * rows_per_iter;
+  uint4 n0 = make_uint4(0, 0, 0, 0), n1 = n0;
+  int64_t r = (int64_t)blockIdx.x * rows_per_iter + rsub;
+  if (active && r < rows) {
     const uint16_t* xr = xt + r * ldx + (int64_t)c * 16;
-    uint4 v0 = *reinterpret_cast<const uint4*>(xr);
-    uint4 v1 = *reinterpret_cast<const uint4*>(xr + 8);
+    n0 = *reinterpret_cast<const uint4*>(xr);
+    n1 = *reinterpret_cast<const uint4*>(xr + 8);
+  }
+  for (; active && r < rows; r += rstep) {
+    // the next row's loads are issued before this row's arithmetic
+    const uint4 v0 = n0, v1 = n1;
+    if (r + rstep < rows) {
+      const uint16_t* xn = xt + (r + rstep) * ldx + (int64_t)c * 16;
+      n0 = *reinterpret_cast<const uint4*>(xn);
+      n1 = *reinterpret_cast<const uint4*>(xn + 8);
+    }
     uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     float xf[16];
     uint32_t bmax = 0;
@@ -249,15 +289,25 @@ k_quantize(const uint16_t* __restrict__ x, int64_t rows, int64_t ldx, int64_t K,
   }
 }
 
-// score[j] = sum over workgroups of partial[w][j]
+// score[j] += sum over workgroups of partial[w][j]: a block sums a tile of
+// 64 channels x 64 partial rows (four row groups, LDS combine), then one
+// 64-bit integer atomic per channel.  Integer sums: any order, same bits.
 __global__ void __launch_bounds__(256)
 k_score_reduce(const uint64_t* __restrict__ partial, int nparts, int64_t K,
                uint64_t* __restrict__ score) {
-  int64_t j = blockIdx.x * 256LL + threadIdx.x;
-  if (j >= K) return;
+  __shared__ uint64_t red4[4][64];
+  const int ch = threadIdx.x & 63, pg = threadIdx.x >> 6;
+  const int64_t j = blockIdx.x * 64LL + ch;
+  const int p0 = blockIdx.y * 64;
   uint64_t s = 0;
-  for (int w = 0; w < nparts; ++w) s += partial[(int64_t)w * K + j];
-  score[j] = s;
+  if (j < K)
+    for (int q = pg; q < 64 && p0 + q < nparts; q += 4) s += partial[(int64_t)(p0 + q) * K + j];
+  red4[pg][ch] = s;
+  __syncthreads();
+  if (pg == 0 && j < K) {
+    s = red4[0][ch] + red4[1][ch] + red4[2][ch] + red4[3][ch];
+    if (s) atomicAdd(reinterpret_cast<unsigned long long*>(score + j), (unsigned long long)s);
+  }
 }
 
 static unsigned grid_rows(int64_t rows, int rows_per_iter, int64_t cap) {
@@ -274,7 +324,7 @@ extern "C" {
 
 static int quant_grid(int64_t M, int64_t K) {
   RowTiling t16 = row_tiling(K / 16);
-  return (int)grid_rows(M, t16.rows_per_iter, 4LL * num_cus());
+  return (int)grid_rows(M, t16.rows_per_iter, 8LL * num_cus());
 }
 
 size_t nvfp4_quantize_act_workspace_size(int64_t M, int64_t K) {
@@ -319,6 +369,11 @@ int nvfp4_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, int glu
                                          static_cast<uint16_t*>(x_used), amax);
       src = static_cast<const uint16_t*>(x_used);
       ld = K;
+    } else if (ldx == K) {
+      const int64_t n8 = M * K / 8;
+      int64_t nb = (n8 + 1023) / 1024;
+      if (nb > 8LL * cus) nb = 8LL * cus;
+      k_amax_flat<<<dim3((unsigned)(nb > 0 ? nb : 1), 1, 1), 256, 0, s>>>(src, n8, 0, amax);
     } else {
       k_amax<<<grid, 256, 0, s>>>(src, M, ldx, 0, t8.chunks, t8.rows_per_iter, amax);
     }
@@ -326,9 +381,15 @@ int nvfp4_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, int glu
   RowTiling t16 = row_tiling(K / 16);
   const int nq = quant_grid(M, K);
   dim3 grid(nq, t16.col_groups, 1);
-  k_quantize<<<grid, 256, 0, s>>>(src, M, ld, K, 0, 1, t16.chunks, t16.rows_per_iter, amax,
-                                  codes, scales, g_x, score ? partial : nullptr, nullptr);
-  if (score) k_score_reduce<<<(unsigned)((K + 255) / 256), 256, 0, s>>>(partial, nq, K, score);
+  const size_t red_bytes = (score && t16.rows_per_iter > 1) ? 256 * 16 * sizeof(uint64_t) : 0;
+  k_quantize<<<grid, 256, red_bytes, s>>>(src, M, ld, K, 0, 1, t16.chunks, t16.rows_per_iter,
+                                          amax, codes, scales, g_x, score ? partial : nullptr,
+                                          nullptr);
+  if (score) {
+    fill_u64(score, K, 0ull, s);
+    k_score_reduce<<<dim3((unsigned)((K + 63) / 64), (unsigned)((nq + 63) / 64)), 256, 0, s>>>(
+        partial, nq, K, score);
+  }
   return check_launch("nvfp4_quantize_act");
 }
 
@@ -348,10 +409,13 @@ int nvfp4_qdq_weights(const void* w, int64_t E, int64_t N, int64_t K, uint8_t* c
   fill_u32(amax, E, 0u, s);
   const int cus = num_cus();
   const int64_t per_e = (8LL * cus + E - 1) / E;
-  RowTiling t8 = row_tiling(K / 8);
-  dim3 g1(grid_rows(N, t8.rows_per_iter, per_e > 1 ? per_e : 1), t8.col_groups, (unsigned)E);
-  k_amax<<<g1, 256, 0, s>>>(static_cast<const uint16_t*>(w), N, K, N * K, t8.chunks,
-                            t8.rows_per_iter, amax);
+  {
+    const int64_t n8 = N * K / 8;
+    int64_t nb = (n8 + 1023) / 1024;
+    if (nb > per_e) nb = per_e;
+    k_amax_flat<<<dim3((unsigned)(nb > 0 ? nb : 1), (unsigned)E, 1), 256, 0, s>>>(
+        static_cast<const uint16_t*>(w), n8, N * K, amax);
+  }
   RowTiling t16 = row_tiling(K / 16);
   dim3 g2(grid_rows(N, t16.rows_per_iter, per_e > 1 ? per_e : 1), t16.col_groups, (unsigned)E);
   k_quantize<<<g2, 256, 0, s>>>(static_cast<const uint16_t*>(w), N, K, K, N * K, (int)E,
