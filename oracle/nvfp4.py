@@ -44,8 +44,11 @@ def tensor_scale(A: np.float32) -> np.float32:
     return np.float32(np.float32(A) / SCALE_DEN)
 
 
-def quantize(x):
+def quantize(x, A=None):
     """Quantize a [M][K] tensor (K % 16 == 0) to NVFP4.
+
+    A: the tensor's absolute maximum, when x is a slice (rows or 16-aligned
+    column blocks) of a larger tensor; by default max |x|.
 
     Returns (codes uint8 [M][K] one code per element, scales uint8
     [M][K/16] E4M3 bytes, g float32, A float32).
@@ -62,7 +65,9 @@ def quantize(x):
     M, K = x.shape
     if K % BLOCK:
         raise ValueError("K must be a multiple of 16")
-    A = tensor_amax(x)
+    A = tensor_amax(x) if A is None else np.float32(A)
+    if x.size and tensor_amax(x) > A:
+        raise ValueError("A is below max |x|")
     g = tensor_scale(A)
     xf = x.astype(np.float32)                      # exact (bf16 values)
     xb = xf.reshape(M, K // BLOCK, BLOCK)

@@ -214,3 +214,15 @@ def test_weight_qdq_is_trainer_fake_quant():
     assert np.array_equal(g2, g_w)
     ok = np.repeat(scales >= 0x08, 16, axis=-1)
     assert np.array_equal((c2 & 7)[ok], (codes & 7)[ok])
+
+
+def test_quantize_slices_with_given_amax_match_whole_tensor():
+    rng = np.random.default_rng(15)
+    x = _rand_x(rng, 24, 96)
+    codes, scales, g, A = Q.quantize(x)
+    c1, s1, g1, _ = Q.quantize(x[5:11], A=A)                       # a row slice
+    assert np.array_equal(c1, codes[5:11]) and np.array_equal(s1, scales[5:11]) and g1 == g
+    c2, s2, _, _ = Q.quantize(x[:, 32:64], A=A)                    # a column-block slice
+    assert np.array_equal(c2, codes[:, 32:64]) and np.array_equal(s2, scales[:, 2:4])
+    with pytest.raises(ValueError):
+        Q.quantize(x, A=A / 2)
