@@ -44,16 +44,34 @@ def maxabs_err(y, ref):
     return np.max(np.abs(y - ref)) / m if m > 0 else np.max(np.abs(y))
 
 
+def bf16_ulp(v):
+    """Spacing of bf16 values at |v| (8 significant bits)."""
+    m, e = np.frexp(np.abs(v))
+    return np.where(m == 0, 2.0 ** -133, np.ldexp(1.0, np.maximum(e, -125) - 8))
+
+
 def assert_gemm_close(y, ref, tol=2e-3, min_exact=0.98):
-    """The output tolerance: row-normwise and max-abs-over-max relative error
-    both <= tol against the oracle's bf16-rounded float64 result, and most
-    elements bit-identical (float32 vs float64 accumulation differs by at most
-    one bf16 rounding step on a few elements)."""
+    """The output tolerance, against the oracle's float64 result rounded once
+    to bf16.  The GPU accumulates in float32 and rounds once to bf16, so an
+    element may land one bf16 step (up to 2^-7 relative) from the oracle's
+    when the two sums straddle a rounding boundary; near-zero outputs may
+    differ by float32 accumulation error, small on the row's scale.  So:
+      * row-normwise relative error <= tol;
+      * every element within one bf16 step of the oracle's value, or within
+        tol times the row's RMS;
+      * at least min_exact of the elements bit-identical."""
     assert y.shape == ref.shape
     assert np.all(np.isfinite(y))
     e1, e2 = rownorm_err(y, ref), maxabs_err(y, ref)
     exact = np.mean(y == ref)
     assert e1 <= tol, f"row-normwise error {e1:.3e}"
-    assert e2 <= tol, f"max-abs error {e2:.3e}"
+    d = np.abs(y - ref)
+    rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True)) if ref.ndim > 1 else np.sqrt(np.mean(ref * ref))
+    allowed = np.maximum(bf16_ulp(ref), tol * rms)
+    bad = d > allowed
+    if bad.any():
+        i = np.unravel_index(np.argmax(d / allowed), d.shape)
+        raise AssertionError(f"{int(bad.sum())} elements beyond one bf16 step; worst at {i}: "
+                             f"got {y[i]!r} want {ref[i]!r} (step {bf16_ulp(ref[i])!r})")
     assert exact >= min_exact, f"only {exact:.4f} of elements bit-identical"
     return e1, e2, exact
