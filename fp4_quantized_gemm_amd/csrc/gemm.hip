@@ -277,7 +277,7 @@ k_gemm_generic(GemmArgs p) {
 // 16 accumulators of a lane hold column l % 32, rows 8 (r/4) + 4 kg + r % 4.
 // ---------------------------------------------------------------------------
 namespace big {
-constexpr int BM = 256, BN = 256, BK = 64, NSTAGE = 2;
+constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int A_BYTES = BM * BK * 2;           // f16 [256][64]: 8 chunks/row, chunk c at c ^ (row & 7)
 constexpr int B_CODES = BN * 32;               // [256][32 B]: chunk c at c ^ ((row >> 2) & 1)
 constexpr int B_SCALES = BN * 4;               // [256][4 B]
@@ -285,10 +285,9 @@ constexpr int STAGE = A_BYTES + B_CODES + B_SCALES;   // 41984
 constexpr int KMAX = 128;                      // residual channels held in LDS
 constexpr int KSTEPS_MAX = 1024;               // K <= 65536
 constexpr int WSROW = KMAX * 2 + 16;           // bf16 row of the W_S tile (+pad)
-constexpr int WS_OFF = NSTAGE * STAGE;
 constexpr int OUTROW = BN * 2 + 16;            // bf16 output staging row (+pad)
-constexpr int LDS_MAIN = WS_OFF + BN * WSROW;  // 153600
-constexpr int LDS = LDS_MAIN > BM * OUTROW ? LDS_MAIN : BM * OUTROW;
+constexpr int OUT_ROWS = BM / 2;               // output staged in two halves
+constexpr int WS_BYTES = BN * WSROW > OUT_ROWS * OUTROW ? BN * WSROW : OUT_ROWS * OUTROW;
 }  // namespace big
 
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
@@ -316,7 +315,6 @@ __device__ __forceinline__ void scale_prep(uint32_t byte, float& sc, h2_t& mu) {
 }
 
 __device__ __forceinline__ void wait_vmem0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 __device__ __forceinline__ f32x16_t mfma32_f16(const u32x4& a, const u32x4& b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
                                                 __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
@@ -355,11 +353,17 @@ k_decode_a(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales
 __global__ void __launch_bounds__(512, 1)
 k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_tiles) {
   using namespace big;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS];
+  // The two k-step stages are separate LDS objects and the loop below is
+  // unrolled by two, so every access names its stage statically: the
+  // compiler can then tell the asynchronous global->LDS fill of one stage
+  // from the reads of the other and does not wait for that fill before
+  // computing on the current stage.
+  __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t wsl[WS_BYTES];   // W_S tile, then output staging
   __shared__ int32_t rows_src[BM];
   __shared__ int32_t s_local[KMAX];
   __shared__ int32_t j_first[KSTEPS_MAX + 1];     // first selected channel at or after step kt
-  uint8_t* const wsl = smem + WS_OFF;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -443,8 +447,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
     if (n >= p.N) n = p.N - 1;
     off_s = (uint32_t)n * Ks;
   }
-  auto issue_loads = [&](int buf, uint32_t k0) {
-    uint8_t* st = smem + buf * STAGE;
+  auto issue_loads = [&](uint8_t* st, uint32_t k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_global_load_lds(a_img + off_a[i] + k0 * 2, st + (i * 8 + wave) * 1024, 16, 0, 0);
@@ -464,13 +467,10 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
 
   const int swa = r32 & 7;                         // A rows = 32 i + r32 (+ multiples of 32)
   const int physb = kg ^ ((r32 >> 2) & 1);
-  issue_loads(0, 0);
-  wait_vmem0();
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) issue_loads(buf ^ 1, (uint32_t)(kt + 1) * BK);
-    const uint8_t* ab = smem + buf * STAGE;
+
+  // one k-step on stage `ab` while stage `nxt` fills with step kt + 1
+  auto kstep = [&](const uint8_t* ab, uint8_t* nxt, int kt) {
+    if (kt + 1 < nk) issue_loads(nxt, (uint32_t)(kt + 1) * BK);
     const uint8_t* bb = ab + A_BYTES;
     const uint8_t* sb = bb + B_CODES;
 
@@ -529,6 +529,14 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
 
     wait_vmem0();
     __syncthreads();
+  };
+
+  issue_loads(st0, 0);
+  wait_vmem0();
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {    // nk is even (K % 128 == 0)
+    kstep(st0, st1, kt);
+    kstep(st1, st0, kt + 1);
   }
 
   // epilogue: x g_x, residual K-extension (16 channels per MFMA), x g_w.
@@ -574,28 +582,34 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
     }
   }
 
-  // y = bf16(g_w * acc), staged through LDS for 16-byte row stores
+  // y = bf16(g_w * acc), staged through LDS (one 128-row half at a time, by
+  // the four waves that own it) for 16-byte row stores
   const float gw = p.g_w[e];
-  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int h = 0; h < 2; ++h) {
+    __syncthreads();
+    if (wm == h) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * 128 + 32 * i + 8 * (r >> 2) + 4 * kg + (r & 3);
-        const int col = wn * 64 + 32 * j + r32;
-        *reinterpret_cast<uint16_t*>(smem + row * OUTROW + 2 * col) =
-            (uint16_t)f32_to_bf16_rne(acc[i][j][r] * gw);
-      }
-  __syncthreads();
-  for (int q = tid; q < BM * (BN / 8); q += 512) {
-    const int row = q / (BN / 8), ch = q % (BN / 8);
-    const int64_t prow = p0 + row;
-    const int64_t n = n0 + ch * 8;
-    if (prow < e_hi && n < p.N)
-      *reinterpret_cast<uint4*>(p.y + prow * p.N + n) =
-          *reinterpret_cast<const uint4*>(smem + row * OUTROW + ch * 16);
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = 32 * i + 8 * (r >> 2) + 4 * kg + (r & 3);
+            const int col = wn * 64 + 32 * j + r32;
+            *reinterpret_cast<uint16_t*>(wsl + row * OUTROW + 2 * col) =
+                (uint16_t)f32_to_bf16_rne(acc[i][j][r] * gw);
+          }
+    }
+    __syncthreads();
+    for (int q = tid; q < OUT_ROWS * (BN / 8); q += 512) {
+      const int row = q / (BN / 8), ch = q % (BN / 8);
+      const int64_t prow = p0 + h * OUT_ROWS + row;
+      const int64_t n = n0 + ch * 8;
+      if (prow < e_hi && n < p.N)
+        *reinterpret_cast<uint4*>(p.y + prow * p.N + n) =
+            *reinterpret_cast<const uint4*>(wsl + row * OUTROW + ch * 16);
+    }
   }
 }
 
