@@ -278,8 +278,12 @@ k_gemm_generic(GemmArgs p) {
 // ---------------------------------------------------------------------------
 namespace big {
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int A_BYTES = BM * BK * 2;           // f16 [256][64]: 8 chunks/row, chunk c at c ^ (row & 7)
-constexpr int B_CODES = BN * 32;               // [256][32 B]: chunk c at c ^ ((row >> 2) & 1)
+// LDS reads of 16 bytes serve 16 lanes per pass over 64 four-byte banks, so
+// 16 consecutive rows of a fragment must land in 16 distinct 16-byte bank
+// groups: with 128-byte A rows two rows share a 256-byte bank line, hence the
+// A swizzle on row >> 1; with 32-byte B rows eight rows share one.
+constexpr int A_BYTES = BM * BK * 2;           // f16 [256][64]: 8 chunks/row, chunk c at c ^ ((row >> 1) & 7)
+constexpr int B_CODES = BN * 32;               // [256][32 B]: chunk c at c ^ ((row >> 3) & 1)
 constexpr int B_SCALES = BN * 4;               // [256][4 B]
 constexpr int STAGE = A_BYTES + B_CODES + B_SCALES;   // 41984
 constexpr int KMAX = 128;                      // residual channels held in LDS
@@ -432,12 +436,12 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int q = (i * 8 + wave) * 64 + lane;
-    const int r = q >> 3, c = (q & 7) ^ (r & 7);
+    const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
     off_a[i] = (uint32_t)rows_src[r] * K2 + 16u * c;
   }
   {
     const int q = wave * 64 + lane;
-    const int r = q >> 1, c = (q & 1) ^ ((r >> 2) & 1);
+    const int r = q >> 1, c = (q & 1) ^ ((r >> 3) & 1);
     int64_t n = n0 + r;
     if (n >= p.N) n = p.N - 1;
     off_b = (uint32_t)n * Kh + 16u * c;
@@ -465,8 +469,8 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int swa = r32 & 7;                         // A rows = 32 i + r32 (+ multiples of 32)
-  const int physb = kg ^ ((r32 >> 2) & 1);
+  const int swa = (r32 >> 1) & 7;                  // A rows = 32 i + r32 (+ multiples of 32)
+  const int physb = kg ^ ((r32 >> 3) & 1);
 
   // one k-step on stage `ab` while stage `nxt` fills with step kt + 1
   auto kstep = [&](const uint8_t* ab, uint8_t* nxt, int kt) {
@@ -481,7 +485,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
       const int jhi = j_first[kt + 1];
       const int row = tid & 255;
       const uint8_t* rowc = bb + row * 32;
-      const int sw = (row >> 2) & 1;
+      const int sw = (row >> 3) & 1;
       for (int j = j_first[kt] + (tid >> 8); j < jhi; j += 2) {
         const int c = s_local[j] - k0;
         const int byte = c >> 1;
