@@ -617,6 +617,249 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode-sized grouped GEMM: a few rows per expert, so the weights dominate
+// the traffic and every expert's weights should cross HBM once.  One
+// workgroup per (expert, 256 weight rows); each of its 4 waves streams 64
+// weight rows (4 blocks of 16) over K in chunks of 128 with register loads
+// two chunks ahead, and multiplies them with all of the expert's rows (token
+// tiles of 16, up to TMAX per pass) on 16x16x32 f16 MFMAs.  Both operands are
+// decoded from NVFP4 codes in registers (exact in f16), so no activation
+// image is needed.  Weight rows are the MFMA's M side, tokens its N side.
+//
+// Lane l covers weight (or token) row l % 16 and, within a chunk at k0,
+// k in [k0 + 32 (l / 16), +32) -- 16 code bytes, two block scales.  MFMA step
+// s (0..3) takes the lane's code dword s, i.e. k0 + 32 (l / 16) + 8 s + i in
+// the instruction's k slot 8 (l / 16) + i; both operands use this order.
+// The residual correction runs after the loop (bf16 MFMAs over the selected
+// channels, whose weights are copied to LDS as the chunks pass).
+// ---------------------------------------------------------------------------
+namespace dec {
+constexpr int ROWS = 256;
+constexpr int KC = 128;
+constexpr int TMAX = 2;
+constexpr int KMAX = 128;
+constexpr int WSROW = KMAX * 2 + 16;
+constexpr int CHUNKS_MAX = 512;
+}  // namespace dec
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma16_f16(const u32x4& a, const u32x4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma16_bf16(const u32x4& a, const u32x4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t dword_of(const uint4& v, int s) {
+  return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
+}
+
+struct DecChunk {
+  uint4 wc[4];             // weight codes, row blocks 0..3
+  uint32_t ws[4];          // their two block scales (low 16 bits)
+  uint4 tc[dec::TMAX];     // token codes, tiles 0..TMAX-1
+  uint32_t ts[dec::TMAX];
+};
+
+__global__ void __launch_bounds__(256, 2)
+k_gemm_decode(GemmArgs p, int n_blocks) {
+  using namespace dec;
+  __shared__ __attribute__((aligned(16))) uint8_t wsl[ROWS * WSROW];
+  __shared__ int32_t s_local[KMAX];
+  __shared__ int32_t jf[CHUNKS_MAX + 1];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int e = (int)blockIdx.x / n_blocks;
+  const int nb = (int)blockIdx.x - e * n_blocks;
+  int64_t e_lo = p.offsets[e], e_hi = p.offsets[e + 1];
+  e_lo = e_lo < 0 ? 0 : (e_lo > p.M_total ? p.M_total : e_lo);
+  e_hi = e_hi < e_lo ? e_lo : (e_hi > p.M_total ? p.M_total : e_hi);
+  const int64_t Me = e_hi - e_lo;
+  if (Me == 0) return;                       // uniform over the workgroup
+  const int64_t n0 = (int64_t)nb * ROWS;
+  const int64_t Kh = p.K / 2, Ks = p.K / 16;
+  const int nc = (int)(p.K / KC);
+  const int kk = p.k;
+
+  if (kk > 0) {
+    for (int j = tid; j < kk; j += 256) {
+      const int c = p.S[j];
+      s_local[j] = c < 0 ? 0 : (c >= p.K ? (int)p.K - 1 : c);
+    }
+    const int kpad = (kk + 31) & ~31;        // zero channels k .. next multiple of 32
+    for (int j = kk; j < kpad; ++j) *reinterpret_cast<uint16_t*>(wsl + tid * WSROW + 2 * j) = 0;
+    __syncthreads();
+    for (int c = tid; c <= nc; c += 256) {
+      int a = 0, b = kk;
+      while (a < b) {
+        const int m = (a + b) >> 1;
+        if (s_local[m] < c * KC) a = m + 1; else b = m;
+      }
+      jf[c] = a;
+    }
+    __syncthreads();
+  }
+
+  const uint8_t* wc = p.w_codes + (int64_t)e * p.N * Kh;
+  const uint8_t* wsc = p.w_scales + (int64_t)e * p.N * Ks;
+  uint32_t woff_c[4], woff_s[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    int64_t n = n0 + 64 * wave + 16 * b + r16;
+    if (n >= p.N) n = p.N - 1;
+    woff_c[b] = (uint32_t)(n * Kh) + 16u * kq;
+    woff_s[b] = (uint32_t)(n * Ks) + 2u * kq;
+  }
+  const float gx = *p.g_x;
+  const float gw = p.g_w[e];
+
+  for (int64_t t0 = 0; t0 < Me; t0 += 16 * TMAX) {
+    const int ntile = (int)((Me - t0 + 15) / 16 < TMAX ? (Me - t0 + 15) / 16 : TMAX);
+    int64_t src[TMAX];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      int64_t q = t0 + 16 * t + r16;
+      if (q >= Me) q = Me - 1;
+      const int64_t pr = e_lo + q;
+      int64_t sr = p.a_rows ? (int64_t)p.a_rows[pr] : pr;
+      src[t] = sr < 0 ? 0 : (sr >= p.M_src ? p.M_src - 1 : sr);
+    }
+    const bool extract = kk > 0 && t0 == 0;
+
+    auto load = [&](DecChunk& d, int c) {
+      c = c < nc ? c : nc - 1;               // past the end: re-read the last chunk
+      const uint32_t kc2 = (uint32_t)c * (KC / 2), kc16 = (uint32_t)c * (KC / 16);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        d.wc[b] = *reinterpret_cast<const uint4*>(wc + woff_c[b] + kc2);
+        d.ws[b] = *reinterpret_cast<const uint16_t*>(wsc + woff_s[b] + kc16);
+      }
+#pragma unroll
+      for (int t = 0; t < TMAX; ++t) {
+        d.tc[t] = *reinterpret_cast<const uint4*>(p.a_codes + src[t] * Kh + 16 * kq + kc2);
+        d.ts[t] = *reinterpret_cast<const uint16_t*>(p.a_scales + src[t] * Ks + 2 * kq + kc16);
+      }
+    };
+
+    f32x4_t acc[4][TMAX];
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int t = 0; t < TMAX; ++t) acc[b][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const DecChunk& d, int c) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4 tf[TMAX];
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+          if (t >= ntile) continue;
+          float sc;
+          h2_t mu;
+          scale_prep((d.ts[t] >> (8 * (s >> 1))) & 0xFFu, sc, mu);
+          tf[t] = decode8_f16(dword_of(d.tc[t], s), sc, mu);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          float sc;
+          h2_t mu;
+          scale_prep((d.ws[b] >> (8 * (s >> 1))) & 0xFFu, sc, mu);
+          const u32x4 wf = decode8_f16(dword_of(d.wc[b], s), sc, mu);
+#pragma unroll
+          for (int t = 0; t < TMAX; ++t)
+            if (t < ntile) acc[b][t] = mfma16_f16(wf, tf[t], acc[b][t]);
+        }
+      }
+      if (extract) {
+        // weights of the selected channels in this chunk -> W_S rows
+        const int k0 = c * KC;
+        for (int j = jf[c]; j < jf[c + 1]; ++j) {
+          const int ch = s_local[j] - k0;
+          if ((ch >> 5) != kq) continue;
+          const int sd = (ch >> 3) & 3, ii = ch & 7;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const uint32_t code = (dword_of(d.wc[b], sd) >> (4 * ii)) & 0xFu;
+            const float q = e2m1_unpack2<0>(code).x;
+            const float sv = e4m3_decode((d.ws[b] >> (8 * (sd >> 1))) & 0xFFu);
+            *reinterpret_cast<uint16_t*>(wsl + (64 * wave + 16 * b + r16) * WSROW + 2 * j) =
+                (uint16_t)(__float_as_uint(q * sv) >> 16);
+          }
+        }
+      }
+    };
+
+    DecChunk b0, b1, b2;
+    load(b0, 0);
+    load(b1, 1);
+    for (int c = 0; c < nc; c += 3) {
+      load(b2, c + 2);
+      compute(b0, c);
+      if (c + 1 >= nc) break;
+      load(b0, c + 3);
+      compute(b1, c + 1);
+      if (c + 2 >= nc) break;
+      load(b1, c + 4);
+      compute(b2, c + 2);
+    }
+
+    // epilogue: x g_x, residual (32 channels per MFMA), x g_w, store
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int t = 0; t < TMAX; ++t) acc[b][t] *= gx;
+    if (kk > 0) {
+      __syncthreads();                       // W_S complete
+      for (int cb = 0; cb < kk; cb += 32) {
+        const int slot = cb + 8 * kq;
+        u32x4 rf[TMAX];
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+          const uint16_t* rr = p.R + src[t] * kk + slot;
+          if ((kk & 7) == 0 && slot + 8 <= kk) {
+            const uint4 v = *reinterpret_cast<const uint4*>(rr);
+            rf[t] = u32x4{v.x, v.y, v.z, v.w};
+          } else {
+            uint32_t v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = (slot + q < kk) ? rr[q] : 0u;
+            rf[t] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
+                          v[6] | (v[7] << 16)};
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const uint4 v = *reinterpret_cast<const uint4*>(wsl + (64 * wave + 16 * b + r16) * WSROW + 2 * slot);
+          const u32x4 wf = u32x4{v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int t = 0; t < TMAX; ++t)
+            if (t < ntile) acc[b][t] = mfma16_bf16(wf, rf[t], acc[b][t]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+      const int64_t q = t0 + 16 * t + r16;
+      if (t >= ntile || q >= Me) continue;
+      uint16_t* yr = p.y + (e_lo + q) * p.N;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int64_t n = n0 + 64 * wave + 16 * b + 4 * kq;
+        if (n >= p.N) continue;
+        const f32x4_t v = acc[b][t];
+        const uint32_t lo = f32_to_bf16_rne(v[0] * gw) | (f32_to_bf16_rne(v[1] * gw) << 16);
+        const uint32_t hi = f32_to_bf16_rne(v[2] * gw) | (f32_to_bf16_rne(v[3] * gw) << 16);
+        *reinterpret_cast<uint2*>(yr + n) = make_uint2(lo, hi);
+      }
+    }
+  }
+}
+
 }  // namespace nvfp4
 
 using namespace nvfp4;
@@ -688,9 +931,18 @@ int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const
   // small shapes).  The large-tile path holds at most KMAX residual channels,
   // needs the f16 image of A in the workspace and 32-bit image offsets.
   const char* force = getenv("NVFP4RAC_GEMM");
+  // few rows per expert (decode): stream each expert's weights once
+  bool use_dec = M_total <= 48 * E;
   bool use_big = (M_total / big::BM) * n_tiles_big >= 2LL * num_cus();
-  if (force && strcmp(force, "big") == 0) use_big = true;
-  if (force && strcmp(force, "generic") == 0) use_big = false;
+  if (force && strcmp(force, "big") == 0) use_big = true, use_dec = false;
+  if (force && strcmp(force, "generic") == 0) use_big = false, use_dec = false;
+  if (force && strcmp(force, "decode") == 0) use_dec = true;
+  use_dec = use_dec && k <= dec::KMAX && K / dec::KC <= dec::CHUNKS_MAX;
+  if (use_dec) {
+    const int64_t n_blocks = (N + dec::ROWS - 1) / dec::ROWS;
+    k_gemm_decode<<<(unsigned)(E * n_blocks), 256, 0, s>>>(a, (int)n_blocks);
+    return check_launch("grouped_w4a4_gemm_rac");
+  }
   const size_t need_big = grouped_w4a4_gemm_rac_workspace_size(E, M_src, M_total, N, K, k);
   use_big = use_big && k <= big::KMAX && K / big::BK <= big::KSTEPS_MAX && ws_bytes >= need_big &&
             (uint64_t)M_src * K * 2 < (1ULL << 32);

@@ -190,7 +190,7 @@ def _gemm_case(rng, M_src, counts, N, K, k, gather):
     return host_vals(y), ref
 
 
-@pytest.fixture(params=["generic", "big"])
+@pytest.fixture(params=["generic", "big", "decode"])
 def gemm_kernel(request, monkeypatch):
     monkeypatch.setenv("NVFP4RAC_GEMM", request.param)
     return request.param
@@ -203,6 +203,7 @@ def gemm_kernel(request, monkeypatch):
     (96, [50, 46], 128, 256, 256, False),             # every channel compensated
     (500, [17, 0, 0, 400, 83], 272, 1024, 128, True),
     (700, [300, 1, 511, 0, 255], 528, 768, 64, True),  # several 256-row tiles, N tail
+    (64, [3, 0, 17, 33, 1, 0, 16, 40], 512, 1024, 64, True),  # decode-sized: 0-40 rows each
 ])
 def test_grouped_gemm_rac(dev, gemm_kernel, M_src, counts, N, K, k, gather):
     say(f"gemm[{gemm_kernel}] counts={counts} N={N} K={K} k={k} gather={gather}")
