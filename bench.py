@@ -12,15 +12,25 @@ down grouped GEMM with correction, and the combine.
 
 Prints ONE JSON line.  `value` = algorithmic GEMM flops of a step (2 * rows *
 N * (K + k) summed over both GEMMs) / wall time per step, in TFLOP/s.
-`roofline` covers the grouped GEMM kernel: algorithmic flops / its average
-launch duration, measured with HIP events on the launch stream over the
-timed steps, against the bf16 dense MFMA peak (the exact NVFP4 product runs
-on the bf16 matrix path).  `cpu_baseline` times the CPU oracle on a bounded
-sample of the same block.
+`roofline` covers the grouped GEMM call (grouped_w4a4_gemm_rac: its small
+operand-preparation kernels plus the main GEMM kernel), timed with HIP events
+on the launch stream over the timed steps:
+  * many rows per expert (prefill): algorithmic flops / duration against the
+    dense f16/bf16 MFMA peak (the exact NVFP4 product runs on that path);
+  * few rows per expert (decode): algorithmic bytes -- weights of experts
+    with rows, activation codes, residual rows, output -- / duration against
+    HBM bandwidth.
+`traffic` is the HBM byte count of the same calls from rocprofv3 counters
+(profiles/hbm_traffic.json), or null when the GEMM source has changed since
+they were taken.  `cpu_baseline` times the CPU oracle on a bounded sample of
+the same block.
+
+    python bench.py --calibrate-copy     # 1 GiB device copy, for counter scaling
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -44,7 +54,42 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=128)
     ap.add_argument("--cpu-experts", type=int, default=4)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device-to-device copy three times")
     return ap.parse_args()
+
+
+GEMM_SOURCE = os.path.join(ROOT, "fp4_quantized_gemm_amd", "csrc", "gemm.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def gemm_source_hash():
+    with open(GEMM_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def recorded_traffic(workload):
+    """HBM bytes per step of the two GEMM calls, from the committed counter
+    runs, if they were taken on the current GEMM source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("gemm_source_sha256") != gemm_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_step")
+
+
+def calibrate_copy():
+    import torch
+    n = 1 << 28
+    a = torch.ones(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n * 4, "copies": 3}), flush=True)
 
 
 def to_dev(bits, dev):
@@ -174,7 +219,12 @@ def run_gpu(cfg, wl, steps, warmup):
             rac[kk] = tm.mean_ms()
         rac = {"gemm1_ms_k": rac["k"], "gemm1_ms_k0": rac["0"],
                "overhead": rac["k"] / rac["0"] - 1.0}
-    return wall / steps * 1e3, stage_ms, rac
+    if cfg.kind == "dense":
+        counts = [cfg.T]
+    else:
+        o = F.moe_permute(logits, cfg.topk, bias)[2].cpu().numpy()
+        counts = list(o[1:] - o[:-1])
+    return wall / steps * 1e3, stage_ms, rac, counts
 
 
 def cpu_baseline(cfg, wl, tokens, experts):
@@ -215,22 +265,56 @@ def cpu_baseline(cfg, wl, tokens, experts):
             "sample": desc, "seconds": round(dt, 2)}
 
 
+def gemm_algorithmic_bytes(cfg, counts):
+    """Bytes one step's GEMM calls must move: NVFP4 weights (codes + E4M3
+    scales, 0.5625 B/elem) of experts that have rows, the activation codes of
+    every routed row, the residual rows, and the bf16 output."""
+    busy = sum(1 for c in counts if c > 0)
+    total = 0.0
+    for _, m, n, k, kk in cfg.gemm_shapes():
+        total += busy * n * k * 0.5625 + m * k * 0.5625 + m * kk * 2 + m * n * 2
+    return total
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
               f"multi-GPU path", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     import synth
 
     cfg = synth.get(args.config)
     wl = synth.make(cfg)
-    ms, stage_ms, rac = run_gpu(cfg, wl, args.steps, args.warmup)
+    ms, stage_ms, rac, counts = run_gpu(cfg, wl, args.steps, args.warmup)
     shapes = cfg.gemm_shapes()
     flops_step = cfg.gemm_flops()
     value = flops_step / (ms * 1e-3) / 1e12
     gemm_ms = stage_ms.get("gemm1", 0.0) + stage_ms.get("gemm2", 0.0)
-    achieved = flops_step / (gemm_ms * 1e-3) / 1e12 if gemm_ms > 0 else None
+    alg_bytes = gemm_algorithmic_bytes(cfg, counts)
+    decode = cfg.rows <= 48 * cfg.E and cfg.kind != "dense"
+    if decode:
+        achieved = alg_bytes / (gemm_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4)}
+        kernel = "grouped_w4a4_gemm_rac: k_gemm_decode"
+    else:
+        achieved = flops_step / (gemm_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "frac_of_fp4_peak": round(achieved / PEAK_FP4_TFLOPS, 4)}
+        # the library's choice for large workloads (on a 256-CU MI355X)
+        _, m, n, _, _ = shapes[0]
+        big = (m // 256) * ((n + 255) // 256) >= 512
+        kernel = ("grouped_w4a4_gemm_rac: k_decode_a + k_tile_prefix + k_gemm_big" if big
+                  else "grouped_w4a4_gemm_rac: k_tile_prefix + k_gemm_generic")
+    roof["traffic"] = recorded_traffic(cfg.name)
+    roof["kernel"] = kernel
+    roof["algorithmic_bytes"] = round(alg_bytes)
+    roof["gemm_ms_per_step"] = round(gemm_ms, 4)
     q_bytes = 2.5625 * cfg.T * cfg.H
     quant = {"quant1_GBps": q_bytes / (stage_ms["quant1"] * 1e-3) / 1e9}
     if "quant2" in stage_ms:
@@ -247,17 +331,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "storage": "nvfp4 (E2M1 + E4M3/16 + f32), decoded exactly to bf16 MFMA operands, f32 acc",
+        "dtype": "f16",
+        "storage": "nvfp4 (E2M1 + E4M3/16 + f32) decoded exactly to f16 MFMA operands, bf16 "
+                   "residual term, f32 accumulate",
         "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E,
                    "topk": cfg.topk, "inter": cfg.inter, "rac_k": [s[4] for s in shapes],
                    "gemms": [f"{n} {m}x{nn}x{k}" for n, m, nn, k, _ in shapes]},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2) if achieved else None,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4) if achieved else None,
-                     "traffic": None, "kernel": "k_gemm_rac",
-                     "frac_of_fp4_peak": round(achieved / PEAK_FP4_TFLOPS, 4) if achieved else None},
+        "roofline": roof,
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "quantizer": {k: round(v, 1) for k, v in quant.items()},
         "rac_overhead": {k: round(v, 4) for k, v in rac.items()},

@@ -621,26 +621,28 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
 // Decode-sized grouped GEMM: a few rows per expert, so the weights dominate
 // the traffic and every expert's weights should cross HBM once.  One
 // workgroup per (expert, 256 weight rows); each of its 4 waves streams 64
-// weight rows (4 blocks of 16) over K in chunks of 128 with register loads
-// two chunks ahead, and multiplies them with all of the expert's rows (token
-// tiles of 16, up to TMAX per pass) on 16x16x32 f16 MFMAs.  Both operands are
+// weight rows (4 blocks of 16) over K in chunks of 256 with register loads one
+// chunk ahead, and multiplies them with all of the expert's rows (token tiles
+// of 16, up to TMAX per pass) on 16x16x32 f16 MFMAs.  Both operands are
 // decoded from NVFP4 codes in registers (exact in f16), so no activation
 // image is needed.  Weight rows are the MFMA's M side, tokens its N side.
 //
 // Lane l covers weight (or token) row l % 16 and, within a chunk at k0,
-// k in [k0 + 32 (l / 16), +32) -- 16 code bytes, two block scales.  MFMA step
-// s (0..3) takes the lane's code dword s, i.e. k0 + 32 (l / 16) + 8 s + i in
-// the instruction's k slot 8 (l / 16) + i; both operands use this order.
+// k in [k0 + 64 (l / 16), +64): 32 code bytes and four block scales, so the
+// four lanes of a row read its whole 128-byte line of the chunk together (a
+// line split over two chunks was evicted from L2 between its halves).  MFMA
+// step s (0..7) takes the lane's code dword s, i.e. k0 + 64 (l / 16) + 8 s + i
+// in the instruction's k slot 8 (l / 16) + i; both operands use this order.
 // The residual correction runs after the loop (bf16 MFMAs over the selected
 // channels, whose weights are copied to LDS as the chunks pass).
 // ---------------------------------------------------------------------------
 namespace dec {
 constexpr int ROWS = 256;
-constexpr int KC = 128;
+constexpr int KC = 256;
 constexpr int TMAX = 2;
 constexpr int KMAX = 128;
 constexpr int WSROW = KMAX * 2 + 16;
-constexpr int CHUNKS_MAX = 512;
+constexpr int CHUNKS_MAX = 256;
 }  // namespace dec
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -654,14 +656,19 @@ __device__ __forceinline__ f32x4_t mfma16_bf16(const u32x4& a, const u32x4& b, f
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t dword_of(const uint4& v, int s) {
-  return s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w;
+// dword s (0..7) of a lane's 32 code bytes
+// (selects, not indexing: a runtime index would put the arrays in scratch)
+__device__ __forceinline__ uint32_t dword_of(const uint4 (&v)[2], int s) {
+  const uint32_t a = (s & 1) ? v[0].y : v[0].x, b = (s & 1) ? v[0].w : v[0].z;
+  const uint32_t c = (s & 1) ? v[1].y : v[1].x, d = (s & 1) ? v[1].w : v[1].z;
+  const uint32_t lo = (s & 2) ? b : a, hi = (s & 2) ? d : c;
+  return (s & 4) ? hi : lo;
 }
 
 struct DecChunk {
-  uint4 wc[4];             // weight codes, row blocks 0..3
-  uint32_t ws[4];          // their two block scales (low 16 bits)
-  uint4 tc[dec::TMAX];     // token codes, tiles 0..TMAX-1
+  uint4 wc[4][2];          // weight codes, row blocks 0..3, 32 bytes each
+  uint32_t ws[4];          // their four block scales
+  uint4 tc[dec::TMAX][2];  // token codes, tiles 0..TMAX-1
   uint32_t ts[dec::TMAX];
 };
 
@@ -683,7 +690,7 @@ k_gemm_decode(GemmArgs p, int n_blocks) {
   if (Me == 0) return;                       // uniform over the workgroup
   const int64_t n0 = (int64_t)nb * ROWS;
   const int64_t Kh = p.K / 2, Ks = p.K / 16;
-  const int nc = (int)(p.K / KC);
+  const int nc = (int)((p.K + KC - 1) / KC);
   const int kk = p.k;
 
   if (kk > 0) {
@@ -712,8 +719,8 @@ k_gemm_decode(GemmArgs p, int n_blocks) {
   for (int b = 0; b < 4; ++b) {
     int64_t n = n0 + 64 * wave + 16 * b + r16;
     if (n >= p.N) n = p.N - 1;
-    woff_c[b] = (uint32_t)(n * Kh) + 16u * kq;
-    woff_s[b] = (uint32_t)(n * Ks) + 2u * kq;
+    woff_c[b] = (uint32_t)(n * Kh);
+    woff_s[b] = (uint32_t)(n * Ks);
   }
   const float gx = *p.g_x;
   const float gw = p.g_w[e];
@@ -731,18 +738,34 @@ k_gemm_decode(GemmArgs p, int n_blocks) {
     }
     const bool extract = kk > 0 && t0 == 0;
 
+    // K is a multiple of 128: the lanes of a half chunk past the end (kq >= 2
+    // in the last chunk when K % 256 == 128) re-read the chunk's first half
+    // (offsets >= 0 since kq >= 2) and their products vanish: their weight
+    // codes are zeroed
     auto load = [&](DecChunk& d, int c) {
       c = c < nc ? c : nc - 1;               // past the end: re-read the last chunk
-      const uint32_t kc2 = (uint32_t)c * (KC / 2), kc16 = (uint32_t)c * (KC / 16);
+      // this lane's byte offsets within a row: codes and scales
+      int64_t o2 = (int64_t)c * (KC / 2) + 32 * kq, o16 = (int64_t)c * (KC / 16) + 4 * kq;
+      const bool tail = o2 >= Kh;            // only when K % 256 == 128 and kq >= 2
+      if (tail) o2 -= 64, o16 -= 8;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        d.wc[b] = *reinterpret_cast<const uint4*>(wc + woff_c[b] + kc2);
-        d.ws[b] = *reinterpret_cast<const uint16_t*>(wsc + woff_s[b] + kc16);
+        // weight codes are read exactly once: stream them past L2 (evict
+        // first) so they do not push out the scale lines, each of which
+        // serves eight chunks
+        const u32x4* src4 = reinterpret_cast<const u32x4*>(wc + woff_c[b] + o2);
+        const u32x4 c0 = __builtin_nontemporal_load(src4), c1 = __builtin_nontemporal_load(src4 + 1);
+        d.wc[b][0] = make_uint4(c0.x, c0.y, c0.z, c0.w);
+        d.wc[b][1] = make_uint4(c1.x, c1.y, c1.z, c1.w);
+        d.ws[b] = *reinterpret_cast<const uint32_t*>(wsc + woff_s[b] + o16);
+        if (tail) d.wc[b][0] = d.wc[b][1] = make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int t = 0; t < TMAX; ++t) {
-        d.tc[t] = *reinterpret_cast<const uint4*>(p.a_codes + src[t] * Kh + 16 * kq + kc2);
-        d.ts[t] = *reinterpret_cast<const uint16_t*>(p.a_scales + src[t] * Ks + 2 * kq + kc16);
+        const uint4* src4 = reinterpret_cast<const uint4*>(p.a_codes + src[t] * Kh + o2);
+        d.tc[t][0] = src4[0];
+        d.tc[t][1] = src4[1];
+        d.ts[t] = *reinterpret_cast<const uint32_t*>(p.a_scales + src[t] * Ks + o16);
       }
     };
 
@@ -754,7 +777,7 @@ k_gemm_decode(GemmArgs p, int n_blocks) {
 
     auto compute = [&](const DecChunk& d, int c) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < 8; ++s) {
         u32x4 tf[TMAX];
 #pragma unroll
         for (int t = 0; t < TMAX; ++t) {
@@ -780,8 +803,8 @@ k_gemm_decode(GemmArgs p, int n_blocks) {
         const int k0 = c * KC;
         for (int j = jf[c]; j < jf[c + 1]; ++j) {
           const int ch = s_local[j] - k0;
-          if ((ch >> 5) != kq) continue;
-          const int sd = (ch >> 3) & 3, ii = ch & 7;
+          if ((ch >> 6) != kq) continue;
+          const int sd = (ch >> 3) & 7, ii = ch & 7;
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
             const uint32_t code = (dword_of(d.wc[b], sd) >> (4 * ii)) & 0xFu;
@@ -794,18 +817,14 @@ k_gemm_decode(GemmArgs p, int n_blocks) {
       }
     };
 
-    DecChunk b0, b1, b2;
+    DecChunk b0, b1;
     load(b0, 0);
-    load(b1, 1);
-    for (int c = 0; c < nc; c += 3) {
-      load(b2, c + 2);
+    for (int c = 0; c < nc; c += 2) {
+      load(b1, c + 1);
       compute(b0, c);
       if (c + 1 >= nc) break;
-      load(b0, c + 3);
+      load(b0, c + 2);
       compute(b1, c + 1);
-      if (c + 2 >= nc) break;
-      load(b1, c + 4);
-      compute(b2, c + 2);
     }
 
     // epilogue: x g_x, residual (32 channels per MFMA), x g_w, store
