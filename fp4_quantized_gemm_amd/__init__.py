@@ -116,14 +116,15 @@ def _need(t, dtype, name):
 
 
 def nvfp4_qdq_weights(w, want_qdq=True):
-    """w [E][N][K] bf16 -> (codes [E][N][K/2] u8, scales [E][N][K/16] u8,
-    g_w [E] f32, w_qdq [E][N][K] bf16 or None)."""
+    """w [E][N][K] bf16 -> (codes [E][N][K/2] u8, scales [E][N/16][K/64][16][4]
+    u8 (block scales in 64-byte tiles of 16 rows x 64 columns), g_w [E] f32,
+    w_qdq [E][N][K] bf16 or None)."""
     L = _load()
     _need(w, torch.bfloat16, "w")
     E, N, K = w.shape
     dev = w.device
     codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=dev)
-    scales = torch.empty((E, N, K // 16), dtype=torch.uint8, device=dev)
+    scales = torch.empty((E, N // 16, K // 64, 16, 4), dtype=torch.uint8, device=dev)
     g_w = torch.empty(E, dtype=torch.float32, device=dev)
     w_qdq = torch.empty_like(w) if want_qdq else None
     ws = _ws(L.nvfp4_qdq_weights_workspace_size(E), dev)

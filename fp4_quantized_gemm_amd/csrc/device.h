@@ -114,6 +114,15 @@ __device__ __forceinline__ void block_atomic_max(uint32_t v, uint32_t* dst) {
   }
 }
 
+// Weight block scales are stored in 64-byte tiles, one per 16 rows x 64 k:
+// [N/16][K/64][16 rows][4 blocks].  A GEMM reads a row block's scales for a
+// stretch of K as whole tiles (row-major [N][K/16] would give each 64-k step
+// 4 bytes of every row and a 128-byte line shared by 32 steps).  Byte offset
+// of block kb (= k / 16) of row n, for K columns:
+__device__ __forceinline__ int64_t wscale_offset(int64_t n, int64_t kb, int64_t K) {
+  return (((n >> 4) * (K >> 6) + (kb >> 2)) << 6) + ((n & 15) << 2) + (kb & 3);
+}
+
 __device__ __forceinline__ int frexp_exponent(float a) {
   return (int)((__float_as_uint(a) >> 23) & 0xFFu) - 126;   // a normal and > 0
 }

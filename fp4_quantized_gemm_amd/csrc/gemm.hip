@@ -146,7 +146,8 @@ k_gemm_generic(GemmArgs p) {
     } else {
       int64_t n = n0 + (tid - kBM);
       if (n >= p.N) n = p.N - 1;
-      gsb = *reinterpret_cast<const uint2*>(wsc + n * Ks + k0 / 16);
+      const uint8_t* t0 = wsc + wscale_offset(n, k0 / 16, p.K);   // two 64-k tiles
+      gsb = make_uint2(*reinterpret_cast<const uint32_t*>(t0), *reinterpret_cast<const uint32_t*>(t0 + 64));
     }
     __syncthreads();
 #pragma unroll
@@ -224,7 +225,7 @@ k_gemm_generic(GemmArgs p) {
         if (ch[q] < 0) { v[q] = 0u; continue; }
         const uint32_t byte = wc[n * Kh + (ch[q] >> 1)];
         const float wq = e2m1_unpack2<0>((byte >> (4 * (ch[q] & 1))) & 0xFu).x;
-        const float ws = e4m3_decode(wsc[n * Ks + (ch[q] >> 4)]);
+        const float ws = e4m3_decode(wsc[wscale_offset(n, ch[q] >> 4, p.K)]);
         v[q] = __float_as_uint(wq * ws) >> 16;
       }
       B[j] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
@@ -449,7 +450,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   if (wave < 4) {
     int64_t n = n0 + wave * 64 + lane;
     if (n >= p.N) n = p.N - 1;
-    off_s = (uint32_t)n * Ks;
+    off_s = (uint32_t)wscale_offset(n, 0, p.K);   // + k0: the step's tile
   }
   auto issue_loads = [&](uint8_t* st, uint32_t k0) {
 #pragma unroll
@@ -457,7 +458,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
       __builtin_amdgcn_global_load_lds(a_img + off_a[i] + k0 * 2, st + (i * 8 + wave) * 1024, 16, 0, 0);
     __builtin_amdgcn_global_load_lds(wc + off_b + k0 / 2, st + A_BYTES + wave * 1024, 16, 0, 0);
     if (wave < 4)
-      __builtin_amdgcn_global_load_lds(wsc + off_s + k0 / 16, st + A_BYTES + B_CODES + wave * 256, 4,
+      __builtin_amdgcn_global_load_lds(wsc + off_s + k0, st + A_BYTES + B_CODES + wave * 256, 4,
                                        0, 0);
   };
 
@@ -720,7 +721,7 @@ k_gemm_decode(GemmArgs p, int n_blocks) {
     int64_t n = n0 + 64 * wave + 16 * b + r16;
     if (n >= p.N) n = p.N - 1;
     woff_c[b] = (uint32_t)(n * Kh);
-    woff_s[b] = (uint32_t)(n * Ks);
+    woff_s[b] = (uint32_t)wscale_offset(n, 0, p.K);
   }
   const float gx = *p.g_x;
   const float gw = p.g_w[e];
@@ -745,9 +746,11 @@ k_gemm_decode(GemmArgs p, int n_blocks) {
     auto load = [&](DecChunk& d, int c) {
       c = c < nc ? c : nc - 1;               // past the end: re-read the last chunk
       // this lane's byte offsets within a row: codes and scales
+      // (weight scales: the lane's 64-k tile, 4c + kq, of its row block)
       int64_t o2 = (int64_t)c * (KC / 2) + 32 * kq, o16 = (int64_t)c * (KC / 16) + 4 * kq;
+      int64_t og = ((int64_t)c * 4 + kq) * 64;
       const bool tail = o2 >= Kh;            // only when K % 256 == 128 and kq >= 2
-      if (tail) o2 -= 64, o16 -= 8;
+      if (tail) o2 -= 64, o16 -= 8, og -= 128;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         // weight codes are read exactly once: stream them past L2 (evict
@@ -757,7 +760,7 @@ k_gemm_decode(GemmArgs p, int n_blocks) {
         const u32x4 c0 = __builtin_nontemporal_load(src4), c1 = __builtin_nontemporal_load(src4 + 1);
         d.wc[b][0] = make_uint4(c0.x, c0.y, c0.z, c0.w);
         d.wc[b][1] = make_uint4(c1.x, c1.y, c1.z, c1.w);
-        d.ws[b] = *reinterpret_cast<const uint32_t*>(wsc + woff_s[b] + o16);
+        d.ws[b] = *reinterpret_cast<const uint32_t*>(wsc + woff_s[b] + og);
         if (tail) d.wc[b][0] = d.wc[b][1] = make_uint4(0, 0, 0, 0);
       }
 #pragma unroll

@@ -159,7 +159,7 @@ k_quantize(const uint16_t* __restrict__ x, int64_t rows, int64_t ldx, int64_t K,
            int64_t tensor_stride, int ntensors, int blocks, int rows_per_iter,
            const uint32_t* __restrict__ amax, uint8_t* __restrict__ codes,
            uint8_t* __restrict__ scales, float* __restrict__ g_out,
-           uint64_t* __restrict__ partial, uint16_t* __restrict__ w_qdq) {
+           uint64_t* __restrict__ partial, uint16_t* __restrict__ w_qdq, int tiled_scales) {
   // partial: [gridDim.x][K] per-workgroup channel sums (or NULL: no scores)
   extern __shared__ uint64_t red[];               // 256 * 16 entries when rows_per_iter > 1
   uint64_t* score = partial;
@@ -231,7 +231,10 @@ k_quantize(const uint16_t* __restrict__ x, int64_t rows, int64_t ldx, int64_t K,
     }
     const int64_t orow = row0 + r;
     *reinterpret_cast<uint2*>(codes + orow * (K / 2) + (int64_t)c * 8) = make_uint2(pk[0], pk[1]);
-    scales[orow * (K / 16) + c] = (uint8_t)sbyte;
+    if (tiled_scales)       // weights: 64-byte tiles per 16 rows x 64 k
+      scales[row0 * (K / 16) + wscale_offset(r, c, K)] = (uint8_t)sbyte;
+    else
+      scales[orow * (K / 16) + c] = (uint8_t)sbyte;
 
     if (score != nullptr || w_qdq != nullptr) {
       float qs[16];
@@ -384,7 +387,7 @@ int nvfp4_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, int glu
   const size_t red_bytes = (score && t16.rows_per_iter > 1) ? 256 * 16 * sizeof(uint64_t) : 0;
   k_quantize<<<grid, 256, red_bytes, s>>>(src, M, ld, K, 0, 1, t16.chunks, t16.rows_per_iter,
                                           amax, codes, scales, g_x, score ? partial : nullptr,
-                                          nullptr);
+                                          nullptr, 0);
   if (score) {
     fill_u64(score, K, 0ull, s);
     k_score_reduce<<<dim3((unsigned)((K + 63) / 64), (unsigned)((nq + 63) / 64)), 256, 0, s>>>(
@@ -398,8 +401,10 @@ int nvfp4_qdq_weights(const void* w, int64_t E, int64_t N, int64_t K, uint8_t* c
                       void* stream) {
   NV_REQUIRE(w && codes && scales && g_w && ws, NVFP4_ERR_NULL,
              "nvfp4_qdq_weights: w, codes, scales, g_w and ws are required");
-  NV_REQUIRE(E >= 1 && E <= 65535 && N >= 1 && K >= 32 && K % 32 == 0, NVFP4_ERR_SHAPE,
-             "nvfp4_qdq_weights: need 1 <= E <= 65535, N >= 1, K %% 32 == 0");
+  NV_REQUIRE(E >= 1 && E <= 65535 && N >= 16 && N % 16 == 0 && K >= 64 && K % 64 == 0,
+             NVFP4_ERR_SHAPE,
+             "nvfp4_qdq_weights: need 1 <= E <= 65535, N %% 16 == 0, K %% 64 == 0 "
+             "(N=%lld K=%lld)", (long long)N, (long long)K);
   NV_REQUIRE(aligned(w, 16) && aligned(codes, 8) && aligned(w_qdq, 16) && aligned(ws, 16),
              NVFP4_ERR_ALIGN, "nvfp4_qdq_weights: misaligned pointer");
   NV_REQUIRE(ws_bytes >= nvfp4_qdq_weights_workspace_size(E), NVFP4_ERR_WORKSPACE,
@@ -420,7 +425,7 @@ int nvfp4_qdq_weights(const void* w, int64_t E, int64_t N, int64_t K, uint8_t* c
   dim3 g2(grid_rows(N, t16.rows_per_iter, per_e > 1 ? per_e : 1), t16.col_groups, (unsigned)E);
   k_quantize<<<g2, 256, 0, s>>>(static_cast<const uint16_t*>(w), N, K, K, N * K, (int)E,
                                 t16.chunks, t16.rows_per_iter, amax, codes, scales, g_w,
-                                nullptr, static_cast<uint16_t*>(w_qdq));
+                                nullptr, static_cast<uint16_t*>(w_qdq), 1);
   return check_launch("nvfp4_qdq_weights");
 }
 

@@ -21,7 +21,7 @@ from . import (grouped_w4a4_gemm_rac, moe_permute, moe_unpermute_combine, nvfp4_
 @dataclass
 class QuantWeights:
     codes: torch.Tensor      # [E][N][K/2] u8
-    scales: torch.Tensor     # [E][N][K/16] u8
+    scales: torch.Tensor     # [E][N/16][K/64][16][4] u8 (tiled block scales)
     g: torch.Tensor          # [E] f32
     qdq: torch.Tensor        # [E][N][K] bf16 or None
 

@@ -73,14 +73,19 @@ const char* nvfp4_last_error(void);
  * §2.2 A, asymmetric W4A16 QAT).
  *
  * w      [E][N][K] bf16, K contiguous (each expert's weight, out x in).
- * codes  [E][N][K/2] packed E2M1.        scales [E][N][K/16] E4M3.
+ * codes  [E][N][K/2] packed E2M1, row-major.
+ * scales [E][N/16][K/64][16][4] E4M3 (E * N * K/16 bytes): the block scales
+ *        in 64-byte tiles, one per 16 rows x 64 columns; the scale of block
+ *        kb (columns 16 kb .. 16 kb + 15) of row n of expert e is at byte
+ *        e*N*K/16 + ((n/16) * (K/64) + kb/4) * 64 + (n%16) * 4 + kb%4.
+ *        The grouped GEMM reads whole tiles for a stretch of K.
  * g_w    [E] float32: per-expert tensor scale g = fp32(amax_e / 2688).
  * w_qdq  [E][N][K] bf16 or NULL: bf16(fp32(e2m1 * e4m3) * g), the weight the
  *        trainer's forward sees.
  * Scale recipe per 16-block (all float32, round to nearest even):
  *   s = e4m3((blockmax * 448) / amax);  code = e2m1(x * (2688 / (s * amax)))
  *   (s == 0 gives magnitude 0); the sign bit of a code is the sign of x.
- * Requires 1 <= E <= 65535, N >= 1, K >= 32, K % 32 == 0.
+ * Requires 1 <= E <= 65535, N % 16 == 0, K % 64 == 0.
  * ---------------------------------------------------------------------- */
 size_t nvfp4_qdq_weights_workspace_size(int64_t E);
 int nvfp4_qdq_weights(const void* w, int64_t E, int64_t N, int64_t K,
@@ -162,7 +167,8 @@ int moe_permute(const float* logits, const float* bias, int64_t T, int64_t E, in
  * in the bf16/fp16 operands of the matrix cores), float32 accumulation.
  * a_codes [M_src][K/2], a_scales [M_src][K/16], g_x [1]; a_rows [M_total] or
  * NULL (then M_src >= M_total); R_S [M_src][k] bf16 (NULL iff k == 0);
- * S [k] int32 ascending; w_codes [E][N][K/2], w_scales [E][N][K/16], g_w [E];
+ * S [k] int32 ascending; w_codes [E][N][K/2], w_scales [E][N/16][K/64][16][4]
+ * (the tiles nvfp4_qdq_weights writes), g_w [E];
  * expert_offsets [E+1] (device; off[0] = 0, off[E] = M_total); y [M_total][N]
  * bf16.  Requires K % 128 == 0, N % 16 == 0, 0 <= k <= K.
  * ---------------------------------------------------------------------- */

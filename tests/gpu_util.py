@@ -18,6 +18,19 @@ def host_vals(t: torch.Tensor) -> np.ndarray:
     return OF.bf16_bits_to_f64(host_bits(t))
 
 
+def tile_wscales(s: np.ndarray) -> np.ndarray:
+    """Row-major weight block scales [E][N][K/16] -> the library's tiles
+    [E][N/16][K/64][16][4] (a layout change only)."""
+    E, N, KB = s.shape
+    return np.ascontiguousarray(s.reshape(E, N // 16, 16, KB // 4, 4).transpose(0, 1, 3, 2, 4))
+
+
+def untile_wscales(t: np.ndarray) -> np.ndarray:
+    """The library's weight-scale tiles [E][N/16][K/64][16][4] -> [E][N][K/16]."""
+    E, NB, KG, _, _ = t.shape
+    return np.ascontiguousarray(t.transpose(0, 1, 3, 2, 4)).reshape(E, NB * 16, KG * 4)
+
+
 def bits_of(vals: np.ndarray) -> np.ndarray:
     return OF.f64_to_bf16_bits(vals)
 

@@ -69,10 +69,12 @@ def test_quantize_act_validation():
 
 def test_qdq_weights_validation():
     L = F.lib()
-    assert L.nvfp4_qdq_weights(FAKE, 0, 8, 64, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == ERR_SHAPE
-    assert L.nvfp4_qdq_weights(FAKE, 2, 8, 40, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == ERR_SHAPE
-    assert L.nvfp4_qdq_weights(None, 2, 8, 64, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == ERR_NULL
-    assert L.nvfp4_qdq_weights(FAKE, 2, 8, 64, FAKE, FAKE, FAKE, None, FAKE, 4, None) == ERR_WS
+    assert L.nvfp4_qdq_weights(FAKE, 0, 16, 64, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == ERR_SHAPE
+    # scales are tiled per 16 rows x 64 columns: N % 16 and K % 64
+    assert L.nvfp4_qdq_weights(FAKE, 2, 24, 64, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == ERR_SHAPE
+    assert L.nvfp4_qdq_weights(FAKE, 2, 16, 96, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == ERR_SHAPE
+    assert L.nvfp4_qdq_weights(None, 2, 16, 64, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == ERR_NULL
+    assert L.nvfp4_qdq_weights(FAKE, 2, 16, 64, FAKE, FAKE, FAKE, None, FAKE, 4, None) == ERR_WS
 
 
 def test_select_validation():

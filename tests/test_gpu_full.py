@@ -30,7 +30,8 @@ from oracle import formats as OF
 from oracle import gemm as OG
 from oracle import moe as OM
 from oracle import nvfp4 as OQ
-from tests.gpu_util import assert_gemm_close, f32_bits, host_bits, host_vals, to_dev_bf16
+from tests.gpu_util import (assert_gemm_close, f32_bits, host_bits, host_vals, to_dev_bf16,
+                             untile_wscales)
 
 pytestmark = pytest.mark.gpu
 
@@ -59,7 +60,8 @@ def check_weights(w_bits, wq, experts, rng, n_rows=256):
         r = np.arange(N) if N <= n_rows else np.sort(rng.choice(N, n_rows, replace=False))
         c, s, _, _ = OQ.quantize(w[r], A=OQ.tensor_amax(w))
         assert np.array_equal(OQ.unpack_codes(wq.codes[e][r].cpu().numpy()), c), f"expert {e} codes"
-        assert np.array_equal(wq.scales[e][r].cpu().numpy(), s), f"expert {e} scales"
+        s_gpu = untile_wscales(wq.scales[e:e + 1].cpu().numpy())[0]
+        assert np.array_equal(s_gpu[r], s), f"expert {e} scales"
 
 
 def check_activation(x, st, k, rows, blocks):

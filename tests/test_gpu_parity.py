@@ -17,7 +17,7 @@ from oracle import gemm as OG
 from oracle import moe as OM
 from oracle import nvfp4 as OQ
 from tests.gpu_util import (assert_gemm_close, f32_bits, heavy_bf16, host_bits, host_vals,
-                            to_dev_bf16)
+                            tile_wscales, to_dev_bf16, untile_wscales)
 
 pytestmark = pytest.mark.gpu
 
@@ -98,7 +98,7 @@ def test_quantize_glu(dev, M, I):
     check_quant_against_oracle(q, h_gpu)                 # teacher-forced on the GPU's h
 
 
-@pytest.mark.parametrize("E,N,K", [(1, 16, 32), (3, 48, 96), (2, 130, 512)])
+@pytest.mark.parametrize("E,N,K", [(1, 16, 64), (3, 48, 192), (2, 144, 512)])
 def test_qdq_weights_bitexact(dev, E, N, K):
     say(f"qdq E={E} N={N} K={K}")
     rng = np.random.default_rng(E * N + K)
@@ -109,7 +109,8 @@ def test_qdq_weights_bitexact(dev, E, N, K):
     torch.cuda.synchronize()
     rc, rs, rg, rq = OQ.qdq_weights(w)
     assert np.array_equal(OQ.unpack_codes(codes.cpu().numpy()), rc)
-    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert scales.shape == (E, N // 16, K // 64, 16, 4)
+    assert np.array_equal(untile_wscales(scales.cpu().numpy()), rs)
     assert np.array_equal(f32_bits(g_w.cpu().numpy()), f32_bits(rg))
     assert np.array_equal(host_bits(w_qdq), OF.f64_to_bf16_bits(rq))
 
@@ -185,7 +186,7 @@ def _gemm_case(rng, M_src, counts, N, K, k, gather):
         cu(a_rows) if gather else None,
         to_dev_bf16(OF.f64_to_bf16_bits(qa["R_S"])) if k else None,
         cu(qa["S"]) if k else None,
-        cu(OQ.pack_codes(wc)), cu(ws), cu(gw), cu(offs), M_total=M_total)
+        cu(OQ.pack_codes(wc)), cu(tile_wscales(ws)), cu(gw), cu(offs), M_total=M_total)
     torch.cuda.synchronize()
     return host_vals(y), ref
 
