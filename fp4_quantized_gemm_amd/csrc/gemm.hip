@@ -21,6 +21,7 @@
 // the dot products unchanged.
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 #include "device.h"
 #include "runtime.h"
@@ -642,7 +643,6 @@ constexpr int ROWS = 256;
 constexpr int KC = 256;
 constexpr int TMAX = 2;
 constexpr int KMAX = 128;
-constexpr int WSROW = KMAX * 2 + 16;
 constexpr int CHUNKS_MAX = 256;
 }  // namespace dec
 
@@ -669,16 +669,22 @@ __device__ __forceinline__ uint32_t dword_of(const uint4 (&v)[2], int s) {
 struct DecChunk {
   uint4 wc[4][2];          // weight codes, row blocks 0..3, 32 bytes each
   uint32_t ws[4];          // their four block scales
-  uint4 tc[dec::TMAX][2];  // token codes, tiles 0..TMAX-1
-  uint32_t ts[dec::TMAX];
+  uint2 tc[dec::TMAX];     // token codes of this wave's two MFMA steps
+  uint32_t ts[dec::TMAX];  // the token rows' four block scales
 };
 
+// Dynamic LDS: token fragments [2][TMAX][8 steps][64 lanes][16 B], then the
+// W_S tile [256][wsrow] (wsrow = 2 * k rounded up to 32, + 16; none for k = 0).
+constexpr int kDecTokBytes = 2 * dec::TMAX * 8 * 64 * 16;
+
 __global__ void __launch_bounds__(256, 2)
-k_gemm_decode(GemmArgs p, int n_blocks) {
+k_gemm_decode(GemmArgs p, int n_blocks, int wsrow) {
   using namespace dec;
-  __shared__ __attribute__((aligned(16))) uint8_t wsl[ROWS * WSROW];
+  extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
   __shared__ int32_t s_local[KMAX];
   __shared__ int32_t jf[CHUNKS_MAX + 1];
+  uint8_t* const tok = dsm;
+  uint8_t* const wsl = dsm + kDecTokBytes;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, kq = lane >> 4;
@@ -700,7 +706,7 @@ k_gemm_decode(GemmArgs p, int n_blocks) {
       s_local[j] = c < 0 ? 0 : (c >= p.K ? (int)p.K - 1 : c);
     }
     const int kpad = (kk + 31) & ~31;        // zero channels k .. next multiple of 32
-    for (int j = kk; j < kpad; ++j) *reinterpret_cast<uint16_t*>(wsl + tid * WSROW + 2 * j) = 0;
+    for (int j = kk; j < kpad; ++j) *reinterpret_cast<uint16_t*>(wsl + tid * wsrow + 2 * j) = 0;
     __syncthreads();
     for (int c = tid; c <= nc; c += 256) {
       int a = 0, b = kk;
@@ -741,35 +747,36 @@ k_gemm_decode(GemmArgs p, int n_blocks) {
 
     // K is a multiple of 128: the lanes of a half chunk past the end (kq >= 2
     // in the last chunk when K % 256 == 128) re-read the chunk's first half
-    // (offsets >= 0 since kq >= 2) and their products vanish: their weight
-    // codes are zeroed
-    auto load = [&](DecChunk& d, int c) {
-      c = c < nc ? c : nc - 1;               // past the end: re-read the last chunk
+    // (offsets >= 0 since kq >= 2) and their products vanish: their token
+    // fragments are zero (zeroing the loaded weight registers instead would
+    // make the compiler wait for those loads).  Token codes: each wave loads
+    // (and decodes for the whole workgroup) only its MFMA steps 2 wave and
+    // 2 wave + 1.
+    // the loads of chunk c in six parts (weight row blocks 0..3: codes and
+    // scales; token tiles 0..TMAX-1), issued one per MFMA step of the chunk
+    // before: issued in one burst right after the barrier, all eight waves of
+    // a CU stalled for thousands of cycles at vector-memory issue
+    auto load_part = [&](DecChunk& d, int c, int part) {
       // this lane's byte offsets within a row: codes and scales
       // (weight scales: the lane's 64-k tile, 4c + kq, of its row block)
       int64_t o2 = (int64_t)c * (KC / 2) + 32 * kq, o16 = (int64_t)c * (KC / 16) + 4 * kq;
       int64_t og = ((int64_t)c * 4 + kq) * 64;
       const bool tail = o2 >= Kh;            // only when K % 256 == 128 and kq >= 2
       if (tail) o2 -= 64, o16 -= 8, og -= 128;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        // weight codes are read exactly once: stream them past L2 (evict
-        // first) so they do not push out the scale lines, each of which
-        // serves eight chunks
-        const u32x4* src4 = reinterpret_cast<const u32x4*>(wc + woff_c[b] + o2);
-        const u32x4 c0 = __builtin_nontemporal_load(src4), c1 = __builtin_nontemporal_load(src4 + 1);
-        d.wc[b][0] = make_uint4(c0.x, c0.y, c0.z, c0.w);
-        d.wc[b][1] = make_uint4(c1.x, c1.y, c1.z, c1.w);
-        d.ws[b] = *reinterpret_cast<const uint32_t*>(wsc + woff_s[b] + og);
-        if (tail) d.wc[b][0] = d.wc[b][1] = make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int t = 0; t < TMAX; ++t) {
-        const uint4* src4 = reinterpret_cast<const uint4*>(p.a_codes + src[t] * Kh + o2);
-        d.tc[t][0] = src4[0];
-        d.tc[t][1] = src4[1];
+      if (part < 4) {
+        const uint4* src4 = reinterpret_cast<const uint4*>(wc + woff_c[part] + o2);
+        d.wc[part][0] = src4[0];
+        d.wc[part][1] = src4[1];
+        d.ws[part] = *reinterpret_cast<const uint32_t*>(wsc + woff_s[part] + og);
+      } else if (part - 4 < TMAX) {
+        const int t = part - 4;
+        d.tc[t] = *reinterpret_cast<const uint2*>(p.a_codes + src[t] * Kh + o2 + 8 * wave);
         d.ts[t] = *reinterpret_cast<const uint32_t*>(p.a_scales + src[t] * Ks + o16);
       }
+    };
+    auto load = [&](DecChunk& d, int c) {
+#pragma unroll
+      for (int part = 0; part < 4 + TMAX; ++part) load_part(d, c, part);
     };
 
     f32x4_t acc[4][TMAX];
@@ -778,18 +785,38 @@ k_gemm_decode(GemmArgs p, int n_blocks) {
 #pragma unroll
       for (int t = 0; t < TMAX; ++t) acc[b][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](const DecChunk& d, int c) {
+    // token fragment of tile t, step s, this lane, in buffer `buf`
+    auto frag = [&](int buf, int t, int s) {
+      return tok + ((((buf * TMAX + t) * 8 + s) * 64 + lane) << 4);
+    };
+
+    // chunk c's arithmetic; with NEXT, the parts of chunk cn are loaded into
+    // dn along the way (part s before MFMA step s)
+    auto compute = [&](const DecChunk& d, int c, DecChunk& dn, int cn, auto next) {
+      constexpr bool NEXT = decltype(next)::value;
+      const int buf = c & 1;
+      // decode this wave's two steps of every token tile for the workgroup;
+      // the barrier also ends every wave's reads of this buffer two chunks ago
+#pragma unroll
+      for (int t = 0; t < TMAX; ++t) {
+        if (t >= ntile) continue;
+        float sc;
+        h2_t mu;
+        scale_prep((d.ts[t] >> (8 * wave)) & 0xFFu, sc, mu);
+        u32x4 f0 = decode8_f16(d.tc[t].x, sc, mu), f1 = decode8_f16(d.tc[t].y, sc, mu);
+        if ((int64_t)c * KC + 64 * kq >= p.K) f0 = f1 = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(frag(buf, t, 2 * wave)) = f0;
+        *reinterpret_cast<u32x4*>(frag(buf, t, 2 * wave + 1)) = f1;
+      }
+      __syncthreads();
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
+        // token tiles first: their fragments are decoded first next chunk
+        if (NEXT && s < 4 + TMAX) load_part(dn, cn, (s + 4) % (4 + TMAX));
         u32x4 tf[TMAX];
 #pragma unroll
-        for (int t = 0; t < TMAX; ++t) {
-          if (t >= ntile) continue;
-          float sc;
-          h2_t mu;
-          scale_prep((d.ts[t] >> (8 * (s >> 1))) & 0xFFu, sc, mu);
-          tf[t] = decode8_f16(dword_of(d.tc[t], s), sc, mu);
-        }
+        for (int t = 0; t < TMAX; ++t)
+          if (t < ntile) tf[t] = *reinterpret_cast<const u32x4*>(frag(buf, t, s));
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           float sc;
@@ -813,21 +840,29 @@ k_gemm_decode(GemmArgs p, int n_blocks) {
             const uint32_t code = (dword_of(d.wc[b], sd) >> (4 * ii)) & 0xFu;
             const float q = e2m1_unpack2<0>(code).x;
             const float sv = e4m3_decode((d.ws[b] >> (8 * (sd >> 1))) & 0xFFu);
-            *reinterpret_cast<uint16_t*>(wsl + (64 * wave + 16 * b + r16) * WSROW + 2 * j) =
+            *reinterpret_cast<uint16_t*>(wsl + (64 * wave + 16 * b + r16) * wsrow + 2 * j) =
                 (uint16_t)(__float_as_uint(q * sv) >> 16);
           }
         }
       }
     };
 
+    // steady state loading one chunk ahead, then the last one or two chunks
+    // (no load past the end)
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
     DecChunk b0, b1;
     load(b0, 0);
-    for (int c = 0; c < nc; c += 2) {
-      load(b1, c + 1);
-      compute(b0, c);
-      if (c + 1 >= nc) break;
-      load(b0, c + 2);
-      compute(b1, c + 1);
+    int c = 0;
+    for (; c + 2 < nc; c += 2) {
+      compute(b0, c, b1, c + 1, yes());
+      compute(b1, c + 1, b0, c + 2, yes());
+    }
+    if (c + 1 < nc) {
+      compute(b0, c, b1, c + 1, yes());
+      compute(b1, c + 1, b0, 0, no());
+    } else {
+      compute(b0, c, b1, 0, no());
     }
 
     // epilogue: x g_x, residual (32 channels per MFMA), x g_w, store
@@ -856,7 +891,7 @@ k_gemm_decode(GemmArgs p, int n_blocks) {
         }
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          const uint4 v = *reinterpret_cast<const uint4*>(wsl + (64 * wave + 16 * b + r16) * WSROW + 2 * slot);
+          const uint4 v = *reinterpret_cast<const uint4*>(wsl + (64 * wave + 16 * b + r16) * wsrow + 2 * slot);
           const u32x4 wf = u32x4{v.x, v.y, v.z, v.w};
 #pragma unroll
           for (int t = 0; t < TMAX; ++t)
@@ -962,7 +997,21 @@ int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const
   use_dec = use_dec && k <= dec::KMAX && K / dec::KC <= dec::CHUNKS_MAX;
   if (use_dec) {
     const int64_t n_blocks = (N + dec::ROWS - 1) / dec::ROWS;
-    k_gemm_decode<<<(unsigned)(E * n_blocks), 256, 0, s>>>(a, (int)n_blocks);
+    const int wsrow = k > 0 ? (int)(((k + 31) & ~31) * 2 + 16) : 0;
+    const size_t lds = (size_t)kDecTokBytes + (size_t)dec::ROWS * wsrow;
+    // dynamic LDS above 64 KB needs the kernel's limit raised (once per device)
+    static int dec_lds_limit[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+      return fail(NVFP4_ERR_HIP, "grouped_w4a4_gemm_rac: hipGetDevice failed");
+    if ((size_t)dec_lds_limit[dev] < lds) {
+      const int want = (int)kDecTokBytes + dec::ROWS * (dec::KMAX * 2 + 16);
+      if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_decode),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, want) != hipSuccess)
+        return fail(NVFP4_ERR_HIP, "grouped_w4a4_gemm_rac: cannot raise the LDS limit");
+      dec_lds_limit[dev] = want;
+    }
+    k_gemm_decode<<<(unsigned)(E * n_blocks), 256, lds, s>>>(a, (int)n_blocks, wsrow);
     return check_launch("grouped_w4a4_gemm_rac");
   }
   const size_t need_big = grouped_w4a4_gemm_rac_workspace_size(E, M_src, M_total, N, K, k);
