@@ -378,8 +378,21 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   const int kg = lane >> 5, r32 = lane & 31;
 
   // tile order: groups of 4 row tiles x all column tiles, so the workgroups
-  // in flight share A and weight tiles through L2
-  const int v = (int)blockIdx.x;
+  // in flight share A and weight tiles through L2.  Workgroup b runs on XCD
+  // b % 8 (each XCD has its own L2), so each XCD takes a contiguous range of
+  // that order, counted over the real tiles (the grid is sized for the most
+  // padding tiles the expert boundaries can add; the rest exit).
+  int v;
+  {
+    const int real_m = p.tile_prefix[p.E];
+    const int real_blocks = ((real_m + 3) / 4) * 4 * n_tiles;
+    const int per_xcd = (real_blocks + 7) / 8;
+    const int b = (int)blockIdx.x;
+    const int loc = b >> 3;
+    if (loc >= per_xcd) return;
+    v = (b & 7) * per_xcd + loc;
+    if (v >= real_blocks) return;
+  }
   const int group = 4 * n_tiles;
   const int gi = v / group, gr = v - gi * group;
   if (4 * gi >= m_tiles) return;
@@ -1024,7 +1037,7 @@ int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const
     if (nb > 16LL * num_cus()) nb = 16LL * num_cus();
     k_decode_a<<<(unsigned)nb, 256, 0, s>>>(a_codes, a_scales, M_src, K, img);
     k_tile_prefix<<<1, 1024, 0, s>>>(expert_offsets, (int)E, M_total, big::BM, prefix);
-    const int64_t nblk = ((m_tiles_big + 3) / 4) * 4 * n_tiles_big;
+    const int64_t nblk = (((m_tiles_big + 3) / 4) * 4 * n_tiles_big + 7) / 8 * 8;
     k_gemm_big<<<(unsigned)nblk, 512, 0, s>>>(a, reinterpret_cast<const uint8_t*>(img),
                                              (int)n_tiles_big, (int)m_tiles_big);
   } else {
