@@ -656,7 +656,7 @@ constexpr int ROWS = 256;
 constexpr int KC = 256;
 constexpr int TMAX = 2;
 constexpr int KMAX = 128;
-constexpr int CHUNKS_MAX = 256;
+constexpr int CHUNKS_MAX = 64;            // K <= 16384
 }  // namespace dec
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -689,26 +689,34 @@ struct DecChunk {
 // Dynamic LDS: token fragments [2][TMAX][8 steps][64 lanes][16 B], then the
 // W_S tile [256][wsrow] (wsrow = 2 * k rounded up to 32, + 16; none for k = 0).
 constexpr int kDecTokBytes = 2 * dec::TMAX * 8 * 64 * 16;
+constexpr int kDecStaticLds = 4 * dec::KMAX + 32 * dec::CHUNKS_MAX + 2 * (4 * dec::CHUNKS_MAX + 1);
+constexpr int kLdsPerCu = 160 * 1024;
 
 __global__ void __launch_bounds__(256, 2)
-k_gemm_decode(GemmArgs p, int n_blocks, int wsrow) {
+k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
   using namespace dec;
   extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
   __shared__ int32_t s_local[KMAX];
-  __shared__ int32_t jf[CHUNKS_MAX + 1];
+  // selected columns as a bitmap over K (rounded up to whole chunks), and
+  // rank64[g] = number of selected columns below column 64 g
+  __shared__ uint32_t sel_bm[8 * CHUNKS_MAX];
+  __shared__ uint16_t rank64[4 * CHUNKS_MAX + 1];
   uint8_t* const tok = dsm;
   uint8_t* const wsl = dsm + kDecTokBytes;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, kq = lane >> 4;
-  const int e = (int)blockIdx.x / n_blocks;
-  const int nb = (int)blockIdx.x - e * n_blocks;
+  // workgroup (e, g) takes the expert's row blocks g * bpw .. + bpw
+  const int groups = (n_blocks + bpw - 1) / bpw;
+  const int e = (int)blockIdx.x / groups;
+  const int g = (int)blockIdx.x - e * groups;
+  const int blk_lo = g * bpw;
+  const int nbw = n_blocks - blk_lo < bpw ? n_blocks - blk_lo : bpw;
   int64_t e_lo = p.offsets[e], e_hi = p.offsets[e + 1];
   e_lo = e_lo < 0 ? 0 : (e_lo > p.M_total ? p.M_total : e_lo);
   e_hi = e_hi < e_lo ? e_lo : (e_hi > p.M_total ? p.M_total : e_hi);
   const int64_t Me = e_hi - e_lo;
-  if (Me == 0) return;                       // uniform over the workgroup
-  const int64_t n0 = (int64_t)nb * ROWS;
+  if (Me == 0 || nbw <= 0) return;           // uniform over the workgroup
   const int64_t Kh = p.K / 2, Ks = p.K / 16;
   const int nc = (int)((p.K + KC - 1) / KC);
   const int kk = p.k;
@@ -720,33 +728,42 @@ k_gemm_decode(GemmArgs p, int n_blocks, int wsrow) {
     }
     const int kpad = (kk + 31) & ~31;        // zero channels k .. next multiple of 32
     for (int j = kk; j < kpad; ++j) *reinterpret_cast<uint16_t*>(wsl + tid * wsrow + 2 * j) = 0;
+    for (int w = tid; w < 8 * nc; w += 256) sel_bm[w] = 0u;
     __syncthreads();
-    for (int c = tid; c <= nc; c += 256) {
+    // (S is strictly ascending, so bit ranks are the indices j)
+    for (int j = tid; j < kk; j += 256) atomicOr(&sel_bm[s_local[j] >> 5], 1u << (s_local[j] & 31));
+    for (int g = tid; g <= 4 * nc; g += 256) {
       int a = 0, b = kk;
       while (a < b) {
         const int m = (a + b) >> 1;
-        if (s_local[m] < c * KC) a = m + 1; else b = m;
+        if (s_local[m] < g * 64) a = m + 1; else b = m;
       }
-      jf[c] = a;
+      rank64[g] = (uint16_t)a;
     }
     __syncthreads();
   }
 
   const uint8_t* wc = p.w_codes + (int64_t)e * p.N * Kh;
   const uint8_t* wsc = p.w_scales + (int64_t)e * p.N * Ks;
-  uint32_t woff_c[4], woff_s[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    int64_t n = n0 + 64 * wave + 16 * b + r16;
-    if (n >= p.N) n = p.N - 1;
-    woff_c[b] = (uint32_t)(n * Kh);
-    woff_s[b] = (uint32_t)wscale_offset(n, 0, p.K);
-  }
+  // load addresses = a uniform offset (row block, chunk) + a per-lane
+  // offset fixed over the stream: code byte 32 kq of row r16, scale byte
+  // 4 r16 + 64 kq of the row block's tile (weight scales are tiled per 16
+  // rows x 64 columns, so row block rb starts at byte rb / 16 * K)
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t lane_c0 = (uint32_t)(r16 * Kh + 32 * kq);
+  const uint32_t lane_s0 = (uint32_t)(4 * r16 + 64 * kq);
+  const bool half_last = (p.K % KC) != 0;    // the last chunk holds 128 columns
   const float gx = *p.g_x;
   const float gw = p.g_w[e];
 
+  // position in the workgroup's chunk stream: local row block, chunk
+  struct Pos {
+    int blk, c;
+  };
+  auto advance = [&](Pos q) { return q.c + 1 == nc ? Pos{q.blk + 1, 0} : Pos{q.blk, q.c + 1}; };
+
   for (int64_t t0 = 0; t0 < Me; t0 += 16 * TMAX) {
-    const int ntile = (int)((Me - t0 + 15) / 16 < TMAX ? (Me - t0 + 15) / 16 : TMAX);
+    const int ntile_rt = (int)((Me - t0 + 15) / 16 < TMAX ? (Me - t0 + 15) / 16 : TMAX);
     int64_t src[TMAX];
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
@@ -756,7 +773,6 @@ k_gemm_decode(GemmArgs p, int n_blocks, int wsrow) {
       int64_t sr = p.a_rows ? (int64_t)p.a_rows[pr] : pr;
       src[t] = sr < 0 ? 0 : (sr >= p.M_src ? p.M_src - 1 : sr);
     }
-    const bool extract = kk > 0 && t0 == 0;
 
     // K is a multiple of 128: the lanes of a half chunk past the end (kq >= 2
     // in the last chunk when K % 256 == 128) re-read the chunk's first half
@@ -765,168 +781,218 @@ k_gemm_decode(GemmArgs p, int n_blocks, int wsrow) {
     // make the compiler wait for those loads).  Token codes: each wave loads
     // (and decodes for the whole workgroup) only its MFMA steps 2 wave and
     // 2 wave + 1.
-    // the loads of chunk c in six parts (weight row blocks 0..3: codes and
+    // the loads of chunk q in six parts (weight row blocks 0..3: codes and
     // scales; token tiles 0..TMAX-1), issued one per MFMA step of the chunk
     // before: issued in one burst right after the barrier, all eight waves of
     // a CU stalled for thousands of cycles at vector-memory issue
-    auto load_part = [&](DecChunk& d, int c, int part) {
-      // this lane's byte offsets within a row: codes and scales
-      // (weight scales: the lane's 64-k tile, 4c + kq, of its row block)
-      int64_t o2 = (int64_t)c * (KC / 2) + 32 * kq, o16 = (int64_t)c * (KC / 16) + 4 * kq;
-      int64_t og = ((int64_t)c * 4 + kq) * 64;
-      const bool tail = o2 >= Kh;            // only when K % 256 == 128 and kq >= 2
-      if (tail) o2 -= 64, o16 -= 8, og -= 128;
-      if (part < 4) {
-        const uint4* src4 = reinterpret_cast<const uint4*>(wc + woff_c[part] + o2);
-        d.wc[part][0] = src4[0];
-        d.wc[part][1] = src4[1];
-        d.ws[part] = *reinterpret_cast<const uint32_t*>(wsc + woff_s[part] + og);
-      } else if (part - 4 < TMAX) {
-        const int t = part - 4;
-        d.tc[t] = *reinterpret_cast<const uint2*>(p.a_codes + src[t] * Kh + o2 + 8 * wave);
-        d.ts[t] = *reinterpret_cast<const uint32_t*>(p.a_scales + src[t] * Ks + o16);
-      }
-    };
-    auto load = [&](DecChunk& d, int c) {
-#pragma unroll
-      for (int part = 0; part < 4 + TMAX; ++part) load_part(d, c, part);
-    };
-
-    f32x4_t acc[4][TMAX];
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int t = 0; t < TMAX; ++t) acc[b][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    // token fragment of tile t, step s, this lane, in buffer `buf`
-    auto frag = [&](int buf, int t, int s) {
-      return tok + ((((buf * TMAX + t) * 8 + s) * 64 + lane) << 4);
-    };
-
-    // chunk c's arithmetic; with NEXT, the parts of chunk cn are loaded into
-    // dn along the way (part s before MFMA step s)
-    auto compute = [&](const DecChunk& d, int c, DecChunk& dn, int cn, auto next) {
-      constexpr bool NEXT = decltype(next)::value;
-      const int buf = c & 1;
-      // decode this wave's two steps of every token tile for the workgroup;
-      // the barrier also ends every wave's reads of this buffer two chunks ago
-#pragma unroll
-      for (int t = 0; t < TMAX; ++t) {
-        if (t >= ntile) continue;
-        float sc;
-        h2_t mu;
-        scale_prep((d.ts[t] >> (8 * wave)) & 0xFFu, sc, mu);
-        u32x4 f0 = decode8_f16(d.tc[t].x, sc, mu), f1 = decode8_f16(d.tc[t].y, sc, mu);
-        if ((int64_t)c * KC + 64 * kq >= p.K) f0 = f1 = u32x4{0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(frag(buf, t, 2 * wave)) = f0;
-        *reinterpret_cast<u32x4*>(frag(buf, t, 2 * wave + 1)) = f1;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        // token tiles first: their fragments are decoded first next chunk
-        if (NEXT && s < 4 + TMAX) load_part(dn, cn, (s + 4) % (4 + TMAX));
-        u32x4 tf[TMAX];
-#pragma unroll
-        for (int t = 0; t < TMAX; ++t)
-          if (t < ntile) tf[t] = *reinterpret_cast<const u32x4*>(frag(buf, t, s));
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          float sc;
-          h2_t mu;
-          scale_prep((d.ws[b] >> (8 * (s >> 1))) & 0xFFu, sc, mu);
-          const u32x4 wf = decode8_f16(dword_of(d.wc[b], s), sc, mu);
-#pragma unroll
-          for (int t = 0; t < TMAX; ++t)
-            if (t < ntile) acc[b][t] = mfma16_f16(wf, tf[t], acc[b][t]);
-        }
-      }
-      if (extract) {
-        // weights of the selected channels in this chunk -> W_S rows
-        const int k0 = c * KC;
-        for (int j = jf[c]; j < jf[c + 1]; ++j) {
-          const int ch = s_local[j] - k0;
-          if ((ch >> 6) != kq) continue;
-          const int sd = (ch >> 3) & 7, ii = ch & 7;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const uint32_t code = (dword_of(d.wc[b], sd) >> (4 * ii)) & 0xFu;
-            const float q = e2m1_unpack2<0>(code).x;
-            const float sv = e4m3_decode((d.ws[b] >> (8 * (sd >> 1))) & 0xFFu);
-            *reinterpret_cast<uint16_t*>(wsl + (64 * wave + 16 * b + r16) * wsrow + 2 * j) =
-                (uint16_t)(__float_as_uint(q * sv) >> 16);
-          }
-        }
-      }
-    };
-
-    // steady state loading one chunk ahead, then the last one or two chunks
-    // (no load past the end)
-    using yes = std::integral_constant<bool, true>;
-    using no = std::integral_constant<bool, false>;
-    DecChunk b0, b1;
-    load(b0, 0);
-    int c = 0;
-    for (; c + 2 < nc; c += 2) {
-      compute(b0, c, b1, c + 1, yes());
-      compute(b1, c + 1, b0, c + 2, yes());
-    }
-    if (c + 1 < nc) {
-      compute(b0, c, b1, c + 1, yes());
-      compute(b1, c + 1, b0, 0, no());
-    } else {
-      compute(b0, c, b1, 0, no());
-    }
-
-    // epilogue: x g_x, residual (32 channels per MFMA), x g_w, store
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int t = 0; t < TMAX; ++t) acc[b][t] *= gx;
-    if (kk > 0) {
-      __syncthreads();                       // W_S complete
-      for (int cb = 0; cb < kk; cb += 32) {
-        const int slot = cb + 8 * kq;
-        u32x4 rf[TMAX];
-#pragma unroll
-        for (int t = 0; t < TMAX; ++t) {
-          const uint16_t* rr = p.R + src[t] * kk + slot;
-          if ((kk & 7) == 0 && slot + 8 <= kk) {
-            const uint4 v = *reinterpret_cast<const uint4*>(rr);
-            rf[t] = u32x4{v.x, v.y, v.z, v.w};
-          } else {
-            uint32_t v[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = (slot + q < kk) ? rr[q] : 0u;
-            rf[t] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
-                          v[6] | (v[7] << 16)};
-          }
-        }
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const uint4 v = *reinterpret_cast<const uint4*>(wsl + (64 * wave + 16 * b + r16) * wsrow + 2 * slot);
-          const u32x4 wf = u32x4{v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int t = 0; t < TMAX; ++t)
-            if (t < ntile) acc[b][t] = mfma16_bf16(wf, rf[t], acc[b][t]);
-        }
-      }
-    }
+    // per-lane offsets as values of this pass (else the prologue's load
+    // addresses are hoisted out of the pass loop and held in registers)
+    uint32_t lane_c = lane_c0, lane_s = lane_s0;
+    asm volatile("" : "+v"(lane_c), "+v"(lane_s));
+    uint32_t lane_tc[TMAX], lane_ts[TMAX];
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
-      const int64_t q = t0 + 16 * t + r16;
-      if (t >= ntile || q >= Me) continue;
-      uint16_t* yr = p.y + (e_lo + q) * p.N;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int64_t n = n0 + 64 * wave + 16 * b + 4 * kq;
-        if (n >= p.N) continue;
-        const f32x4_t v = acc[b][t];
-        const uint32_t lo = f32_to_bf16_rne(v[0] * gw) | (f32_to_bf16_rne(v[1] * gw) << 16);
-        const uint32_t hi = f32_to_bf16_rne(v[2] * gw) | (f32_to_bf16_rne(v[3] * gw) << 16);
-        *reinterpret_cast<uint2*>(yr + n) = make_uint2(lo, hi);
-      }
+      lane_tc[t] = (uint32_t)(src[t] * Kh) + 8 * wave + 32 * kq;
+      lane_ts[t] = (uint32_t)(src[t] * Ks) + 4 * kq;
     }
+    // the chunk stream for ntile token tiles (a constant, so the unrolled
+    // MFMA steps hold no branches)
+    auto run = [&](auto ntc) __attribute__((always_inline)) {
+      constexpr int ntile = decltype(ntc)::value;
+      auto load_part = [&](DecChunk& d, Pos q, int part) __attribute__((always_inline)) {
+        // lanes kq >= 2 of a last half chunk re-read the chunk's first half
+        const bool tl = half_last && q.c == nc - 1 && kq >= 2;
+        if (part < 4) {
+          // a row block past N (N % 16 == 0) reads the last one instead
+          int64_t rb = (int64_t)(blk_lo + q.blk) * ROWS + 64 * wave_u + 16 * part;
+          if (rb >= p.N) rb = p.N - 16;
+          const uint8_t* cb = wc + (uint32_t)(rb * Kh) + (uint32_t)q.c * (KC / 2);
+          const uint8_t* sb = wsc + (uint32_t)((rb >> 4) * p.K) + (uint32_t)q.c * (KC / 64) * 64;
+          const uint4* src4 = reinterpret_cast<const uint4*>(cb + (lane_c - (tl ? 64u : 0u)));
+          d.wc[part][0] = src4[0];
+          d.wc[part][1] = src4[1];
+          d.ws[part] = *reinterpret_cast<const uint32_t*>(sb + (lane_s - (tl ? 128u : 0u)));
+        } else if (part - 4 < TMAX) {
+          const int t = part - 4;
+          d.tc[t] = *reinterpret_cast<const uint2*>(p.a_codes + (uint32_t)q.c * (KC / 2) +
+                                                    (lane_tc[t] - (tl ? 64u : 0u)));
+          d.ts[t] = *reinterpret_cast<const uint32_t*>(p.a_scales + (uint32_t)q.c * (KC / 16) +
+                                                       (lane_ts[t] - (tl ? 8u : 0u)));
+        }
+      };
+      auto load = [&](DecChunk& d, Pos q) __attribute__((always_inline)) {
+  #pragma unroll
+        for (int part = 0; part < 4 + TMAX; ++part) load_part(d, q, part);
+      };
+
+      f32x4_t acc[4][TMAX];
+  #pragma unroll
+      for (int b = 0; b < 4; ++b)
+  #pragma unroll
+        for (int t = 0; t < TMAX; ++t) acc[b][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+      // token fragment of tile t, step s, this lane, in buffer `buf`
+      auto frag = [&](int buf, int t, int s) {
+        return tok + ((((buf * TMAX + t) * 8 + s) * 64 + lane) << 4);
+      };
+
+      // the block's epilogue: x g_x, residual (32 channels per MFMA), x g_w,
+      // store; then the accumulators restart for the next block
+      auto finish = [&](int blk) __attribute__((always_inline)) {
+        const int64_t n0 = (int64_t)(blk_lo + blk) * ROWS;
+  #pragma unroll
+        for (int b = 0; b < 4; ++b)
+  #pragma unroll
+          for (int t = 0; t < TMAX; ++t) acc[b][t] *= gx;
+        if (kk > 0) {
+          __syncthreads();                     // W_S complete
+          for (int cb = 0; cb < kk; cb += 32) {
+            const int slot = cb + 8 * kq;
+            u32x4 rf[TMAX];
+  #pragma unroll
+            for (int t = 0; t < TMAX; ++t) {
+              const uint16_t* rr = p.R + src[t] * kk + slot;
+              if ((kk & 7) == 0 && slot + 8 <= kk) {
+                const uint4 v = *reinterpret_cast<const uint4*>(rr);
+                rf[t] = u32x4{v.x, v.y, v.z, v.w};
+              } else {
+                uint32_t v[8];
+  #pragma unroll
+                for (int q = 0; q < 8; ++q) v[q] = (slot + q < kk) ? rr[q] : 0u;
+                rf[t] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
+                              v[6] | (v[7] << 16)};
+              }
+            }
+  #pragma unroll
+            for (int b = 0; b < 4; ++b) {
+              const uint4 v = *reinterpret_cast<const uint4*>(wsl + (64 * wave + 16 * b + r16) * wsrow + 2 * slot);
+              const u32x4 wf = u32x4{v.x, v.y, v.z, v.w};
+  #pragma unroll
+              for (int t = 0; t < TMAX; ++t)
+                if (t < ntile) acc[b][t] = mfma16_bf16(wf, rf[t], acc[b][t]);
+            }
+          }
+        }
+  #pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+          const int64_t q = t0 + 16 * t + r16;
+          if (t >= ntile || q >= Me) continue;
+          uint16_t* yr = p.y + (e_lo + q) * p.N;
+  #pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int64_t n = n0 + 64 * wave + 16 * b + 4 * kq;
+            if (n >= p.N) continue;
+            const f32x4_t v = acc[b][t];
+            const uint32_t lo = f32_to_bf16_rne(v[0] * gw) | (f32_to_bf16_rne(v[1] * gw) << 16);
+            const uint32_t hi = f32_to_bf16_rne(v[2] * gw) | (f32_to_bf16_rne(v[3] * gw) << 16);
+            *reinterpret_cast<uint2*>(yr + n) = make_uint2(lo, hi);
+          }
+        }
+  #pragma unroll
+        for (int b = 0; b < 4; ++b)
+  #pragma unroll
+          for (int t = 0; t < TMAX; ++t) acc[b][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      };
+
+      // chunk q's arithmetic (buffer parity buf); with NEXT, the parts of
+      // chunk qn are loaded into dn along the way (part s before MFMA step s);
+      // after a block's last chunk, its epilogue
+      auto compute = [&](const DecChunk& d, Pos q, int buf, DecChunk& dn, Pos qn, auto next) __attribute__((always_inline)) {
+        constexpr bool NEXT = decltype(next)::value;
+        const int c = q.c;
+        // decode this wave's two steps of every token tile for the workgroup;
+        // the barrier also ends every wave's reads of this buffer two chunks ago
+  #pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+          if (t >= ntile) continue;
+          float sc;
+          h2_t mu;
+          scale_prep((d.ts[t] >> (8 * wave)) & 0xFFu, sc, mu);
+          u32x4 f0 = decode8_f16(d.tc[t].x, sc, mu), f1 = decode8_f16(d.tc[t].y, sc, mu);
+          if ((int64_t)c * KC + 64 * kq >= p.K) f0 = f1 = u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(frag(buf, t, 2 * wave)) = f0;
+          *reinterpret_cast<u32x4*>(frag(buf, t, 2 * wave + 1)) = f1;
+        }
+        __syncthreads();
+  #pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          // token tiles first: their fragments are decoded first next chunk
+          if (NEXT && s < 4 + TMAX) load_part(dn, qn, (s + 4) % (4 + TMAX));
+          u32x4 tf[TMAX];
+  #pragma unroll
+          for (int t = 0; t < TMAX; ++t)
+            if (t < ntile) tf[t] = *reinterpret_cast<const u32x4*>(frag(buf, t, s));
+  #pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            float sc;
+            h2_t mu;
+            scale_prep((d.ws[b] >> (8 * (s >> 1))) & 0xFFu, sc, mu);
+            const u32x4 wf = decode8_f16(dword_of(d.wc[b], s), sc, mu);
+  #pragma unroll
+            for (int t = 0; t < TMAX; ++t)
+              if (t < ntile) acc[b][t] = mfma16_f16(wf, tf[t], acc[b][t]);
+          }
+        }
+        if (kk > 0) {
+          // weights of the selected channels in this chunk -> W_S rows (each
+          // wave writes, and later reads, only its own 64 rows): each lane
+          // walks the selected columns of its own 64, code dword by code
+          // dword (static, so no register selects), the four row blocks at once
+          const int g64 = 4 * c + kq;
+          const uint32_t m0 = sel_bm[2 * g64], m1 = sel_bm[2 * g64 + 1];
+          const int jb = rank64[g64];
+  #pragma unroll
+          for (int sd = 0; sd < 8; ++sd) {
+            uint32_t mb = ((sd < 4 ? m0 : m1) >> (8 * (sd & 3))) & 0xFFu;
+            while (mb) {
+              const int ii = __builtin_ctz(mb);
+              mb &= mb - 1;
+              const uint32_t below = (1u << (8 * (sd & 3) + ii)) - 1u;
+              const int j = jb + (sd < 4 ? __builtin_popcount(m0 & below)
+                                         : __builtin_popcount(m0) + __builtin_popcount(m1 & below));
+  #pragma unroll
+              for (int b = 0; b < 4; ++b) {
+                const uint32_t code = (dword_of(d.wc[b], sd) >> (4 * ii)) & 0xFu;
+                const float qv = e2m1_unpack2<0>(code).x;
+                const float sv = e4m3_decode((d.ws[b] >> (8 * (sd >> 1))) & 0xFFu);
+                *reinterpret_cast<uint16_t*>(wsl + (64 * wave + 16 * b + r16) * wsrow + 2 * j) =
+                    (uint16_t)(__float_as_uint(qv * sv) >> 16);
+              }
+            }
+          }
+        }
+        if (c + 1 == nc) finish(q.blk);
+      };
+
+      // one stream of nbw * nc chunks: steady state loading one chunk ahead
+      // (across block boundaries, so a block's epilogue overlaps the next
+      // block's first loads), then the last one or two chunks (no load past
+      // the end)
+      using yes = std::integral_constant<bool, true>;
+      using no = std::integral_constant<bool, false>;
+      const int total = nbw * nc;
+      DecChunk b0, b1;
+      Pos qa{0, 0};
+      load(b0, qa);
+      int i = 0;
+      for (; i + 2 < total; i += 2) {
+        const Pos qb = advance(qa), qc = advance(qb);
+        compute(b0, qa, 0, b1, qb, yes());
+        compute(b1, qb, 1, b0, qc, yes());
+        qa = qc;
+      }
+      if (i + 1 < total) {
+        const Pos qb = advance(qa);
+        compute(b0, qa, 0, b1, qb, yes());
+        compute(b1, qb, 1, b0, qa, no());
+      } else {
+        compute(b0, qa, 0, b1, qa, no());
+      }
+    };
+    if (ntile_rt >= 2)
+      run(std::integral_constant<int, 2>());
+    else
+      run(std::integral_constant<int, 1>());
   }
 }
 
@@ -1007,7 +1073,9 @@ int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const
   if (force && strcmp(force, "big") == 0) use_big = true, use_dec = false;
   if (force && strcmp(force, "generic") == 0) use_big = false, use_dec = false;
   if (force && strcmp(force, "decode") == 0) use_dec = true;
-  use_dec = use_dec && k <= dec::KMAX && K / dec::KC <= dec::CHUNKS_MAX;
+  use_dec = use_dec && k <= dec::KMAX && K / dec::KC <= dec::CHUNKS_MAX &&
+            (uint64_t)N * (uint64_t)K / 2 < (1ULL << 32) &&
+            (uint64_t)M_src * (uint64_t)K / 2 < (1ULL << 32);
   if (use_dec) {
     const int64_t n_blocks = (N + dec::ROWS - 1) / dec::ROWS;
     const int wsrow = k > 0 ? (int)(((k + 31) & ~31) * 2 + 16) : 0;
@@ -1024,7 +1092,14 @@ int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const
         return fail(NVFP4_ERR_HIP, "grouped_w4a4_gemm_rac: cannot raise the LDS limit");
       dec_lds_limit[dev] = want;
     }
-    k_gemm_decode<<<(unsigned)(E * n_blocks), 256, lds, s>>>(a, (int)n_blocks, wsrow);
+    // one round of workgroups: each takes bpw consecutive row blocks of its
+    // expert (two workgroups per CU when the LDS allows it)
+    const int64_t slots = (int64_t)num_cus() * (2 * (lds + kDecStaticLds) <= kLdsPerCu ? 2 : 1);
+    int64_t bpw = (E * n_blocks + slots - 1) / slots;
+    if (const char* o = getenv("NVFP4RAC_DEC_BPW")) bpw = atoll(o);
+    bpw = bpw < 1 ? 1 : (bpw > n_blocks ? n_blocks : bpw);
+    const int64_t groups = (n_blocks + bpw - 1) / bpw;
+    k_gemm_decode<<<(unsigned)(E * groups), 256, lds, s>>>(a, (int)n_blocks, (int)bpw, wsrow);
     return check_launch("grouped_w4a4_gemm_rac");
   }
   const size_t need_big = grouped_w4a4_gemm_rac_workspace_size(E, M_src, M_total, N, K, k);
