@@ -312,7 +312,7 @@ constexpr int B_CODES = BN * 32;               // [256][32 B]: chunk c at c ^ ((
 constexpr int B_SCALES = BN * 4;               // [256][4 B]
 constexpr int STAGE = A_BYTES + B_CODES + B_SCALES;   // 41984
 constexpr int KMAX = 128;                      // residual channels held in LDS
-constexpr int KSTEPS_MAX = 1024;               // K <= 65536
+constexpr int KSTEPS_MAX = 256;                // K <= 16384
 constexpr int WSROW = KMAX * 2 + 16;           // bf16 row of the W_S tile (+pad)
 constexpr int OUTROW = BN * 2 + 16;            // bf16 output staging row (+pad)
 constexpr int OUT_ROWS = BM / 2;               // output staged in two halves
@@ -392,7 +392,10 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   __shared__ __attribute__((aligned(16))) uint8_t wsl[WS_BYTES];   // W_S tile, then output staging
   __shared__ int32_t rows_src[BM];
   __shared__ int32_t s_local[KMAX];
-  __shared__ int32_t j_first[KSTEPS_MAX + 1];     // first selected channel at or after step kt
+  // selected columns as a bitmap over K, and rank32[g] = number of selected
+  // columns below column 32 g
+  __shared__ uint32_t sel_bm[2 * KSTEPS_MAX];
+  __shared__ uint16_t rank32[2 * KSTEPS_MAX + 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -452,14 +455,17 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   __syncthreads();
   const int nk = (int)(p.K / BK);
   if (kk > 0) {
-    // j_first[kt] = first j with S[j] >= kt * BK (S ascending), by binary search
-    for (int kt = tid; kt <= nk; kt += 512) {
+    // (S is strictly ascending, so bit ranks are the indices j)
+    for (int w = tid; w < 2 * nk; w += 512) sel_bm[w] = 0u;
+    __syncthreads();
+    for (int j = tid; j < kk; j += 512) atomicOr(&sel_bm[s_local[j] >> 5], 1u << (s_local[j] & 31));
+    for (int g = tid; g <= 2 * nk; g += 512) {
       int a = 0, b = kk;
       while (a < b) {
         const int m = (a + b) >> 1;
-        if (s_local[m] < kt * BK) a = m + 1; else b = m;
+        if (s_local[m] < g * 32) a = m + 1; else b = m;
       }
-      j_first[kt] = a;
+      rank32[g] = (uint16_t)a;
     }
     __syncthreads();
   }
@@ -516,25 +522,6 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
     const uint8_t* bb = ab + A_BYTES;
     const uint8_t* sb = bb + B_CODES;
 
-    if (kk > 0) {
-      // copy the weights of the selected channels in [k0, k0 + BK) out of
-      // this stage: thread t owns weight row t % 256, channels of parity t / 256
-      const int k0 = kt * BK;
-      const int jhi = j_first[kt + 1];
-      const int row = tid & 255;
-      const uint8_t* rowc = bb + row * 32;
-      const int sw = (row >> 3) & 1;
-      for (int j = j_first[kt] + (tid >> 8); j < jhi; j += 2) {
-        const int c = s_local[j] - k0;
-        const int byte = c >> 1;
-        const uint32_t code = (rowc[(((byte >> 4) ^ sw) << 4) | (byte & 15)] >> (4 * (c & 1))) & 0xFu;
-        const float q = e2m1_unpack2<0>(code).x;
-        const float sc = e4m3_decode(sb[row * 4 + (c >> 4)]);
-        *reinterpret_cast<uint16_t*>(wsl + row * WSROW + 2 * j) =
-            (uint16_t)(__float_as_uint(q * sc) >> 16);
-      }
-    }
-
     uint4 br[2];
     uint32_t bs[2];
 #pragma unroll
@@ -542,6 +529,14 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
       const int rb = wn * 64 + 32 * j + r32;
       br[j] = *reinterpret_cast<const uint4*>(bb + rb * 32 + physb * 16);
       bs[j] = *reinterpret_cast<const uint16_t*>(sb + rb * 4 + 2 * kg);
+    }
+    // the selected columns among this lane's 32 (k0 + 32 kg ..), and the
+    // index j of the first of them
+    uint32_t selm = 0u;
+    int jb = 0;
+    if (kk > 0) {
+      selm = sel_bm[2 * kt + kg];
+      jb = rank32[2 * kt + kg];
     }
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
@@ -565,6 +560,30 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
           const u32x4 B = decode8_f16(w, sbv[j], mb[j]);
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[i][j] = mfma32_f16(A[i], B, acc[i][j]);
+        }
+      }
+    }
+
+    // copy the selected columns' weights (exact in bf16) into the W_S rows,
+    // from the codes this lane holds (after the MFMAs are issued, which run
+    // meanwhile): the waves of row half wm take code dwords 2 wm, 2 wm + 1
+    if (selm != 0u) {
+#pragma unroll
+      for (int tq = 0; tq < 2; ++tq) {
+        const int t = 2 * wm + tq;               // wave-uniform
+        uint32_t mb = (selm >> (8 * t)) & 0xFFu;
+        while (mb) {
+          const int ii = __builtin_ctz(mb);
+          mb &= mb - 1;
+          const int j = jb + __builtin_popcount(selm & ((1u << (8 * t + ii)) - 1u));
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            const uint32_t w = t == 0 ? br[jj].x : t == 1 ? br[jj].y : t == 2 ? br[jj].z : br[jj].w;
+            const float qv = e2m1_unpack2<0>((w >> (4 * ii)) & 0xFu).x;
+            const float sv = e4m3_decode((bs[jj] >> (8 * (t >> 1))) & 0xFFu);
+            *reinterpret_cast<uint16_t*>(wsl + (wn * 64 + 32 * jj + r32) * WSROW + 2 * j) =
+                (uint16_t)(__float_as_uint(qv * sv) >> 16);
+          }
         }
       }
     }
