@@ -76,29 +76,6 @@ k_tile_prefix(const int32_t* __restrict__ offsets, int E, int64_t M_total, int b
   if (tid == E - 1) prefix[E] = base + incl;
 }
 
-// order[0..E) = the experts by descending row count (ties by index), so the
-// decode kernel's workgroups for the costliest experts are dispatched first
-// and the cheap ones fill the tail
-__global__ void __launch_bounds__(1024)
-k_expert_order(const int32_t* __restrict__ offsets, int E, int64_t M_total,
-               int32_t* __restrict__ order) {
-  __shared__ int32_t cnt[1024];
-  const int tid = threadIdx.x;
-  if (tid < E) {
-    int64_t lo = offsets[tid], hi = offsets[tid + 1];
-    lo = lo < 0 ? 0 : (lo > M_total ? M_total : lo);
-    hi = hi < lo ? lo : (hi > M_total ? M_total : hi);
-    cnt[tid] = (int32_t)(hi - lo);
-  }
-  __syncthreads();
-  if (tid < E) {
-    const int32_t me = cnt[tid];
-    int rank = 0;
-    for (int f = 0; f < E; ++f) rank += (cnt[f] > me) || (cnt[f] == me && f < tid);
-    order[rank] = tid;
-  }
-}
-
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4_t mfma_bf16(const u32x4& a, const u32x4& b, f32x4_t c) {
@@ -735,7 +712,7 @@ constexpr int kDecStaticLds = 4 * dec::KMAX + 32 * dec::CHUNKS_MAX + 2 * (4 * de
 constexpr int kLdsPerCu = 160 * 1024;
 
 __global__ void __launch_bounds__(256, 2)
-k_gemm_decode(GemmArgs p, const int32_t* __restrict__ order, int n_blocks, int bpw, int wsrow) {
+k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
   using namespace dec;
   extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
   __shared__ int32_t s_local[KMAX];
@@ -748,11 +725,32 @@ k_gemm_decode(GemmArgs p, const int32_t* __restrict__ order, int n_blocks, int b
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, kq = lane >> 4;
-  // workgroup (eo, g) takes row blocks g * bpw .. + bpw of expert order[eo]
+  // workgroup (eo, g) takes row blocks g * bpw .. + bpw of the expert of
+  // rank eo by descending row count (ties by index): the costliest experts'
+  // workgroups are dispatched first and single-tile experts fill the tail.
+  // The token-fragment area holds the row counts meanwhile.
   const int groups = (n_blocks + bpw - 1) / bpw;
   const int eo = (int)blockIdx.x / groups;
   const int g = (int)blockIdx.x - eo * groups;
-  const int e = order[eo];
+  __shared__ int32_t e_rank_sel;
+  {
+    int32_t* cnt = reinterpret_cast<int32_t*>(tok);   // E <= 1024 entries, 4 KB
+    for (int f = tid; f < p.E; f += 256) {
+      int64_t lo = p.offsets[f], hi = p.offsets[f + 1];
+      lo = lo < 0 ? 0 : (lo > p.M_total ? p.M_total : lo);
+      hi = hi < lo ? lo : (hi > p.M_total ? p.M_total : hi);
+      cnt[f] = (int32_t)(hi - lo);
+    }
+    __syncthreads();
+    for (int f = tid; f < p.E; f += 256) {
+      const int32_t me = cnt[f];
+      int rank = 0;
+      for (int h = 0; h < p.E; ++h) rank += (cnt[h] > me) || (cnt[h] == me && h < f);
+      if (rank == eo) e_rank_sel = f;
+    }
+    __syncthreads();
+  }
+  const int e = e_rank_sel;
   const int blk_lo = g * bpw;
   const int nbw = n_blocks - blk_lo < bpw ? n_blocks - blk_lo : bpw;
   int64_t e_lo = p.offsets[e], e_hi = p.offsets[e + 1];
@@ -1142,9 +1140,7 @@ int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const
     if (const char* o = getenv("NVFP4RAC_DEC_BPW")) bpw = atoll(o);
     bpw = bpw < 1 ? 1 : (bpw > n_blocks ? n_blocks : bpw);
     const int64_t groups = (n_blocks + bpw - 1) / bpw;
-    k_expert_order<<<1, 1024, 0, s>>>(expert_offsets, (int)E, M_total, prefix);
-    k_gemm_decode<<<(unsigned)(E * groups), 256, lds, s>>>(a, prefix, (int)n_blocks, (int)bpw,
-                                                           wsrow);
+    k_gemm_decode<<<(unsigned)(E * groups), 256, lds, s>>>(a, (int)n_blocks, (int)bpw, wsrow);
     return check_launch("grouped_w4a4_gemm_rac");
   }
   const size_t need_big = grouped_w4a4_gemm_rac_workspace_size(E, M_src, M_total, N, K, k);
