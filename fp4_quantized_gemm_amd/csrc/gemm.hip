@@ -653,11 +653,13 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
 
 // ---------------------------------------------------------------------------
 // Decode-sized grouped GEMM: a few rows per expert, so the weights dominate
-// the traffic and every expert's weights should cross HBM once.  One
-// workgroup per (expert, 256 weight rows); each of its 4 waves streams 64
-// weight rows (4 blocks of 16) over K in chunks of 256 with register loads one
-// chunk ahead, and multiplies them with all of the expert's rows (token tiles
-// of 16, up to TMAX per pass) on 16x16x32 f16 MFMAs.  Both operands are
+// the traffic and every expert's weights should cross HBM once.  A
+// workgroup takes a few consecutive blocks of 256 weight rows of one expert
+// (one round of workgroups fills the chip) and streams them as one sequence
+// of K chunks of 256; each of its 4 waves streams 64 weight rows (4 blocks of
+// 16) with register loads one chunk ahead, and multiplies them with all of
+// the expert's rows (token tiles of 16, up to TMAX per pass) on 16x16x32 f16
+// MFMAs.  Both operands are
 // decoded from NVFP4 codes in registers (exact in f16), so no activation
 // image is needed.  Weight rows are the MFMA's M side, tokens its N side.
 //
@@ -667,8 +669,8 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
 // line split over two chunks was evicted from L2 between its halves).  MFMA
 // step s (0..7) takes the lane's code dword s, i.e. k0 + 64 (l / 16) + 8 s + i
 // in the instruction's k slot 8 (l / 16) + i; both operands use this order.
-// The residual correction runs after the loop (bf16 MFMAs over the selected
-// channels, whose weights are copied to LDS as the chunks pass).
+// The residual correction runs after each block (bf16 MFMAs over the
+// selected channels, whose weights are copied to LDS as the chunks pass).
 // ---------------------------------------------------------------------------
 namespace dec {
 constexpr int ROWS = 256;
