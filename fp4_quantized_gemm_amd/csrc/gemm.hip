@@ -482,6 +482,21 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
                                        0, 0);
   };
 
+  // residual rows for the correction, staged like the A image: 64 channels
+  // of the tile's 256 rows per stage, 8-channel chunks swizzled as A's
+  // (whole 64-channel halves, so only when k % 64 == 0)
+  const bool rdma = kk > 0 && (kk & 63) == 0;
+  auto issue_r = [&](uint8_t* st, int cb0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = (i * 8 + wave) * 64 + lane;
+      const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(p.R) +
+                           (uint32_t)rows_src[r] * (uint32_t)(2 * kk) + 2u * (uint32_t)(cb0 + 8 * c);
+      __builtin_amdgcn_global_load_lds(src, st + (i * 8 + wave) * 1024, 16, 0, 0);
+    }
+  };
+
   f32x16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -496,6 +511,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   // one k-step on stage `ab` while stage `nxt` fills with step kt + 1
   auto kstep = [&](const uint8_t* ab, uint8_t* nxt, int kt) {
     if (kt + 1 < nk) issue_loads(nxt, (uint32_t)(kt + 1) * BK);
+    else if (rdma) issue_r(nxt, 0);
     const uint8_t* bb = ab + A_BYTES;
     const uint8_t* sb = bb + B_CODES;
 
@@ -585,7 +601,37 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] *= gx;
 
-  for (int cb0 = 0; cb0 < kk; cb0 += 64) {
+  // (the loop ends on stage st1: the first residual half is in st0)
+  auto rac_half = [&](const uint8_t* rb, int cb0) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      u32x4 A[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ra = wm * 128 + 32 * i + r32;
+        const uint4 v4 = *reinterpret_cast<const uint4*>(rb + ra * 128 + (((2 * c + kg) ^ swa) << 4));
+        A[i] = u32x4{v4.x, v4.y, v4.z, v4.w};
+      }
+      const int slot = cb0 + 16 * c + 8 * kg;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint4 vv = *reinterpret_cast<const uint4*>(wsl + (wn * 64 + 32 * j + r32) * WSROW + 2 * slot);
+        const u32x4 B = u32x4{vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][j] = mfma32_bf16(A[i], B, acc[i][j]);
+      }
+    }
+  };
+  if (rdma) {
+    if (kk > 64) issue_r(st1, 64);
+    rac_half(st0, 0);
+    if (kk > 64) {
+      wait_vmem0();
+      __syncthreads();
+      rac_half(st1, 64);
+    }
+  }
+  for (int cb0 = 0; !rdma && cb0 < kk; cb0 += 64) {
     u32x4 A[4][4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -1147,7 +1193,7 @@ int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const
   }
   const size_t need_big = grouped_w4a4_gemm_rac_workspace_size(E, M_src, M_total, N, K, k);
   use_big = use_big && k <= big::KMAX && K / big::BK <= big::KSTEPS_MAX && ws_bytes >= need_big &&
-            (uint64_t)M_src * K * 2 < (1ULL << 32);
+            (uint64_t)M_src * K * 2 < (1ULL << 32) && (uint64_t)M_src * k * 2 < (1ULL << 32);
   if (use_big) {
     uint16_t* img = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + img_offset(E));
     const int64_t chunks = M_src * (K / 8);
