@@ -157,6 +157,14 @@ def quantize_activation(x, k: int):
     return dict(codes=codes, scales=scales, g=g, A=A, r=r, score=score, S=S, R_S=r[:, S])
 
 
+def fake_quant(codes, scales, g) -> np.ndarray:
+    """The QDQ output handed to bf16 arithmetic: bf16(float32(q * s_b) * g).
+    q * s_b is exact in float32, so this is one float32 product with the
+    tensor scale, then one rounding to bf16."""
+    qs = dequantize_unscaled(codes, scales).astype(np.float32)           # exact
+    return round_to_bf16((qs * np.float32(g)).astype(np.float32).astype(np.float64))
+
+
 def qdq_weights(w):
     """Weight QDQ for each expert of w [E][N][K] (bf16 values as float64).
 
@@ -173,9 +181,25 @@ def qdq_weights(w):
     for e in range(E):
         c, s, g, _ = quantize(w[e])
         codes[e], scales[e], g_w[e] = c, s, g
-        qs = dequantize_unscaled(c, s).astype(np.float32)             # exact
-        w_qdq[e] = round_to_bf16((qs * g).astype(np.float32).astype(np.float64))
+        w_qdq[e] = fake_quant(c, s, g)
     return codes, scales, g_w, w_qdq
+
+
+def qdq_residual(R_S):
+    """Second-pass quantization of the compensated residual (the variant in
+    which the selected residual is itself quantized to NVFP4 before it is
+    added back; gist.science technical summary §2.2 B, 'second-pass
+    quantization').
+
+    R_S [M][k] (k % 16 == 0, bf16 values as float64) goes through the same
+    QDQ path as the weights: one tensor scale over the whole [M][k] tensor,
+    16-element blocks along the selected-channel axis (channel order of S),
+    and the bf16 fake-quantized value r^ = bf16(float32(q * s_b) * g_r) is
+    what the GEMM's correction multiplies with the weights.
+
+    Returns (codes [M][k], scales [M][k/16], g_r float32, r_qdq [M][k])."""
+    codes, scales, g, _ = quantize(R_S)
+    return codes, scales, g, fake_quant(codes, scales, g)
 
 
 def pack_codes(codes) -> np.ndarray:
