@@ -26,6 +26,7 @@ they were taken.  `cpu_baseline` times the CPU oracle on a bounded sample of
 the same block.
 
     python bench.py --calibrate-copy     # 1 GiB device copy, for counter scaling
+    python bench.py --rac-sweep [--config C]   # compensation strength against cost
 """
 from __future__ import annotations
 
@@ -56,6 +57,8 @@ def parse():
     ap.add_argument("--cpu-experts", type=int, default=4)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device-to-device copy three times")
+    ap.add_argument("--rac-sweep", action="store_true",
+                    help="only sweep the number of compensated channels k on the first GEMM")
     return ap.parse_args()
 
 
@@ -265,6 +268,106 @@ def cpu_baseline(cfg, wl, tokens, experts):
             "sample": desc, "seconds": round(dt, 2)}
 
 
+def gemm_kernel_name(cfg, m, n, k, E):
+    """The kernel grouped_w4a4_gemm_rac picks for this shape on a 256-CU
+    MI355X (the library's own dispatch rule, restated for the report)."""
+    if m <= 48 * E and k <= 128:
+        return "k_gemm_decode"
+    if k <= 128 and (m // 256) * ((n + 255) // 256) >= 512:
+        return "k_gemm_big"
+    return "k_gemm_generic"
+
+
+def rac_sweep(cfg, wl, reps, n_experts=8):
+    """Compensation strength against cost on the block's first GEMM.  For k
+    from 0 to half the hidden size (the pages' "top 50%" of channels): the
+    GEMM's duration (HIP events, median of `reps` calls), the duration of the
+    second-pass residual QDQ, and the relative Frobenius error of the GEMM
+    output against the trainer's W4A16 forward on the same rows (bf16
+    activations times the trainer's bf16 fake-quantized weights, float32
+    accumulation), over all rows of `n_experts` experts, for the bf16
+    residual and for the NVFP4-quantized one."""
+    import numpy as np
+    import torch
+
+    import fp4_quantized_gemm_amd as F
+
+    dev = torch.device("cuda:0")
+    x = to_dev(wl.x, dev)
+    w1 = to_dev(wl.w_first, dev)
+    c1, s1, g1, wq = F.nvfp4_qdq_weights(w1, want_qdq=True)
+    del w1
+    if cfg.kind == "dense":
+        offs = torch.tensor([0, cfg.T], dtype=torch.int32, device=dev)
+        perm, rows = None, cfg.T
+    else:
+        logits = torch.from_numpy(wl.logits).to(dev)
+        bias = torch.from_numpy(wl.bias).to(dev) if wl.bias is not None else None
+        _, _, offs, perm, _ = F.moe_permute(logits, cfg.topk, bias)
+        rows = perm.numel()
+    q = F.nvfp4_quantize_act(x, False, True)
+    o = offs.cpu().numpy()
+    busy = [e for e in range(len(o) - 1) if o[e + 1] > o[e]][:n_experts]
+    xf = x.float()
+    refs = []
+    for e in busy:
+        idx = torch.arange(int(o[e]), int(o[e + 1]), device=dev)
+        src = perm[idx].long() if perm is not None else idx
+        refs.append((idx, xf[src] @ wq[e].float().t().contiguous()))
+    torch.cuda.synchronize()
+
+    def err(y):
+        num = den = 0.0
+        for idx, ref in refs:
+            d = y[idx].float() - ref
+            num += float((d * d).sum())
+            den += float((ref * ref).sum())
+        return (num / den) ** 0.5
+
+    def median_ms(fn):
+        ts = []
+        for _ in range(reps + 2):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ts[2:]]))
+
+    def gemm(R, S):
+        return F.grouped_w4a4_gemm_rac(q["codes"], q["scales"], q["g"], perm, R, S, c1, s1, g1,
+                                       offs, M_total=rows)
+
+    E, N, Kh = c1.shape
+    K = 2 * Kh
+    ks = [k for k in (0, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096) if k <= K // 2]
+    points = []
+    t0 = None
+    for k in ks:
+        pt = {"k": k, "kernel": gemm_kernel_name(cfg, rows, N, k, E)}
+        if k == 0:
+            pt["gemm_ms"] = t0 = median_ms(lambda: gemm(None, None))
+            pt["err"] = err(gemm(None, None))
+        else:
+            S, R = F.select_residual_channels(q["x_used"], q["codes"], q["scales"], q["g"],
+                                              q["score"], k)
+            rq = F.nvfp4_qdq_residual(R)
+            pt["gemm_ms"] = median_ms(lambda: gemm(R, S))
+            pt["qdq_residual_ms"] = median_ms(lambda: F.nvfp4_qdq_residual(R))
+            pt["err_bf16_residual"] = err(gemm(R, S))
+            pt["err_nvfp4_residual"] = err(gemm(rq[3], S))
+        pt["overhead"] = pt["gemm_ms"] / t0 - 1.0
+        points.append({kk: (round(v, 6) if isinstance(v, float) else v) for kk, v in pt.items()})
+        print(f"# k={k} {points[-1]}", file=sys.stderr, flush=True)
+    return {"mode": "rac_sweep", "workload": cfg.name,
+            "gemm": f"first {rows}x{N}x{K}", "reference": "trainer W4A16 forward "
+            "(bf16 x times bf16 fake-quantized weight, fp32 accumulate)",
+            "error": "relative Frobenius norm over all rows of the first "
+            f"{len(busy)} experts with rows", "reps": reps, "points": points}
+
+
 def gemm_algorithmic_bytes(cfg, counts):
     """Bytes one step's GEMM calls must move: NVFP4 weights (codes + E4M3
     scales, 0.5625 B/elem) of experts that have rows, the activation codes of
@@ -289,6 +392,9 @@ def main():
 
     cfg = synth.get(args.config)
     wl = synth.make(cfg)
+    if args.rac_sweep:
+        print(json.dumps(rac_sweep(cfg, wl, max(args.steps // 2, 5))), flush=True)
+        return
     ms, stage_ms, rac, counts = run_gpu(cfg, wl, args.steps, args.warmup)
     shapes = cfg.gemm_shapes()
     flops_step = cfg.gemm_flops()

@@ -10,6 +10,8 @@ there is no fallback: importing the library fails loudly if it is missing.
 Calls (same names as the C ABI):
     nvfp4_qdq_weights, nvfp4_quantize_act, select_residual_channels,
     moe_permute, grouped_w4a4_gemm_rac, moe_unpermute_combine
+and, for the NVFP4-quantized-residual variant of the correction,
+    nvfp4_qdq_residual
 """
 from __future__ import annotations
 
@@ -21,7 +23,8 @@ import torch
 from .build import LIB as LIB_PATH
 
 __all__ = ["lib", "nvfp4_qdq_weights", "nvfp4_quantize_act", "select_residual_channels",
-           "moe_permute", "grouped_w4a4_gemm_rac", "moe_unpermute_combine", "NvfpError",
+           "moe_permute", "grouped_w4a4_gemm_rac", "moe_unpermute_combine", "nvfp4_qdq_residual",
+           "NvfpError",
            "EXPORTED_SYMBOLS"]
 
 EXPORTED_SYMBOLS = [
@@ -32,6 +35,7 @@ EXPORTED_SYMBOLS = [
     "moe_permute_workspace_size", "moe_permute",
     "grouped_w4a4_gemm_rac_workspace_size", "grouped_w4a4_gemm_rac",
     "moe_unpermute_combine",
+    "nvfp4_qdq_residual_workspace_size", "nvfp4_qdq_residual",
 ]
 
 
@@ -62,6 +66,7 @@ def _load():
         "select_residual_channels_workspace_size": [_I64, _I64, _I64],
         "moe_permute_workspace_size": [_I64, _I64],
         "grouped_w4a4_gemm_rac_workspace_size": [_I64, _I64, _I64, _I64, _I64, _I64],
+        "nvfp4_qdq_residual_workspace_size": [_I64, _I64],
     }.items():
         f = getattr(L, name)
         f.restype = _SZ
@@ -74,6 +79,7 @@ def _load():
         "grouped_w4a4_gemm_rac": [_P, _P, _P, _P, _I64, _P, _P, _I64, _P, _P, _P, _P, _I64, _I64,
                                   _I64, _I64, _P, _P, _SZ, _P],
         "moe_unpermute_combine": [_P, _P, _P, _I64, _I64, _I64, _P, _P],
+        "nvfp4_qdq_residual": [_P, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P],
     }
     for name, args in sigs.items():
         f = getattr(L, name)
@@ -167,6 +173,25 @@ def select_residual_channels(x_used, codes, scales, g, score, k):
                                       ws.numel(), _stream(dev)),
            "select_residual_channels")
     return S, R
+
+
+def nvfp4_qdq_residual(R_S):
+    """Second-pass NVFP4 quantization of the selected residual R_S [M][k]
+    bf16 -> (codes [M][k/2] u8, scales [M][k/16] u8, g_r [1] f32, r_qdq
+    [M][k] bf16).  Pass r_qdq as R_S to grouped_w4a4_gemm_rac."""
+    L = _load()
+    _need(R_S, torch.bfloat16, "R_S")
+    M, k = R_S.shape
+    dev = R_S.device
+    codes = torch.empty((M, k // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((M, k // 16), dtype=torch.uint8, device=dev)
+    g = torch.empty(1, dtype=torch.float32, device=dev)
+    r_qdq = torch.empty_like(R_S)
+    ws = _ws(L.nvfp4_qdq_residual_workspace_size(M, k), dev)
+    _check(L.nvfp4_qdq_residual(_ptr(R_S), M, k, _ptr(codes), _ptr(scales), _ptr(g), _ptr(r_qdq),
+                                _ptr(ws), ws.numel(), _stream(dev)),
+           "nvfp4_qdq_residual")
+    return codes, scales, g, r_qdq
 
 
 def moe_permute(logits, topk, bias=None):

@@ -396,6 +396,46 @@ int nvfp4_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, int glu
   return check_launch("nvfp4_quantize_act");
 }
 
+size_t nvfp4_qdq_residual_workspace_size(int64_t M, int64_t k) {
+  (void)M;
+  (void)k;
+  return 256;
+}
+
+// Second-pass quantization of the selected residual: the [M][k] tensor goes
+// through the weight QDQ path (its own amax, 16-blocks along the selected
+// channels, row-major scales) and r^ = bf16(fp32(q * s) * g_r) is written for
+// the GEMM's correction.
+int nvfp4_qdq_residual(const void* r, int64_t M, int64_t k, uint8_t* codes, uint8_t* scales,
+                       float* g_r, void* r_qdq, void* ws, size_t ws_bytes, void* stream) {
+  NV_REQUIRE(g_r && ws, NVFP4_ERR_NULL, "nvfp4_qdq_residual: g_r and ws are required");
+  NV_REQUIRE(M >= 0 && k >= 16 && k % 16 == 0 && M * k < (1LL << 40), NVFP4_ERR_SHAPE,
+             "nvfp4_qdq_residual: need M >= 0, k >= 16, k %% 16 == 0 (M=%lld k=%lld)",
+             (long long)M, (long long)k);
+  NV_REQUIRE(M == 0 || (r && codes && scales && r_qdq), NVFP4_ERR_NULL,
+             "nvfp4_qdq_residual: r, codes, scales and r_qdq are required");
+  NV_REQUIRE(aligned(r, 16) && aligned(codes, 8) && aligned(r_qdq, 16) && aligned(ws, 16),
+             NVFP4_ERR_ALIGN, "nvfp4_qdq_residual: misaligned pointer");
+  NV_REQUIRE(ws_bytes >= nvfp4_qdq_residual_workspace_size(M, k), NVFP4_ERR_WORKSPACE,
+             "nvfp4_qdq_residual: workspace too small");
+  hipStream_t s = as_stream(stream);
+  uint32_t* amax = static_cast<uint32_t*>(ws);
+  fill_u32(amax, 1, 0u, s);
+  const int cus = num_cus();
+  const uint16_t* src = static_cast<const uint16_t*>(r);
+  if (M > 0) {
+    const int64_t n8 = M * k / 8;
+    int64_t nb = (n8 + 1023) / 1024;
+    if (nb > 8LL * cus) nb = 8LL * cus;
+    k_amax_flat<<<dim3((unsigned)(nb > 0 ? nb : 1), 1, 1), 256, 0, s>>>(src, n8, 0, amax);
+  }
+  RowTiling t16 = row_tiling(k / 16);
+  dim3 grid(grid_rows(M, t16.rows_per_iter, 8LL * cus), t16.col_groups, 1);
+  k_quantize<<<grid, 256, 0, s>>>(src, M, k, k, 0, 1, t16.chunks, t16.rows_per_iter, amax, codes,
+                                  scales, g_r, nullptr, static_cast<uint16_t*>(r_qdq), 0);
+  return check_launch("nvfp4_qdq_residual");
+}
+
 int nvfp4_qdq_weights(const void* w, int64_t E, int64_t N, int64_t K, uint8_t* codes,
                       uint8_t* scales, float* g_w, void* w_qdq, void* ws, size_t ws_bytes,
                       void* stream) {

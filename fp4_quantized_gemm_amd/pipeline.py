@@ -14,8 +14,8 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (grouped_w4a4_gemm_rac, moe_permute, moe_unpermute_combine, nvfp4_qdq_weights,
-               nvfp4_quantize_act, select_residual_channels)
+from . import (grouped_w4a4_gemm_rac, moe_permute, moe_unpermute_combine, nvfp4_qdq_residual,
+               nvfp4_qdq_weights, nvfp4_quantize_act, select_residual_channels)
 
 
 @dataclass
@@ -31,13 +31,19 @@ def prepare_weights(w, want_qdq=False) -> QuantWeights:
 
 
 def quantized_linear_rac(x, wq: QuantWeights, k, a_rows=None, offsets=None, M_total=None,
-                         glu=False):
+                         glu=False, rac="bf16"):
     """Quantize x (or SwiGLU of x), select k channels, grouped GEMM.
-    Returns (y, stage dict)."""
+    rac="bf16" adds the bf16 residual of the selected channels back;
+    rac="nvfp4" quantizes that residual a second time to NVFP4 first and adds
+    its fake-quantized value back.  Returns (y, stage dict)."""
+    if rac not in ("bf16", "nvfp4"):
+        raise ValueError(f"rac must be 'bf16' or 'nvfp4', not {rac!r}")
     q = nvfp4_quantize_act(x, glu=glu, want_score=k > 0)
     S = R = None
     if k > 0:
         S, R = select_residual_channels(q["x_used"], q["codes"], q["scales"], q["g"], q["score"], k)
+        if rac == "nvfp4":
+            R = nvfp4_qdq_residual(R)[3]
     if offsets is None:
         offsets = torch.tensor([0, x.shape[0]], dtype=torch.int32, device=x.device)
     y = grouped_w4a4_gemm_rac(q["codes"], q["scales"], q["g"], a_rows, R, S, wq.codes, wq.scales,
@@ -46,20 +52,21 @@ def quantized_linear_rac(x, wq: QuantWeights, k, a_rows=None, offsets=None, M_to
 
 
 def moe_forward(x, logits, topk, w_first: QuantWeights, w_down: QuantWeights, k_first, k_down,
-                bias=None, keep=False):
+                bias=None, keep=False, rac="bf16"):
     """x [T][H] bf16, logits [T][E] f32.  w_first [E][N1][H] (N1 = 2I for
     gate+up, I for an up-only block); w_down [E][H][I] or None.  Returns the
     combined output [T][H] (or the first GEMM's permuted output when there is
     no down projection) and, with keep=True, every intermediate."""
     ids, tw, offs, perm, inv = moe_permute(logits, topk, bias)
     rows = perm.numel()
-    y1, st1 = quantized_linear_rac(x, w_first, k_first, a_rows=perm, offsets=offs, M_total=rows)
+    y1, st1 = quantized_linear_rac(x, w_first, k_first, a_rows=perm, offsets=offs, M_total=rows,
+                                   rac=rac)
     out = dict(topk_ids=ids, topk_w=tw, offsets=offs, perm_token=perm, inv_perm=inv, y1=y1,
                st1=st1) if keep else {}
     if w_down is None:
         return y1, out
     y2, st2 = quantized_linear_rac(y1, w_down, k_down, a_rows=None, offsets=offs, M_total=rows,
-                                   glu=True)
+                                   glu=True, rac=rac)
     o = moe_unpermute_combine(y2, inv, tw)
     if keep:
         out.update(y2=y2, st2=st2, out=o)

@@ -135,6 +135,27 @@ int select_residual_channels(const void* x_used, int64_t ldx, const uint8_t* cod
                              void* stream);
 
 /* ------------------------------------------------------------------------
+ * Second-pass quantization of the compensated residual: the variant of
+ * Residual Activation Compensation in which the selected residual is itself
+ * quantized to NVFP4 before it is added back (gist.science summary §2.2 B,
+ * "second-pass quantization").  The residual goes through the same QDQ path
+ * as the weights.
+ *
+ * r      [M][k] bf16, contiguous: R_S from select_residual_channels.
+ * codes  [M][k/2] packed E2M1; scales [M][k/16] E4M3, row-major (blocks of
+ *        16 along the selected channels, in the ascending order of S).
+ * g_r    [1] float32 = fp32(amax(r) / 2688), amax over the whole [M][k].
+ * r_qdq  [M][k] bf16 = bf16(fp32(e2m1 * e4m3) * g_r): pass it as R_S to
+ *        grouped_w4a4_gemm_rac to add the quantized residual back.
+ * Same scale recipe as nvfp4_qdq_weights.  Requires M >= 0, k >= 16,
+ * k % 16 == 0.  M == 0 writes g_r = 0 only.
+ * ---------------------------------------------------------------------- */
+size_t nvfp4_qdq_residual_workspace_size(int64_t M, int64_t k);
+int nvfp4_qdq_residual(const void* r, int64_t M, int64_t k, uint8_t* codes,
+                       uint8_t* scales, float* g_r, void* r_qdq,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * MoE routing and expert-major permutation (the MoE model of the pages,
  * gist.science summary §4; the router itself is not described there).
  *

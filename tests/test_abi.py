@@ -127,3 +127,15 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(F.NvfpError):
         F.nvfp4_quantize_act(torch.zeros(4, 64, dtype=torch.bfloat16))
+
+
+def test_qdq_residual_validation():
+    L = F.lib()
+    ws = L.nvfp4_qdq_residual_workspace_size(8, 32)
+    assert ws > 0
+    assert L.nvfp4_qdq_residual(FAKE, 8, 24, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == ERR_SHAPE
+    assert L.nvfp4_qdq_residual(FAKE, 8, 0, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == ERR_SHAPE
+    assert L.nvfp4_qdq_residual(FAKE, 8, 32, FAKE, FAKE, None, FAKE, FAKE, ws, None) == ERR_NULL
+    assert L.nvfp4_qdq_residual(FAKE, 8, 32, FAKE, FAKE, FAKE, None, FAKE, ws, None) == ERR_NULL
+    assert L.nvfp4_qdq_residual(FAKE_MIS, 8, 32, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == ERR_ALIGN
+    assert L.nvfp4_qdq_residual(FAKE, 8, 32, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == ERR_WS

@@ -1,0 +1,157 @@
+"""GPU parity of the compensation variant with an NVFP4-quantized residual
+(gist.science technical summary §2.2 B, 'second-pass quantization'):
+nvfp4_qdq_residual bit-exact against the oracle, and the grouped GEMM fed
+its fake-quantized residual within the GEMM tolerance, on small cases for
+every GEMM kernel and on the first GEMM of the decode and large-prefill
+workloads at full size (sampled rows)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import fp4_quantized_gemm_amd as F
+import synth
+from fp4_quantized_gemm_amd import pipeline
+from oracle import formats as OF
+from oracle import gemm as OG
+from oracle import nvfp4 as OQ
+from tests.gpu_util import (assert_gemm_close, f32_bits, heavy_bf16, host_bits, host_vals,
+                            tile_wscales, to_dev_bf16)
+from tests.test_gpu_full import sample_rows, weight_host
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def check_qdq_residual(R_vals, got):
+    codes, scales, g, r_hat = got
+    rc, rs, rg, rq = OQ.qdq_residual(R_vals)
+    assert np.array_equal(OQ.unpack_codes(codes.cpu().numpy()), rc)
+    assert np.array_equal(scales.cpu().numpy(), rs)
+    assert f32_bits(g.cpu().numpy()[0]) == f32_bits(rg)
+    assert np.array_equal(host_bits(r_hat), OF.f64_to_bf16_bits(rq))
+    return rq
+
+
+@pytest.mark.parametrize("M,K,k", [(1, 64, 16), (37, 512, 48), (300, 768, 128), (2048, 4096, 64),
+                                   (5, 1024, 256)])
+def test_qdq_residual_bitexact(dev, M, K, k):
+    say(f"qdq residual M={M} K={K} k={k}")
+    rng = np.random.default_rng(M + K + k)
+    x = heavy_bf16(rng, (M, K))
+    R = OQ.quantize_activation(x, k)["R_S"]
+    Rd = to_dev_bf16(OF.f64_to_bf16_bits(R))
+    got = F.nvfp4_qdq_residual(Rd)
+    torch.cuda.synchronize()
+    check_qdq_residual(R, got)
+
+
+def test_qdq_residual_zero_and_empty(dev):
+    say("qdq residual zeros / empty")
+    Rd = torch.zeros((4, 32), dtype=torch.bfloat16, device="cuda")
+    codes, scales, g, r_hat = F.nvfp4_qdq_residual(Rd)
+    torch.cuda.synchronize()
+    assert g.item() == 0.0 and not codes.cpu().numpy().any() and not scales.cpu().numpy().any()
+    assert not host_bits(r_hat).any()
+    codes, scales, g, r_hat = F.nvfp4_qdq_residual(torch.empty((0, 64), dtype=torch.bfloat16,
+                                                               device="cuda"))
+    torch.cuda.synchronize()
+    assert g.item() == 0.0
+
+
+@pytest.fixture(params=["generic", "big", "decode"])
+def gemm_kernel(request, monkeypatch):
+    monkeypatch.setenv("NVFP4RAC_GEMM", request.param)
+    return request.param
+
+
+@pytest.mark.parametrize("M_src,counts,N,K,k", [
+    (64, [64], 512, 512, 16),
+    (500, [17, 0, 0, 400, 83], 272, 1024, 128),
+    (64, [3, 0, 17, 33, 1, 0, 16, 40], 512, 1024, 64),
+])
+def test_gemm_with_quantized_residual(dev, gemm_kernel, M_src, counts, N, K, k):
+    say(f"gemm[{gemm_kernel}] nvfp4 residual counts={counts} N={N} K={K} k={k}")
+    rng = np.random.default_rng(sum(counts) + N + K + k)
+    E = len(counts)
+    x = heavy_bf16(rng, (M_src, K))
+    w = OF.round_to_bf16(rng.standard_normal((E, N, K)) * 0.02)
+    offs = np.zeros(E + 1, dtype=np.int32)
+    offs[1:] = np.cumsum(counts)
+    M_total = int(offs[-1])
+    a_rows = rng.integers(0, M_src, M_total).astype(np.int32)
+    cu = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    # the library chain
+    q = F.nvfp4_quantize_act(to_dev_bf16(OF.f64_to_bf16_bits(x)))
+    S, R = F.select_residual_channels(q["x_used"], q["codes"], q["scales"], q["g"], q["score"], k)
+    rq = F.nvfp4_qdq_residual(R)
+    wc_d, ws_d, gw_d, _ = F.nvfp4_qdq_weights(to_dev_bf16(OF.f64_to_bf16_bits(w)), want_qdq=False)
+    y = F.grouped_w4a4_gemm_rac(q["codes"], q["scales"], q["g"], cu(a_rows), rq[3], S, wc_d, ws_d,
+                                gw_d, cu(offs), M_total=M_total)
+    torch.cuda.synchronize()
+    # the oracle chain
+    qa = OQ.quantize_activation(x, k)
+    assert np.array_equal(S.cpu().numpy(), qa["S"])
+    assert np.array_equal(host_bits(R), OF.f64_to_bf16_bits(qa["R_S"]))
+    r_hat = check_qdq_residual(qa["R_S"], rq)
+    wc, ws, gw, _ = OQ.qdq_weights(w)
+    ref = OG.grouped_gemm_rac(qa["codes"], qa["scales"], qa["g"], a_rows, r_hat, qa["S"], wc, ws,
+                              gw, offs)
+    e1, e2, ex = assert_gemm_close(host_vals(y), ref)
+    say(f"   rownorm {e1:.2e} maxabs {e2:.2e} exact {ex:.5f}")
+
+
+@pytest.mark.parametrize("idx", [4, 5])
+def test_full_size_first_gemm_with_quantized_residual(dev, idx):
+    # the decode and large-prefill workloads' first GEMM, in the launch
+    # configuration the benchmark uses, with the residual quantized again
+    cfg = synth.get(idx)
+    say(f"workload {cfg.name}: generating")
+    wl = synth.make(cfg)
+    rng = np.random.default_rng(1)
+    x_dev = to_dev_bf16(wl.x)
+    w1 = pipeline.prepare_weights(to_dev_bf16(wl.w_first))
+    logits = torch.from_numpy(wl.logits).cuda()
+    bias = torch.from_numpy(wl.bias).cuda() if wl.bias is not None else None
+    say(f"workload {cfg.name}: running the library")
+    ids, tw, offs, perm, inv = F.moe_permute(logits, cfg.topk, bias)
+    q = F.nvfp4_quantize_act(x_dev)
+    S, R = F.select_residual_channels(q["x_used"], q["codes"], q["scales"], q["g"], q["score"],
+                                      cfg.k_first)
+    rq = F.nvfp4_qdq_residual(R)
+    y = F.grouped_w4a4_gemm_rac(q["codes"], q["scales"], q["g"], perm, rq[3], S, w1.codes,
+                                w1.scales, w1.g, offs, M_total=perm.numel())
+    torch.cuda.synchronize()
+    # the quantized residual, in full, teacher-forced on the GPU's R_S (which
+    # the full-size pipeline test checks against the oracle)
+    say("  residual QDQ (full)")
+    R_vals = host_vals(R)
+    r_hat = check_qdq_residual(R_vals, rq)
+    # sampled GEMM rows
+    x = OF.bf16_bits_to_f64(wl.x)
+    A = OQ.tensor_amax(x)
+    g = OQ.tensor_scale(A)
+    S_np = S.cpu().numpy()
+    offs_np, perm_np = offs.cpu().numpy(), perm.cpu().numpy()
+    rows_p = sample_rows(offs_np, rng)
+    say(f"  GEMM rows: {len(rows_p)}")
+    wq_host = weight_host(wl.w_first, rng)
+    y_h = host_vals(y)
+    got, ref = [], []
+    for e in np.unique(np.searchsorted(offs_np, rows_p, side="right") - 1):
+        ps = rows_p[(rows_p >= offs_np[e]) & (rows_p < offs_np[e + 1])]
+        t = perm_np[ps]
+        c, s, _, _ = OQ.quantize(x[t], A=A)
+        r = OQ.residual(x[t], c, s, g)[:, S_np]
+        assert np.array_equal(OF.f64_to_bf16_bits(r), host_bits(R)[t])
+        wc, ws, gw = wq_host(e)
+        ref.append(OG.grouped_gemm_rac(c, s, g, None, r_hat[t], S_np, wc[None], ws[None],
+                                       gw[None], [0, len(ps)]))
+        got.append(y_h[ps][:, wq_host.cols])
+    e1, e2, ex = assert_gemm_close(np.concatenate(got), np.concatenate(ref))
+    say(f"    rownorm {e1:.2e} maxabs {e2:.2e} exact {ex:.4f}")
