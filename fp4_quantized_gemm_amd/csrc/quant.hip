@@ -14,6 +14,8 @@
 //   2. quantize: one thread per 16-element block; block max -> E4M3 scale,
 //      codes via the hardware E2M1 conversion, residual and fixed-point
 //      channel score in the same pass.
+#include <cstdlib>
+
 #include "device.h"
 #include "runtime.h"
 
@@ -142,6 +144,60 @@ k_swiglu_amax(const uint16_t* __restrict__ y, int64_t rows, int64_t ldy, int64_t
   block_atomic_max<256>(m, amax);
 }
 
+// One 16-element block (two 16-byte halves of bf16 bits) against tensor amax
+// A: the elements as float32, the E4M3 scale byte and value, and the 16
+// codes packed two per byte (element 2j in bits 3:0 of byte j).
+__device__ __forceinline__ void quant_block16(const uint4& v0, const uint4& v1, float A,
+                                              float xf[16], uint32_t& sbyte, float& s,
+                                              uint32_t pk[2]) {
+  const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  uint32_t bmax = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    xf[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+    xf[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+    bmax = max(bmax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  }
+  sbyte = 0;
+  s = 0.0f;
+  pk[0] = pk[1] = 0u;
+  if (A > 0.0f) {
+    float u = (bf16_bits_to_f32(bmax) * kE4M3Max) / A;
+    sbyte = e4m3_encode_nonneg(u);
+    s = e4m3_decode(sbyte);
+  }
+  if (s > 0.0f) {
+    const float rho = kScaleDen / (s * A);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t b = e2m1_pack2(xf[2 * i] * rho, xf[2 * i + 1] * rho);
+      pk[i >> 2] |= b << (8 * (i & 3));
+    }
+  } else {
+    // magnitude 0 everywhere; keep the signs
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t b = ((w[i] >> 12) & 0x8u) | ((w[i] >> 24) & 0x80u);
+      pk[i >> 2] |= b << (8 * (i & 3));
+    }
+  }
+}
+
+// The fake-quantized value of a block's 16 codes, bf16(fp32(q * s) * g), sign
+// from the code bit, as 8 dwords of bf16 pairs.
+__device__ __forceinline__ void fake_quant16(const uint32_t pk[2], float s, float g,
+                                             uint32_t o[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t c0 = (pk[i >> 2] >> (8 * (i & 3))) & 0xFu;
+    const uint32_t c1 = (pk[i >> 2] >> (8 * (i & 3) + 4)) & 0xFu;
+    const f32x2 q = e2m1_unpack2<0>(c0 | (c1 << 4));
+    const uint32_t h0 = f32_to_bf16_rne(__builtin_fabsf(q.x * s) * g) | ((c0 & 8u) << 12);
+    const uint32_t h1 = f32_to_bf16_rne(__builtin_fabsf(q.y * s) * g) | ((c1 & 8u) << 12);
+    o[i] = h0 | (h1 << 16);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Pass 2: block quantizer.  One thread per 16-element block; tensors stacked
 // by row (blockIdx.z), each with its own amax (bf16 bits) and tensor scale.
@@ -159,7 +215,7 @@ k_quantize(const uint16_t* __restrict__ x, int64_t rows, int64_t ldx, int64_t K,
            int64_t tensor_stride, int ntensors, int blocks, int rows_per_iter,
            const uint32_t* __restrict__ amax, uint8_t* __restrict__ codes,
            uint8_t* __restrict__ scales, float* __restrict__ g_out,
-           uint64_t* __restrict__ partial, uint16_t* __restrict__ w_qdq, int tiled_scales) {
+           uint64_t* __restrict__ partial, uint16_t* __restrict__ w_qdq) {
   // partial: [gridDim.x][K] per-workgroup channel sums (or NULL: no scores)
   extern __shared__ uint64_t red[];               // 256 * 16 entries when rows_per_iter > 1
   uint64_t* score = partial;
@@ -197,44 +253,13 @@ k_quantize(const uint16_t* __restrict__ x, int64_t rows, int64_t ldx, int64_t K,
       n0 = *reinterpret_cast<const uint4*>(xn);
       n1 = *reinterpret_cast<const uint4*>(xn + 8);
     }
-    uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     float xf[16];
-    uint32_t bmax = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      xf[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
-      xf[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
-      bmax = max(bmax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
-    }
-    uint32_t sbyte = 0;
-    float s = 0.0f;
-    uint32_t pk[2] = {0u, 0u};
-    if (A > 0.0f) {
-      float u = (bf16_bits_to_f32(bmax) * kE4M3Max) / A;
-      sbyte = e4m3_encode_nonneg(u);
-      s = e4m3_decode(sbyte);
-    }
-    if (s > 0.0f) {
-      const float rho = kScaleDen / (s * A);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint32_t b = e2m1_pack2(xf[2 * i] * rho, xf[2 * i + 1] * rho);
-        pk[i >> 2] |= b << (8 * (i & 3));
-      }
-    } else {
-      // magnitude 0 everywhere; keep the signs
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint32_t b = ((w[i] >> 12) & 0x8u) | ((w[i] >> 24) & 0x80u);
-        pk[i >> 2] |= b << (8 * (i & 3));
-      }
-    }
+    uint32_t sbyte, pk[2];
+    float s;
+    quant_block16(v0, v1, A, xf, sbyte, s, pk);
     const int64_t orow = row0 + r;
     *reinterpret_cast<uint2*>(codes + orow * (K / 2) + (int64_t)c * 8) = make_uint2(pk[0], pk[1]);
-    if (tiled_scales)       // weights: 64-byte tiles per 16 rows x 64 k
-      scales[row0 * (K / 16) + wscale_offset(r, c, K)] = (uint8_t)sbyte;
-    else
-      scales[orow * (K / 16) + c] = (uint8_t)sbyte;
+    scales[orow * (K / 16) + c] = (uint8_t)sbyte;
 
     if (score != nullptr || w_qdq != nullptr) {
       float qs[16];
@@ -257,14 +282,7 @@ k_quantize(const uint16_t* __restrict__ x, int64_t rows, int64_t ldx, int64_t K,
       }
       if (w_qdq != nullptr) {
         uint32_t o[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          uint32_t c0 = (pk[i >> 2] >> (8 * (i & 3))) & 0xFu;
-          uint32_t c1 = (pk[i >> 2] >> (8 * (i & 3) + 4)) & 0xFu;
-          uint32_t h0 = f32_to_bf16_rne(__builtin_fabsf(qs[2 * i]) * g) | ((c0 & 8u) << 12);
-          uint32_t h1 = f32_to_bf16_rne(__builtin_fabsf(qs[2 * i + 1]) * g) | ((c1 & 8u) << 12);
-          o[i] = h0 | (h1 << 16);
-        }
+        fake_quant16(pk, s, g, o);
         uint16_t* wo = w_qdq + orow * K + (int64_t)c * 16;
         *reinterpret_cast<uint4*>(wo) = make_uint4(o[0], o[1], o[2], o[3]);
         *reinterpret_cast<uint4*>(wo + 8) = make_uint4(o[4], o[5], o[6], o[7]);
@@ -310,6 +328,68 @@ k_score_reduce(const uint64_t* __restrict__ partial, int nparts, int64_t K,
   if (pg == 0 && j < K) {
     s = red4[0][ch] + red4[1][ch] + red4[2][ch] + red4[3][ch];
     if (s) atomicAdd(reinterpret_cast<unsigned long long*>(score + j), (unsigned long long)s);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Weight quantize pass (after the per-expert amax pass): one workgroup per
+// 16-row slice of an expert, one thread per 16-element block with
+// kQdqRound blocks' loads in flight, and the 4 scale bytes of a 64-byte
+// scale tile row written as one dword.  Experts run last to first: the amax
+// pass read them first to last, so the first slices here re-read the rows
+// it read last, which may still be in the Infinity Cache.
+// ---------------------------------------------------------------------------
+constexpr int kQdqRound = 8;
+
+__global__ void __launch_bounds__(256)
+k_qdq_slices(const uint16_t* __restrict__ w, int64_t N, int64_t K, int E,
+             const uint32_t* __restrict__ amax, uint8_t* __restrict__ codes,
+             uint8_t* __restrict__ scales, float* __restrict__ g_w, uint16_t* __restrict__ w_qdq) {
+  const int tid = threadIdx.x;
+  const int e = E - 1 - (int)blockIdx.y;
+  const int64_t row0 = (int64_t)blockIdx.x * 16;
+  const int64_t KB = K / 16;
+  const uint16_t* src = w + ((int64_t)e * N + row0) * K;
+  const float A = bf16_bits_to_f32(amax[e]);
+  const float g = A / kScaleDen;
+  if (blockIdx.x == 0 && tid == 0) g_w[e] = g;
+  // 16 * KB is a multiple of 64 (K % 64 == 0), so a wave's blocks are all in
+  // range or all out, and lanes 4j..4j+3 hold blocks 4i..4i+3 of one row
+  const int64_t nblk = 16 * KB;
+  uint8_t* sc_e = scales + (int64_t)e * N * KB;
+  for (int64_t b0 = 0; b0 < nblk; b0 += 256 * kQdqRound) {
+    uint4 c0[kQdqRound], c1[kQdqRound];
+#pragma unroll
+    for (int u = 0; u < kQdqRound; ++u) {
+      const int64_t b = b0 + u * 256 + tid;
+      if (b < nblk) {
+        const int64_t r = b / KB, c = b - r * KB;
+        const uint16_t* xr = src + r * K + c * 16;
+        c0[u] = *reinterpret_cast<const uint4*>(xr);
+        c1[u] = *reinterpret_cast<const uint4*>(xr + 8);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kQdqRound; ++u) {
+      const int64_t b = b0 + u * 256 + tid;
+      if (b >= nblk) break;                  // wave-uniform
+      const int64_t r = b / KB, c = b - r * KB;
+      float xf[16], s;
+      uint32_t sbyte, pk[2];
+      quant_block16(c0[u], c1[u], A, xf, sbyte, s, pk);
+      const int64_t orow = (int64_t)e * N + row0 + r;
+      *reinterpret_cast<uint2*>(codes + orow * (K / 2) + c * 8) = make_uint2(pk[0], pk[1]);
+      const uint32_t s4 = sbyte | (__shfl_down(sbyte, 1) << 8) | (__shfl_down(sbyte, 2) << 16) |
+                          (__shfl_down(sbyte, 3) << 24);
+      if ((c & 3) == 0) *reinterpret_cast<uint32_t*>(sc_e + wscale_offset(row0 + r, c, K)) = s4;
+      if (w_qdq != nullptr) {
+        uint32_t o[8];
+        fake_quant16(pk, s, g, o);
+        uint16_t* wo = w_qdq + orow * K + c * 16;
+        *reinterpret_cast<uint4*>(wo) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4*>(wo + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+      }
+    }
   }
 }
 
@@ -387,7 +467,7 @@ int nvfp4_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, int glu
   const size_t red_bytes = (score && t16.rows_per_iter > 1) ? 256 * 16 * sizeof(uint64_t) : 0;
   k_quantize<<<grid, 256, red_bytes, s>>>(src, M, ld, K, 0, 1, t16.chunks, t16.rows_per_iter,
                                           amax, codes, scales, g_x, score ? partial : nullptr,
-                                          nullptr, 0);
+                                          nullptr);
   if (score) {
     fill_u64(score, K, 0ull, s);
     k_score_reduce<<<dim3((unsigned)((K + 63) / 64), (unsigned)((nq + 63) / 64)), 256, 0, s>>>(
@@ -432,7 +512,7 @@ int nvfp4_qdq_residual(const void* r, int64_t M, int64_t k, uint8_t* codes, uint
   RowTiling t16 = row_tiling(k / 16);
   dim3 grid(grid_rows(M, t16.rows_per_iter, 8LL * cus), t16.col_groups, 1);
   k_quantize<<<grid, 256, 0, s>>>(src, M, k, k, 0, 1, t16.chunks, t16.rows_per_iter, amax, codes,
-                                  scales, g_r, nullptr, static_cast<uint16_t*>(r_qdq), 0);
+                                  scales, g_r, nullptr, static_cast<uint16_t*>(r_qdq));
   return check_launch("nvfp4_qdq_residual");
 }
 
@@ -451,8 +531,8 @@ int nvfp4_qdq_weights(const void* w, int64_t E, int64_t N, int64_t K, uint8_t* c
              "nvfp4_qdq_weights: workspace too small");
   hipStream_t s = as_stream(stream);
   uint32_t* amax = static_cast<uint32_t*>(ws);
-  fill_u32(amax, E, 0u, s);
   const int cus = num_cus();
+  fill_u32(amax, E, 0u, s);
   const int64_t per_e = (8LL * cus + E - 1) / E;
   {
     const int64_t n8 = N * K / 8;
@@ -461,11 +541,9 @@ int nvfp4_qdq_weights(const void* w, int64_t E, int64_t N, int64_t K, uint8_t* c
     k_amax_flat<<<dim3((unsigned)(nb > 0 ? nb : 1), (unsigned)E, 1), 256, 0, s>>>(
         static_cast<const uint16_t*>(w), n8, N * K, amax);
   }
-  RowTiling t16 = row_tiling(K / 16);
-  dim3 g2(grid_rows(N, t16.rows_per_iter, per_e > 1 ? per_e : 1), t16.col_groups, (unsigned)E);
-  k_quantize<<<g2, 256, 0, s>>>(static_cast<const uint16_t*>(w), N, K, K, N * K, (int)E,
-                                t16.chunks, t16.rows_per_iter, amax, codes, scales, g_w,
-                                nullptr, static_cast<uint16_t*>(w_qdq), 1);
+  k_qdq_slices<<<dim3((unsigned)(N / 16), (unsigned)E, 1), 256, 0, s>>>(
+      static_cast<const uint16_t*>(w), N, K, (int)E, amax, codes, scales, g_w,
+      static_cast<uint16_t*>(w_qdq));
   return check_launch("nvfp4_qdq_weights");
 }
 

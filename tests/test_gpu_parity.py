@@ -98,12 +98,15 @@ def test_quantize_glu(dev, M, I):
     check_quant_against_oracle(q, h_gpu)                 # teacher-forced on the GPU's h
 
 
-@pytest.mark.parametrize("E,N,K", [(1, 16, 64), (3, 48, 192), (2, 144, 512)])
+@pytest.mark.parametrize("E,N,K", [(1, 16, 64), (3, 48, 192), (2, 144, 512), (40, 32, 128),
+                                   (6, 256, 1536)])
 def test_qdq_weights_bitexact(dev, E, N, K):
     say(f"qdq E={E} N={N} K={K}")
     rng = np.random.default_rng(E * N + K)
     w = OF.round_to_bf16(rng.standard_normal((E, N, K)) * 0.02)
     w[0, 0, :16] = 0.0
+    if E > 3:
+        w[2] = 0.0                                   # an all-zero expert: g = 0, codes 0
     wd = to_dev_bf16(OF.f64_to_bf16_bits(w))
     codes, scales, g_w, w_qdq = F.nvfp4_qdq_weights(wd, want_qdq=True)
     torch.cuda.synchronize()
