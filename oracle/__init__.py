@@ -11,7 +11,8 @@ Modules:
   nvfp4    tensor/block scales, quantize, dequantize, residual, channel
            scores, channel selection, weight QDQ, nibble packing
   moe      router top-k + softmax, expert-major permutation, SwiGLU, combine
-  gemm     expert-grouped W4A4 GEMM plus the residual correction
+  gemm     expert-grouped W4A4 GEMM plus the residual correction, and the
+           trainer-side W4A16 product with the same dequantized weights
   layer    the whole MoE layer chained from the pieces above
 
 Every function is pinned by tests under tests/ against facts that do not come

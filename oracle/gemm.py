@@ -55,3 +55,34 @@ def grouped_gemm_rac(a_codes, a_scales, g_x, a_rows, R_S, S, w_codes, w_scales, 
             y = y + np.asarray(R_S, dtype=np.float64)[t] @ w_hat[:, S].T
         out[p] = round_to_bf16(y)
     return out
+
+
+def grouped_gemm_w4a16(x, a_rows, w_codes, w_scales, g_w, expert_offsets, rows=None):
+    """The trainer-side forward of asymmetric W4A16 QAT (gist.science
+    technical summary §2.2 A): bf16 activations times the dequantized NVFP4
+    weights of each row's expert, the same weights the rollout's W4A4 GEMM
+    uses (one QDQ path for both sides; arXiv abstract).
+
+    x [M_src][K] bf16 values as float64; a_rows int [M_total] or None
+    (identity); w_codes [E][N][K]; w_scales [E][N][K/16]; g_w float32 [E];
+    expert_offsets int [E+1].  For output row p of expert e taking row
+    t = a_rows[p]:
+        y[p, n] = bf16( sum_k x[t, k] * w^_e[n, k] )   (float64, one rounding)
+    rows: optional output rows to evaluate (others NaN).
+    Returns float64 [M_total][N] holding bf16 values."""
+    offs = np.asarray(expert_offsets, dtype=np.int64)
+    E = len(offs) - 1
+    M_total = int(offs[-1])
+    N = w_codes.shape[1]
+    x = np.asarray(x, dtype=np.float64)
+    out = np.full((M_total, N), np.nan)
+    want = np.ones(M_total, dtype=bool) if rows is None else np.isin(np.arange(M_total), rows)
+    for e in range(E):
+        p = np.arange(offs[e], offs[e + 1])
+        p = p[want[p]]
+        if p.size == 0:
+            continue
+        t = p if a_rows is None else np.asarray(a_rows, dtype=np.int64)[p]
+        w_hat = dequantize(w_codes[e], w_scales[e], g_w[e])          # [N][K]
+        out[p] = round_to_bf16(x[t] @ w_hat.T)
+    return out

@@ -128,3 +128,63 @@ def test_quantized_residual_on_a_k_subset(k):
     c_ref, s_ref, g_ref, _ = Q.quantize(qa["r"][:, qa["S"]])
     assert np.array_equal(codes, c_ref) and np.array_equal(scales, s_ref) and g == g_ref
     assert np.array_equal(r_hat, Q.fake_quant(c_ref, s_ref, g_ref))
+
+
+# ---------------------------------------------------------- W4A16 forward
+
+def test_w4a16_matches_exact_rational_sum():
+    rng = np.random.default_rng(50)
+    x, w = _problem(rng, 3, 4, 64)
+    wc, ws, gw, _ = Q.qdq_weights(w)
+    y = G.grouped_gemm_w4a16(x, None, wc, ws, gw, [0, 3])
+    g0 = Fraction(float(gw[0]))
+    for m in range(3):
+        for n in range(4):
+            acc = Fraction(0)
+            for kk in range(64):
+                wv = (Fraction(float(F.e2m1_decode(wc[0, n, kk])))
+                      * Fraction(float(F.e4m3_decode(ws[0, n, kk // 16]))) * g0)
+                acc += Fraction(float(x[m, kk])) * wv
+            assert Fraction(float(y[m, n])) == exact.to_bf16(acc)
+
+
+def test_w4a16_equals_w4a4_on_nvfp4_exact_activations():
+    # activations that are their own NVFP4 dequantization (tensor amax
+    # 2688 * 2^-10, so g = 2^-10 and every q*s*g is a bf16 value): the W4A16
+    # product and the plain W4A4 GEMM are then the same sum
+    rng = np.random.default_rng(51)
+    x0, w = _problem(rng, 40, 24, 256, heavy=False)
+    x0 = x0 / np.abs(x0).max() * (2688 * 2.0 ** -10)
+    x0 = _bf16(x0)
+    assert np.abs(x0).max() == 2688 * 2.0 ** -10
+    c, s, g, A = Q.quantize(x0)
+    assert g == np.float32(2.0 ** -10)
+    x = Q.dequantize(c, s, g)
+    assert np.array_equal(_bf16(x), x)
+    c1, s1, g1, _ = Q.quantize(x)
+    assert g1 == g and np.array_equal(s1, s)
+    wc, ws, gw, _ = Q.qdq_weights(w)
+    y16 = G.grouped_gemm_w4a16(x, None, wc, ws, gw, [0, 40])
+    y4 = G.grouped_gemm_rac(c1, s1, g1, None, None, [], wc, ws, gw, [0, 40])
+    assert np.array_equal(y16, y4)
+
+
+def test_w4a16_grouped_gather_and_the_compensation_limit():
+    rng = np.random.default_rng(52)
+    x, _ = _problem(rng, 20, 16, 128)
+    w = _bf16(rng.standard_normal((3, 16, 128)) * 0.02)
+    wc, ws, gw, _ = Q.qdq_weights(w)
+    offs = [0, 9, 9, 31]
+    a_rows = rng.integers(0, 20, 31)
+    y = G.grouped_gemm_w4a16(x, a_rows, wc, ws, gw, offs)
+    for e, (lo, hi) in enumerate(zip(offs[:-1], offs[1:])):
+        if lo == hi:
+            continue
+        w_hat = Q.dequantize(wc[e], ws[e], gw[e])
+        assert np.array_equal(y[lo:hi], _bf16(x[a_rows[lo:hi]] @ w_hat.T))
+    # compensating every channel approaches the W4A16 product (bf16 residual)
+    qa = Q.quantize_activation(x, 128)
+    yk = G.grouped_gemm_rac(qa["codes"], qa["scales"], qa["g"], a_rows, qa["R_S"], qa["S"],
+                            wc, ws, gw, offs)
+    y0 = G.grouped_gemm_rac(qa["codes"], qa["scales"], qa["g"], a_rows, None, [], wc, ws, gw, offs)
+    assert _rownorm_err(yk, y) <= 2e-3 < _rownorm_err(y0, y)
