@@ -27,6 +27,7 @@ the same block.
 
     python bench.py --calibrate-copy     # 1 GiB device copy, for counter scaling
     python bench.py --rac-sweep [--config C]   # compensation strength against cost
+    python bench.py --w4a16 [--config C]       # trainer-side W4A16 product, same shapes
 """
 from __future__ import annotations
 
@@ -59,6 +60,8 @@ def parse():
                     help="only run a 1 GiB device-to-device copy three times")
     ap.add_argument("--rac-sweep", action="store_true",
                     help="only sweep the number of compensated channels k on the first GEMM")
+    ap.add_argument("--w4a16", action="store_true",
+                    help="only time the trainer-side W4A16 product on the block's GEMM shapes")
     return ap.parse_args()
 
 
@@ -368,6 +371,64 @@ def rac_sweep(cfg, wl, reps, n_experts=8):
             f"{len(busy)} experts with rows", "reps": reps, "points": points}
 
 
+def w4a16_bench(cfg, wl, reps):
+    """The trainer-side W4A16 product (grouped_w4a16_gemm) on the block's
+    GEMM shapes, beside the W4A4 GEMM without correction on the same shapes:
+    HIP-event medians of `reps` calls, flops 2 * rows * N * K against the
+    dense bf16 MFMA peak.  The down GEMM's bf16 input is a synthetic N(0,1)
+    tensor of the SwiGLU output's shape."""
+    import numpy as np
+    import torch
+
+    import fp4_quantized_gemm_amd as F
+
+    dev = torch.device("cuda:0")
+    x = to_dev(wl.x, dev)
+    if cfg.kind == "dense":
+        offs = torch.tensor([0, cfg.T], dtype=torch.int32, device=dev)
+        perm, rows = None, cfg.T
+    else:
+        logits = torch.from_numpy(wl.logits).to(dev)
+        bias = torch.from_numpy(wl.bias).to(dev) if wl.bias is not None else None
+        _, _, offs, perm, _ = F.moe_permute(logits, cfg.topk, bias)
+        rows = perm.numel()
+    gemms = [("first", x, perm, to_dev(wl.w_first, dev))]
+    if wl.w_down is not None:
+        g = torch.Generator(device=dev).manual_seed(0)
+        h = torch.randn((rows, cfg.inter), generator=g, device=dev).to(torch.bfloat16)
+        gemms.append(("down", h, None, to_dev(wl.w_down, dev)))
+
+    def median_ms(fn):
+        ts = []
+        for _ in range(reps + 2):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ts[2:]]))
+
+    out = []
+    for name, a, a_rows, w in gemms:
+        c, s, gw, _ = F.nvfp4_qdq_weights(w, want_qdq=False)
+        del w
+        q = F.nvfp4_quantize_act(a, False, False)
+        E, N, Kh = c.shape
+        K = 2 * Kh
+        t16 = median_ms(lambda: F.grouped_w4a16_gemm(a, a_rows, c, s, gw, offs, M_total=rows))
+        t4 = median_ms(lambda: F.grouped_w4a4_gemm_rac(q["codes"], q["scales"], q["g"], a_rows,
+                                                       None, None, c, s, gw, offs, M_total=rows))
+        fl = 2.0 * rows * N * K
+        out.append({"gemm": f"{name} {rows}x{N}x{K}", "w4a16_ms": round(t16, 4),
+                    "w4a16_tflops": round(fl / t16 / 1e9, 1),
+                    "w4a16_frac_bf16_peak": round(fl / t16 / 1e9 / PEAK_BF16_TFLOPS, 4),
+                    "w4a4_k0_ms": round(t4, 4)})
+        print(f"# {out[-1]}", file=sys.stderr, flush=True)
+    return {"mode": "w4a16", "workload": cfg.name, "reps": reps, "gemms": out}
+
+
 def gemm_algorithmic_bytes(cfg, counts):
     """Bytes one step's GEMM calls must move: NVFP4 weights (codes + E4M3
     scales, 0.5625 B/elem) of experts that have rows, the activation codes of
@@ -394,6 +455,9 @@ def main():
     wl = synth.make(cfg)
     if args.rac_sweep:
         print(json.dumps(rac_sweep(cfg, wl, max(args.steps // 2, 5))), flush=True)
+        return
+    if args.w4a16:
+        print(json.dumps(w4a16_bench(cfg, wl, max(args.steps // 2, 5))), flush=True)
         return
     ms, stage_ms, rac, counts = run_gpu(cfg, wl, args.steps, args.warmup)
     shapes = cfg.gemm_shapes()

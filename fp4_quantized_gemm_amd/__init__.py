@@ -10,8 +10,9 @@ there is no fallback: importing the library fails loudly if it is missing.
 Calls (same names as the C ABI):
     nvfp4_qdq_weights, nvfp4_quantize_act, select_residual_channels,
     moe_permute, grouped_w4a4_gemm_rac, moe_unpermute_combine
-and, for the NVFP4-quantized-residual variant of the correction,
-    nvfp4_qdq_residual
+and, for the NVFP4-quantized-residual variant of the correction and the
+trainer-side W4A16 product,
+    nvfp4_qdq_residual, grouped_w4a16_gemm
 """
 from __future__ import annotations
 
@@ -24,7 +25,7 @@ from .build import LIB as LIB_PATH
 
 __all__ = ["lib", "nvfp4_qdq_weights", "nvfp4_quantize_act", "select_residual_channels",
            "moe_permute", "grouped_w4a4_gemm_rac", "moe_unpermute_combine", "nvfp4_qdq_residual",
-           "NvfpError",
+           "grouped_w4a16_gemm", "NvfpError",
            "EXPORTED_SYMBOLS"]
 
 EXPORTED_SYMBOLS = [
@@ -36,6 +37,7 @@ EXPORTED_SYMBOLS = [
     "grouped_w4a4_gemm_rac_workspace_size", "grouped_w4a4_gemm_rac",
     "moe_unpermute_combine",
     "nvfp4_qdq_residual_workspace_size", "nvfp4_qdq_residual",
+    "grouped_w4a16_gemm_workspace_size", "grouped_w4a16_gemm",
 ]
 
 
@@ -67,6 +69,7 @@ def _load():
         "moe_permute_workspace_size": [_I64, _I64],
         "grouped_w4a4_gemm_rac_workspace_size": [_I64, _I64, _I64, _I64, _I64, _I64],
         "nvfp4_qdq_residual_workspace_size": [_I64, _I64],
+        "grouped_w4a16_gemm_workspace_size": [_I64],
     }.items():
         f = getattr(L, name)
         f.restype = _SZ
@@ -80,6 +83,8 @@ def _load():
                                   _I64, _I64, _P, _P, _SZ, _P],
         "moe_unpermute_combine": [_P, _P, _P, _I64, _I64, _I64, _P, _P],
         "nvfp4_qdq_residual": [_P, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P],
+        "grouped_w4a16_gemm": [_P, _P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _SZ,
+                               _P],
     }
     for name, args in sigs.items():
         f = getattr(L, name)
@@ -232,6 +237,27 @@ def grouped_w4a4_gemm_rac(a_codes, a_scales, g_x, a_rows, R_S, S, w_codes, w_sca
                                    _ptr(w_codes), _ptr(w_scales), _ptr(g_w), _ptr(expert_offsets),
                                    E, M_total, N, K, _ptr(y), _ptr(ws), ws.numel(), _stream(dev)),
            "grouped_w4a4_gemm_rac")
+    return y
+
+
+def grouped_w4a16_gemm(x, a_rows, w_codes, w_scales, g_w, expert_offsets, M_total=None,
+                       out=None):
+    """Y [M_total][N] bf16 = x (bf16, gathered by a_rows) times the
+    dequantized NVFP4 weights of each row's expert: the trainer-side W4A16
+    product."""
+    L = _load()
+    _need(x, torch.bfloat16, "x")
+    M_src, K = x.shape
+    E, N, _ = w_codes.shape
+    if M_total is None:
+        M_total = int(a_rows.numel()) if a_rows is not None else M_src
+    dev = x.device
+    y = out if out is not None else torch.empty((M_total, N), dtype=torch.bfloat16, device=dev)
+    ws = _ws(L.grouped_w4a16_gemm_workspace_size(E), dev)
+    _check(L.grouped_w4a16_gemm(_ptr(x), _ptr(a_rows), M_src, _ptr(w_codes), _ptr(w_scales),
+                                _ptr(g_w), _ptr(expert_offsets), E, M_total, N, K, _ptr(y),
+                                _ptr(ws), ws.numel(), _stream(dev)),
+           "grouped_w4a16_gemm")
     return y
 
 

@@ -356,6 +356,13 @@ k_decode_a(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales
 // Eight waves (two per SIMD, so one wave's waits are covered by the other's
 // MFMAs): wave w owns rows 128 * (w / 4) .. +128 and columns 64 * (w % 4) .. +64
 // of the 256x256 tile.
+//
+// W16 = true is the trainer-side W4A16 product (bf16 activations times the
+// same dequantized weights): A is the bf16 activation itself, staged the same
+// way (the 8-element chunk the image would hold in slot c is chunk
+// 4 (c & 1) + (c >> 1) of the row's 64-wide block), the weights are decoded to
+// bf16 (q * s, exact), the MFMA is bf16, and there is no correction.
+template <bool W16>
 __global__ void __launch_bounds__(512, 1)
 k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_tiles) {
   using namespace big;
@@ -415,7 +422,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   const int64_t p0 = e_lo + (int64_t)(gt - p.tile_prefix[e]) * BM;
   const int64_t n0 = (int64_t)nt * BN;
   const uint32_t Kh = (uint32_t)(p.K / 2), Ks = (uint32_t)(p.K / 16), K2 = (uint32_t)(p.K * 2);
-  const int kk = p.k;
+  const int kk = W16 ? 0 : p.k;
 
   if (tid < BM) {
     int64_t pr = p0 + tid;
@@ -458,7 +465,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   for (int i = 0; i < 4; ++i) {
     const int q = (i * 8 + wave) * 64 + lane;
     const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
-    off_a[i] = (uint32_t)rows_src[r] * K2 + 16u * c;
+    off_a[i] = (uint32_t)rows_src[r] * K2 + 16u * (W16 ? 4 * (c & 1) + (c >> 1) : c);
   }
   {
     const int q = wave * 64 + lane;
@@ -536,7 +543,10 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
       float sbv[2];
       h2_t mb[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) scale_prep((bs[j] >> (8 * hb)) & 0xFFu, sbv[j], mb[j]);
+      for (int j = 0; j < 2; ++j) {
+        if constexpr (W16) sbv[j] = e4m3_decode((bs[j] >> (8 * hb)) & 0xFFu);
+        else scale_prep((bs[j] >> (8 * hb)) & 0xFFu, sbv[j], mb[j]);
+      }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const int t = 2 * hb + s2;
@@ -550,9 +560,15 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const uint32_t w = t == 0 ? br[j].x : t == 1 ? br[j].y : t == 2 ? br[j].z : br[j].w;
-          const u32x4 B = decode8_f16(w, sbv[j], mb[j]);
+          if constexpr (W16) {
+            const u32x4 B = decode8_bf16(w, sbv[j]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i][j] = mfma32_f16(A[i], B, acc[i][j]);
+            for (int i = 0; i < 4; ++i) acc[i][j] = mfma32_bf16(A[i], B, acc[i][j]);
+          } else {
+            const u32x4 B = decode8_f16(w, sbv[j], mb[j]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i][j] = mfma32_f16(A[i], B, acc[i][j]);
+          }
         }
       }
     }
@@ -560,7 +576,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
     // copy the selected columns' weights (exact in bf16) into the W_S rows,
     // from the codes this lane holds (after the MFMAs are issued, which run
     // meanwhile): the waves of row half wm take code dwords 2 wm, 2 wm + 1
-    if (selm != 0u) {
+    if (!W16 && selm != 0u) {
 #pragma unroll
       for (int tq = 0; tq < 2; ++tq) {
         const int t = 2 * wm + tq;               // wave-uniform
@@ -595,11 +611,13 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
 
   // epilogue: x g_x, residual K-extension (16 channels per MFMA), x g_w.
   // Residual operand loads are issued in batches of four chunks, then consumed.
-  const float gx = *p.g_x;
+  if constexpr (!W16) {
+    const float gx = *p.g_x;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] *= gx;
+      for (int j = 0; j < 2; ++j) acc[i][j] *= gx;
+  }
 
   // (the loop ends on stage st1: the first residual half is in st0)
   auto rac_half = [&](const uint8_t* rb, int cb0) {
@@ -1202,13 +1220,66 @@ int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const
     k_decode_a<<<(unsigned)nb, 256, 0, s>>>(a_codes, a_scales, M_src, K, img);
     k_tile_prefix<<<1, 1024, 0, s>>>(expert_offsets, (int)E, M_total, big::BM, prefix);
     const int64_t nblk = (((m_tiles_big + 3) / 4) * 4 * n_tiles_big + 7) / 8 * 8;
-    k_gemm_big<<<(unsigned)nblk, 512, 0, s>>>(a, reinterpret_cast<const uint8_t*>(img),
-                                             (int)n_tiles_big, (int)m_tiles_big);
+    k_gemm_big<false><<<(unsigned)nblk, 512, 0, s>>>(a, reinterpret_cast<const uint8_t*>(img),
+                                                    (int)n_tiles_big, (int)m_tiles_big);
   } else {
     k_tile_prefix<<<1, 1024, 0, s>>>(expert_offsets, (int)E, M_total, kBM, prefix);
     k_gemm_generic<<<dim3((unsigned)m_tiles, (unsigned)n_tiles), 256, 0, s>>>(a);
   }
   return check_launch("grouped_w4a4_gemm_rac");
+}
+
+size_t grouped_w4a16_gemm_workspace_size(int64_t E) {
+  return img_offset(E < 1 ? 1 : E);
+}
+
+int grouped_w4a16_gemm(const void* x, const int32_t* a_rows, int64_t M_src,
+                       const uint8_t* w_codes, const uint8_t* w_scales, const float* g_w,
+                       const int32_t* expert_offsets, int64_t E, int64_t M_total, int64_t N,
+                       int64_t K, void* y, void* ws, size_t ws_bytes, void* stream) {
+  NV_REQUIRE(E >= 1 && E <= 1024 && M_total >= 0 && N >= 16 && N % 16 == 0 && K >= 128 &&
+                 K % 128 == 0 && K / big::BK <= big::KSTEPS_MAX && M_src >= 0,
+             NVFP4_ERR_SHAPE,
+             "grouped_w4a16_gemm: need 1 <= E <= 1024, N %% 16 == 0, K %% 128 == 0, K <= 16384 "
+             "(E=%lld N=%lld K=%lld)",
+             (long long)E, (long long)N, (long long)K);
+  NV_REQUIRE(a_rows != nullptr || M_src >= M_total, NVFP4_ERR_SHAPE,
+             "grouped_w4a16_gemm: without a_rows, M_src must be >= M_total");
+  NV_REQUIRE(M_total == 0 || M_src >= 1, NVFP4_ERR_SHAPE, "grouped_w4a16_gemm: M_src == 0");
+  NV_REQUIRE((uint64_t)M_src * (uint64_t)K * 2 < (1ULL << 32) &&
+                 (uint64_t)N * (uint64_t)K / 2 < (1ULL << 32),
+             NVFP4_ERR_UNSUPPORTED, "grouped_w4a16_gemm: x or one expert's codes exceed 4 GiB");
+  NV_REQUIRE(w_codes && w_scales && g_w && expert_offsets && ws && (M_total == 0 || (x && y)),
+             NVFP4_ERR_NULL, "grouped_w4a16_gemm: missing pointer");
+  NV_REQUIRE(aligned(x, 16) && aligned(w_codes, 16) && aligned(w_scales, 8) && aligned(ws, 16) &&
+                 aligned(y, 16),
+             NVFP4_ERR_ALIGN, "grouped_w4a16_gemm: misaligned pointer");
+  NV_REQUIRE(ws_bytes >= grouped_w4a16_gemm_workspace_size(E), NVFP4_ERR_WORKSPACE,
+             "grouped_w4a16_gemm: workspace too small");
+  if (M_total == 0) return ok();
+  hipStream_t s = as_stream(stream);
+  int32_t* prefix = static_cast<int32_t*>(ws);
+  GemmArgs a{};
+  a.a_rows = a_rows;
+  a.w_codes = w_codes;
+  a.w_scales = w_scales;
+  a.g_w = g_w;
+  a.offsets = expert_offsets;
+  a.tile_prefix = prefix;
+  a.y = static_cast<uint16_t*>(y);
+  a.M_src = M_src;
+  a.M_total = M_total;
+  a.N = N;
+  a.K = K;
+  a.E = (int)E;
+  a.k = 0;
+  const int64_t n_tiles = (N + big::BN - 1) / big::BN;
+  const int64_t m_tiles = (M_total + big::BM - 1) / big::BM + E;
+  k_tile_prefix<<<1, 1024, 0, s>>>(expert_offsets, (int)E, M_total, big::BM, prefix);
+  const int64_t nblk = (((m_tiles + 3) / 4) * 4 * n_tiles + 7) / 8 * 8;
+  k_gemm_big<true><<<(unsigned)nblk, 512, 0, s>>>(a, static_cast<const uint8_t*>(x), (int)n_tiles,
+                                                  (int)m_tiles);
+  return check_launch("grouped_w4a16_gemm");
 }
 
 }  // extern "C"

@@ -135,6 +135,28 @@ int select_residual_channels(const void* x_used, int64_t ldx, const uint8_t* cod
                              void* stream);
 
 /* ------------------------------------------------------------------------
+ * Trainer-side W4A16 product: the forward of asymmetric W4A16 QAT, bf16
+ * activations against weights that went through the shared QDQ path
+ * (gist.science summary §2.2 A; arXiv abstract).  Same expert grouping,
+ * gather, weight layout and workspace rules as grouped_w4a4_gemm_rac; the
+ * activation is not quantized and there is no correction.
+ *
+ * x      [M_src][K] bf16, contiguous.
+ * y[p][n] (bf16, [M_total][N]) = bf16(sum_k x[t][k] * e2m1 * e4m3 * g_w[e])
+ *        for row p of expert e, t = a_rows ? a_rows[p] : p: exact products
+ *        (q * s decoded exactly to bf16), float32 accumulation, g_w applied
+ *        in float32, one rounding to bf16.
+ * Requires 1 <= E <= 1024, N % 16 == 0, K % 128 == 0, K <= 16384,
+ * M_src * K * 2 < 2^32; a_rows == NULL needs M_src >= M_total.
+ * ---------------------------------------------------------------------- */
+size_t grouped_w4a16_gemm_workspace_size(int64_t E);
+int grouped_w4a16_gemm(const void* x, const int32_t* a_rows, int64_t M_src,
+                       const uint8_t* w_codes, const uint8_t* w_scales, const float* g_w,
+                       const int32_t* expert_offsets, int64_t E, int64_t M_total,
+                       int64_t N, int64_t K, void* y, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* ------------------------------------------------------------------------
  * Second-pass quantization of the compensated residual: the variant of
  * Residual Activation Compensation in which the selected residual is itself
  * quantized to NVFP4 before it is added back (gist.science summary §2.2 B,

@@ -139,3 +139,18 @@ def test_qdq_residual_validation():
     assert L.nvfp4_qdq_residual(FAKE, 8, 32, FAKE, FAKE, FAKE, None, FAKE, ws, None) == ERR_NULL
     assert L.nvfp4_qdq_residual(FAKE_MIS, 8, 32, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None) == ERR_ALIGN
     assert L.nvfp4_qdq_residual(FAKE, 8, 32, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == ERR_WS
+
+
+def test_w4a16_gemm_validation():
+    L = F.lib()
+    ws = L.grouped_w4a16_gemm_workspace_size(4)
+    args = lambda **kw: [kw.get("x", FAKE), kw.get("rows", None), kw.get("msrc", 64), FAKE, FAKE,
+                         FAKE, FAKE, kw.get("E", 4), 64, kw.get("N", 128), kw.get("K", 256),
+                         FAKE, FAKE, kw.get("ws", ws), None]
+    assert L.grouped_w4a16_gemm(*args(K=192)) == ERR_SHAPE              # K % 128
+    assert L.grouped_w4a16_gemm(*args(K=32768)) == ERR_SHAPE            # K > 16384
+    assert L.grouped_w4a16_gemm(*args(N=120)) == ERR_SHAPE              # N % 16
+    assert L.grouped_w4a16_gemm(*args(msrc=10)) == ERR_SHAPE            # no gather, M_src < M_total
+    assert L.grouped_w4a16_gemm(*args(x=None)) == ERR_NULL
+    assert L.grouped_w4a16_gemm(*args(x=FAKE_MIS)) == ERR_ALIGN
+    assert L.grouped_w4a16_gemm(*args(ws=0)) == ERR_WS
