@@ -276,8 +276,8 @@ def gemm_kernel_name(cfg, m, n, k, E):
     MI355X (the library's own dispatch rule, restated for the report)."""
     if m <= 48 * E and k <= 128:
         return "k_gemm_decode"
-    if k <= 128 and (m // 256) * ((n + 255) // 256) >= 512:
-        return "k_gemm_big"
+    if (k <= 128 or k % 128 == 0) and (m // 256) * ((n + 255) // 256) >= 512:
+        return "k_gemm_big" if k <= 128 else "k_extract_ws + k_gemm_big"
     return "k_gemm_generic"
 
 

@@ -43,6 +43,7 @@ struct GemmArgs {
   const uint8_t* w_codes;
   const uint8_t* w_scales;
   const float* g_w;
+  const uint16_t* wsel;        // [E][N][k] bf16 q * s of the selected columns (large k only)
   const int32_t* offsets;
   const int32_t* tile_prefix;
   uint16_t* y;
@@ -423,28 +424,32 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   const int64_t n0 = (int64_t)nt * BN;
   const uint32_t Kh = (uint32_t)(p.K / 2), Ks = (uint32_t)(p.K / 16), K2 = (uint32_t)(p.K * 2);
   const int kk = W16 ? 0 : p.k;
+  // more than KMAX channels (a multiple of KMAX): the selected weight columns
+  // come from p.wsel after the loop instead of being copied as it passes
+  const bool sws = kk > KMAX;
+  const int kl = sws ? 0 : kk;                 // channels copied in the loop
 
   if (tid < BM) {
     int64_t pr = p0 + tid;
     if (pr >= e_hi) pr = e_hi - 1;
     int64_t t = p.a_rows ? (int64_t)p.a_rows[pr] : pr;
     rows_src[tid] = (int32_t)(t < 0 ? 0 : (t >= p.M_src ? p.M_src - 1 : t));
-    if (tid < kk) {
+    if (tid < kl) {
       int c = p.S[tid];
       s_local[tid] = c < 0 ? 0 : (c >= p.K ? (int)p.K - 1 : c);
     }
-    const int kpad = (kk + 15) & ~15;          // zero slots k .. next multiple of 16
-    for (int j = kk; j < kpad; ++j) *reinterpret_cast<uint16_t*>(wsl + tid * WSROW + 2 * j) = 0;
+    const int kpad = (kl + 15) & ~15;          // zero slots k .. next multiple of 16
+    for (int j = kl; j < kpad; ++j) *reinterpret_cast<uint16_t*>(wsl + tid * WSROW + 2 * j) = 0;
   }
   __syncthreads();
   const int nk = (int)(p.K / BK);
-  if (kk > 0) {
+  if (kl > 0) {
     // (S is strictly ascending, so bit ranks are the indices j)
     for (int w = tid; w < 2 * nk; w += 512) sel_bm[w] = 0u;
     __syncthreads();
-    for (int j = tid; j < kk; j += 512) atomicOr(&sel_bm[s_local[j] >> 5], 1u << (s_local[j] & 31));
+    for (int j = tid; j < kl; j += 512) atomicOr(&sel_bm[s_local[j] >> 5], 1u << (s_local[j] & 31));
     for (int g = tid; g <= 2 * nk; g += 512) {
-      int a = 0, b = kk;
+      int a = 0, b = kl;
       while (a < b) {
         const int m = (a + b) >> 1;
         if (s_local[m] < g * 32) a = m + 1; else b = m;
@@ -492,7 +497,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   // residual rows for the correction, staged like the A image: 64 channels
   // of the tile's 256 rows per stage, 8-channel chunks swizzled as A's
   // (whole 64-channel halves, so only when k % 64 == 0)
-  const bool rdma = kk > 0 && (kk & 63) == 0;
+  const bool rdma = kl > 0 && (kl & 63) == 0;
   auto issue_r = [&](uint8_t* st, int cb0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -534,7 +539,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
     // index j of the first of them
     uint32_t selm = 0u;
     int jb = 0;
-    if (kk > 0) {
+    if (kl > 0) {
       selm = sel_bm[2 * kt + kg];
       jb = rank32[2 * kt + kg];
     }
@@ -649,7 +654,32 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
       rac_half(st1, 64);
     }
   }
-  for (int cb0 = 0; !rdma && cb0 < kk; cb0 += 64) {
+  if (sws) {
+    // the correction in chunks of KMAX channels: the chunk's weight columns
+    // (bf16 q * s from k_extract_ws) go to the W_S tile by global->LDS loads
+    // (1 KB per wave instruction; the 16-byte row pads are skipped), its
+    // residual rows to the two stages, then the same bf16 MFMAs
+    const uint16_t* wse = p.wsel + (int64_t)e * p.N * kk;
+    for (int c0 = 0; c0 < kk; c0 += KMAX) {
+      __syncthreads();                         // the last reads of wsl and the stages are done
+      for (int b = wave; b * 1024 < BN * WSROW; b += 8) {
+        const int o = b * 1024 + lane * 16;
+        const int row = o / WSROW, cb = o - row * WSROW;
+        if (row < BN && cb < KMAX * 2) {
+          int64_t n = n0 + row;
+          if (n >= p.N) n = p.N - 1;
+          __builtin_amdgcn_global_load_lds(wse + n * kk + c0 + cb / 2, wsl + b * 1024, 16, 0, 0);
+        }
+      }
+      issue_r(st0, c0);
+      issue_r(st1, c0 + 64);
+      wait_vmem0();
+      __syncthreads();
+      rac_half(st0, 0);
+      rac_half(st1, 64);
+    }
+  }
+  for (int cb0 = 0; !rdma && !sws && cb0 < kk; cb0 += 64) {
     u32x4 A[4][4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -712,6 +742,27 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
         *reinterpret_cast<uint4*>(p.y + prow * p.N + n) =
             *reinterpret_cast<const uint4*>(wsl + row * OUTROW + ch * 16);
     }
+  }
+}
+
+// Weight columns of the selected channels for the large-k correction: bf16
+// q * s (exact; no tensor scale) of column S[j] of each expert row,
+// wsel[e][n][j].  One workgroup per weight row.
+__global__ void __launch_bounds__(256)
+k_extract_ws(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+             const int32_t* __restrict__ S, int64_t N, int64_t K, int k,
+             uint16_t* __restrict__ wsel) {
+  const int64_t row = blockIdx.x;                // e * N + n
+  const int64_t e = row / N, n = row - e * N;
+  const uint8_t* cr = codes + row * (K / 2);
+  const uint8_t* sc = scales + e * N * (K / 16);
+  for (int j = threadIdx.x; j < k; j += 256) {
+    int c = S[j];
+    c = c < 0 ? 0 : (c >= K ? (int)K - 1 : c);
+    const uint32_t code = (cr[c >> 1] >> (4 * (c & 1))) & 0xFu;
+    const float q = e2m1_unpack2<0>(code).x;
+    const float sv = e4m3_decode(sc[wscale_offset(n, c >> 4, K)]);
+    wsel[row * k + j] = (uint16_t)(__float_as_uint(q * sv) >> 16);
   }
 }
 
@@ -1112,13 +1163,17 @@ extern "C" {
 // prefix [E+1] int32, then (large-tile path) the f16 image of A [M_src][K]
 static size_t img_offset(int64_t E) { return round_up((size_t)(E + 1) * sizeof(int32_t), 256); }
 
+// large k (more than the large-tile kernel's W_S tile, a multiple of it):
+// the selected weight columns, bf16 [E][N][k], after the image
+static bool big_streams_ws(int64_t k) { return k > big::KMAX && k % big::KMAX == 0; }
+
 size_t grouped_w4a4_gemm_rac_workspace_size(int64_t E, int64_t M_src, int64_t M_total, int64_t N,
                                             int64_t K, int64_t k) {
   (void)M_total;
-  (void)N;
-  (void)k;
-  if (E < 1 || M_src < 0 || K < 0) return 256;
-  return img_offset(E) + round_up((size_t)M_src * (size_t)K * 2, 256);
+  if (E < 1 || M_src < 0 || K < 0 || N < 0) return 256;
+  size_t n = img_offset(E) + round_up((size_t)M_src * (size_t)K * 2, 256);
+  if (big_streams_ws(k)) n += round_up((size_t)E * (size_t)N * (size_t)k * 2, 256);
+  return n;
 }
 
 int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
@@ -1147,7 +1202,7 @@ int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const
   if (M_total == 0) return ok();
   hipStream_t s = as_stream(stream);
   int32_t* prefix = static_cast<int32_t*>(ws);
-  GemmArgs a;
+  GemmArgs a{};
   a.a_codes = a_codes;
   a.a_scales = a_scales;
   a.g_x = g_x;
@@ -1210,10 +1265,17 @@ int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const
     return check_launch("grouped_w4a4_gemm_rac");
   }
   const size_t need_big = grouped_w4a4_gemm_rac_workspace_size(E, M_src, M_total, N, K, k);
-  use_big = use_big && k <= big::KMAX && K / big::BK <= big::KSTEPS_MAX && ws_bytes >= need_big &&
-            (uint64_t)M_src * K * 2 < (1ULL << 32) && (uint64_t)M_src * k * 2 < (1ULL << 32);
+  use_big = use_big && (k <= big::KMAX || big_streams_ws(k)) && K / big::BK <= big::KSTEPS_MAX &&
+            ws_bytes >= need_big && (uint64_t)M_src * K * 2 < (1ULL << 32) &&
+            (uint64_t)M_src * k * 2 < (1ULL << 32);
   if (use_big) {
     uint16_t* img = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + img_offset(E));
+    if (big_streams_ws(k)) {
+      uint16_t* wsel = reinterpret_cast<uint16_t*>(
+          static_cast<char*>(ws) + img_offset(E) + round_up((size_t)M_src * (size_t)K * 2, 256));
+      k_extract_ws<<<(unsigned)(E * N), 256, 0, s>>>(w_codes, w_scales, S, N, K, (int)k, wsel);
+      a.wsel = wsel;
+    }
     const int64_t chunks = M_src * (K / 8);
     int64_t nb = (chunks + 255) / 256;
     if (nb > 16LL * num_cus()) nb = 16LL * num_cus();

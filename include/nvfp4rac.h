@@ -214,6 +214,10 @@ int moe_permute(const float* logits, const float* bias, int64_t T, int64_t E, in
  * (the tiles nvfp4_qdq_weights writes), g_w [E];
  * expert_offsets [E+1] (device; off[0] = 0, off[E] = M_total); y [M_total][N]
  * bf16.  Requires K % 128 == 0, N % 16 == 0, 0 <= k <= K.
+ * The workspace holds the per-expert tile prefix and, for large problems,
+ * an exact f16 image of the activation (2 bytes per element) and, when k
+ * exceeds 128 and is a multiple of 128, the selected weight columns as bf16
+ * (E * N * k * 2 bytes).
  * ---------------------------------------------------------------------- */
 size_t grouped_w4a4_gemm_rac_workspace_size(int64_t E, int64_t M_src, int64_t M_total,
                                             int64_t N, int64_t K, int64_t k);

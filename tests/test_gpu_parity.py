@@ -208,6 +208,9 @@ def gemm_kernel(request, monkeypatch):
     (500, [17, 0, 0, 400, 83], 272, 1024, 128, True),
     (700, [300, 1, 511, 0, 255], 528, 768, 64, True),  # several 256-row tiles, N tail
     (64, [3, 0, 17, 33, 1, 0, 16, 40], 512, 1024, 64, True),  # decode-sized: 0-40 rows each
+    (300, [100, 200], 256, 1024, 256, True),           # large k: two 128-channel chunks
+    (500, [17, 0, 0, 400, 83], 272, 1024, 384, True),  # three chunks, N tail
+    (96, [50, 46], 128, 512, 512, False),              # large k = K: every channel
 ])
 def test_grouped_gemm_rac(dev, gemm_kernel, M_src, counts, N, K, k, gather):
     say(f"gemm[{gemm_kernel}] counts={counts} N={N} K={K} k={k} gather={gather}")
