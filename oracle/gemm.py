@@ -86,3 +86,32 @@ def grouped_gemm_w4a16(x, a_rows, w_codes, w_scales, g_w, expert_offsets, rows=N
         w_hat = dequantize(w_codes[e], w_scales[e], g_w[e])          # [N][K]
         out[p] = round_to_bf16(x[t] @ w_hat.T)
     return out
+
+
+def grouped_gemm_rac_per_expert(a_codes, a_scales, g_x, a_rows, R_P, S_E, w_codes, w_scales, g_w,
+                                expert_offsets, rows=None):
+    """grouped_gemm_rac with a channel set per expert: S_E int [E][k], and
+    the residual indexed by permuted row, R_P [M_total][k] (R_P[p] holds the
+    residual of row a_rows[p] on the channels S_E[e] of p's expert e):
+        y64[p, n] = sum_k x^[t, k] w^_e[n, k] + sum_j R_P[p, j] w^_e[n, S_E[e, j]]
+    and y = bf16(y64)."""
+    offs = np.asarray(expert_offsets, dtype=np.int64)
+    E = len(offs) - 1
+    M_total = int(offs[-1])
+    N = w_codes.shape[1]
+    x_hat = dequantize(a_codes, a_scales, g_x)
+    out = np.full((M_total, N), np.nan)
+    want = np.ones(M_total, dtype=bool) if rows is None else np.isin(np.arange(M_total), rows)
+    S_E = np.asarray(S_E, dtype=np.int64)
+    for e in range(E):
+        p = np.arange(offs[e], offs[e + 1])
+        p = p[want[p]]
+        if p.size == 0:
+            continue
+        t = p if a_rows is None else np.asarray(a_rows, dtype=np.int64)[p]
+        w_hat = dequantize(w_codes[e], w_scales[e], g_w[e])
+        y = x_hat[t] @ w_hat.T
+        if S_E.shape[1]:
+            y = y + np.asarray(R_P, dtype=np.float64)[p] @ w_hat[:, S_E[e]].T
+        out[p] = round_to_bf16(y)
+    return out

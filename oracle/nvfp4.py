@@ -215,3 +215,35 @@ def unpack_codes(packed) -> np.ndarray:
     out[..., 0::2] = p & 0xF
     out[..., 1::2] = p >> 4
     return out
+
+
+def select_channels_per_expert(x, codes, scales, g, A, a_rows, expert_offsets, k: int):
+    """Per-expert channel selection (a variant of the binary channel mask of
+    gist.science technical summary §2.2 B in which each expert ranks the
+    channels by the residual of its own rows).
+
+    x, codes, scales, g, A: the quantized activation [M_src][K] as from
+    quantize(); a_rows int [M_total] or None (identity): the activation row
+    of each permuted row; expert_offsets int [E+1].  For expert e with
+    permuted rows p in [off[e], off[e+1]) taking rows t = a_rows[p]:
+        score_e[j] = sum over its rows of floor(|r[t, j]| * 2**(31 - E_A))
+    (the channel_scores statistic restricted to those rows, E_A from the
+    tensor amax A), S_e = the k channels of largest score_e (ties: lower
+    index) ascending, and R[p] = r[t, S_e].
+
+    Returns (S int32 [E][k], R float64 [M_total][k], score uint64 [E][K])."""
+    offs = np.asarray(expert_offsets, dtype=np.int64)
+    E = len(offs) - 1
+    M_total = int(offs[-1])
+    K = np.asarray(codes).shape[1]
+    r = residual(x, codes, scales, g)
+    rows = np.arange(M_total) if a_rows is None else np.asarray(a_rows, dtype=np.int64)
+    S = np.zeros((E, k), dtype=np.int32)
+    R = np.zeros((M_total, k))
+    score = np.zeros((E, K), dtype=np.uint64)
+    for e in range(E):
+        t = rows[offs[e]:offs[e + 1]]
+        score[e] = channel_scores(r[t], A) if t.size else np.zeros(K, dtype=np.uint64)
+        S[e] = select_channels(score[e], k)
+        R[offs[e]:offs[e + 1]] = r[t][:, S[e]]
+    return S, R, score

@@ -188,3 +188,76 @@ def test_w4a16_grouped_gather_and_the_compensation_limit():
                             wc, ws, gw, offs)
     y0 = G.grouped_gemm_rac(qa["codes"], qa["scales"], qa["g"], a_rows, None, [], wc, ws, gw, offs)
     assert _rownorm_err(yk, y) <= 2e-3 < _rownorm_err(y0, y)
+
+
+# ------------------------------------------------- per-expert selection
+
+def _routed(rng, M_src, counts):
+    offs = np.zeros(len(counts) + 1, dtype=np.int64)
+    offs[1:] = np.cumsum(counts)
+    a_rows = rng.integers(0, M_src, int(offs[-1]))
+    return offs, a_rows
+
+
+def test_per_expert_selection_with_one_expert_is_the_shared_selection():
+    rng = np.random.default_rng(60)
+    x, _ = _problem(rng, 48, 8, 256)
+    qa = Q.quantize_activation(x, 40)
+    S, R, score = Q.select_channels_per_expert(x, qa["codes"], qa["scales"], qa["g"], qa["A"],
+                                               None, [0, 48], 40)
+    assert np.array_equal(score[0], qa["score"])
+    assert np.array_equal(S[0], qa["S"]) and np.array_equal(R, qa["R_S"])
+
+
+def test_per_expert_scores_exact_and_dominant():
+    rng = np.random.default_rng(61)
+    x, _ = _problem(rng, 30, 8, 64)
+    codes, scales, g, A = Q.quantize(x)
+    offs, a_rows = _routed(rng, 30, [11, 0, 25, 7])
+    S, R, score = Q.select_channels_per_expert(x, codes, scales, g, A, a_rows, offs, 9)
+    r = Q.residual(x, codes, scales, g)
+    m, E_A = np.frexp(float(A))
+    for e in (0, 2, 3):
+        t = a_rows[offs[e]:offs[e + 1]]
+        for j in (0, 5, 40, 63):
+            want = sum(int((abs(Fraction(float(r[i, j]))) * Fraction(2) ** (31 - E_A)).__floor__())
+                       for i in t)
+            assert int(score[e, j]) == want
+        sel = set(S[e].tolist())
+        for a in sel:
+            for b in set(range(64)) - sel:
+                assert score[e, a] > score[e, b] or (score[e, a] == score[e, b] and a < b)
+        assert np.array_equal(R[offs[e]:offs[e + 1]], r[t][:, S[e]])
+        # the order of an expert's rows does not matter
+        perm = rng.permutation(t.size)
+        a2 = a_rows.copy()
+        a2[offs[e]:offs[e + 1]] = t[perm]
+        S2, _, sc2 = Q.select_channels_per_expert(x, codes, scales, g, A, a2, offs, 9)
+        assert np.array_equal(S2, S) and np.array_equal(sc2, score)
+    # an expert with no rows scores zero everywhere and takes channels 0..k-1
+    assert not score[1].any() and list(S[1]) == list(range(9))
+
+
+def test_per_expert_gemm_with_a_common_set_is_the_shared_gemm():
+    rng = np.random.default_rng(62)
+    x, _ = _problem(rng, 40, 8, 128)
+    w = _bf16(rng.standard_normal((3, 16, 128)) * 0.02)
+    wc, ws, gw, _ = Q.qdq_weights(w)
+    offs, a_rows = _routed(rng, 40, [13, 20, 9])
+    qa = Q.quantize_activation(x, 24)
+    y_shared = G.grouped_gemm_rac(qa["codes"], qa["scales"], qa["g"], a_rows, qa["R_S"], qa["S"],
+                                  wc, ws, gw, offs)
+    S_E = np.tile(qa["S"], (3, 1))
+    y_pe = G.grouped_gemm_rac_per_expert(qa["codes"], qa["scales"], qa["g"], a_rows,
+                                         qa["R_S"][a_rows], S_E, wc, ws, gw, offs)
+    assert np.array_equal(y_pe, y_shared)
+    # with each expert's own channels, the correction is linear in R_P
+    S, R, _ = Q.select_channels_per_expert(x, qa["codes"], qa["scales"], qa["g"], qa["A"], a_rows,
+                                           offs, 24)
+    y = G.grouped_gemm_rac_per_expert(qa["codes"], qa["scales"], qa["g"], a_rows, R, S, wc, ws, gw,
+                                      offs)
+    x_hat = Q.dequantize(qa["codes"], qa["scales"], qa["g"])
+    for e in range(3):
+        p = np.arange(offs[e], offs[e + 1])
+        w_hat = Q.dequantize(wc[e], ws[e], gw[e])
+        assert np.array_equal(y[p], _bf16(x_hat[a_rows[p]] @ w_hat.T + R[p] @ w_hat[:, S[e]].T))
