@@ -10,9 +10,9 @@ there is no fallback: importing the library fails loudly if it is missing.
 Calls (same names as the C ABI):
     nvfp4_qdq_weights, nvfp4_quantize_act, select_residual_channels,
     moe_permute, grouped_w4a4_gemm_rac, moe_unpermute_combine
-and, for the NVFP4-quantized-residual variant of the correction and the
-trainer-side W4A16 product,
-    nvfp4_qdq_residual, grouped_w4a16_gemm
+and, for the variants of the correction and the trainer-side W4A16 product,
+    nvfp4_qdq_residual, select_residual_channels_per_expert,
+    grouped_w4a4_gemm_rac_per_expert, grouped_w4a16_gemm
 """
 from __future__ import annotations
 
@@ -25,7 +25,8 @@ from .build import LIB as LIB_PATH
 
 __all__ = ["lib", "nvfp4_qdq_weights", "nvfp4_quantize_act", "select_residual_channels",
            "moe_permute", "grouped_w4a4_gemm_rac", "moe_unpermute_combine", "nvfp4_qdq_residual",
-           "grouped_w4a16_gemm", "NvfpError",
+           "grouped_w4a16_gemm", "select_residual_channels_per_expert",
+           "grouped_w4a4_gemm_rac_per_expert", "NvfpError",
            "EXPORTED_SYMBOLS"]
 
 EXPORTED_SYMBOLS = [
@@ -38,6 +39,8 @@ EXPORTED_SYMBOLS = [
     "moe_unpermute_combine",
     "nvfp4_qdq_residual_workspace_size", "nvfp4_qdq_residual",
     "grouped_w4a16_gemm_workspace_size", "grouped_w4a16_gemm",
+    "select_residual_channels_per_expert_workspace_size", "select_residual_channels_per_expert",
+    "grouped_w4a4_gemm_rac_per_expert",
 ]
 
 
@@ -70,6 +73,7 @@ def _load():
         "grouped_w4a4_gemm_rac_workspace_size": [_I64, _I64, _I64, _I64, _I64, _I64],
         "nvfp4_qdq_residual_workspace_size": [_I64, _I64],
         "grouped_w4a16_gemm_workspace_size": [_I64],
+        "select_residual_channels_per_expert_workspace_size": [_I64, _I64],
     }.items():
         f = getattr(L, name)
         f.restype = _SZ
@@ -85,6 +89,10 @@ def _load():
         "nvfp4_qdq_residual": [_P, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P],
         "grouped_w4a16_gemm": [_P, _P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _SZ,
                                _P],
+        "select_residual_channels_per_expert": [_P, _I64, _P, _P, _P, _P, _P, _I64, _I64, _I64,
+                                                _I64, _I64, _P, _P, _P, _SZ, _P],
+        "grouped_w4a4_gemm_rac_per_expert": [_P, _P, _P, _P, _I64, _P, _P, _I64, _P, _P, _P, _P,
+                                             _I64, _I64, _I64, _I64, _P, _P, _SZ, _P],
     }
     for name, args in sigs.items():
         f = getattr(L, name)
@@ -218,26 +226,61 @@ def moe_permute(logits, topk, bias=None):
     return ids, w, offs, perm, inv
 
 
-def grouped_w4a4_gemm_rac(a_codes, a_scales, g_x, a_rows, R_S, S, w_codes, w_scales, g_w,
-                          expert_offsets, M_total=None, out=None):
-    """Y [M_total][N] bf16 for the expert-grouped W4A4 GEMM plus the residual
-    correction on the channels S (k = len(S), 0 disables it)."""
+def select_residual_channels_per_expert(x_used, codes, scales, g, score_unused, k, a_rows,
+                                        expert_offsets, M_total=None):
+    """Per-expert selection -> (S [E][k] int32, R [M_total][k] bf16 by
+    permuted row).  score_unused is accepted for symmetry with
+    select_residual_channels and ignored (the per-expert scores are formed
+    from the activation itself)."""
+    L = _load()
+    M_src, K = x_used.shape
+    E = int(expert_offsets.numel()) - 1
+    if M_total is None:
+        M_total = int(a_rows.numel()) if a_rows is not None else M_src
+    dev = x_used.device
+    S = torch.empty((E, k), dtype=torch.int32, device=dev)
+    R = torch.empty((M_total, k), dtype=torch.bfloat16, device=dev)
+    ws = _ws(L.select_residual_channels_per_expert_workspace_size(E, K), dev)
+    _check(L.select_residual_channels_per_expert(
+        _ptr(x_used), x_used.stride(0), _ptr(codes), _ptr(scales), _ptr(g), _ptr(a_rows),
+        _ptr(expert_offsets), E, M_src, M_total, K, k, _ptr(S), _ptr(R), _ptr(ws), ws.numel(),
+        _stream(dev)), "select_residual_channels_per_expert")
+    return S, R
+
+
+def _gemm_rac(fn_name, a_codes, a_scales, g_x, a_rows, R, S, w_codes, w_scales, g_w,
+              expert_offsets, M_total, out):
     L = _load()
     M_src, Kh = a_codes.shape
     K = Kh * 2
     E, N, _ = w_codes.shape
-    k = 0 if S is None else int(S.numel())
+    k = 0 if S is None else int(S.shape[-1])
     if M_total is None:
         M_total = int(a_rows.numel()) if a_rows is not None else M_src
     dev = a_codes.device
     y = out if out is not None else torch.empty((M_total, N), dtype=torch.bfloat16, device=dev)
     ws = _ws(L.grouped_w4a4_gemm_rac_workspace_size(E, M_src, M_total, N, K, k), dev)
-    _check(L.grouped_w4a4_gemm_rac(_ptr(a_codes), _ptr(a_scales), _ptr(g_x), _ptr(a_rows), M_src,
-                                   _ptr(R_S) if k else None, _ptr(S) if k else None, k,
-                                   _ptr(w_codes), _ptr(w_scales), _ptr(g_w), _ptr(expert_offsets),
-                                   E, M_total, N, K, _ptr(y), _ptr(ws), ws.numel(), _stream(dev)),
-           "grouped_w4a4_gemm_rac")
+    _check(getattr(L, fn_name)(_ptr(a_codes), _ptr(a_scales), _ptr(g_x), _ptr(a_rows), M_src,
+                               _ptr(R) if k else None, _ptr(S) if k else None, k,
+                               _ptr(w_codes), _ptr(w_scales), _ptr(g_w), _ptr(expert_offsets),
+                               E, M_total, N, K, _ptr(y), _ptr(ws), ws.numel(), _stream(dev)),
+           fn_name)
     return y
+
+
+def grouped_w4a4_gemm_rac_per_expert(a_codes, a_scales, g_x, a_rows, R_P, S_E, w_codes,
+                                     w_scales, g_w, expert_offsets, M_total=None, out=None):
+    """grouped_w4a4_gemm_rac with S_E [E][k] and R_P [M_total][k] by permuted row."""
+    return _gemm_rac("grouped_w4a4_gemm_rac_per_expert", a_codes, a_scales, g_x, a_rows, R_P,
+                     S_E, w_codes, w_scales, g_w, expert_offsets, M_total, out)
+
+
+def grouped_w4a4_gemm_rac(a_codes, a_scales, g_x, a_rows, R_S, S, w_codes, w_scales, g_w,
+                          expert_offsets, M_total=None, out=None):
+    """Y [M_total][N] bf16 for the expert-grouped W4A4 GEMM plus the residual
+    correction on the channels S (k = len(S), 0 disables it)."""
+    return _gemm_rac("grouped_w4a4_gemm_rac", a_codes, a_scales, g_x, a_rows, R_S, S, w_codes,
+                     w_scales, g_w, expert_offsets, M_total, out)
 
 
 def grouped_w4a16_gemm(x, a_rows, w_codes, w_scales, g_w, expert_offsets, M_total=None,

@@ -49,6 +49,11 @@ struct GemmArgs {
   uint16_t* y;
   int64_t M_src, M_total, N, K;
   int E, k;
+  // per-expert compensation: expert e's channels are S[e * s_stride ..]
+  // (s_stride = k; 0 = one set for all experts), and R is indexed by
+  // permuted row (r_perm = 1) instead of by activation row
+  int64_t s_stride;
+  int r_perm;
 };
 
 // tile_prefix[e] = number of 128-row tiles of experts before e; [E] = total
@@ -205,12 +210,14 @@ k_gemm_generic(GemmArgs p) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int slot = kc + 8 * g + t;
-      int c = slot < p.k ? p.S[slot] : -1;
+      int c = slot < p.k ? p.S[(int64_t)e * p.s_stride + slot] : -1;
       ch[t] = c < 0 ? -1 : (c >= p.K ? (int)p.K - 1 : c);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t t = rows_src[wm * 64 + 16 * i + r16];
+      const int lr = wm * 64 + 16 * i + r16;
+      int64_t t = rows_src[lr];
+      if (p.r_perm) t = p0 + lr < e_hi ? p0 + lr : e_hi - 1;
       const uint16_t* rr = p.R + t * p.k + kc + 8 * g;
       uint32_t v[8];
 #pragma unroll
@@ -435,7 +442,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
     int64_t t = p.a_rows ? (int64_t)p.a_rows[pr] : pr;
     rows_src[tid] = (int32_t)(t < 0 ? 0 : (t >= p.M_src ? p.M_src - 1 : t));
     if (tid < kl) {
-      int c = p.S[tid];
+      int c = p.S[(int64_t)e * p.s_stride + tid];
       s_local[tid] = c < 0 ? 0 : (c >= p.K ? (int)p.K - 1 : c);
     }
     const int kpad = (kl + 15) & ~15;          // zero slots k .. next multiple of 16
@@ -503,8 +510,9 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
     for (int i = 0; i < 4; ++i) {
       const int q = (i * 8 + wave) * 64 + lane;
       const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
+      const int64_t rr = p.r_perm ? (p0 + r < e_hi ? p0 + r : e_hi - 1) : rows_src[r];
       const uint8_t* src = reinterpret_cast<const uint8_t*>(p.R) +
-                           (uint32_t)rows_src[r] * (uint32_t)(2 * kk) + 2u * (uint32_t)(cb0 + 8 * c);
+                           (uint32_t)rr * (uint32_t)(2 * kk) + 2u * (uint32_t)(cb0 + 8 * c);
       __builtin_amdgcn_global_load_lds(src, st + (i * 8 + wave) * 1024, 16, 0, 0);
     }
   };
@@ -686,7 +694,9 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
       const int slot = cb0 + 16 * c + 8 * kg;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t t = rows_src[wm * 128 + 32 * i + r32];
+        const int lr = wm * 128 + 32 * i + r32;
+        int64_t t = rows_src[lr];
+        if (p.r_perm) t = p0 + lr < e_hi ? p0 + lr : e_hi - 1;
         const uint16_t* rr = p.R + t * kk + slot;
         if ((kk & 7) == 0 && slot + 8 <= kk) {
           const uint4 vv = *reinterpret_cast<const uint4*>(rr);
@@ -750,10 +760,11 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
 // wsel[e][n][j].  One workgroup per weight row.
 __global__ void __launch_bounds__(256)
 k_extract_ws(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-             const int32_t* __restrict__ S, int64_t N, int64_t K, int k,
+             const int32_t* __restrict__ S, int64_t s_stride, int64_t N, int64_t K, int k,
              uint16_t* __restrict__ wsel) {
   const int64_t row = blockIdx.x;                // e * N + n
   const int64_t e = row / N, n = row - e * N;
+  S += e * s_stride;
   const uint8_t* cr = codes + row * (K / 2);
   const uint8_t* sc = scales + e * N * (K / 16);
   for (int j = threadIdx.x; j < k; j += 256) {
@@ -881,7 +892,7 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
 
   if (kk > 0) {
     for (int j = tid; j < kk; j += 256) {
-      const int c = p.S[j];
+      const int c = p.S[(int64_t)e * p.s_stride + j];
       s_local[j] = c < 0 ? 0 : (c >= p.K ? (int)p.K - 1 : c);
     }
     const int kpad = (kk + 31) & ~31;        // zero channels k .. next multiple of 32
@@ -922,7 +933,7 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
 
   for (int64_t t0 = 0; t0 < Me; t0 += 16 * TMAX) {
     const int ntile_rt = (int)((Me - t0 + 15) / 16 < TMAX ? (Me - t0 + 15) / 16 : TMAX);
-    int64_t src[TMAX];
+    int64_t src[TMAX], rrow[TMAX];
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
       int64_t q = t0 + 16 * t + r16;
@@ -930,6 +941,7 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
       const int64_t pr = e_lo + q;
       int64_t sr = p.a_rows ? (int64_t)p.a_rows[pr] : pr;
       src[t] = sr < 0 ? 0 : (sr >= p.M_src ? p.M_src - 1 : sr);
+      rrow[t] = p.r_perm ? pr : src[t];
     }
 
     // K is a multiple of 128: the lanes of a half chunk past the end (kq >= 2
@@ -1009,7 +1021,7 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
             u32x4 rf[TMAX];
   #pragma unroll
             for (int t = 0; t < TMAX; ++t) {
-              const uint16_t* rr = p.R + src[t] * kk + slot;
+              const uint16_t* rr = p.R + rrow[t] * kk + slot;
               if ((kk & 7) == 0 && slot + 8 <= kk) {
                 const uint4 v = *reinterpret_cast<const uint4*>(rr);
                 rf[t] = u32x4{v.x, v.y, v.z, v.w};
@@ -1176,12 +1188,12 @@ size_t grouped_w4a4_gemm_rac_workspace_size(int64_t E, int64_t M_src, int64_t M_
   return n;
 }
 
-int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
-                          const int32_t* a_rows, int64_t M_src, const void* R_S, const int32_t* S,
-                          int64_t k, const uint8_t* w_codes, const uint8_t* w_scales,
-                          const float* g_w, const int32_t* expert_offsets, int64_t E,
-                          int64_t M_total, int64_t N, int64_t K, void* y, void* ws,
-                          size_t ws_bytes, void* stream) {
+// per_expert: S is [E][k] and R_S is [M_total][k] by permuted row
+static int gemm_rac(bool per_expert, const uint8_t* a_codes, const uint8_t* a_scales,
+                    const float* g_x, const int32_t* a_rows, int64_t M_src, const void* R_S,
+                    const int32_t* S, int64_t k, const uint8_t* w_codes, const uint8_t* w_scales,
+                    const float* g_w, const int32_t* expert_offsets, int64_t E, int64_t M_total,
+                    int64_t N, int64_t K, void* y, void* ws, size_t ws_bytes, void* stream) {
   NV_REQUIRE(E >= 1 && E <= 1024 && M_total >= 0 && N >= 16 && N % 16 == 0 && K >= kBK &&
                  K % kBK == 0 && k >= 0 && k <= K && M_src >= 0,
              NVFP4_ERR_SHAPE,
@@ -1221,6 +1233,8 @@ int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const
   a.K = K;
   a.E = (int)E;
   a.k = (int)k;
+  a.s_stride = per_expert ? k : 0;
+  a.r_perm = per_expert ? 1 : 0;
   const int64_t m_tiles = (M_total + kBM - 1) / kBM + E;
   const int64_t n_tiles = (N + kBN - 1) / kBN;
     const int64_t n_tiles_big = (N + big::BN - 1) / big::BN;
@@ -1267,13 +1281,14 @@ int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const
   const size_t need_big = grouped_w4a4_gemm_rac_workspace_size(E, M_src, M_total, N, K, k);
   use_big = use_big && (k <= big::KMAX || big_streams_ws(k)) && K / big::BK <= big::KSTEPS_MAX &&
             ws_bytes >= need_big && (uint64_t)M_src * K * 2 < (1ULL << 32) &&
-            (uint64_t)M_src * k * 2 < (1ULL << 32);
+            (uint64_t)(per_expert ? M_total : M_src) * k * 2 < (1ULL << 32);
   if (use_big) {
     uint16_t* img = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + img_offset(E));
     if (big_streams_ws(k)) {
       uint16_t* wsel = reinterpret_cast<uint16_t*>(
           static_cast<char*>(ws) + img_offset(E) + round_up((size_t)M_src * (size_t)K * 2, 256));
-      k_extract_ws<<<(unsigned)(E * N), 256, 0, s>>>(w_codes, w_scales, S, N, K, (int)k, wsel);
+      k_extract_ws<<<(unsigned)(E * N), 256, 0, s>>>(w_codes, w_scales, S, a.s_stride, N, K,
+                                                     (int)k, wsel);
       a.wsel = wsel;
     }
     const int64_t chunks = M_src * (K / 8);
@@ -1289,6 +1304,27 @@ int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const
     k_gemm_generic<<<dim3((unsigned)m_tiles, (unsigned)n_tiles), 256, 0, s>>>(a);
   }
   return check_launch("grouped_w4a4_gemm_rac");
+}
+
+int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
+                          const int32_t* a_rows, int64_t M_src, const void* R_S, const int32_t* S,
+                          int64_t k, const uint8_t* w_codes, const uint8_t* w_scales,
+                          const float* g_w, const int32_t* expert_offsets, int64_t E,
+                          int64_t M_total, int64_t N, int64_t K, void* y, void* ws,
+                          size_t ws_bytes, void* stream) {
+  return gemm_rac(false, a_codes, a_scales, g_x, a_rows, M_src, R_S, S, k, w_codes, w_scales, g_w,
+                  expert_offsets, E, M_total, N, K, y, ws, ws_bytes, stream);
+}
+
+int grouped_w4a4_gemm_rac_per_expert(const uint8_t* a_codes, const uint8_t* a_scales,
+                                     const float* g_x, const int32_t* a_rows, int64_t M_src,
+                                     const void* R_P, const int32_t* S_E, int64_t k,
+                                     const uint8_t* w_codes, const uint8_t* w_scales,
+                                     const float* g_w, const int32_t* expert_offsets, int64_t E,
+                                     int64_t M_total, int64_t N, int64_t K, void* y, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  return gemm_rac(true, a_codes, a_scales, g_x, a_rows, M_src, R_P, S_E, k, w_codes, w_scales, g_w,
+                  expert_offsets, E, M_total, N, K, y, ws, ws_bytes, stream);
 }
 
 size_t grouped_w4a16_gemm_workspace_size(int64_t E) {

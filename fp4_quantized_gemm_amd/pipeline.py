@@ -14,8 +14,9 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (grouped_w4a4_gemm_rac, moe_permute, moe_unpermute_combine, nvfp4_qdq_residual,
-               nvfp4_qdq_weights, nvfp4_quantize_act, select_residual_channels)
+from . import (grouped_w4a4_gemm_rac, grouped_w4a4_gemm_rac_per_expert, moe_permute,
+               moe_unpermute_combine, nvfp4_qdq_residual, nvfp4_qdq_weights, nvfp4_quantize_act,
+               select_residual_channels, select_residual_channels_per_expert)
 
 
 @dataclass
@@ -31,28 +32,40 @@ def prepare_weights(w, want_qdq=False) -> QuantWeights:
 
 
 def quantized_linear_rac(x, wq: QuantWeights, k, a_rows=None, offsets=None, M_total=None,
-                         glu=False, rac="bf16"):
+                         glu=False, rac="bf16", select="shared"):
     """Quantize x (or SwiGLU of x), select k channels, grouped GEMM.
     rac="bf16" adds the bf16 residual of the selected channels back;
     rac="nvfp4" quantizes that residual a second time to NVFP4 first and adds
-    its fake-quantized value back.  Returns (y, stage dict)."""
+    its fake-quantized value back.  select="shared" picks one channel set
+    for the whole call; select="per_expert" one per expert, from the rows
+    routed to it.  Returns (y, stage dict)."""
     if rac not in ("bf16", "nvfp4"):
         raise ValueError(f"rac must be 'bf16' or 'nvfp4', not {rac!r}")
-    q = nvfp4_quantize_act(x, glu=glu, want_score=k > 0)
-    S = R = None
-    if k > 0:
-        S, R = select_residual_channels(q["x_used"], q["codes"], q["scales"], q["g"], q["score"], k)
-        if rac == "nvfp4":
-            R = nvfp4_qdq_residual(R)[3]
+    if select not in ("shared", "per_expert"):
+        raise ValueError(f"select must be 'shared' or 'per_expert', not {select!r}")
+    per_expert = select == "per_expert"
+    q = nvfp4_quantize_act(x, glu=glu, want_score=k > 0 and not per_expert)
     if offsets is None:
         offsets = torch.tensor([0, x.shape[0]], dtype=torch.int32, device=x.device)
-    y = grouped_w4a4_gemm_rac(q["codes"], q["scales"], q["g"], a_rows, R, S, wq.codes, wq.scales,
-                              wq.g, offsets, M_total=M_total)
+    S = R = None
+    if k > 0:
+        if per_expert:
+            S, R = select_residual_channels_per_expert(q["x_used"], q["codes"], q["scales"],
+                                                       q["g"], None, k, a_rows, offsets,
+                                                       M_total=M_total)
+        else:
+            S, R = select_residual_channels(q["x_used"], q["codes"], q["scales"], q["g"],
+                                            q["score"], k)
+        if rac == "nvfp4":
+            R = nvfp4_qdq_residual(R)[3]
+    gemm = grouped_w4a4_gemm_rac_per_expert if per_expert else grouped_w4a4_gemm_rac
+    y = gemm(q["codes"], q["scales"], q["g"], a_rows, R, S, wq.codes, wq.scales, wq.g, offsets,
+             M_total=M_total)
     return y, dict(q=q, S=S, R=R)
 
 
 def moe_forward(x, logits, topk, w_first: QuantWeights, w_down: QuantWeights, k_first, k_down,
-                bias=None, keep=False, rac="bf16"):
+                bias=None, keep=False, rac="bf16", select="shared"):
     """x [T][H] bf16, logits [T][E] f32.  w_first [E][N1][H] (N1 = 2I for
     gate+up, I for an up-only block); w_down [E][H][I] or None.  Returns the
     combined output [T][H] (or the first GEMM's permuted output when there is
@@ -60,13 +73,13 @@ def moe_forward(x, logits, topk, w_first: QuantWeights, w_down: QuantWeights, k_
     ids, tw, offs, perm, inv = moe_permute(logits, topk, bias)
     rows = perm.numel()
     y1, st1 = quantized_linear_rac(x, w_first, k_first, a_rows=perm, offsets=offs, M_total=rows,
-                                   rac=rac)
+                                   rac=rac, select=select)
     out = dict(topk_ids=ids, topk_w=tw, offsets=offs, perm_token=perm, inv_perm=inv, y1=y1,
                st1=st1) if keep else {}
     if w_down is None:
         return y1, out
     y2, st2 = quantized_linear_rac(y1, w_down, k_down, a_rows=None, offsets=offs, M_total=rows,
-                                   glu=True, rac=rac)
+                                   glu=True, rac=rac, select=select)
     o = moe_unpermute_combine(y2, inv, tw)
     if keep:
         out.update(y2=y2, st2=st2, out=o)

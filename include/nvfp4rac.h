@@ -135,6 +135,45 @@ int select_residual_channels(const void* x_used, int64_t ldx, const uint8_t* cod
                              void* stream);
 
 /* ------------------------------------------------------------------------
+ * Per-expert compensation: the variant of Residual Activation Compensation
+ * in which each expert ranks the channels by the residual of its own rows
+ * (the binary channel mask of gist.science summary §2.2 B, one per expert).
+ *
+ * select_residual_channels_per_expert: for expert e with permuted rows p in
+ * [off[e], off[e+1]) taking activation rows t = a_rows ? a_rows[p] : p,
+ *   score_e[j] = sum over those rows of floor(|r[t][j]| * 2^(31 - E_A))
+ * (the nvfp4_quantize_act statistic restricted to the expert's rows; E_A the
+ * binary exponent of the tensor amax, recovered exactly from g_x), S [E][k]
+ * int32 = the k channels of largest score_e (ties: lower index), ascending,
+ * and R [M_total][k] bf16, R[p][j] = bf16(fp32(x - dequant(x))) of row t on
+ * channel S[e][j].  An expert with no rows gets channels 0 .. k-1.
+ * x_used (row stride ldx), codes, scales, g_x as from nvfp4_quantize_act.
+ * Requires 1 <= E <= 1024, 0 <= k <= K <= 4096, K % 32 == 0, ldx % 8 == 0;
+ * k == 0 enqueues nothing.  ws: the per-expert scores, E * K * 8 bytes.
+ *
+ * grouped_w4a4_gemm_rac_per_expert: grouped_w4a4_gemm_rac with S_E [E][k]
+ * (expert e corrects its rows on S_E[e]) and R_P [M_total][k] indexed by
+ * permuted row p, as select_residual_channels_per_expert writes them:
+ *   y[p][n] = bf16( g_w[e] * ( g_x * sum_k x~[t][k] w~e[n][k]
+ *                              + sum_{j<k} R_P[p][j] w~e[n][S_E[e][j]] ) )
+ * Same arguments, requirements and workspace query as grouped_w4a4_gemm_rac.
+ * ---------------------------------------------------------------------- */
+size_t select_residual_channels_per_expert_workspace_size(int64_t E, int64_t K);
+int select_residual_channels_per_expert(const void* x_used, int64_t ldx, const uint8_t* codes,
+                                        const uint8_t* scales, const float* g_x,
+                                        const int32_t* a_rows, const int32_t* expert_offsets,
+                                        int64_t E, int64_t M_src, int64_t M_total, int64_t K,
+                                        int64_t k, int32_t* S, void* R, void* ws,
+                                        size_t ws_bytes, void* stream);
+int grouped_w4a4_gemm_rac_per_expert(const uint8_t* a_codes, const uint8_t* a_scales,
+                                     const float* g_x, const int32_t* a_rows, int64_t M_src,
+                                     const void* R_P, const int32_t* S_E, int64_t k,
+                                     const uint8_t* w_codes, const uint8_t* w_scales,
+                                     const float* g_w, const int32_t* expert_offsets, int64_t E,
+                                     int64_t M_total, int64_t N, int64_t K, void* y, void* ws,
+                                     size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Trainer-side W4A16 product: the forward of asymmetric W4A16 QAT, bf16
  * activations against weights that went through the shared QDQ path
  * (gist.science summary §2.2 A; arXiv abstract).  Same expert grouping,

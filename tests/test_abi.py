@@ -154,3 +154,24 @@ def test_w4a16_gemm_validation():
     assert L.grouped_w4a16_gemm(*args(x=None)) == ERR_NULL
     assert L.grouped_w4a16_gemm(*args(x=FAKE_MIS)) == ERR_ALIGN
     assert L.grouped_w4a16_gemm(*args(ws=0)) == ERR_WS
+
+
+def test_per_expert_validation():
+    L = F.lib()
+    ws = L.select_residual_channels_per_expert_workspace_size(4, 64)
+    assert ws >= 4 * 64 * 8
+    sel = lambda **kw: [FAKE, kw.get("ldx", 64), FAKE, FAKE, FAKE, kw.get("rows", FAKE), FAKE,
+                        kw.get("E", 4), 32, 32, kw.get("K", 64), kw.get("k", 8), kw.get("S", FAKE),
+                        FAKE, FAKE, kw.get("ws", ws), None]
+    assert L.select_residual_channels_per_expert(*sel(k=65)) == ERR_SHAPE
+    assert L.select_residual_channels_per_expert(*sel(E=0)) == ERR_SHAPE
+    assert L.select_residual_channels_per_expert(*sel(K=8192, ldx=8192)) == ERR_SHAPE
+    assert L.select_residual_channels_per_expert(*sel(S=None)) == ERR_NULL
+    assert L.select_residual_channels_per_expert(*sel(ws=8)) == ERR_WS
+    assert L.select_residual_channels_per_expert(*sel(k=0, S=None, ws=0)) == OK   # no-op
+    g = L.grouped_w4a4_gemm_rac_workspace_size(4, 64, 64, 128, 256, 8)
+    args = lambda **kw: [FAKE, FAKE, FAKE, None, 64, kw.get("R", FAKE), kw.get("S", FAKE),
+                         kw.get("k", 8), FAKE, FAKE, FAKE, FAKE, 4, 64, 128, kw.get("K", 256),
+                         FAKE, FAKE, g, None]
+    assert L.grouped_w4a4_gemm_rac_per_expert(*args(K=192)) == ERR_SHAPE
+    assert L.grouped_w4a4_gemm_rac_per_expert(*args(R=None)) == ERR_NULL

@@ -155,3 +155,110 @@ def test_full_size_first_gemm_with_quantized_residual(dev, idx):
         got.append(y_h[ps][:, wq_host.cols])
     e1, e2, ex = assert_gemm_close(np.concatenate(got), np.concatenate(ref))
     say(f"    rownorm {e1:.2e} maxabs {e2:.2e} exact {ex:.4f}")
+
+
+# ------------------------------------------------- per-expert selection
+
+def _routing(rng, M_src, counts, gather):
+    offs = np.zeros(len(counts) + 1, dtype=np.int32)
+    offs[1:] = np.cumsum(counts)
+    M_total = int(offs[-1])
+    a_rows = rng.integers(0, M_src, M_total).astype(np.int32) if gather else None
+    return offs, a_rows, M_total
+
+
+@pytest.mark.parametrize("M_src,counts,K,k,gather", [
+    (64, [64], 512, 16, False),
+    (200, [0, 130, 1, 257, 0], 256, 37, True),
+    (100, [3, 0, 17, 33, 1, 0, 16, 40], 1024, 64, True),
+    (40, [20, 20], 96, 96, True),                        # every channel
+    (300, [120, 200, 80], 4096, 128, True),
+])
+def test_select_per_expert_bitexact(dev, M_src, counts, K, k, gather):
+    say(f"select per expert counts={counts} K={K} k={k}")
+    rng = np.random.default_rng(M_src + K + k)
+    x = heavy_bf16(rng, (M_src, K))
+    offs, a_rows, M_total = _routing(rng, M_src, counts, gather)
+    cu = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q = F.nvfp4_quantize_act(to_dev_bf16(OF.f64_to_bf16_bits(x)), want_score=False)
+    S, R = F.select_residual_channels_per_expert(q["x_used"], q["codes"], q["scales"], q["g"], None,
+                                                 k, cu(a_rows) if gather else None, cu(offs),
+                                                 M_total=M_total)
+    torch.cuda.synchronize()
+    codes, scales, g, A = OQ.quantize(x)
+    S_ref, R_ref, _ = OQ.select_channels_per_expert(x, codes, scales, g, A, a_rows, offs, k)
+    assert np.array_equal(S.cpu().numpy(), S_ref)
+    assert np.array_equal(host_bits(R), OF.f64_to_bf16_bits(R_ref))
+
+
+@pytest.mark.parametrize("M_src,counts,N,K,k", [
+    (64, [64], 512, 512, 16),
+    (500, [17, 0, 0, 400, 83], 272, 1024, 128),
+    (64, [3, 0, 17, 33, 1, 0, 16, 40], 512, 1024, 64),
+    (300, [100, 200], 256, 1024, 256),                  # large k: streamed columns per expert
+])
+def test_gemm_per_expert(dev, gemm_kernel, M_src, counts, N, K, k):
+    say(f"gemm[{gemm_kernel}] per expert counts={counts} N={N} K={K} k={k}")
+    rng = np.random.default_rng(sum(counts) + N + K + k + 1)
+    E = len(counts)
+    x = heavy_bf16(rng, (M_src, K))
+    w = OF.round_to_bf16(rng.standard_normal((E, N, K)) * 0.02)
+    offs, a_rows, M_total = _routing(rng, M_src, counts, True)
+    cu = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q = F.nvfp4_quantize_act(to_dev_bf16(OF.f64_to_bf16_bits(x)), want_score=False)
+    S, R = F.select_residual_channels_per_expert(q["x_used"], q["codes"], q["scales"], q["g"], None,
+                                                 k, cu(a_rows), cu(offs), M_total=M_total)
+    wc, ws, gw, _ = OQ.qdq_weights(w)
+    y = F.grouped_w4a4_gemm_rac_per_expert(q["codes"], q["scales"], q["g"], cu(a_rows), R, S,
+                                           cu(OQ.pack_codes(wc)), cu(tile_wscales(ws)), cu(gw),
+                                           cu(offs), M_total=M_total)
+    torch.cuda.synchronize()
+    codes, scales, g, A = OQ.quantize(x)
+    S_ref, R_ref, _ = OQ.select_channels_per_expert(x, codes, scales, g, A, a_rows, offs, k)
+    assert np.array_equal(S.cpu().numpy(), S_ref)
+    ref = OG.grouped_gemm_rac_per_expert(codes, scales, g, a_rows, R_ref, S_ref, wc, ws, gw, offs)
+    e1, e2, ex = assert_gemm_close(host_vals(y), ref)
+    say(f"   rownorm {e1:.2e} maxabs {e2:.2e} exact {ex:.5f}")
+
+
+def test_full_size_first_gemm_per_expert(dev):
+    # the large-prefill workload's first GEMM with per-expert channel sets:
+    # S of sampled experts from the oracle's scores over their rows, R and
+    # the GEMM on sampled rows
+    cfg = synth.get(5)
+    say(f"workload {cfg.name}: generating")
+    wl = synth.make(cfg)
+    rng = np.random.default_rng(3)
+    x_dev = to_dev_bf16(wl.x)
+    w1 = pipeline.prepare_weights(to_dev_bf16(wl.w_first))
+    logits = torch.from_numpy(wl.logits).cuda()
+    say(f"workload {cfg.name}: running the library")
+    ids, tw, offs, perm, inv = F.moe_permute(logits, cfg.topk, None)
+    y, st = pipeline.quantized_linear_rac(x_dev, w1, cfg.k_first, a_rows=perm, offsets=offs,
+                                          M_total=perm.numel(), select="per_expert")
+    torch.cuda.synchronize()
+    x = OF.bf16_bits_to_f64(wl.x)
+    A = OQ.tensor_amax(x)
+    g = OQ.tensor_scale(A)
+    offs_np, perm_np = offs.cpu().numpy(), perm.cpu().numpy()
+    S_gpu, R_gpu = st["S"].cpu().numpy(), host_bits(st["R"])
+    rows_p = sample_rows(offs_np, rng, n_experts=3)
+    wq_host = weight_host(wl.w_first, rng)
+    y_h = host_vals(y)
+    got, ref = [], []
+    for e in np.unique(np.searchsorted(offs_np, rows_p, side="right") - 1):
+        say(f"  expert {e}: {offs_np[e + 1] - offs_np[e]} rows")
+        t_all = perm_np[offs_np[e]:offs_np[e + 1]]
+        c, s, _, _ = OQ.quantize(x[t_all], A=A)
+        r = OQ.residual(x[t_all], c, s, g)
+        S_e = OQ.select_channels(OQ.channel_scores(r, A), cfg.k_first)
+        assert np.array_equal(S_gpu[e], S_e), f"expert {e} S"
+        ps = rows_p[(rows_p >= offs_np[e]) & (rows_p < offs_np[e + 1])]
+        loc = ps - offs_np[e]
+        assert np.array_equal(R_gpu[ps], OF.f64_to_bf16_bits(r[loc][:, S_e]))
+        wc, ws, gw = wq_host(e)
+        ref.append(OG.grouped_gemm_rac(c[loc], s[loc], g, None, r[loc][:, S_e], S_e, wc[None],
+                                       ws[None], gw[None], [0, len(ps)]))
+        got.append(y_h[ps][:, wq_host.cols])
+    e1, e2, ex = assert_gemm_close(np.concatenate(got), np.concatenate(ref))
+    say(f"    rownorm {e1:.2e} maxabs {e2:.2e} exact {ex:.4f}")
