@@ -289,7 +289,8 @@ def rac_sweep(cfg, wl, reps, n_experts=8):
     output against the trainer's W4A16 forward on the same rows (bf16
     activations times the trainer's bf16 fake-quantized weights, float32
     accumulation), over all rows of `n_experts` experts, for the bf16
-    residual and for the NVFP4-quantized one."""
+    residual and for the NVFP4-quantized one; for MoE blocks also the shared
+    and per-expert selection calls, the per-expert GEMM and its error."""
     import numpy as np
     import torch
 
@@ -361,6 +362,20 @@ def rac_sweep(cfg, wl, reps, n_experts=8):
             pt["qdq_residual_ms"] = median_ms(lambda: F.nvfp4_qdq_residual(R))
             pt["err_bf16_residual"] = err(gemm(R, S))
             pt["err_nvfp4_residual"] = err(gemm(rq[3], S))
+            if cfg.kind != "dense":
+                # one channel set per expert, from the rows routed to it
+                sel_pe = lambda: F.select_residual_channels_per_expert(
+                    q["x_used"], q["codes"], q["scales"], q["g"], None, k, perm, offs,
+                    M_total=rows)
+                S_e, R_p = sel_pe()
+                gemm_pe = lambda: F.grouped_w4a4_gemm_rac_per_expert(
+                    q["codes"], q["scales"], q["g"], perm, R_p, S_e, c1, s1, g1, offs,
+                    M_total=rows)
+                pt["select_ms"] = median_ms(lambda: F.select_residual_channels(
+                    q["x_used"], q["codes"], q["scales"], q["g"], q["score"], k))
+                pt["per_expert_select_ms"] = median_ms(sel_pe)
+                pt["per_expert_gemm_ms"] = median_ms(gemm_pe)
+                pt["err_per_expert"] = err(gemm_pe())
         pt["overhead"] = pt["gemm_ms"] / t0 - 1.0
         points.append({kk: (round(v, 6) if isinstance(v, float) else v) for kk, v in pt.items()})
         print(f"# k={k} {points[-1]}", file=sys.stderr, flush=True)
