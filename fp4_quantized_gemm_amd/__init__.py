@@ -10,9 +10,11 @@ there is no fallback: importing the library fails loudly if it is missing.
 Calls (same names as the C ABI):
     nvfp4_qdq_weights, nvfp4_quantize_act, select_residual_channels,
     moe_permute, grouped_w4a4_gemm_rac, moe_unpermute_combine
-and, for the variants of the correction and the trainer-side W4A16 product,
+and, for the variants of the correction, the fused SwiGLU and the
+trainer-side W4A16 product,
     nvfp4_qdq_residual, select_residual_channels_per_expert,
-    grouped_w4a4_gemm_rac_per_expert, grouped_w4a16_gemm
+    grouped_w4a4_gemm_rac_per_expert, grouped_w4a4_gemm_rac_swiglu,
+    grouped_w4a16_gemm
 """
 from __future__ import annotations
 
@@ -26,7 +28,7 @@ from .build import LIB as LIB_PATH
 __all__ = ["lib", "nvfp4_qdq_weights", "nvfp4_quantize_act", "select_residual_channels",
            "moe_permute", "grouped_w4a4_gemm_rac", "moe_unpermute_combine", "nvfp4_qdq_residual",
            "grouped_w4a16_gemm", "select_residual_channels_per_expert",
-           "grouped_w4a4_gemm_rac_per_expert", "NvfpError",
+           "grouped_w4a4_gemm_rac_per_expert", "grouped_w4a4_gemm_rac_swiglu", "NvfpError",
            "EXPORTED_SYMBOLS"]
 
 EXPORTED_SYMBOLS = [
@@ -41,6 +43,7 @@ EXPORTED_SYMBOLS = [
     "grouped_w4a16_gemm_workspace_size", "grouped_w4a16_gemm",
     "select_residual_channels_per_expert_workspace_size", "select_residual_channels_per_expert",
     "grouped_w4a4_gemm_rac_per_expert",
+    "grouped_w4a4_gemm_rac_swiglu_workspace_size", "grouped_w4a4_gemm_rac_swiglu",
 ]
 
 
@@ -74,6 +77,7 @@ def _load():
         "nvfp4_qdq_residual_workspace_size": [_I64, _I64],
         "grouped_w4a16_gemm_workspace_size": [_I64],
         "select_residual_channels_per_expert_workspace_size": [_I64, _I64],
+        "grouped_w4a4_gemm_rac_swiglu_workspace_size": [_I64, _I64, _I64, _I64, _I64, _I64],
     }.items():
         f = getattr(L, name)
         f.restype = _SZ
@@ -93,6 +97,8 @@ def _load():
                                                 _I64, _I64, _P, _P, _P, _SZ, _P],
         "grouped_w4a4_gemm_rac_per_expert": [_P, _P, _P, _P, _I64, _P, _P, _I64, _P, _P, _P, _P,
                                              _I64, _I64, _I64, _I64, _P, _P, _SZ, _P],
+        "grouped_w4a4_gemm_rac_swiglu": [_P, _P, _P, _P, _I64, _P, _P, _I64, _P, _P, _P, _P, _I64,
+                                         _I64, _I64, _I64, _P, _P, _SZ, _P],
     }
     for name, args in sigs.items():
         f = getattr(L, name)
@@ -249,7 +255,7 @@ def select_residual_channels_per_expert(x_used, codes, scales, g, score_unused, 
 
 
 def _gemm_rac(fn_name, a_codes, a_scales, g_x, a_rows, R, S, w_codes, w_scales, g_w,
-              expert_offsets, M_total, out):
+              expert_offsets, M_total, out, glu=False):
     L = _load()
     M_src, Kh = a_codes.shape
     K = Kh * 2
@@ -258,14 +264,25 @@ def _gemm_rac(fn_name, a_codes, a_scales, g_x, a_rows, R, S, w_codes, w_scales, 
     if M_total is None:
         M_total = int(a_rows.numel()) if a_rows is not None else M_src
     dev = a_codes.device
-    y = out if out is not None else torch.empty((M_total, N), dtype=torch.bfloat16, device=dev)
-    ws = _ws(L.grouped_w4a4_gemm_rac_workspace_size(E, M_src, M_total, N, K, k), dev)
+    cols = N // 2 if glu else N
+    y = out if out is not None else torch.empty((M_total, cols), dtype=torch.bfloat16, device=dev)
+    wsq = (L.grouped_w4a4_gemm_rac_swiglu_workspace_size if glu
+           else L.grouped_w4a4_gemm_rac_workspace_size)
+    ws = _ws(wsq(E, M_src, M_total, N, K, k), dev)
     _check(getattr(L, fn_name)(_ptr(a_codes), _ptr(a_scales), _ptr(g_x), _ptr(a_rows), M_src,
                                _ptr(R) if k else None, _ptr(S) if k else None, k,
                                _ptr(w_codes), _ptr(w_scales), _ptr(g_w), _ptr(expert_offsets),
                                E, M_total, N, K, _ptr(y), _ptr(ws), ws.numel(), _stream(dev)),
            fn_name)
     return y
+
+
+def grouped_w4a4_gemm_rac_swiglu(a_codes, a_scales, g_x, a_rows, R_S, S, w_codes, w_scales, g_w,
+                                 expert_offsets, M_total=None, out=None):
+    """h [M_total][N/2] bf16 = SwiGLU of the grouped W4A4 GEMM plus correction,
+    whose weights' N rows are [gate | up]."""
+    return _gemm_rac("grouped_w4a4_gemm_rac_swiglu", a_codes, a_scales, g_x, a_rows, R_S, S,
+                     w_codes, w_scales, g_w, expert_offsets, M_total, out, glu=True)
 
 
 def grouped_w4a4_gemm_rac_per_expert(a_codes, a_scales, g_x, a_rows, R_P, S_E, w_codes,

@@ -123,6 +123,24 @@ __device__ __forceinline__ int64_t wscale_offset(int64_t n, int64_t kb, int64_t 
   return (((n >> 4) * (K >> 6) + (kb >> 2)) << 6) + ((n & 15) << 2) + (kb & 3);
 }
 
+// SwiGLU of bf16 gate and up values: silu(g) * u in float32 with the
+// hardware exp2 and reciprocal (a few float32 ulps), then one rounding to
+// bf16: the correctly rounded bf16 value except when the float32 value lies
+// within those ulps of a bf16 rounding boundary, i.e. at most one bf16 step
+// away from it.  Shared by the quantizer's SwiGLU pass and the gate+up GEMM
+// epilogue, so both give the same bits.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
+// two bf16 gates and two bf16 ups (packed pairs) -> two bf16 h (packed)
+__device__ __forceinline__ uint32_t swiglu_pair(uint32_t g2, uint32_t u2) {
+  float g0 = bf16_bits_to_f32(g2 & 0xFFFFu), g1 = bf16_bits_to_f32(g2 >> 16);
+  float u0 = bf16_bits_to_f32(u2 & 0xFFFFu), u1 = bf16_bits_to_f32(u2 >> 16);
+  return f32_to_bf16_rne(silu_mul(g0, u0)) | (f32_to_bf16_rne(silu_mul(g1, u1)) << 16);
+}
+
 __device__ __forceinline__ int frexp_exponent(float a) {
   return (int)((__float_as_uint(a) >> 23) & 0xFFu) - 126;   // a normal and > 0
 }

@@ -54,6 +54,10 @@ struct GemmArgs {
   // permuted row (r_perm = 1) instead of by activation row
   int64_t s_stride;
   int r_perm;
+  // fused SwiGLU (large-tile kernel): glu_i = I > 0 means the weight rows
+  // are [gate (I) | up (I)], a column tile pairs gate columns with the same
+  // up columns, and y receives h = bf16(silu(gate) * up), [M_total][I]
+  int64_t glu_i;
 };
 
 // tile_prefix[e] = number of 128-row tiles of experts before e; [E] = total
@@ -429,6 +433,15 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   e_hi = e_hi < e_lo ? e_lo : (e_hi > p.M_total ? p.M_total : e_hi);
   const int64_t p0 = e_lo + (int64_t)(gt - p.tile_prefix[e]) * BM;
   const int64_t n0 = (int64_t)nt * BN;
+  // weight row of the tile's local row r; with the fused SwiGLU the tile
+  // holds gate columns 128 nt .. +127 (rows 0..127) and the same up columns
+  // I + 128 nt .. (rows 128..255)
+  auto wrow = [&](int r) -> int64_t {
+    if (W16 || p.glu_i == 0) return n0 + r;
+    int64_t c = (int64_t)nt * 128 + (r & 127);
+    c = c < p.glu_i ? c : p.glu_i - 1;
+    return r < 128 ? c : p.glu_i + c;
+  };
   const uint32_t Kh = (uint32_t)(p.K / 2), Ks = (uint32_t)(p.K / 16), K2 = (uint32_t)(p.K * 2);
   const int kk = W16 ? 0 : p.k;
   // more than KMAX channels (a multiple of KMAX): the selected weight columns
@@ -482,12 +495,12 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   {
     const int q = wave * 64 + lane;
     const int r = q >> 1, c = (q & 1) ^ ((r >> 3) & 1);
-    int64_t n = n0 + r;
+    int64_t n = wrow(r);
     if (n >= p.N) n = p.N - 1;
     off_b = (uint32_t)n * Kh + 16u * c;
   }
   if (wave < 4) {
-    int64_t n = n0 + wave * 64 + lane;
+    int64_t n = wrow(wave * 64 + lane);
     if (n >= p.N) n = p.N - 1;
     off_s = (uint32_t)wscale_offset(n, 0, p.K);   // + k0: the step's tile
   }
@@ -674,7 +687,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
         const int o = b * 1024 + lane * 16;
         const int row = o / WSROW, cb = o - row * WSROW;
         if (row < BN && cb < KMAX * 2) {
-          int64_t n = n0 + row;
+          int64_t n = wrow(row);
           if (n >= p.N) n = p.N - 1;
           __builtin_amdgcn_global_load_lds(wse + n * kk + c0 + cb / 2, wsl + b * 1024, 16, 0, 0);
         }
@@ -744,14 +757,46 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
           }
     }
     __syncthreads();
-    for (int q = tid; q < OUT_ROWS * (BN / 8); q += 512) {
-      const int row = q / (BN / 8), ch = q % (BN / 8);
-      const int64_t prow = p0 + h * OUT_ROWS + row;
-      const int64_t n = n0 + ch * 8;
-      if (prow < e_hi && n < p.N)
-        *reinterpret_cast<uint4*>(p.y + prow * p.N + n) =
-            *reinterpret_cast<const uint4*>(wsl + row * OUTROW + ch * 16);
+    if (p.glu_i > 0) {
+      // h = bf16(silu(gate) * up) of the staged bf16 outputs: gate columns
+      // in the first 128 of the row, the matching up columns in the next 128
+      for (int q = tid; q < OUT_ROWS * (BN / 16); q += 512) {
+        const int row = q / (BN / 16), ch = q % (BN / 16);
+        const int64_t prow = p0 + h * OUT_ROWS + row;
+        const int64_t c = (int64_t)nt * 128 + ch * 8;
+        if (prow < e_hi && c < p.glu_i) {
+          const uint4 g4 = *reinterpret_cast<const uint4*>(wsl + row * OUTROW + ch * 16);
+          const uint4 u4 = *reinterpret_cast<const uint4*>(wsl + row * OUTROW + 256 + ch * 16);
+          *reinterpret_cast<uint4*>(p.y + prow * p.glu_i + c) =
+              make_uint4(swiglu_pair(g4.x, u4.x), swiglu_pair(g4.y, u4.y),
+                         swiglu_pair(g4.z, u4.z), swiglu_pair(g4.w, u4.w));
+        }
+      }
+    } else {
+      for (int q = tid; q < OUT_ROWS * (BN / 8); q += 512) {
+        const int row = q / (BN / 8), ch = q % (BN / 8);
+        const int64_t prow = p0 + h * OUT_ROWS + row;
+        const int64_t n = n0 + ch * 8;
+        if (prow < e_hi && n < p.N)
+          *reinterpret_cast<uint4*>(p.y + prow * p.N + n) =
+              *reinterpret_cast<const uint4*>(wsl + row * OUTROW + ch * 16);
+      }
     }
+  }
+}
+
+// h [M][I] = bf16(silu(gate) * up) of y [M][2I] = [gate | up], 8 columns per
+// thread (the fused SwiGLU for shapes the large-tile kernel does not take)
+__global__ void __launch_bounds__(256)
+k_swiglu_rows(const uint16_t* __restrict__ y, int64_t M, int64_t I, uint16_t* __restrict__ h) {
+  const int64_t n8 = M * (I / 8);
+  for (int64_t q = blockIdx.x * 256LL + threadIdx.x; q < n8; q += (int64_t)gridDim.x * 256) {
+    const int64_t m = q / (I / 8), c = (q - m * (I / 8)) * 8;
+    const uint4 g4 = *reinterpret_cast<const uint4*>(y + m * 2 * I + c);
+    const uint4 u4 = *reinterpret_cast<const uint4*>(y + m * 2 * I + I + c);
+    *reinterpret_cast<uint4*>(h + m * I + c) =
+        make_uint4(swiglu_pair(g4.x, u4.x), swiglu_pair(g4.y, u4.y), swiglu_pair(g4.z, u4.z),
+                   swiglu_pair(g4.w, u4.w));
   }
 }
 
@@ -1189,7 +1234,10 @@ size_t grouped_w4a4_gemm_rac_workspace_size(int64_t E, int64_t M_src, int64_t M_
 }
 
 // per_expert: S is [E][k] and R_S is [M_total][k] by permuted row
-static int gemm_rac(bool per_expert, const uint8_t* a_codes, const uint8_t* a_scales,
+// glu: y receives h = bf16(silu(gate) * up) [M_total][N/2] of the [gate | up]
+// product, fused into the large-tile kernel's epilogue, else formed from a
+// product staged in the workspace
+static int gemm_rac(bool per_expert, bool glu, const uint8_t* a_codes, const uint8_t* a_scales,
                     const float* g_x, const int32_t* a_rows, int64_t M_src, const void* R_S,
                     const int32_t* S, int64_t k, const uint8_t* w_codes, const uint8_t* w_scales,
                     const float* g_w, const int32_t* expert_offsets, int64_t E, int64_t M_total,
@@ -1235,9 +1283,21 @@ static int gemm_rac(bool per_expert, const uint8_t* a_codes, const uint8_t* a_sc
   a.k = (int)k;
   a.s_stride = per_expert ? k : 0;
   a.r_perm = per_expert ? 1 : 0;
+  // the [gate | up] product for the fused SwiGLU outside the large-tile
+  // kernel: after the plain GEMM's workspace
+  uint16_t* glu_stage = glu ? reinterpret_cast<uint16_t*>(
+      static_cast<char*>(ws) + grouped_w4a4_gemm_rac_workspace_size(E, M_src, M_total, N, K, k))
+                            : nullptr;
+  auto launch_swiglu = [&]() {
+    const int64_t n8 = M_total * (N / 16);
+    int64_t nb = (n8 + 255) / 256;
+    if (nb > 16LL * num_cus()) nb = 16LL * num_cus();
+    k_swiglu_rows<<<(unsigned)(nb > 0 ? nb : 1), 256, 0, s>>>(glu_stage, M_total, N / 2,
+                                                             static_cast<uint16_t*>(y));
+  };
   const int64_t m_tiles = (M_total + kBM - 1) / kBM + E;
   const int64_t n_tiles = (N + kBN - 1) / kBN;
-    const int64_t n_tiles_big = (N + big::BN - 1) / big::BN;
+  const int64_t n_tiles_big = glu ? (N / 2 + 127) / 128 : (N + big::BN - 1) / big::BN;
   const int64_t m_tiles_big = (M_total + big::BM - 1) / big::BM + E;
   // NVFP4RAC_GEMM=generic|big forces a kernel (tests use it to cover both on
   // small shapes).  The large-tile path holds at most KMAX residual channels,
@@ -1275,7 +1335,9 @@ static int gemm_rac(bool per_expert, const uint8_t* a_codes, const uint8_t* a_sc
     if (const char* o = getenv("NVFP4RAC_DEC_BPW")) bpw = atoll(o);
     bpw = bpw < 1 ? 1 : (bpw > n_blocks ? n_blocks : bpw);
     const int64_t groups = (n_blocks + bpw - 1) / bpw;
+    if (glu) a.y = glu_stage;
     k_gemm_decode<<<(unsigned)(E * groups), 256, lds, s>>>(a, (int)n_blocks, (int)bpw, wsrow);
+    if (glu) launch_swiglu();
     return check_launch("grouped_w4a4_gemm_rac");
   }
   const size_t need_big = grouped_w4a4_gemm_rac_workspace_size(E, M_src, M_total, N, K, k);
@@ -1297,11 +1359,14 @@ static int gemm_rac(bool per_expert, const uint8_t* a_codes, const uint8_t* a_sc
     k_decode_a<<<(unsigned)nb, 256, 0, s>>>(a_codes, a_scales, M_src, K, img);
     k_tile_prefix<<<1, 1024, 0, s>>>(expert_offsets, (int)E, M_total, big::BM, prefix);
     const int64_t nblk = (((m_tiles_big + 3) / 4) * 4 * n_tiles_big + 7) / 8 * 8;
+    if (glu) a.glu_i = N / 2;
     k_gemm_big<false><<<(unsigned)nblk, 512, 0, s>>>(a, reinterpret_cast<const uint8_t*>(img),
                                                     (int)n_tiles_big, (int)m_tiles_big);
   } else {
+    if (glu) a.y = glu_stage;
     k_tile_prefix<<<1, 1024, 0, s>>>(expert_offsets, (int)E, M_total, kBM, prefix);
     k_gemm_generic<<<dim3((unsigned)m_tiles, (unsigned)n_tiles), 256, 0, s>>>(a);
+    if (glu) launch_swiglu();
   }
   return check_launch("grouped_w4a4_gemm_rac");
 }
@@ -1312,8 +1377,8 @@ int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const
                           const float* g_w, const int32_t* expert_offsets, int64_t E,
                           int64_t M_total, int64_t N, int64_t K, void* y, void* ws,
                           size_t ws_bytes, void* stream) {
-  return gemm_rac(false, a_codes, a_scales, g_x, a_rows, M_src, R_S, S, k, w_codes, w_scales, g_w,
-                  expert_offsets, E, M_total, N, K, y, ws, ws_bytes, stream);
+  return gemm_rac(false, false, a_codes, a_scales, g_x, a_rows, M_src, R_S, S, k, w_codes, w_scales,
+                  g_w, expert_offsets, E, M_total, N, K, y, ws, ws_bytes, stream);
 }
 
 int grouped_w4a4_gemm_rac_per_expert(const uint8_t* a_codes, const uint8_t* a_scales,
@@ -1323,8 +1388,30 @@ int grouped_w4a4_gemm_rac_per_expert(const uint8_t* a_codes, const uint8_t* a_sc
                                      const float* g_w, const int32_t* expert_offsets, int64_t E,
                                      int64_t M_total, int64_t N, int64_t K, void* y, void* ws,
                                      size_t ws_bytes, void* stream) {
-  return gemm_rac(true, a_codes, a_scales, g_x, a_rows, M_src, R_P, S_E, k, w_codes, w_scales, g_w,
-                  expert_offsets, E, M_total, N, K, y, ws, ws_bytes, stream);
+  return gemm_rac(true, false, a_codes, a_scales, g_x, a_rows, M_src, R_P, S_E, k, w_codes,
+                  w_scales, g_w, expert_offsets, E, M_total, N, K, y, ws, ws_bytes, stream);
+}
+
+size_t grouped_w4a4_gemm_rac_swiglu_workspace_size(int64_t E, int64_t M_src, int64_t M_total,
+                                                   int64_t N, int64_t K, int64_t k) {
+  return grouped_w4a4_gemm_rac_workspace_size(E, M_src, M_total, N, K, k) +
+         round_up((size_t)(M_total > 0 ? M_total : 0) * (size_t)(N > 0 ? N : 0) * 2, 256);
+}
+
+int grouped_w4a4_gemm_rac_swiglu(const uint8_t* a_codes, const uint8_t* a_scales, const float* g_x,
+                                 const int32_t* a_rows, int64_t M_src, const void* R_S,
+                                 const int32_t* S, int64_t k, const uint8_t* w_codes,
+                                 const uint8_t* w_scales, const float* g_w,
+                                 const int32_t* expert_offsets, int64_t E, int64_t M_total,
+                                 int64_t N, int64_t K, void* h, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  NV_REQUIRE(N % 32 == 0, NVFP4_ERR_SHAPE,
+             "grouped_w4a4_gemm_rac_swiglu: N = 2 I needs N %% 32 == 0 (N=%lld)", (long long)N);
+  NV_REQUIRE(aligned(h, 16), NVFP4_ERR_ALIGN, "grouped_w4a4_gemm_rac_swiglu: misaligned h");
+  NV_REQUIRE(ws_bytes >= grouped_w4a4_gemm_rac_swiglu_workspace_size(E, M_src, M_total, N, K, k),
+             NVFP4_ERR_WORKSPACE, "grouped_w4a4_gemm_rac_swiglu: workspace too small");
+  return gemm_rac(false, true, a_codes, a_scales, g_x, a_rows, M_src, R_S, S, k, w_codes, w_scales,
+                  g_w, expert_offsets, E, M_total, N, K, h, ws, ws_bytes, stream);
 }
 
 size_t grouped_w4a16_gemm_workspace_size(int64_t E) {

@@ -98,21 +98,6 @@ k_amax_flat(const uint16_t* __restrict__ x, int64_t n8, int64_t tensor_stride,
 // Pass 1b: h = bf16(silu(gate) * up) from y = [gate | up] ([M][2I], row stride
 // ldy); writes h [M][I] and its amax.  silu(g) = g / (1 + exp(-g)), float32.
 // ---------------------------------------------------------------------------
-// silu(g) * u in float32 with the hardware exp2 and reciprocal (a few float32
-// ulps), then one rounding to bf16: the result is the correctly rounded bf16
-// value except when the float32 value lies within those ulps of a bf16
-// rounding boundary, i.e. at most one bf16 step away from it.
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
-  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
-}
-
-__device__ __forceinline__ uint32_t swiglu_pair(uint32_t g2, uint32_t u2) {
-  float g0 = bf16_bits_to_f32(g2 & 0xFFFFu), g1 = bf16_bits_to_f32(g2 >> 16);
-  float u0 = bf16_bits_to_f32(u2 & 0xFFFFu), u1 = bf16_bits_to_f32(u2 >> 16);
-  return f32_to_bf16_rne(silu_mul(g0, u0)) | (f32_to_bf16_rne(silu_mul(g1, u1)) << 16);
-}
-
 __global__ void __launch_bounds__(256)
 k_swiglu_amax(const uint16_t* __restrict__ y, int64_t rows, int64_t ldy, int64_t inter,
               int chunks, int rows_per_iter, uint16_t* __restrict__ h,

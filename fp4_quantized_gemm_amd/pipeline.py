@@ -14,7 +14,8 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (grouped_w4a4_gemm_rac, grouped_w4a4_gemm_rac_per_expert, moe_permute,
+from . import (grouped_w4a4_gemm_rac, grouped_w4a4_gemm_rac_per_expert,
+               grouped_w4a4_gemm_rac_swiglu, moe_permute,
                moe_unpermute_combine, nvfp4_qdq_residual, nvfp4_qdq_weights, nvfp4_quantize_act,
                select_residual_channels, select_residual_channels_per_expert)
 
@@ -32,13 +33,15 @@ def prepare_weights(w, want_qdq=False) -> QuantWeights:
 
 
 def quantized_linear_rac(x, wq: QuantWeights, k, a_rows=None, offsets=None, M_total=None,
-                         glu=False, rac="bf16", select="shared"):
+                         glu=False, rac="bf16", select="shared", swiglu_out=False):
     """Quantize x (or SwiGLU of x), select k channels, grouped GEMM.
     rac="bf16" adds the bf16 residual of the selected channels back;
     rac="nvfp4" quantizes that residual a second time to NVFP4 first and adds
     its fake-quantized value back.  select="shared" picks one channel set
     for the whole call; select="per_expert" one per expert, from the rows
-    routed to it.  Returns (y, stage dict)."""
+    routed to it.  swiglu_out=True returns h = SwiGLU of the [gate | up]
+    product instead of the product (fused into the GEMM; shared selection
+    only).  Returns (y or h, stage dict)."""
     if rac not in ("bf16", "nvfp4"):
         raise ValueError(f"rac must be 'bf16' or 'nvfp4', not {rac!r}")
     if select not in ("shared", "per_expert"):
@@ -58,28 +61,33 @@ def quantized_linear_rac(x, wq: QuantWeights, k, a_rows=None, offsets=None, M_to
                                             q["score"], k)
         if rac == "nvfp4":
             R = nvfp4_qdq_residual(R)[3]
-    gemm = grouped_w4a4_gemm_rac_per_expert if per_expert else grouped_w4a4_gemm_rac
+    if swiglu_out and per_expert:
+        raise ValueError("the fused SwiGLU output takes the shared channel selection")
+    gemm = (grouped_w4a4_gemm_rac_per_expert if per_expert else
+            grouped_w4a4_gemm_rac_swiglu if swiglu_out else grouped_w4a4_gemm_rac)
     y = gemm(q["codes"], q["scales"], q["g"], a_rows, R, S, wq.codes, wq.scales, wq.g, offsets,
              M_total=M_total)
     return y, dict(q=q, S=S, R=R)
 
 
 def moe_forward(x, logits, topk, w_first: QuantWeights, w_down: QuantWeights, k_first, k_down,
-                bias=None, keep=False, rac="bf16", select="shared"):
+                bias=None, keep=False, rac="bf16", select="shared", fuse_swiglu=False):
     """x [T][H] bf16, logits [T][E] f32.  w_first [E][N1][H] (N1 = 2I for
     gate+up, I for an up-only block); w_down [E][H][I] or None.  Returns the
     combined output [T][H] (or the first GEMM's permuted output when there is
-    no down projection) and, with keep=True, every intermediate."""
+    no down projection) and, with keep=True, every intermediate.
+    fuse_swiglu=True forms h inside the gate+up GEMM (y1 is then h)."""
     ids, tw, offs, perm, inv = moe_permute(logits, topk, bias)
     rows = perm.numel()
+    fuse = fuse_swiglu and w_down is not None
     y1, st1 = quantized_linear_rac(x, w_first, k_first, a_rows=perm, offsets=offs, M_total=rows,
-                                   rac=rac, select=select)
+                                   rac=rac, select=select, swiglu_out=fuse)
     out = dict(topk_ids=ids, topk_w=tw, offsets=offs, perm_token=perm, inv_perm=inv, y1=y1,
                st1=st1) if keep else {}
     if w_down is None:
         return y1, out
     y2, st2 = quantized_linear_rac(y1, w_down, k_down, a_rows=None, offsets=offs, M_total=rows,
-                                   glu=True, rac=rac, select=select)
+                                   glu=not fuse, rac=rac, select=select)
     o = moe_unpermute_combine(y2, inv, tw)
     if keep:
         out.update(y2=y2, st2=st2, out=o)

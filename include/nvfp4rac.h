@@ -135,6 +135,28 @@ int select_residual_channels(const void* x_used, int64_t ldx, const uint8_t* cod
                              void* stream);
 
 /* ------------------------------------------------------------------------
+ * Gate+up GEMM with SwiGLU fused into its output: grouped_w4a4_gemm_rac on
+ * weights whose N = 2 I rows are [gate | up], writing h [M_total][I] bf16,
+ *   h[p][i] = bf16(silu(y[p][i]) * y[p][I + i]),  silu(g) = g / (1 + e^-g),
+ * from the bf16-rounded products y (the same bits as the plain call followed
+ * by the SwiGLU of nvfp4_quantize_act with glu = 1; float32 arithmetic).  On
+ * large problems the SwiGLU runs in the GEMM's epilogue, whose column tiles
+ * pair gate and up columns, so the [M_total][2 I] product is never written.
+ * Same arguments as grouped_w4a4_gemm_rac with y -> h; requires N % 32 == 0.
+ * Workspace: grouped_w4a4_gemm_rac_swiglu_workspace_size (the plain GEMM's
+ * plus M_total * N * 2 bytes).
+ * ---------------------------------------------------------------------- */
+size_t grouped_w4a4_gemm_rac_swiglu_workspace_size(int64_t E, int64_t M_src, int64_t M_total,
+                                                   int64_t N, int64_t K, int64_t k);
+int grouped_w4a4_gemm_rac_swiglu(const uint8_t* a_codes, const uint8_t* a_scales,
+                                 const float* g_x, const int32_t* a_rows, int64_t M_src,
+                                 const void* R_S, const int32_t* S, int64_t k,
+                                 const uint8_t* w_codes, const uint8_t* w_scales,
+                                 const float* g_w, const int32_t* expert_offsets, int64_t E,
+                                 int64_t M_total, int64_t N, int64_t K, void* h, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Per-expert compensation: the variant of Residual Activation Compensation
  * in which each expert ranks the channels by the residual of its own rows
  * (the binary channel mask of gist.science summary §2.2 B, one per expert).

@@ -175,3 +175,14 @@ def test_per_expert_validation():
                          FAKE, FAKE, g, None]
     assert L.grouped_w4a4_gemm_rac_per_expert(*args(K=192)) == ERR_SHAPE
     assert L.grouped_w4a4_gemm_rac_per_expert(*args(R=None)) == ERR_NULL
+
+
+def test_swiglu_gemm_validation():
+    L = F.lib()
+    ws = L.grouped_w4a4_gemm_rac_swiglu_workspace_size(4, 64, 64, 128, 256, 0)
+    assert ws >= L.grouped_w4a4_gemm_rac_workspace_size(4, 64, 64, 128, 256, 0) + 64 * 128 * 2
+    args = lambda **kw: [FAKE, FAKE, FAKE, None, 64, None, None, 0, FAKE, FAKE, FAKE, FAKE, 4, 64,
+                         kw.get("N", 128), 256, kw.get("h", FAKE), FAKE, kw.get("ws", ws), None]
+    assert L.grouped_w4a4_gemm_rac_swiglu(*args(N=144)) == ERR_SHAPE    # N = 2I, N % 32
+    assert L.grouped_w4a4_gemm_rac_swiglu(*args(h=FAKE_MIS)) == ERR_ALIGN
+    assert L.grouped_w4a4_gemm_rac_swiglu(*args(ws=16)) == ERR_WS

@@ -15,6 +15,7 @@ import synth
 from fp4_quantized_gemm_amd import pipeline
 from oracle import formats as OF
 from oracle import gemm as OG
+from oracle import moe as OM
 from oracle import nvfp4 as OQ
 from tests.gpu_util import (assert_gemm_close, f32_bits, heavy_bf16, host_bits, host_vals,
                             tile_wscales, to_dev_bf16)
@@ -262,3 +263,67 @@ def test_full_size_first_gemm_per_expert(dev):
         got.append(y_h[ps][:, wq_host.cols])
     e1, e2, ex = assert_gemm_close(np.concatenate(got), np.concatenate(ref))
     say(f"    rownorm {e1:.2e} maxabs {e2:.2e} exact {ex:.4f}")
+
+
+# ------------------------------------------------- fused SwiGLU output
+
+@pytest.mark.parametrize("M_src,counts,I,K,k", [
+    (64, [64], 256, 512, 16),
+    (500, [17, 0, 0, 400, 83], 160, 1024, 128),          # I not a multiple of 128: a partial tile
+    (64, [3, 0, 17, 33, 1, 0, 16, 40], 256, 1024, 64),
+    (300, [100, 200], 128, 512, 256),                     # large k
+])
+def test_gemm_swiglu_fused(dev, gemm_kernel, M_src, counts, I, K, k):
+    # h from the fused call is bit-identical to the plain GEMM followed by the
+    # quantizer's SwiGLU, and within one bf16 step of the oracle's SwiGLU of
+    # the oracle's GEMM output
+    say(f"gemm[{gemm_kernel}] swiglu counts={counts} I={I} K={K} k={k}")
+    rng = np.random.default_rng(sum(counts) + I + K + k + 7)
+    E = len(counts)
+    x = heavy_bf16(rng, (M_src, K))
+    w = OF.round_to_bf16(rng.standard_normal((E, 2 * I, K)) * 0.02)
+    offs, a_rows, M_total = _routing(rng, M_src, counts, True)
+    cu = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q = F.nvfp4_quantize_act(to_dev_bf16(OF.f64_to_bf16_bits(x)))
+    S, R = F.select_residual_channels(q["x_used"], q["codes"], q["scales"], q["g"], q["score"], k)
+    wc, ws, gw, _ = OQ.qdq_weights(w)
+    args = (q["codes"], q["scales"], q["g"], cu(a_rows), R, S, cu(OQ.pack_codes(wc)),
+            cu(tile_wscales(ws)), cu(gw), cu(offs))
+    h = F.grouped_w4a4_gemm_rac_swiglu(*args, M_total=M_total)
+    y = F.grouped_w4a4_gemm_rac(*args, M_total=M_total)
+    hq = F.nvfp4_quantize_act(y, glu=True)
+    torch.cuda.synchronize()
+    assert h.shape == (M_total, I)
+    assert np.array_equal(host_bits(h), host_bits(hq["x_used"]))
+    qa = OQ.quantize_activation(x, k)
+    y_ref = OG.grouped_gemm_rac(qa["codes"], qa["scales"], qa["g"], a_rows, qa["R_S"], qa["S"],
+                                wc, ws, gw, offs)
+    assert_gemm_close(host_vals(y), y_ref)
+    h_ref = OM.swiglu(host_vals(y), I)                    # teacher-forced on the GPU's y
+    hv = host_vals(h)
+    rel = np.abs(hv - h_ref) / np.maximum(np.abs(h_ref), 1e-30)
+    assert np.all(rel <= 2.0 ** -7) and np.mean(hv == h_ref) > 0.99
+
+
+def test_full_size_fused_swiglu_block(dev):
+    # the large-prefill block with the SwiGLU fused into the gate+up GEMM:
+    # h and the block output bit-identical to the unfused chain
+    cfg = synth.get(5)
+    say(f"workload {cfg.name}: generating")
+    wl = synth.make(cfg)
+    x_dev = to_dev_bf16(wl.x)
+    w1 = pipeline.prepare_weights(to_dev_bf16(wl.w_first))
+    w2 = pipeline.prepare_weights(to_dev_bf16(wl.w_down))
+    logits = torch.from_numpy(wl.logits).cuda()
+    say("  unfused")
+    o0, s0 = pipeline.moe_forward(x_dev, logits, cfg.topk, w1, w2, cfg.k_first, cfg.k_down,
+                                  keep=True)
+    h0 = host_bits(s0["st2"]["q"]["x_used"])
+    o0 = host_bits(o0)
+    del s0
+    say("  fused")
+    o1, s1 = pipeline.moe_forward(x_dev, logits, cfg.topk, w1, w2, cfg.k_first, cfg.k_down,
+                                  keep=True, fuse_swiglu=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(s1["y1"]), h0)
+    assert np.array_equal(host_bits(o1), o0)
