@@ -7,7 +7,8 @@ One step = one pass of the whole path over one batch, inputs resident in HBM:
 weight QDQ of both expert weight tensors (nvfp4_qdq_weights), route and
 permute (moe_permute), online activation quantization with channel scores,
 channel selection and residual gather, the gate+up grouped GEMM with the
-residual correction, SwiGLU fused into the second quantizer, selection, the
+residual correction with SwiGLU fused into its output (--no-fuse-swiglu:
+into the second quantizer instead), the second quantizer, selection, the
 down grouped GEMM with correction, and the combine.
 
 Prints ONE JSON line.  `value` = algorithmic GEMM flops of a step (2 * rows *
@@ -60,6 +61,8 @@ def parse():
                     help="only run a 1 GiB device-to-device copy three times")
     ap.add_argument("--rac-sweep", action="store_true",
                     help="only sweep the number of compensated channels k on the first GEMM")
+    ap.add_argument("--no-fuse-swiglu", action="store_true",
+                    help="time the gate+up GEMM and the SwiGLU pass separately")
     ap.add_argument("--w4a16", action="store_true",
                     help="only time the trainer-side W4A16 product on the block's GEMM shapes")
     return ap.parse_args()
@@ -129,7 +132,7 @@ class Timer:
         return sum(a.elapsed_time(b) for a, b in self.pairs) / len(self.pairs)
 
 
-def run_gpu(cfg, wl, steps, warmup):
+def run_gpu(cfg, wl, steps, warmup, fuse_swiglu=True):
     import torch
 
     import fp4_quantized_gemm_amd as F
@@ -171,12 +174,14 @@ def run_gpu(cfg, wl, steps, warmup):
         if cfg.k_first:
             S, R = timed("select1", F.select_residual_channels, q["x_used"], q["codes"],
                          q["scales"], q["g"], q["score"], cfg.k_first)
-        y1 = timed("gemm1", F.grouped_w4a4_gemm_rac, q["codes"], q["scales"], q["g"], perm, R, S,
-                   c1, s1, g1, offs, M_total=rows)
+        fuse = fuse_swiglu and wd is not None
+        gemm1 = F.grouped_w4a4_gemm_rac_swiglu if fuse else F.grouped_w4a4_gemm_rac
+        y1 = timed("gemm1", gemm1, q["codes"], q["scales"], q["g"], perm, R, S, c1, s1, g1, offs,
+                   M_total=rows)
         if wd is None:
             return y1
         c2, s2, g2, _ = wd
-        q2 = timed("quant2", F.nvfp4_quantize_act, y1, True, cfg.k_down > 0)
+        q2 = timed("quant2", F.nvfp4_quantize_act, y1, not fuse, cfg.k_down > 0)
         S2 = R2 = None
         if cfg.k_down:
             S2, R2 = timed("select2", F.select_residual_channels, q2["x_used"], q2["codes"],
@@ -474,13 +479,16 @@ def main():
     if args.w4a16:
         print(json.dumps(w4a16_bench(cfg, wl, max(args.steps // 2, 5))), flush=True)
         return
-    ms, stage_ms, rac, counts = run_gpu(cfg, wl, args.steps, args.warmup)
+    # the SwiGLU is fused where the large-tile kernel forms it in its epilogue;
+    # on decode-sized blocks the decode kernel's output goes to the quantizer
+    decode = cfg.rows <= 48 * cfg.E and cfg.kind != "dense"
+    fuse = not args.no_fuse_swiglu and wl.w_down is not None and not decode
+    ms, stage_ms, rac, counts = run_gpu(cfg, wl, args.steps, args.warmup, fuse)
     shapes = cfg.gemm_shapes()
     flops_step = cfg.gemm_flops()
     value = flops_step / (ms * 1e-3) / 1e12
     gemm_ms = stage_ms.get("gemm1", 0.0) + stage_ms.get("gemm2", 0.0)
     alg_bytes = gemm_algorithmic_bytes(cfg, counts)
-    decode = cfg.rows <= 48 * cfg.E and cfg.kind != "dense"
     if decode:
         achieved = alg_bytes / (gemm_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
@@ -494,8 +502,10 @@ def main():
         # the library's choice for large workloads (on a 256-CU MI355X)
         _, m, n, _, _ = shapes[0]
         big = (m // 256) * ((n + 255) // 256) >= 512
-        kernel = ("grouped_w4a4_gemm_rac: k_decode_a + k_tile_prefix + k_gemm_big" if big
-                  else "grouped_w4a4_gemm_rac: k_tile_prefix + k_gemm_generic")
+        name = "grouped_w4a4_gemm_rac_swiglu + grouped_w4a4_gemm_rac" if fuse else \
+            "grouped_w4a4_gemm_rac"
+        kernel = (f"{name}: k_decode_a + k_tile_prefix + k_gemm_big" if big
+                  else f"{name}: k_tile_prefix + k_gemm_generic")
     roof["traffic"] = recorded_traffic(cfg.name)
     roof["kernel"] = kernel
     roof["algorithmic_bytes"] = round(alg_bytes)
@@ -503,7 +513,8 @@ def main():
     q_bytes = 2.5625 * cfg.T * cfg.H
     quant = {"quant1_GBps": q_bytes / (stage_ms["quant1"] * 1e-3) / 1e9}
     if "quant2" in stage_ms:
-        q2_bytes = 4.5625 * cfg.rows * cfg.inter
+        # h's quantizer: reads [gate | up] and forms h, or reads h (fused)
+        q2_bytes = (2.5625 if fuse else 4.5625) * cfg.rows * cfg.inter
         quant["quant2_GBps"] = q2_bytes / (stage_ms["quant2"] * 1e-3) / 1e9
     line = {
         "metric": "grouped W4A4+RAC GEMM TFLOP/s and % of MI355X FP4 MFMA peak; quantizer GB/s",
@@ -522,7 +533,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E,
                    "topk": cfg.topk, "inter": cfg.inter, "rac_k": [s[4] for s in shapes],
-                   "gemms": [f"{n} {m}x{nn}x{k}" for n, m, nn, k, _ in shapes]},
+                   "gemms": [f"{n} {m}x{nn}x{k}" for n, m, nn, k, _ in shapes],
+                   "swiglu": ("fused into the gate+up GEMM" if fuse else
+                              "fused into the second quantizer") if wl.w_down is not None
+                   else None},
         "roofline": roof,
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "quantizer": {k: round(v, 1) for k, v in quant.items()},
