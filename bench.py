@@ -175,13 +175,19 @@ def run_gpu(cfg, wl, steps, warmup, fuse_swiglu=True):
             S, R = timed("select1", F.select_residual_channels, q["x_used"], q["codes"],
                          q["scales"], q["g"], q["score"], cfg.k_first)
         fuse = fuse_swiglu and wd is not None
-        gemm1 = F.grouped_w4a4_gemm_rac_swiglu if fuse else F.grouped_w4a4_gemm_rac
-        y1 = timed("gemm1", gemm1, q["codes"], q["scales"], q["g"], perm, R, S, c1, s1, g1, offs,
-                   M_total=rows)
+        gargs = (q["codes"], q["scales"], q["g"], perm, R, S, c1, s1, g1, offs)
+        if fuse:
+            y1, h_amax = timed("gemm1", F.grouped_w4a4_gemm_rac_swiglu, *gargs, M_total=rows,
+                               with_amax=True)
+        else:
+            y1 = timed("gemm1", F.grouped_w4a4_gemm_rac, *gargs, M_total=rows)
         if wd is None:
             return y1
         c2, s2, g2, _ = wd
-        q2 = timed("quant2", F.nvfp4_quantize_act, y1, not fuse, cfg.k_down > 0)
+        if fuse:
+            q2 = timed("quant2", F.nvfp4_quantize_act_amax, y1, h_amax, cfg.k_down > 0)
+        else:
+            q2 = timed("quant2", F.nvfp4_quantize_act, y1, True, cfg.k_down > 0)
         S2 = R2 = None
         if cfg.k_down:
             S2, R2 = timed("select2", F.select_residual_channels, q2["x_used"], q2["codes"],
@@ -513,7 +519,8 @@ def main():
     q_bytes = 2.5625 * cfg.T * cfg.H
     quant = {"quant1_GBps": q_bytes / (stage_ms["quant1"] * 1e-3) / 1e9}
     if "quant2" in stage_ms:
-        # h's quantizer: reads [gate | up] and forms h, or reads h (fused)
+        # h's quantizer: reads [gate | up] and forms h, or reads h once (fused,
+        # amax from the GEMM)
         q2_bytes = (2.5625 if fuse else 4.5625) * cfg.rows * cfg.inter
         quant["quant2_GBps"] = q2_bytes / (stage_ms["quant2"] * 1e-3) / 1e9
     line = {

@@ -28,7 +28,8 @@ from .build import LIB as LIB_PATH
 __all__ = ["lib", "nvfp4_qdq_weights", "nvfp4_quantize_act", "select_residual_channels",
            "moe_permute", "grouped_w4a4_gemm_rac", "moe_unpermute_combine", "nvfp4_qdq_residual",
            "grouped_w4a16_gemm", "select_residual_channels_per_expert",
-           "grouped_w4a4_gemm_rac_per_expert", "grouped_w4a4_gemm_rac_swiglu", "NvfpError",
+           "grouped_w4a4_gemm_rac_per_expert", "grouped_w4a4_gemm_rac_swiglu",
+           "nvfp4_quantize_act_amax", "NvfpError",
            "EXPORTED_SYMBOLS"]
 
 EXPORTED_SYMBOLS = [
@@ -44,6 +45,7 @@ EXPORTED_SYMBOLS = [
     "select_residual_channels_per_expert_workspace_size", "select_residual_channels_per_expert",
     "grouped_w4a4_gemm_rac_per_expert",
     "grouped_w4a4_gemm_rac_swiglu_workspace_size", "grouped_w4a4_gemm_rac_swiglu",
+    "nvfp4_quantize_act_amax",
 ]
 
 
@@ -98,7 +100,8 @@ def _load():
         "grouped_w4a4_gemm_rac_per_expert": [_P, _P, _P, _P, _I64, _P, _P, _I64, _P, _P, _P, _P,
                                              _I64, _I64, _I64, _I64, _P, _P, _SZ, _P],
         "grouped_w4a4_gemm_rac_swiglu": [_P, _P, _P, _P, _I64, _P, _P, _I64, _P, _P, _P, _P, _I64,
-                                         _I64, _I64, _I64, _P, _P, _SZ, _P],
+                                         _I64, _I64, _I64, _P, _P, _P, _SZ, _P],
+        "nvfp4_quantize_act_amax": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P],
     }
     for name, args in sigs.items():
         f = getattr(L, name)
@@ -255,7 +258,7 @@ def select_residual_channels_per_expert(x_used, codes, scales, g, score_unused, 
 
 
 def _gemm_rac(fn_name, a_codes, a_scales, g_x, a_rows, R, S, w_codes, w_scales, g_w,
-              expert_offsets, M_total, out, glu=False):
+              expert_offsets, M_total, out, glu=False, h_amax=None):
     L = _load()
     M_src, Kh = a_codes.shape
     K = Kh * 2
@@ -269,20 +272,43 @@ def _gemm_rac(fn_name, a_codes, a_scales, g_x, a_rows, R, S, w_codes, w_scales, 
     wsq = (L.grouped_w4a4_gemm_rac_swiglu_workspace_size if glu
            else L.grouped_w4a4_gemm_rac_workspace_size)
     ws = _ws(wsq(E, M_src, M_total, N, K, k), dev)
+    tail = [_ptr(y), _ptr(h_amax)] if glu else [_ptr(y)]
     _check(getattr(L, fn_name)(_ptr(a_codes), _ptr(a_scales), _ptr(g_x), _ptr(a_rows), M_src,
                                _ptr(R) if k else None, _ptr(S) if k else None, k,
                                _ptr(w_codes), _ptr(w_scales), _ptr(g_w), _ptr(expert_offsets),
-                               E, M_total, N, K, _ptr(y), _ptr(ws), ws.numel(), _stream(dev)),
+                               E, M_total, N, K, *tail, _ptr(ws), ws.numel(), _stream(dev)),
            fn_name)
     return y
 
 
 def grouped_w4a4_gemm_rac_swiglu(a_codes, a_scales, g_x, a_rows, R_S, S, w_codes, w_scales, g_w,
-                                 expert_offsets, M_total=None, out=None):
+                                 expert_offsets, M_total=None, out=None, with_amax=False):
     """h [M_total][N/2] bf16 = SwiGLU of the grouped W4A4 GEMM plus correction,
-    whose weights' N rows are [gate | up]."""
-    return _gemm_rac("grouped_w4a4_gemm_rac_swiglu", a_codes, a_scales, g_x, a_rows, R_S, S,
-                     w_codes, w_scales, g_w, expert_offsets, M_total, out, glu=True)
+    whose weights' N rows are [gate | up].  with_amax=True returns (h, amax)
+    with amax [1] int32 holding max |h| as bf16 bits."""
+    amax = torch.empty(1, dtype=torch.int32, device=a_codes.device) if with_amax else None
+    h = _gemm_rac("grouped_w4a4_gemm_rac_swiglu", a_codes, a_scales, g_x, a_rows, R_S, S,
+                  w_codes, w_scales, g_w, expert_offsets, M_total, out, glu=True, h_amax=amax)
+    return (h, amax) if with_amax else h
+
+
+def nvfp4_quantize_act_amax(x, amax, want_score=True):
+    """nvfp4_quantize_act (glu=False) with the tensor amax given as bf16 bits
+    in a [1] int32 device tensor (from grouped_w4a4_gemm_rac_swiglu)."""
+    L = _load()
+    _need(x, torch.bfloat16, "x")
+    M, K = x.shape
+    dev = x.device
+    codes = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+    g = torch.empty(1, dtype=torch.float32, device=dev)
+    score = torch.empty(K, dtype=torch.uint64, device=dev) if want_score else None
+    ws = _ws(L.nvfp4_quantize_act_workspace_size(M, K), dev)
+    _check(L.nvfp4_quantize_act_amax(_ptr(x), M, K, x.stride(0), _ptr(amax), _ptr(codes),
+                                     _ptr(scales), _ptr(g), _ptr(score), _ptr(ws), ws.numel(),
+                                     _stream(dev)),
+           "nvfp4_quantize_act_amax")
+    return dict(codes=codes, scales=scales, g=g, score=score, x_used=x)
 
 
 def grouped_w4a4_gemm_rac_per_expert(a_codes, a_scales, g_x, a_rows, R_P, S_E, w_codes,

@@ -98,6 +98,16 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+// max |v| over 8 bf16 values (two per dword) as 15-bit magnitude bits: for
+// finite values the bits order like the magnitudes
+__device__ __forceinline__ uint32_t absmax_bf16x8(uint4 v) {
+  const uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu, d = v.z & 0x7FFF7FFFu,
+                 e = v.w & 0x7FFF7FFFu;
+  const uint32_t hi = max(max(a >> 16, b >> 16), max(d >> 16, e >> 16));
+  const uint32_t lo = max(max(a & 0xFFFFu, b & 0xFFFFu), max(d & 0xFFFFu, e & 0xFFFFu));
+  return max(hi, lo);
+}
+
 // Block-wide max of non-negative 32-bit values, then one device atomic per
 // block (instead of one per wave, which serialises at the L2 on one address).
 template <int NTHREADS>

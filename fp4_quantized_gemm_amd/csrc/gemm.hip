@@ -56,8 +56,10 @@ struct GemmArgs {
   int r_perm;
   // fused SwiGLU (large-tile kernel): glu_i = I > 0 means the weight rows
   // are [gate (I) | up (I)], a column tile pairs gate columns with the same
-  // up columns, and y receives h = bf16(silu(gate) * up), [M_total][I]
+  // up columns, and y receives h = bf16(silu(gate) * up), [M_total][I];
+  // h_amax (nullable) receives max |h| as bf16 bits (atomic max)
   int64_t glu_i;
+  uint32_t* h_amax;
 };
 
 // tile_prefix[e] = number of 128-row tiles of experts before e; [E] = total
@@ -740,6 +742,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   // y = bf16(g_w * acc), staged through LDS (one 128-row half at a time, by
   // the four waves that own it) for 16-byte row stores
   const float gw = p.g_w[e];
+  uint32_t hmax = 0;                             // max |h| bits (fused SwiGLU)
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     __syncthreads();
@@ -767,9 +770,10 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
         if (prow < e_hi && c < p.glu_i) {
           const uint4 g4 = *reinterpret_cast<const uint4*>(wsl + row * OUTROW + ch * 16);
           const uint4 u4 = *reinterpret_cast<const uint4*>(wsl + row * OUTROW + 256 + ch * 16);
-          *reinterpret_cast<uint4*>(p.y + prow * p.glu_i + c) =
-              make_uint4(swiglu_pair(g4.x, u4.x), swiglu_pair(g4.y, u4.y),
-                         swiglu_pair(g4.z, u4.z), swiglu_pair(g4.w, u4.w));
+          const uint4 o = make_uint4(swiglu_pair(g4.x, u4.x), swiglu_pair(g4.y, u4.y),
+                                     swiglu_pair(g4.z, u4.z), swiglu_pair(g4.w, u4.w));
+          *reinterpret_cast<uint4*>(p.y + prow * p.glu_i + c) = o;
+          hmax = max(hmax, absmax_bf16x8(o));
         }
       }
     } else {
@@ -783,21 +787,26 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
       }
     }
   }
+  if (p.glu_i > 0 && p.h_amax != nullptr) block_atomic_max<512>(hmax, p.h_amax);
 }
 
 // h [M][I] = bf16(silu(gate) * up) of y [M][2I] = [gate | up], 8 columns per
 // thread (the fused SwiGLU for shapes the large-tile kernel does not take)
 __global__ void __launch_bounds__(256)
-k_swiglu_rows(const uint16_t* __restrict__ y, int64_t M, int64_t I, uint16_t* __restrict__ h) {
+k_swiglu_rows(const uint16_t* __restrict__ y, int64_t M, int64_t I, uint16_t* __restrict__ h,
+              uint32_t* __restrict__ h_amax) {
   const int64_t n8 = M * (I / 8);
+  uint32_t m8 = 0;
   for (int64_t q = blockIdx.x * 256LL + threadIdx.x; q < n8; q += (int64_t)gridDim.x * 256) {
     const int64_t m = q / (I / 8), c = (q - m * (I / 8)) * 8;
     const uint4 g4 = *reinterpret_cast<const uint4*>(y + m * 2 * I + c);
     const uint4 u4 = *reinterpret_cast<const uint4*>(y + m * 2 * I + I + c);
-    *reinterpret_cast<uint4*>(h + m * I + c) =
-        make_uint4(swiglu_pair(g4.x, u4.x), swiglu_pair(g4.y, u4.y), swiglu_pair(g4.z, u4.z),
-                   swiglu_pair(g4.w, u4.w));
+    const uint4 o = make_uint4(swiglu_pair(g4.x, u4.x), swiglu_pair(g4.y, u4.y),
+                               swiglu_pair(g4.z, u4.z), swiglu_pair(g4.w, u4.w));
+    *reinterpret_cast<uint4*>(h + m * I + c) = o;
+    m8 = max(m8, absmax_bf16x8(o));
   }
+  if (h_amax != nullptr) block_atomic_max<256>(m8, h_amax);
 }
 
 // Weight columns of the selected channels for the large-k correction: bf16
@@ -1237,7 +1246,8 @@ size_t grouped_w4a4_gemm_rac_workspace_size(int64_t E, int64_t M_src, int64_t M_
 // glu: y receives h = bf16(silu(gate) * up) [M_total][N/2] of the [gate | up]
 // product, fused into the large-tile kernel's epilogue, else formed from a
 // product staged in the workspace
-static int gemm_rac(bool per_expert, bool glu, const uint8_t* a_codes, const uint8_t* a_scales,
+static int gemm_rac(bool per_expert, bool glu, uint32_t* h_amax, const uint8_t* a_codes,
+                    const uint8_t* a_scales,
                     const float* g_x, const int32_t* a_rows, int64_t M_src, const void* R_S,
                     const int32_t* S, int64_t k, const uint8_t* w_codes, const uint8_t* w_scales,
                     const float* g_w, const int32_t* expert_offsets, int64_t E, int64_t M_total,
@@ -1293,7 +1303,7 @@ static int gemm_rac(bool per_expert, bool glu, const uint8_t* a_codes, const uin
     int64_t nb = (n8 + 255) / 256;
     if (nb > 16LL * num_cus()) nb = 16LL * num_cus();
     k_swiglu_rows<<<(unsigned)(nb > 0 ? nb : 1), 256, 0, s>>>(glu_stage, M_total, N / 2,
-                                                             static_cast<uint16_t*>(y));
+                                                             static_cast<uint16_t*>(y), h_amax);
   };
   const int64_t m_tiles = (M_total + kBM - 1) / kBM + E;
   const int64_t n_tiles = (N + kBN - 1) / kBN;
@@ -1359,7 +1369,7 @@ static int gemm_rac(bool per_expert, bool glu, const uint8_t* a_codes, const uin
     k_decode_a<<<(unsigned)nb, 256, 0, s>>>(a_codes, a_scales, M_src, K, img);
     k_tile_prefix<<<1, 1024, 0, s>>>(expert_offsets, (int)E, M_total, big::BM, prefix);
     const int64_t nblk = (((m_tiles_big + 3) / 4) * 4 * n_tiles_big + 7) / 8 * 8;
-    if (glu) a.glu_i = N / 2;
+    if (glu) a.glu_i = N / 2, a.h_amax = h_amax;
     k_gemm_big<false><<<(unsigned)nblk, 512, 0, s>>>(a, reinterpret_cast<const uint8_t*>(img),
                                                     (int)n_tiles_big, (int)m_tiles_big);
   } else {
@@ -1377,8 +1387,8 @@ int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const
                           const float* g_w, const int32_t* expert_offsets, int64_t E,
                           int64_t M_total, int64_t N, int64_t K, void* y, void* ws,
                           size_t ws_bytes, void* stream) {
-  return gemm_rac(false, false, a_codes, a_scales, g_x, a_rows, M_src, R_S, S, k, w_codes, w_scales,
-                  g_w, expert_offsets, E, M_total, N, K, y, ws, ws_bytes, stream);
+  return gemm_rac(false, false, nullptr, a_codes, a_scales, g_x, a_rows, M_src, R_S, S, k, w_codes,
+                  w_scales, g_w, expert_offsets, E, M_total, N, K, y, ws, ws_bytes, stream);
 }
 
 int grouped_w4a4_gemm_rac_per_expert(const uint8_t* a_codes, const uint8_t* a_scales,
@@ -1388,8 +1398,9 @@ int grouped_w4a4_gemm_rac_per_expert(const uint8_t* a_codes, const uint8_t* a_sc
                                      const float* g_w, const int32_t* expert_offsets, int64_t E,
                                      int64_t M_total, int64_t N, int64_t K, void* y, void* ws,
                                      size_t ws_bytes, void* stream) {
-  return gemm_rac(true, false, a_codes, a_scales, g_x, a_rows, M_src, R_P, S_E, k, w_codes,
-                  w_scales, g_w, expert_offsets, E, M_total, N, K, y, ws, ws_bytes, stream);
+  return gemm_rac(true, false, nullptr, a_codes, a_scales, g_x, a_rows, M_src, R_P, S_E, k,
+                  w_codes, w_scales, g_w, expert_offsets, E, M_total, N, K, y, ws, ws_bytes,
+                  stream);
 }
 
 size_t grouped_w4a4_gemm_rac_swiglu_workspace_size(int64_t E, int64_t M_src, int64_t M_total,
@@ -1403,15 +1414,17 @@ int grouped_w4a4_gemm_rac_swiglu(const uint8_t* a_codes, const uint8_t* a_scales
                                  const int32_t* S, int64_t k, const uint8_t* w_codes,
                                  const uint8_t* w_scales, const float* g_w,
                                  const int32_t* expert_offsets, int64_t E, int64_t M_total,
-                                 int64_t N, int64_t K, void* h, void* ws, size_t ws_bytes,
-                                 void* stream) {
+                                 int64_t N, int64_t K, void* h, uint32_t* h_amax, void* ws,
+                                 size_t ws_bytes, void* stream) {
   NV_REQUIRE(N % 32 == 0, NVFP4_ERR_SHAPE,
              "grouped_w4a4_gemm_rac_swiglu: N = 2 I needs N %% 32 == 0 (N=%lld)", (long long)N);
   NV_REQUIRE(aligned(h, 16), NVFP4_ERR_ALIGN, "grouped_w4a4_gemm_rac_swiglu: misaligned h");
   NV_REQUIRE(ws_bytes >= grouped_w4a4_gemm_rac_swiglu_workspace_size(E, M_src, M_total, N, K, k),
              NVFP4_ERR_WORKSPACE, "grouped_w4a4_gemm_rac_swiglu: workspace too small");
-  return gemm_rac(false, true, a_codes, a_scales, g_x, a_rows, M_src, R_S, S, k, w_codes, w_scales,
-                  g_w, expert_offsets, E, M_total, N, K, h, ws, ws_bytes, stream);
+  NV_REQUIRE(aligned(h_amax, 4), NVFP4_ERR_ALIGN, "grouped_w4a4_gemm_rac_swiglu: misaligned h_amax");
+  if (h_amax != nullptr) fill_u32(h_amax, 1, 0u, as_stream(stream));
+  return gemm_rac(false, true, h_amax, a_codes, a_scales, g_x, a_rows, M_src, R_S, S, k, w_codes,
+                  w_scales, g_w, expert_offsets, E, M_total, N, K, h, ws, ws_bytes, stream);
 }
 
 size_t grouped_w4a16_gemm_workspace_size(int64_t E) {

@@ -59,12 +59,7 @@ k_amax(const uint16_t* __restrict__ x, int64_t rows, int64_t ldx, int64_t tensor
   if (rsub < rows_per_iter && c < chunks) {
     for (int64_t r = (int64_t)blockIdx.x * rows_per_iter + rsub; r < rows;
          r += (int64_t)gridDim.x * rows_per_iter) {
-      uint4 v = *reinterpret_cast<const uint4*>(xt + r * ldx + (int64_t)c * 8);
-      uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu, d = v.z & 0x7FFF7FFFu,
-               e = v.w & 0x7FFF7FFFu;
-      uint32_t hi = max(max(a >> 16, b >> 16), max(d >> 16, e >> 16));
-      uint32_t lo = max(max(a & 0xFFFFu, b & 0xFFFFu), max(d & 0xFFFFu, e & 0xFFFFu));
-      m = max(m, max(hi, lo));
+      m = max(m, absmax_bf16x8(*reinterpret_cast<const uint4*>(xt + r * ldx + (int64_t)c * 8)));
     }
   }
   block_atomic_max<256>(m, amax + blockIdx.z);
@@ -72,12 +67,6 @@ k_amax(const uint16_t* __restrict__ x, int64_t rows, int64_t ldx, int64_t tensor
 
 // Contiguous tensors: flat loop, four independent 16-byte loads in flight
 // per thread (tensor t = blockIdx.y, n8 chunks of 8 elements each).
-__device__ __forceinline__ uint32_t absmax8(uint4 v) {
-  uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu, d = v.z & 0x7FFF7FFFu, e = v.w & 0x7FFF7FFFu;
-  uint32_t hi = max(max(a >> 16, b >> 16), max(d >> 16, e >> 16));
-  uint32_t lo = max(max(a & 0xFFFFu, b & 0xFFFFu), max(d & 0xFFFFu, e & 0xFFFFu));
-  return max(hi, lo);
-}
 
 __global__ void __launch_bounds__(256)
 k_amax_flat(const uint16_t* __restrict__ x, int64_t n8, int64_t tensor_stride,
@@ -88,9 +77,9 @@ k_amax_flat(const uint16_t* __restrict__ x, int64_t n8, int64_t tensor_stride,
   uint32_t m = 0;
   for (; i + 3 * stride < n8; i += 4 * stride) {
     const uint4 a = xt[i], b = xt[i + stride], c = xt[i + 2 * stride], d = xt[i + 3 * stride];
-    m = max(m, max(max(absmax8(a), absmax8(b)), max(absmax8(c), absmax8(d))));
+    m = max(m, max(max(absmax_bf16x8(a), absmax_bf16x8(b)), max(absmax_bf16x8(c), absmax_bf16x8(d))));
   }
-  for (; i < n8; i += stride) m = max(m, absmax8(xt[i]));
+  for (; i < n8; i += stride) m = max(m, absmax_bf16x8(xt[i]));
   block_atomic_max<256>(m, amax + blockIdx.y);
 }
 
@@ -119,11 +108,7 @@ k_swiglu_amax(const uint16_t* __restrict__ y, int64_t rows, int64_t ldy, int64_t
       o.z = swiglu_pair(g.z, u.z);
       o.w = swiglu_pair(g.w, u.w);
       *reinterpret_cast<uint4*>(h + r * inter + (int64_t)c * 8) = o;
-      uint32_t a = o.x & 0x7FFF7FFFu, b = o.y & 0x7FFF7FFFu, d = o.z & 0x7FFF7FFFu,
-               e = o.w & 0x7FFF7FFFu;
-      uint32_t hi = max(max(a >> 16, b >> 16), max(d >> 16, e >> 16));
-      uint32_t lo = max(max(a & 0xFFFFu, b & 0xFFFFu), max(d & 0xFFFFu, e & 0xFFFFu));
-      m = max(m, max(hi, lo));
+      m = max(m, absmax_bf16x8(o));
     }
   }
   block_atomic_max<256>(m, amax);
@@ -404,6 +389,24 @@ size_t nvfp4_qdq_weights_workspace_size(int64_t E) {
   return round_up((size_t)(E > 0 ? E : 1) * sizeof(uint32_t), 256);
 }
 
+// the quantize pass (and the channel-score reduction) once the amax is known
+static void quantize_pass(const uint16_t* src, int64_t M, int64_t K, int64_t ld,
+                          const uint32_t* amax, uint8_t* codes, uint8_t* scales, float* g_x,
+                          uint64_t* score, uint64_t* partial, hipStream_t s) {
+  RowTiling t16 = row_tiling(K / 16);
+  const int nq = quant_grid(M, K);
+  dim3 grid(nq, t16.col_groups, 1);
+  const size_t red_bytes = (score && t16.rows_per_iter > 1) ? 256 * 16 * sizeof(uint64_t) : 0;
+  k_quantize<<<grid, 256, red_bytes, s>>>(src, M, ld, K, 0, 1, t16.chunks, t16.rows_per_iter,
+                                          amax, codes, scales, g_x, score ? partial : nullptr,
+                                          nullptr);
+  if (score) {
+    fill_u64(score, K, 0ull, s);
+    k_score_reduce<<<dim3((unsigned)((K + 63) / 64), (unsigned)((nq + 63) / 64)), 256, 0, s>>>(
+        partial, nq, K, score);
+  }
+}
+
 int nvfp4_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, int glu,
                        uint8_t* codes, uint8_t* scales, float* g_x, uint64_t* score,
                        void* x_used, void* ws, size_t ws_bytes, void* stream) {
@@ -446,19 +449,29 @@ int nvfp4_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, int glu
       k_amax<<<grid, 256, 0, s>>>(src, M, ldx, 0, t8.chunks, t8.rows_per_iter, amax);
     }
   }
-  RowTiling t16 = row_tiling(K / 16);
-  const int nq = quant_grid(M, K);
-  dim3 grid(nq, t16.col_groups, 1);
-  const size_t red_bytes = (score && t16.rows_per_iter > 1) ? 256 * 16 * sizeof(uint64_t) : 0;
-  k_quantize<<<grid, 256, red_bytes, s>>>(src, M, ld, K, 0, 1, t16.chunks, t16.rows_per_iter,
-                                          amax, codes, scales, g_x, score ? partial : nullptr,
-                                          nullptr);
-  if (score) {
-    fill_u64(score, K, 0ull, s);
-    k_score_reduce<<<dim3((unsigned)((K + 63) / 64), (unsigned)((nq + 63) / 64)), 256, 0, s>>>(
-        partial, nq, K, score);
-  }
+  quantize_pass(src, M, K, ld, amax, codes, scales, g_x, score, partial, s);
   return check_launch("nvfp4_quantize_act");
+}
+
+int nvfp4_quantize_act_amax(const void* x, int64_t M, int64_t K, int64_t ldx,
+                            const uint32_t* amax, uint8_t* codes, uint8_t* scales, float* g_x,
+                            uint64_t* score, void* ws, size_t ws_bytes, void* stream) {
+  NV_REQUIRE(g_x && ws && amax, NVFP4_ERR_NULL,
+             "nvfp4_quantize_act_amax: g_x, amax and ws are required");
+  NV_REQUIRE(M >= 0 && K >= 32 && K % 32 == 0 && ldx >= K && ldx % 8 == 0, NVFP4_ERR_SHAPE,
+             "nvfp4_quantize_act_amax: need M >= 0, K >= 32, K %% 32 == 0, ldx >= K, "
+             "ldx %% 8 == 0 (M=%lld K=%lld)", (long long)M, (long long)K);
+  NV_REQUIRE(M == 0 || (x && codes && scales), NVFP4_ERR_NULL,
+             "nvfp4_quantize_act_amax: x, codes and scales are required");
+  NV_REQUIRE(aligned(x, 16) && aligned(codes, 8) && aligned(score, 8) && aligned(ws, 16) &&
+                 aligned(amax, 4),
+             NVFP4_ERR_ALIGN, "nvfp4_quantize_act_amax: misaligned pointer");
+  NV_REQUIRE(ws_bytes >= nvfp4_quantize_act_workspace_size(M, K), NVFP4_ERR_WORKSPACE,
+             "nvfp4_quantize_act_amax: workspace too small");
+  uint64_t* partial = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + 256);
+  quantize_pass(static_cast<const uint16_t*>(x), M, K, ldx, amax, codes, scales, g_x, score,
+                partial, as_stream(stream));
+  return check_launch("nvfp4_quantize_act_amax");
 }
 
 size_t nvfp4_qdq_residual_workspace_size(int64_t M, int64_t k) {

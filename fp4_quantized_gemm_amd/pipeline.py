@@ -15,7 +15,7 @@ from dataclasses import dataclass
 import torch
 
 from . import (grouped_w4a4_gemm_rac, grouped_w4a4_gemm_rac_per_expert,
-               grouped_w4a4_gemm_rac_swiglu, moe_permute,
+               grouped_w4a4_gemm_rac_swiglu, moe_permute, nvfp4_quantize_act_amax,
                moe_unpermute_combine, nvfp4_qdq_residual, nvfp4_qdq_weights, nvfp4_quantize_act,
                select_residual_channels, select_residual_channels_per_expert)
 
@@ -33,7 +33,7 @@ def prepare_weights(w, want_qdq=False) -> QuantWeights:
 
 
 def quantized_linear_rac(x, wq: QuantWeights, k, a_rows=None, offsets=None, M_total=None,
-                         glu=False, rac="bf16", select="shared", swiglu_out=False):
+                         glu=False, rac="bf16", select="shared", swiglu_out=False, amax=None):
     """Quantize x (or SwiGLU of x), select k channels, grouped GEMM.
     rac="bf16" adds the bf16 residual of the selected channels back;
     rac="nvfp4" quantizes that residual a second time to NVFP4 first and adds
@@ -41,13 +41,17 @@ def quantized_linear_rac(x, wq: QuantWeights, k, a_rows=None, offsets=None, M_to
     for the whole call; select="per_expert" one per expert, from the rows
     routed to it.  swiglu_out=True returns h = SwiGLU of the [gate | up]
     product instead of the product (fused into the GEMM; shared selection
-    only).  Returns (y or h, stage dict)."""
+    only).  amax: x's tensor amax as bf16 bits (from the fused SwiGLU), so the
+    quantizer reads x once.  Returns (y or h, stage dict)."""
     if rac not in ("bf16", "nvfp4"):
         raise ValueError(f"rac must be 'bf16' or 'nvfp4', not {rac!r}")
     if select not in ("shared", "per_expert"):
         raise ValueError(f"select must be 'shared' or 'per_expert', not {select!r}")
     per_expert = select == "per_expert"
-    q = nvfp4_quantize_act(x, glu=glu, want_score=k > 0 and not per_expert)
+    if amax is not None:
+        q = nvfp4_quantize_act_amax(x, amax, want_score=k > 0 and not per_expert)
+    else:
+        q = nvfp4_quantize_act(x, glu=glu, want_score=k > 0 and not per_expert)
     if offsets is None:
         offsets = torch.tensor([0, x.shape[0]], dtype=torch.int32, device=x.device)
     S = R = None
@@ -63,10 +67,12 @@ def quantized_linear_rac(x, wq: QuantWeights, k, a_rows=None, offsets=None, M_to
             R = nvfp4_qdq_residual(R)[3]
     if swiglu_out and per_expert:
         raise ValueError("the fused SwiGLU output takes the shared channel selection")
-    gemm = (grouped_w4a4_gemm_rac_per_expert if per_expert else
-            grouped_w4a4_gemm_rac_swiglu if swiglu_out else grouped_w4a4_gemm_rac)
-    y = gemm(q["codes"], q["scales"], q["g"], a_rows, R, S, wq.codes, wq.scales, wq.g, offsets,
-             M_total=M_total)
+    args = (q["codes"], q["scales"], q["g"], a_rows, R, S, wq.codes, wq.scales, wq.g, offsets)
+    if swiglu_out:
+        y, amax = grouped_w4a4_gemm_rac_swiglu(*args, M_total=M_total, with_amax=True)
+        return y, dict(q=q, S=S, R=R, h_amax=amax)
+    gemm = grouped_w4a4_gemm_rac_per_expert if per_expert else grouped_w4a4_gemm_rac
+    y = gemm(*args, M_total=M_total)
     return y, dict(q=q, S=S, R=R)
 
 
@@ -87,7 +93,8 @@ def moe_forward(x, logits, topk, w_first: QuantWeights, w_down: QuantWeights, k_
     if w_down is None:
         return y1, out
     y2, st2 = quantized_linear_rac(y1, w_down, k_down, a_rows=None, offsets=offs, M_total=rows,
-                                   glu=not fuse, rac=rac, select=select)
+                                   glu=not fuse, rac=rac, select=select,
+                                   amax=st1.get("h_amax") if fuse else None)
     o = moe_unpermute_combine(y2, inv, tw)
     if keep:
         out.update(y2=y2, st2=st2, out=o)

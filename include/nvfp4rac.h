@@ -143,6 +143,8 @@ int select_residual_channels(const void* x_used, int64_t ldx, const uint8_t* cod
  * large problems the SwiGLU runs in the GEMM's epilogue, whose column tiles
  * pair gate and up columns, so the [M_total][2 I] product is never written.
  * Same arguments as grouped_w4a4_gemm_rac with y -> h; requires N % 32 == 0.
+ * h_amax [1] uint32 (device, nullable) receives max |h| as bf16 bits, the
+ * tensor amax nvfp4_quantize_act_amax takes, so h is not read again for it.
  * Workspace: grouped_w4a4_gemm_rac_swiglu_workspace_size (the plain GEMM's
  * plus M_total * N * 2 bytes).
  * ---------------------------------------------------------------------- */
@@ -153,8 +155,16 @@ int grouped_w4a4_gemm_rac_swiglu(const uint8_t* a_codes, const uint8_t* a_scales
                                  const void* R_S, const int32_t* S, int64_t k,
                                  const uint8_t* w_codes, const uint8_t* w_scales,
                                  const float* g_w, const int32_t* expert_offsets, int64_t E,
-                                 int64_t M_total, int64_t N, int64_t K, void* h, void* ws,
-                                 size_t ws_bytes, void* stream);
+                                 int64_t M_total, int64_t N, int64_t K, void* h,
+                                 uint32_t* h_amax, void* ws, size_t ws_bytes, void* stream);
+
+/* nvfp4_quantize_act (glu == 0) with the tensor amax given: amax [1] uint32
+ * (device) holds max |x| as bf16 bits, e.g. from grouped_w4a4_gemm_rac_swiglu,
+ * and x is read once.  The outputs are those nvfp4_quantize_act gives when the
+ * amax is right; the call does not check it.  Same workspace query. */
+int nvfp4_quantize_act_amax(const void* x, int64_t M, int64_t K, int64_t ldx,
+                            const uint32_t* amax, uint8_t* codes, uint8_t* scales, float* g_x,
+                            uint64_t* score, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Per-expert compensation: the variant of Residual Activation Compensation

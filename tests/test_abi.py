@@ -182,7 +182,14 @@ def test_swiglu_gemm_validation():
     ws = L.grouped_w4a4_gemm_rac_swiglu_workspace_size(4, 64, 64, 128, 256, 0)
     assert ws >= L.grouped_w4a4_gemm_rac_workspace_size(4, 64, 64, 128, 256, 0) + 64 * 128 * 2
     args = lambda **kw: [FAKE, FAKE, FAKE, None, 64, None, None, 0, FAKE, FAKE, FAKE, FAKE, 4, 64,
-                         kw.get("N", 128), 256, kw.get("h", FAKE), FAKE, kw.get("ws", ws), None]
+                         kw.get("N", 128), 256, kw.get("h", FAKE), kw.get("amax", None), FAKE,
+                         kw.get("ws", ws), None]
     assert L.grouped_w4a4_gemm_rac_swiglu(*args(N=144)) == ERR_SHAPE    # N = 2I, N % 32
     assert L.grouped_w4a4_gemm_rac_swiglu(*args(h=FAKE_MIS)) == ERR_ALIGN
+    assert L.grouped_w4a4_gemm_rac_swiglu(*args(amax=FAKE_MIS)) == ERR_ALIGN
     assert L.grouped_w4a4_gemm_rac_swiglu(*args(ws=16)) == ERR_WS
+    q = lambda **kw: [FAKE, 4, kw.get("K", 64), kw.get("ldx", 64), kw.get("amax", FAKE), FAKE,
+                      FAKE, FAKE, None, FAKE, 1 << 20, None]
+    assert L.nvfp4_quantize_act_amax(*q(K=48, ldx=48)) == ERR_SHAPE
+    assert L.nvfp4_quantize_act_amax(*q(amax=None)) == ERR_NULL
+    assert L.nvfp4_quantize_act_amax(*q(ldx=32)) == ERR_SHAPE

@@ -289,12 +289,17 @@ def test_gemm_swiglu_fused(dev, gemm_kernel, M_src, counts, I, K, k):
     wc, ws, gw, _ = OQ.qdq_weights(w)
     args = (q["codes"], q["scales"], q["g"], cu(a_rows), R, S, cu(OQ.pack_codes(wc)),
             cu(tile_wscales(ws)), cu(gw), cu(offs))
-    h = F.grouped_w4a4_gemm_rac_swiglu(*args, M_total=M_total)
+    h, amax = F.grouped_w4a4_gemm_rac_swiglu(*args, M_total=M_total, with_amax=True)
     y = F.grouped_w4a4_gemm_rac(*args, M_total=M_total)
     hq = F.nvfp4_quantize_act(y, glu=True)
+    ha = F.nvfp4_quantize_act_amax(h, amax)
     torch.cuda.synchronize()
     assert h.shape == (M_total, I)
     assert np.array_equal(host_bits(h), host_bits(hq["x_used"]))
+    assert int(amax.item()) == int(np.max(host_bits(h) & 0x7FFF))
+    for key in ("codes", "scales", "score"):
+        assert torch.equal(ha[key], hq[key]), key
+    assert np.array_equal(f32_bits(ha["g"].cpu().numpy()), f32_bits(hq["g"].cpu().numpy()))
     qa = OQ.quantize_activation(x, k)
     y_ref = OG.grouped_gemm_rac(qa["codes"], qa["scales"], qa["g"], a_rows, qa["R_S"], qa["S"],
                                 wc, ws, gw, offs)
