@@ -20,113 +20,130 @@ namespace nvfp4 {
 constexpr int kSelectMaxK = 4096;
 constexpr int kSelectThreads = 1024;
 
-__device__ __forceinline__ bool key_before(uint64_t sa, uint32_t ia, uint64_t sb, uint32_t ib) {
-  return sa > sb || (sa == sb && ia < ib);
+__device__ __forceinline__ uint64_t wave_or_u64(uint64_t v) {
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, o), hi = __shfl_xor((uint32_t)(v >> 32), o);
+    v |= ((uint64_t)hi << 32) | lo;
+  }
+  return v;
 }
 
-// One compare-exchange decision: element e with partner value (ps, pi) in a
-// bitonic stage of block `size`; returns true if e should take the partner.
-__device__ __forceinline__ bool take_partner(int e, int partner, int size, uint64_t s, uint32_t i,
-                                             uint64_t ps, uint32_t pi) {
-  const bool first = ((e & size) == 0) == (e < partner);  // e should hold the earlier key
-  return first ? key_before(ps, pi, s, i) : key_before(s, i, ps, pi);
-}
-
-// Bitonic sort of up to 4096 (score desc, index asc) keys by one workgroup.
-// Thread t holds elements 4t .. 4t+3 in registers.  Strides 1 and 2 stay in
-// the thread, strides 4 .. 128 cross lanes of one wave (shuffles), larger
-// strides go through LDS with a barrier.  The first k sorted keys are flagged
-// and compacted in index order, which writes S ascending.
-__global__ void __launch_bounds__(kSelectThreads)
-k_select_topk(const uint64_t* __restrict__ score, int K, int Kpad, int k, int32_t* __restrict__ S) {
-  // one score vector per workgroup (several for the per-expert selection)
-  score += (int64_t)blockIdx.x * K;
-  S += (int64_t)blockIdx.x * k;
-  __shared__ uint64_t xs[kSelectMaxK];
-  __shared__ uint16_t xi[kSelectMaxK];
-  __shared__ uint8_t flag[kSelectMaxK];
-  __shared__ int wsum[kSelectThreads / 64];
+// Exclusive prefix sum of one int per thread over the workgroup (in thread
+// order); wsum holds kSelectThreads / 64 ints.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
   const int tid = threadIdx.x;
-  uint64_t ks[4];
-  uint32_t ki[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = 4 * tid + q;
-    ks[q] = e < K ? score[e] : 0ull;
-    ki[q] = e < K ? (uint32_t)e : 0xFFFFu;
-  }
-  for (int i = tid; i < kSelectMaxK; i += kSelectThreads) flag[i] = 0;
-  const int nt = Kpad / 4;                          // active threads
-  for (int size = 2; size <= Kpad; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      if (stride >= 256) {
-        __syncthreads();
-        if (tid < nt)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) { xs[4 * tid + q] = ks[q]; xi[4 * tid + q] = (uint16_t)ki[q]; }
-        __syncthreads();
-        if (tid < nt)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int e = 4 * tid + q, pe = e ^ stride;
-            const uint64_t ps = xs[pe];
-            const uint32_t pi = xi[pe];
-            if (take_partner(e, pe, size, ks[q], ki[q], ps, pi)) { ks[q] = ps; ki[q] = pi; }
-          }
-      } else if (stride >= 4) {
-        const int lanes = stride >> 2;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t lo = __shfl_xor((uint32_t)ks[q], lanes);
-          const uint32_t hi = __shfl_xor((uint32_t)(ks[q] >> 32), lanes);
-          const uint32_t pi = __shfl_xor(ki[q], lanes);
-          const uint64_t ps = ((uint64_t)hi << 32) | lo;
-          const int e = 4 * tid + q, pe = e ^ stride;
-          if (tid < nt && take_partner(e, pe, size, ks[q], ki[q], ps, pi)) { ks[q] = ps; ki[q] = pi; }
-        }
-      } else {
-        // stride 2 or 1: both elements of each pair are in this thread
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int pq = q ^ stride;
-          if (pq < q) continue;
-          const int e = 4 * tid + q, pe = 4 * tid + pq;
-          if (take_partner(e, pe, size, ks[q], ki[q], ks[pq], ki[pq])) {
-            const uint64_t ts = ks[q]; const uint32_t ti = ki[q];
-            ks[q] = ks[pq]; ki[q] = ki[pq];
-            ks[pq] = ts; ki[pq] = ti;
-          }
-        }
-      }
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    if (4 * tid + q < k) flag[ki[q]] = 1;
-  __syncthreads();
-  // ordered compaction: each thread owns a contiguous run of channels
-  const int per = (Kpad + kSelectThreads - 1) / kSelectThreads;
-  const int lo = tid * per;
-  int cnt = 0;
-  for (int i = lo; i < lo + per && i < K; ++i) cnt += flag[i];
-  int incl = cnt;
+  int incl = v;
   for (int o = 1; o < 64; o <<= 1) {
-    int v = __shfl_up(incl, o);
-    if ((tid & 63) >= o) incl += v;
+    const int w = __shfl_up(incl, o);
+    if ((tid & 63) >= o) incl += w;
   }
+  __syncthreads();
   if ((tid & 63) == 63) wsum[tid >> 6] = incl;
   __syncthreads();
   int base = 0;
   for (int w = 0; w < (tid >> 6); ++w) base += wsum[w];
-  int pos = base + incl - cnt;
-  for (int i = lo; i < lo + per && i < K; ++i)
-    if (flag[i]) S[pos++] = i;
+  return base + incl - v;
 }
 
-// R[m][j] = bf16(fma(-(q*s), g, x[m][S[j]])): a block owns 64 rows; each
-// thread walks channels j = tid, tid + 256, ... of each row.
+// Top-k of up to 4096 (score desc, index asc) keys by one workgroup (one
+// score vector per workgroup: several for the per-expert selection).
+// Thread t holds channels 4t .. 4t+3.  An MSB-first radix select finds the
+// k-th largest score T one byte at a time (a 256-bin LDS histogram of the
+// remaining candidates, then one wave scans the bins from the top); the
+// channels above T are taken, and of the channels equal to T the ones of
+// lowest index, as many as k still needs.  The selected channels are then
+// written in index order, so S is ascending.
+__global__ void __launch_bounds__(kSelectThreads)
+k_select_topk(const uint64_t* __restrict__ score, int K, int Kpad, int k, int32_t* __restrict__ S) {
+  (void)Kpad;
+  score += (int64_t)blockIdx.x * K;
+  S += (int64_t)blockIdx.x * k;
+  __shared__ uint32_t hist[256];
+  __shared__ uint64_t orw[kSelectThreads / 64];
+  __shared__ int wsum[kSelectThreads / 64];
+  __shared__ uint64_t s_prefix;
+  __shared__ int s_need;
+  const int tid = threadIdx.x;
+  uint64_t key[4];
+  bool valid[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = 4 * tid + q;
+    valid[q] = e < K;
+    key[q] = valid[q] ? score[e] : 0ull;
+  }
+  // the highest byte any key uses
+  uint64_t orv = wave_or_u64(key[0] | key[1] | key[2] | key[3]);
+  if ((tid & 63) == 0) orw[tid >> 6] = orv;
+  __syncthreads();
+  orv = 0;
+  for (int w = 0; w < kSelectThreads / 64; ++w) orv |= orw[w];
+  const int top = orv == 0 ? 0 : (63 - __builtin_clzll(orv)) >> 3;
+
+  uint64_t prefix = 0, mask = 0;
+  int need = k;
+  for (int b = top; b >= 0; --b) {
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (valid[q] && (key[q] & mask) == prefix) atomicAdd(&hist[(key[q] >> (8 * b)) & 0xFFu], 1u);
+    __syncthreads();
+    if (tid < 64) {
+      // lane l owns bins 255 - 4l .. 252 - 4l (descending)
+      int cnt[4], sum = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sum += (cnt[i] = (int)hist[255 - 4 * tid - i]);
+      int incl = sum;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int w = __shfl_up(incl, o);
+        if (tid >= o) incl += w;
+      }
+      int c = incl - sum;                      // keys in higher bins
+      if (c < need && need <= incl) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (c + cnt[i] >= need) {
+            s_prefix = prefix | ((uint64_t)(255 - 4 * tid - i) << (8 * b));
+            s_need = need - c;
+            break;
+          }
+          c += cnt[i];
+        }
+      }
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    need = s_need;
+    mask |= 0xFFull << (8 * b);
+  }
+  // prefix is now the k-th largest score T; take everything above it and
+  // the first `need` channels equal to it
+  int ties = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ties += (valid[q] && key[q] == prefix) ? 1 : 0;
+  int tie_rank = block_exclusive_scan(ties, wsum);
+  bool sel[4];
+  int nsel = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    sel[q] = false;
+    if (valid[q] && key[q] > prefix) sel[q] = true;
+    if (valid[q] && key[q] == prefix) sel[q] = tie_rank++ < need;
+    nsel += sel[q] ? 1 : 0;
+  }
+  int pos = block_exclusive_scan(nsel, wsum);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (sel[q]) S[pos++] = 4 * tid + q;
+}
+
+// R[m][j] = bf16(fma(-(q*s), g, x[m][S[j]])): a block owns 64 rows; its 256
+// threads take the (row, channel) pairs of those rows in order, eight pairs
+// in flight per thread (the gathers of one pair are three dependent-free
+// loads, so they overlap across pairs).
 constexpr int kGatherRows = 64;
+constexpr int kGatherInFlight = 8;
 
 __global__ void __launch_bounds__(256)
 k_gather_residual(const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ codes,
@@ -135,16 +152,33 @@ k_gather_residual(const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __
                   uint16_t* __restrict__ R) {
   const float g = *g_x;
   const int64_t m0 = (int64_t)blockIdx.x * kGatherRows;
-  for (int j = threadIdx.x; j < k; j += 256) {
-    const int c = S[j];
-    const int64_t cb = c >> 1, cs = c >> 4;
-    const int sh = 4 * (c & 1);
-    for (int64_t m = m0; m < m0 + kGatherRows && m < M; ++m) {
-      const uint32_t code = (codes[m * (K / 2) + cb] >> sh) & 0xFu;
-      const float q = e2m1_unpack2<0>(code).x;
-      const float s = e4m3_decode(scales[m * (K / 16) + cs]);
-      const float xv = bf16_bits_to_f32(x[m * ldx + c]);
-      R[m * k + j] = (uint16_t)f32_to_bf16_rne(__builtin_fmaf(-(q * s), g, xv));
+  const int64_t rows = M - m0 < kGatherRows ? M - m0 : kGatherRows;
+  const int64_t n = rows * k;
+  for (int64_t q0 = 0; q0 < n; q0 += 256 * kGatherInFlight) {
+    uint32_t cb[kGatherInFlight], sb[kGatherInFlight], xb[kGatherInFlight];
+    int sh[kGatherInFlight];
+#pragma unroll
+    for (int u = 0; u < kGatherInFlight; ++u) {
+      const int64_t q = q0 + u * 256 + threadIdx.x;
+      if (q < n) {
+        const int64_t m = m0 + q / k;
+        const int j = (int)(q % k);
+        const int c = S[j];
+        cb[u] = codes[m * (K / 2) + (c >> 1)];
+        sb[u] = scales[m * (K / 16) + (c >> 4)];
+        xb[u] = x[m * ldx + c];
+        sh[u] = 4 * (c & 1);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kGatherInFlight; ++u) {
+      const int64_t q = q0 + u * 256 + threadIdx.x;
+      if (q < n) {
+        const float qv = e2m1_unpack2<0>((cb[u] >> sh[u]) & 0xFu).x;
+        const float sv = e4m3_decode(sb[u]);
+        R[m0 * k + q] = (uint16_t)f32_to_bf16_rne(
+            __builtin_fmaf(-(qv * sv), g, bf16_bits_to_f32(xb[u])));
+      }
     }
   }
 }
@@ -224,7 +258,9 @@ k_expert_scores(const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __re
 }
 
 // R[p][j] = bf16(fma(-(q*s), g, x[t][S_e[j]])) for permuted row p of expert
-// e, t = a_rows[p]: 64 permuted rows per workgroup, channels j over threads.
+// e, t = a_rows[p]: 64 permuted rows per workgroup, their (row, channel)
+// pairs over the threads with eight in flight per thread, as in
+// k_gather_residual.
 __global__ void __launch_bounds__(256)
 k_gather_residual_rows(const uint16_t* __restrict__ x, int64_t ldx,
                        const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
@@ -233,20 +269,37 @@ k_gather_residual_rows(const uint16_t* __restrict__ x, int64_t ldx,
                        int64_t K, int k, const int32_t* __restrict__ S, uint16_t* __restrict__ R) {
   const float g = *g_x;
   const int64_t p_lo = (int64_t)blockIdx.x * kExpertRows;
-  const int64_t p_hi = p_lo + kExpertRows < M_total ? p_lo + kExpertRows : M_total;
-  int e = expert_of(offsets, E, p_lo);
-  for (int64_t p = p_lo; p < p_hi; ++p) {
-    while (e + 1 < E && offsets[e + 1] <= p) ++e;
-    int64_t t = a_rows ? (int64_t)a_rows[p] : p;
-    t = t < 0 ? 0 : (t >= M_src ? M_src - 1 : t);
-    for (int j = threadIdx.x; j < k; j += 256) {
-      int c = S[(int64_t)e * k + j];
-      c = c < 0 ? 0 : (c >= K ? (int)K - 1 : c);
-      const uint32_t code = (codes[t * (K / 2) + (c >> 1)] >> (4 * (c & 1))) & 0xFu;
-      const float q = e2m1_unpack2<0>(code).x;
-      const float sv = e4m3_decode(scales[t * (K / 16) + (c >> 4)]);
-      const float xv = bf16_bits_to_f32(x[t * ldx + c]);
-      R[p * k + j] = (uint16_t)f32_to_bf16_rne(__builtin_fmaf(-(q * sv), g, xv));
+  const int64_t rows = M_total - p_lo < kExpertRows ? M_total - p_lo : kExpertRows;
+  const int64_t n = rows * k;
+  for (int64_t q0 = 0; q0 < n; q0 += 256 * kGatherInFlight) {
+    uint32_t cb[kGatherInFlight], sb[kGatherInFlight], xb[kGatherInFlight];
+    int sh[kGatherInFlight];
+#pragma unroll
+    for (int u = 0; u < kGatherInFlight; ++u) {
+      const int64_t q = q0 + u * 256 + threadIdx.x;
+      if (q < n) {
+        const int64_t p = p_lo + q / k;
+        const int j = (int)(q % k);
+        const int e = expert_of(offsets, E, p);
+        int64_t t = a_rows ? (int64_t)a_rows[p] : p;
+        t = t < 0 ? 0 : (t >= M_src ? M_src - 1 : t);
+        int c = S[(int64_t)e * k + j];
+        c = c < 0 ? 0 : (c >= K ? (int)K - 1 : c);
+        cb[u] = codes[t * (K / 2) + (c >> 1)];
+        sb[u] = scales[t * (K / 16) + (c >> 4)];
+        xb[u] = x[t * ldx + c];
+        sh[u] = 4 * (c & 1);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kGatherInFlight; ++u) {
+      const int64_t q = q0 + u * 256 + threadIdx.x;
+      if (q < n) {
+        const float qv = e2m1_unpack2<0>((cb[u] >> sh[u]) & 0xFu).x;
+        const float sv = e4m3_decode(sb[u]);
+        R[p_lo * k + q] = (uint16_t)f32_to_bf16_rne(
+            __builtin_fmaf(-(qv * sv), g, bf16_bits_to_f32(xb[u])));
+      }
     }
   }
 }
