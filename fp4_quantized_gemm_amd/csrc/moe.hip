@@ -173,18 +173,28 @@ k_combine(const uint16_t* __restrict__ y, const int32_t* __restrict__ inv_perm,
     wts[threadIdx.x] = tw[t * tk + threadIdx.x];
   }
   __syncthreads();
+  // acc += w_j * y_j in slot order j = 0 .. tk-1; the rows' loads are
+  // issued eight at a time ahead of their multiply-adds
+  auto fma8 = [](float* acc, float wj, const uint4& v) {
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] = __builtin_fmaf(wj, bf16_bits_to_f32(u[i] & 0xFFFFu), acc[2 * i]);
+      acc[2 * i + 1] = __builtin_fmaf(wj, bf16_bits_to_f32(u[i] >> 16), acc[2 * i + 1]);
+    }
+  };
   for (int64_t n = threadIdx.x * 8LL; n < N; n += 256 * 8) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < tk; ++j) {
-      const float wj = wts[j];
-      const uint4 v = *reinterpret_cast<const uint4*>(y + rows[j] * N + n);
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    int j0 = 0;
+    for (; j0 + 8 <= tk; j0 += 8) {
+      uint4 v[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = __builtin_fmaf(wj, bf16_bits_to_f32(u[i] & 0xFFFFu), acc[2 * i]);
-        acc[2 * i + 1] = __builtin_fmaf(wj, bf16_bits_to_f32(u[i] >> 16), acc[2 * i + 1]);
-      }
+      for (int jj = 0; jj < 8; ++jj) v[jj] = *reinterpret_cast<const uint4*>(y + rows[j0 + jj] * N + n);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) fma8(acc, wts[j0 + jj], v[jj]);
     }
+    for (int j = j0; j < tk; ++j)
+      fma8(acc, wts[j], *reinterpret_cast<const uint4*>(y + rows[j] * N + n));
     uint4 o;
     o.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
     o.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
