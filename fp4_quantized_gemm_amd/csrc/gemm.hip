@@ -506,10 +506,19 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
     if (n >= p.N) n = p.N - 1;
     off_s = (uint32_t)wscale_offset(n, 0, p.K);   // + k0: the step's tile
   }
+  // rows of the tile inside the expert: a load instruction covers 8
+  // consecutive rows, and one whose rows all lie past the expert's last row
+  // is skipped (its LDS rows then hold stale values, which only reach output
+  // rows that are never stored: an MFMA's output row depends only on its own
+  // A row)
+  const int64_t vt = e_hi - p0;
+  const int v_tile = vt > BM ? BM : (int)vt;
   auto issue_loads = [&](uint8_t* st, uint32_t k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds(a_img + off_a[i] + k0 * 2, st + (i * 8 + wave) * 1024, 16, 0, 0);
+      if ((i * 8 + wave) * 8 < v_tile)
+        __builtin_amdgcn_global_load_lds(a_img + off_a[i] + k0 * 2, st + (i * 8 + wave) * 1024, 16,
+                                         0, 0);
     __builtin_amdgcn_global_load_lds(wc + off_b + k0 / 2, st + A_BYTES + wave * 1024, 16, 0, 0);
     if (wave < 4)
       __builtin_amdgcn_global_load_lds(wsc + off_s + k0, st + A_BYTES + B_CODES + wave * 256, 4,
@@ -543,8 +552,11 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   const int swa = (r32 >> 1) & 7;                  // A rows = 32 i + r32 (+ multiples of 32)
   const int physb = kg ^ ((r32 >> 3) & 1);
 
-  // one k-step on stage `ab` while stage `nxt` fills with step kt + 1
-  auto kstep = [&](const uint8_t* ab, uint8_t* nxt, int kt) {
+  // one k-step on stage `ab` while stage `nxt` fills with step kt + 1; the
+  // wave computes its first NV 32-row blocks (the others lie past the
+  // expert's last row)
+  auto kstep = [&](const uint8_t* ab, uint8_t* nxt, int kt, auto nv_c) {
+    constexpr int NV = decltype(nv_c)::value;
     if (kt + 1 < nk) issue_loads(nxt, (uint32_t)(kt + 1) * BK);
     else if (rdma) issue_r(nxt, 0);
     const uint8_t* bb = ab + A_BYTES;
@@ -580,22 +592,22 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
         const int t = 2 * hb + s2;
         u32x4 A[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < NV; ++i) {
           const int ra = wm * 128 + 32 * i + r32;
           const uint4 v4 = *reinterpret_cast<const uint4*>(ab + ra * 128 + (((2 * t + kg) ^ swa) << 4));
           A[i] = u32x4{v4.x, v4.y, v4.z, v4.w};
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < (NV > 0 ? 2 : 0); ++j) {
           const uint32_t w = t == 0 ? br[j].x : t == 1 ? br[j].y : t == 2 ? br[j].z : br[j].w;
           if constexpr (W16) {
             const u32x4 B = decode8_bf16(w, sbv[j]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i][j] = mfma32_bf16(A[i], B, acc[i][j]);
+            for (int i = 0; i < NV; ++i) acc[i][j] = mfma32_bf16(A[i], B, acc[i][j]);
           } else {
             const u32x4 B = decode8_f16(w, sbv[j], mb[j]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i][j] = mfma32_f16(A[i], B, acc[i][j]);
+            for (int i = 0; i < NV; ++i) acc[i][j] = mfma32_f16(A[i], B, acc[i][j]);
           }
         }
       }
@@ -632,9 +644,27 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   issue_loads(st0, 0);
   wait_vmem0();
   __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {    // nk is even (K % 128 == 0)
-    kstep(st0, st1, kt);
-    kstep(st1, st0, kt + 1);
+  // this wave's valid rows: expert tail tiles run fewer MFMAs (every wave
+  // still takes part in the loads and barriers).  nk is even (K % 128 == 0).
+  const int v_wave = v_tile - wm * 128;
+  using nv4 = std::integral_constant<int, 4>;
+  using nv1 = std::integral_constant<int, 1>;
+  using nv0 = std::integral_constant<int, 0>;
+  if (W16 || v_wave > 32) {      // (the W4A16 kernel keeps one loop: fewer registers)
+    for (int kt = 0; kt < nk; kt += 2) {
+      kstep(st0, st1, kt, nv4{});
+      kstep(st1, st0, kt + 1, nv4{});
+    }
+  } else if (v_wave > 0) {
+    for (int kt = 0; kt < nk; kt += 2) {
+      kstep(st0, st1, kt, nv1{});
+      kstep(st1, st0, kt + 1, nv1{});
+    }
+  } else {
+    for (int kt = 0; kt < nk; kt += 2) {
+      kstep(st0, st1, kt, nv0{});
+      kstep(st1, st0, kt + 1, nv0{});
+    }
   }
 
   // epilogue: x g_x, residual K-extension (16 channels per MFMA), x g_w.
