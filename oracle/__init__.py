@@ -14,9 +14,11 @@ Modules:
   gemm     expert-grouped W4A4 GEMM plus the residual correction, and the
            trainer-side W4A16 product with the same dequantized weights
   layer    the whole MoE layer chained from the pieces above
+  fp8      the FP8 (E4M3) W8A8 baseline: per-tensor quantization and the
+           expert-grouped product
 
 Every function is pinned by tests under tests/ against facts that do not come
 from the oracle itself (bit definitions, exact rational arithmetic, library
 routines, closed forms and invariants).
 """
-from . import formats, gemm, layer, moe, nvfp4  # noqa: F401
+from . import formats, fp8, gemm, layer, moe, nvfp4  # noqa: F401
