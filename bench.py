@@ -29,6 +29,7 @@ the same block.
     python bench.py --calibrate-copy     # 1 GiB device copy, for counter scaling
     python bench.py --rac-sweep [--config C]   # compensation strength against cost
     python bench.py --w4a16 [--config C]       # trainer-side W4A16 product, same shapes
+    python bench.py --fp8 [--config C]         # FP8 (E4M3) W8A8 baseline, same shapes
 """
 from __future__ import annotations
 
@@ -46,6 +47,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_FP4_TFLOPS = 10100.0      # MI355X dense fp4 MFMA
 PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 
 
 def parse():
@@ -65,6 +67,8 @@ def parse():
                     help="time the gate+up GEMM and the SwiGLU pass separately")
     ap.add_argument("--w4a16", action="store_true",
                     help="only time the trainer-side W4A16 product on the block's GEMM shapes")
+    ap.add_argument("--fp8", action="store_true",
+                    help="only time the FP8 (E4M3) W8A8 baseline on the block's GEMM shapes")
     return ap.parse_args()
 
 
@@ -455,6 +459,79 @@ def w4a16_bench(cfg, wl, reps):
     return {"mode": "w4a16", "workload": cfg.name, "reps": reps, "gemms": out}
 
 
+def fp8_bench(cfg, wl, reps):
+    """The FP8 (E4M3) W8A8 baseline (fp8_quantize + grouped_fp8_gemm) on the
+    block's GEMM shapes, beside the NVFP4 path on the same shapes (activation
+    quantizer, W4A4 GEMM with the block's k compensated channels, and at
+    k = 0): HIP-event medians of `reps` calls.  Flops 2 * rows * N * K against
+    the dense fp8 MFMA peak; bytes (E4M3 weights of experts with rows, the
+    activation codes of every routed row, bf16 output) against HBM.  The
+    down GEMM's input is a synthetic N(0,1) tensor of the SwiGLU output's
+    shape."""
+    import numpy as np
+    import torch
+
+    import fp4_quantized_gemm_amd as F
+
+    dev = torch.device("cuda:0")
+    x = to_dev(wl.x, dev)
+    if cfg.kind == "dense":
+        offs = torch.tensor([0, cfg.T], dtype=torch.int32, device=dev)
+        perm, rows = None, cfg.T
+    else:
+        logits = torch.from_numpy(wl.logits).to(dev)
+        bias = torch.from_numpy(wl.bias).to(dev) if wl.bias is not None else None
+        _, _, offs, perm, _ = F.moe_permute(logits, cfg.topk, bias)
+        rows = perm.numel()
+    busy = int((offs[1:] > offs[:-1]).sum().item())
+    gemms = [("first", x, perm, to_dev(wl.w_first, dev), cfg.gemm_shapes()[0][4])]
+    if wl.w_down is not None:
+        g = torch.Generator(device=dev).manual_seed(0)
+        h = torch.randn((rows, cfg.inter), generator=g, device=dev).to(torch.bfloat16)
+        gemms.append(("down", h, None, to_dev(wl.w_down, dev), cfg.gemm_shapes()[1][4]))
+
+    def median_ms(fn):
+        ts = []
+        for _ in range(reps + 2):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ts[2:]]))
+
+    out = []
+    for name, a, a_rows, w, k in gemms:
+        E, N, K = w.shape
+        wc8, gw8 = F.fp8_quantize(w, stacked=True)
+        c, s, gw, _ = F.nvfp4_qdq_weights(w, want_qdq=False)
+        del w
+        ac8, gx8 = F.fp8_quantize(a)
+        q = F.nvfp4_quantize_act(a, False, k > 0)
+        S, R = (F.select_residual_channels(q["x_used"], q["codes"], q["scales"], q["g"],
+                                           q["score"], k) if k > 0 else (None, None))
+        t8 = median_ms(lambda: F.grouped_fp8_gemm(ac8, gx8, a_rows, wc8, gw8, offs, M_total=rows))
+        tq8 = median_ms(lambda: F.fp8_quantize(a))
+        t4 = median_ms(lambda: F.grouped_w4a4_gemm_rac(q["codes"], q["scales"], q["g"], a_rows,
+                                                       R, S, c, s, gw, offs, M_total=rows))
+        t40 = median_ms(lambda: F.grouped_w4a4_gemm_rac(q["codes"], q["scales"], q["g"], a_rows,
+                                                        None, None, c, s, gw, offs, M_total=rows))
+        tq4 = median_ms(lambda: F.nvfp4_quantize_act(a, False, k > 0))
+        fl = 2.0 * rows * N * K
+        by8 = busy * N * K + rows * K + rows * N * 2
+        out.append({"gemm": f"{name} {rows}x{N}x{K}", "fp8_ms": round(t8, 4),
+                    "fp8_tflops": round(fl / t8 / 1e9, 1),
+                    "fp8_frac_fp8_peak": round(fl / t8 / 1e9 / PEAK_FP8_TFLOPS, 4),
+                    "fp8_gbps": round(by8 / t8 / 1e6, 1),
+                    "fp8_quantize_act_ms": round(tq8, 4),
+                    "nvfp4_k": k, "nvfp4_rac_ms": round(t4, 4), "nvfp4_k0_ms": round(t40, 4),
+                    "nvfp4_quantize_act_ms": round(tq4, 4)})
+        print(f"# {out[-1]}", file=sys.stderr, flush=True)
+    return {"mode": "fp8", "workload": cfg.name, "reps": reps, "gemms": out}
+
+
 def gemm_algorithmic_bytes(cfg, counts):
     """Bytes one step's GEMM calls must move: NVFP4 weights (codes + E4M3
     scales, 0.5625 B/elem) of experts that have rows, the activation codes of
@@ -484,6 +561,9 @@ def main():
         return
     if args.w4a16:
         print(json.dumps(w4a16_bench(cfg, wl, max(args.steps // 2, 5))), flush=True)
+        return
+    if args.fp8:
+        print(json.dumps(fp8_bench(cfg, wl, max(args.steps // 2, 5))), flush=True)
         return
     # the SwiGLU is fused where the large-tile kernel forms it in its epilogue;
     # on decode-sized blocks the decode kernel's output goes to the quantizer

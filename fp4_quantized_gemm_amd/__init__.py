@@ -15,6 +15,8 @@ trainer-side W4A16 product,
     nvfp4_qdq_residual, select_residual_channels_per_expert,
     grouped_w4a4_gemm_rac_per_expert, grouped_w4a4_gemm_rac_swiglu,
     grouped_w4a16_gemm
+and the FP8 (E4M3) W8A8 baseline the method is compared with,
+    fp8_quantize, grouped_fp8_gemm
 """
 from __future__ import annotations
 
@@ -29,7 +31,7 @@ __all__ = ["lib", "nvfp4_qdq_weights", "nvfp4_quantize_act", "select_residual_ch
            "moe_permute", "grouped_w4a4_gemm_rac", "moe_unpermute_combine", "nvfp4_qdq_residual",
            "grouped_w4a16_gemm", "select_residual_channels_per_expert",
            "grouped_w4a4_gemm_rac_per_expert", "grouped_w4a4_gemm_rac_swiglu",
-           "nvfp4_quantize_act_amax", "NvfpError",
+           "nvfp4_quantize_act_amax", "fp8_quantize", "grouped_fp8_gemm", "NvfpError",
            "EXPORTED_SYMBOLS"]
 
 EXPORTED_SYMBOLS = [
@@ -46,6 +48,8 @@ EXPORTED_SYMBOLS = [
     "grouped_w4a4_gemm_rac_per_expert",
     "grouped_w4a4_gemm_rac_swiglu_workspace_size", "grouped_w4a4_gemm_rac_swiglu",
     "nvfp4_quantize_act_amax",
+    "fp8_quantize_workspace_size", "fp8_quantize",
+    "grouped_fp8_gemm_workspace_size", "grouped_fp8_gemm",
 ]
 
 
@@ -80,6 +84,8 @@ def _load():
         "grouped_w4a16_gemm_workspace_size": [_I64],
         "select_residual_channels_per_expert_workspace_size": [_I64, _I64],
         "grouped_w4a4_gemm_rac_swiglu_workspace_size": [_I64, _I64, _I64, _I64, _I64, _I64],
+        "fp8_quantize_workspace_size": [_I64],
+        "grouped_fp8_gemm_workspace_size": [_I64],
     }.items():
         f = getattr(L, name)
         f.restype = _SZ
@@ -102,6 +108,8 @@ def _load():
         "grouped_w4a4_gemm_rac_swiglu": [_P, _P, _P, _P, _I64, _P, _P, _I64, _P, _P, _P, _P, _I64,
                                          _I64, _I64, _I64, _P, _P, _P, _SZ, _P],
         "nvfp4_quantize_act_amax": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P],
+        "fp8_quantize": [_P, _I64, _I64, _I64, _P, _P, _P, _SZ, _P],
+        "grouped_fp8_gemm": [_P, _P, _P, _I64, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P],
     }
     for name, args in sigs.items():
         f = getattr(L, name)
@@ -344,6 +352,48 @@ def grouped_w4a16_gemm(x, a_rows, w_codes, w_scales, g_w, expert_offsets, M_tota
                                 _ptr(g_w), _ptr(expert_offsets), E, M_total, N, K, _ptr(y),
                                 _ptr(ws), ws.numel(), _stream(dev)),
            "grouped_w4a16_gemm")
+    return y
+
+
+def fp8_quantize(x, stacked=False):
+    """FP8 (E4M3) codes of x with one float32 scale per tensor.
+    x bf16 [M][K], or with stacked=True [E][N][K] with one scale per x[e]
+    (the weights of one expert).  Returns (codes uint8 of x's shape,
+    g float32 [1] or [E])."""
+    L = _load()
+    _need(x, torch.bfloat16, "x")
+    if not x.is_contiguous():
+        raise NvfpError("x must be contiguous")
+    if stacked:
+        E, M, K = x.shape
+    else:
+        (M, K), E = x.shape, 1
+    dev = x.device
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=dev)
+    g = torch.empty(E, dtype=torch.float32, device=dev)
+    ws = _ws(L.fp8_quantize_workspace_size(E), dev)
+    _check(L.fp8_quantize(_ptr(x), E, M, K, _ptr(codes), _ptr(g), _ptr(ws), ws.numel(),
+                          _stream(dev)), "fp8_quantize")
+    return codes, g
+
+
+def grouped_fp8_gemm(a, g_x, a_rows, w, g_w, expert_offsets, M_total=None, out=None):
+    """Y [M_total][N] bf16 = g_x g_w[e] (a gathered by a_rows) times the
+    E4M3 weights w [E][N][K] of each row's expert: the FP8 W8A8 baseline."""
+    L = _load()
+    _need(a, torch.uint8, "a")
+    _need(w, torch.uint8, "w")
+    M_src, K = a.shape
+    E, N, _ = w.shape
+    if M_total is None:
+        M_total = int(a_rows.numel()) if a_rows is not None else M_src
+    dev = a.device
+    y = out if out is not None else torch.empty((M_total, N), dtype=torch.bfloat16, device=dev)
+    ws = _ws(L.grouped_fp8_gemm_workspace_size(E), dev)
+    _check(L.grouped_fp8_gemm(_ptr(a), _ptr(g_x), _ptr(a_rows), M_src, _ptr(w), _ptr(g_w),
+                              _ptr(expert_offsets), E, M_total, N, K, _ptr(y), _ptr(ws),
+                              ws.numel(), _stream(dev)),
+           "grouped_fp8_gemm")
     return y
 
 

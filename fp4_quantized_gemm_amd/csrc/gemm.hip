@@ -1250,6 +1250,231 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// FP8 (E4M3) W8A8 grouped GEMM: the low-precision baseline the pages compare
+// NVFP4 against (arXiv abstract; gist.science technical summary §1 and §3).
+// Both operands are E4M3 bytes with one float32 scale per tensor (per expert
+// for the weights): y[p, n] = bf16(g_x g_w[e] sum_k a[t, k] w_e[n, k]).
+//
+// The same 256x256 tile, eight waves, XCD-aware tile order and tail-row
+// skipping as the large-tile NVFP4 kernel; E4M3 needs no decode, so A and B
+// go from global memory to LDS as they are (128 bytes of K per row per step)
+// and feed the gfx950 32x32x64 FP8 MFMA with unit block scales.
+// ---------------------------------------------------------------------------
+namespace f8 {
+constexpr int BM = 256, BN = 256, BK = 128;     // BK in bytes (= elements)
+constexpr int A_BYTES = BM * BK;               // [256][128 B]: chunk c at c ^ ((row >> 1) & 7)
+constexpr int STAGE = A_BYTES + BN * BK;       // 65536
+constexpr int OUTROW = BN * 2 + 16;            // bf16 output staging row (+pad)
+}  // namespace f8
+
+struct Fp8Args {
+  const uint8_t* a;            // [M_src][K] E4M3
+  const float* g_x;
+  const int32_t* a_rows;       // [M_total] or null (identity)
+  const uint8_t* w;            // [E][N][K] E4M3
+  const float* g_w;            // [E]
+  const int32_t* offsets;      // [E + 1]
+  const int32_t* tile_prefix;  // [E + 1], 256-row tiles
+  uint16_t* y;                 // [M_total][N] bf16
+  int64_t M_src, M_total, N, K;
+  int E;
+};
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// D += A B over 64 k: A, B 32 E4M3 bytes per lane; the block scales are
+// E8M0 127 = 2^0, so this is the plain product
+__device__ __forceinline__ f32x16_t mfma32_fp8(const i32x8_t& a, const i32x8_t& b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__global__ void __launch_bounds__(512, 1)
+k_gemm_fp8(Fp8Args p, int n_tiles, int m_tiles) {
+  using namespace f8;
+  __shared__ __attribute__((aligned(16))) uint8_t st0[STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
+  __shared__ int32_t rows_src[BM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
+  const int wm = wave >> 2, wn = wave & 3;      // rows 128 wm .., columns 64 wn ..
+  const int kg = lane >> 5, r32 = lane & 31;
+
+  // tile order as in k_gemm_big: groups of 4 row tiles x all column tiles,
+  // each XCD (workgroup b runs on XCD b % 8) a contiguous range of it
+  int v;
+  {
+    const int real_m = p.tile_prefix[p.E];
+    const int real_blocks = ((real_m + 3) / 4) * 4 * n_tiles;
+    const int per_xcd = (real_blocks + 7) / 8;
+    const int b = (int)blockIdx.x;
+    const int loc = b >> 3;
+    if (loc >= per_xcd) return;
+    v = (b & 7) * per_xcd + loc;
+    if (v >= real_blocks) return;
+  }
+  const int group = 4 * n_tiles;
+  const int gi = v / group, gr = v - gi * group;
+  if (4 * gi >= m_tiles) return;
+  const int gm = m_tiles - 4 * gi < 4 ? m_tiles - 4 * gi : 4;
+  const int gt = 4 * gi + gr % gm;
+  const int nt = gr / gm;
+  if (gt >= p.tile_prefix[p.E] || nt >= n_tiles) return;
+  int lo = 0, hi = p.E;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (p.tile_prefix[mid] <= gt) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  int64_t e_lo = p.offsets[e], e_hi = p.offsets[e + 1];
+  e_lo = e_lo < 0 ? 0 : (e_lo > p.M_total ? p.M_total : e_lo);
+  e_hi = e_hi < e_lo ? e_lo : (e_hi > p.M_total ? p.M_total : e_hi);
+  const int64_t p0 = e_lo + (int64_t)(gt - p.tile_prefix[e]) * BM;
+  const int64_t n0 = (int64_t)nt * BN;
+  const uint32_t K = (uint32_t)p.K;
+
+  if (tid < BM) {
+    int64_t pr = p0 + tid;
+    if (pr >= e_hi) pr = e_hi - 1;
+    int64_t t = p.a_rows ? (int64_t)p.a_rows[pr] : pr;
+    rows_src[tid] = (int32_t)(t < 0 ? 0 : (t >= p.M_src ? p.M_src - 1 : t));
+  }
+  __syncthreads();
+
+  const uint8_t* wc = p.w + (int64_t)e * p.N * p.K;
+  // thread q = (8 i + wave) 64 + lane stages 16 bytes of row q / 8 (A and
+  // B alike): chunk c = (q % 8) ^ ((row >> 1) & 7) of the row's 128 bytes
+  uint32_t off_a[4], off_b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = (i * 8 + wave) * 64 + lane;
+    const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
+    off_a[i] = (uint32_t)rows_src[r] * K + 16u * c;
+    int64_t n = n0 + r;
+    if (n >= p.N) n = p.N - 1;
+    off_b[i] = (uint32_t)n * K + 16u * c;
+  }
+  const int64_t vt = e_hi - p0;
+  const int v_tile = vt > BM ? BM : (int)vt;
+  // (offsets summed in 32 bits, which cannot wrap: M_src K and N K are
+  // below 2^32; the loads then take the scalar base and one VGPR each,
+  // instead of 64-bit per-lane addresses hoisted out of the loop)
+  auto issue_loads = [&](uint8_t* st, uint32_t k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_global_load_lds(p.a + (off_a[i] + k0), st + (i * 8 + wave) * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(wc + (off_b[i] + k0), st + A_BYTES + (i * 8 + wave) * 1024, 16, 0,
+                                       0);
+    }
+  };
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int sw = (r32 >> 1) & 7;                 // rows 32 i + r32 (+ multiples of 32)
+  const int nk = (int)(p.K / BK);
+  // lane (r32, kg) of a 64-k MFMA takes k 32 kg .. +31 of its row, both
+  // operands alike (chunks 2 kg, 2 kg + 1 of the 64)
+  auto ld32 = [&](const uint8_t* base, int row, int c0) -> i32x8_t {
+    const uint4 u = *reinterpret_cast<const uint4*>(base + row * 128 + ((c0 ^ sw) << 4));
+    const uint4 w = *reinterpret_cast<const uint4*>(base + row * 128 + (((c0 + 1) ^ sw) << 4));
+    return i32x8_t{(int)u.x, (int)u.y, (int)u.z, (int)u.w, (int)w.x, (int)w.y, (int)w.z, (int)w.w};
+  };
+  auto kstep = [&](const uint8_t* ab, uint8_t* nxt, int kt, auto nv_c) {
+    constexpr int NV = decltype(nv_c)::value;
+    if (kt + 1 < nk) issue_loads(nxt, (uint32_t)(kt + 1) * BK);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c0 = 4 * u + 2 * kg;
+      i32x8_t B[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) B[j] = ld32(ab + A_BYTES, wn * 64 + 32 * j + r32, c0);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const i32x8_t A = ld32(ab, wm * 128 + 32 * i + r32, c0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32_fp8(A, B[j], acc[i][j]);
+      }
+      // keep the two halves' operand reads apart (32 bytes per operand per
+      // lane: hoisting both halves' reads overflows the register file)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vmem0();
+    __syncthreads();
+  };
+
+  issue_loads(st0, 0);
+  wait_vmem0();
+  __syncthreads();
+  // nk may be odd here (K % 128 == 0): the loop runs pairs, then one step
+  const int v_wave = v_tile - wm * 128;
+  using nv4 = std::integral_constant<int, 4>;
+  using nv1 = std::integral_constant<int, 1>;
+  using nv0 = std::integral_constant<int, 0>;
+  if (v_wave > 32) {
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      kstep(st0, st1, kt, nv4{});
+      kstep(st1, st0, kt + 1, nv4{});
+    }
+    if (kt < nk) kstep(st0, st1, kt, nv4{});
+  } else if (v_wave > 0) {
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      kstep(st0, st1, kt, nv1{});
+      kstep(st1, st0, kt + 1, nv1{});
+    }
+    if (kt < nk) kstep(st0, st1, kt, nv1{});
+  } else {
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      kstep(st0, st1, kt, nv0{});
+      kstep(st1, st0, kt + 1, nv0{});
+    }
+    if (kt < nk) kstep(st0, st1, kt, nv0{});
+  }
+
+  // y = bf16(acc g_x g_w), staged through LDS (a 128-row half at a time:
+  // rows 0..63 in st0, 64..127 in st1) for 16-byte row stores
+  const float sc = *p.g_x * p.g_w[e];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    __syncthreads();
+    if (wm == h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint8_t* half = i < 2 ? st0 : st1;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = 32 * (i & 1) + 8 * (r >> 2) + 4 * kg + (r & 3);
+            const int col = wn * 64 + 32 * j + r32;
+            *reinterpret_cast<uint16_t*>(half + row * OUTROW + 2 * col) =
+                (uint16_t)f32_to_bf16_rne(acc[i][j][r] * sc);
+          }
+      }
+    }
+    __syncthreads();
+    for (int q = tid; q < 128 * (BN / 8); q += 512) {
+      const int row = q / (BN / 8), ch = q % (BN / 8);
+      const int64_t prow = p0 + h * 128 + row;
+      const int64_t n = n0 + ch * 8;
+      const uint8_t* src = (row < 64 ? st0 + row * OUTROW : st1 + (row - 64) * OUTROW) + ch * 16;
+      if (prow < e_hi && n < p.N)
+        *reinterpret_cast<uint4*>(p.y + prow * p.N + n) = *reinterpret_cast<const uint4*>(src);
+    }
+  }
+}
+
 }  // namespace nvfp4
 
 using namespace nvfp4;
@@ -1508,6 +1733,57 @@ int grouped_w4a16_gemm(const void* x, const int32_t* a_rows, int64_t M_src,
   k_gemm_big<true><<<(unsigned)nblk, 512, 0, s>>>(a, static_cast<const uint8_t*>(x), (int)n_tiles,
                                                   (int)m_tiles);
   return check_launch("grouped_w4a16_gemm");
+}
+
+size_t grouped_fp8_gemm_workspace_size(int64_t E) {
+  return img_offset(E < 1 ? 1 : E);
+}
+
+int grouped_fp8_gemm(const uint8_t* a, const float* g_x, const int32_t* a_rows, int64_t M_src,
+                     const uint8_t* w, const float* g_w, const int32_t* expert_offsets, int64_t E,
+                     int64_t M_total, int64_t N, int64_t K, void* y, void* ws, size_t ws_bytes,
+                     void* stream) {
+  NV_REQUIRE(E >= 1 && E <= 1024 && M_total >= 0 && N >= 16 && N % 16 == 0 && K >= f8::BK &&
+                 K % f8::BK == 0 && M_src >= 0,
+             NVFP4_ERR_SHAPE,
+             "grouped_fp8_gemm: need 1 <= E <= 1024, N %% 16 == 0, K %% 128 == 0 "
+             "(E=%lld N=%lld K=%lld)",
+             (long long)E, (long long)N, (long long)K);
+  NV_REQUIRE(a_rows != nullptr || M_src >= M_total, NVFP4_ERR_SHAPE,
+             "grouped_fp8_gemm: without a_rows, M_src must be >= M_total");
+  NV_REQUIRE(M_total == 0 || M_src >= 1, NVFP4_ERR_SHAPE, "grouped_fp8_gemm: M_src == 0");
+  NV_REQUIRE((uint64_t)M_src * (uint64_t)K < (1ULL << 32) &&
+                 (uint64_t)N * (uint64_t)K < (1ULL << 32),
+             NVFP4_ERR_UNSUPPORTED, "grouped_fp8_gemm: a or one expert's weights exceed 4 GiB");
+  NV_REQUIRE(g_x && w && g_w && expert_offsets && ws && (M_total == 0 || (a && y)),
+             NVFP4_ERR_NULL, "grouped_fp8_gemm: missing pointer");
+  NV_REQUIRE(aligned(a, 16) && aligned(w, 16) && aligned(ws, 16) && aligned(y, 16),
+             NVFP4_ERR_ALIGN, "grouped_fp8_gemm: misaligned pointer");
+  NV_REQUIRE(ws_bytes >= grouped_fp8_gemm_workspace_size(E), NVFP4_ERR_WORKSPACE,
+             "grouped_fp8_gemm: workspace too small");
+  if (M_total == 0) return ok();
+  hipStream_t s = as_stream(stream);
+  int32_t* prefix = static_cast<int32_t*>(ws);
+  Fp8Args p{};
+  p.a = a;
+  p.g_x = g_x;
+  p.a_rows = a_rows;
+  p.w = w;
+  p.g_w = g_w;
+  p.offsets = expert_offsets;
+  p.tile_prefix = prefix;
+  p.y = static_cast<uint16_t*>(y);
+  p.M_src = M_src;
+  p.M_total = M_total;
+  p.N = N;
+  p.K = K;
+  p.E = (int)E;
+  const int64_t n_tiles = (N + f8::BN - 1) / f8::BN;
+  const int64_t m_tiles = (M_total + f8::BM - 1) / f8::BM + E;
+  k_tile_prefix<<<1, 1024, 0, s>>>(expert_offsets, (int)E, M_total, f8::BM, prefix);
+  const int64_t nblk = (((m_tiles + 3) / 4) * 4 * n_tiles + 7) / 8 * 8;
+  k_gemm_fp8<<<(unsigned)nblk, 512, 0, s>>>(p, (int)n_tiles, (int)m_tiles);
+  return check_launch("grouped_fp8_gemm");
 }
 
 }  // extern "C"

@@ -363,6 +363,37 @@ k_qdq_slices(const uint16_t* __restrict__ w, int64_t N, int64_t K, int E,
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// FP8 (E4M3) quantization with one float32 scale per tensor (tensor t =
+// blockIdx.y): g = A / 448, code = sign(x) | E4M3(|x| / g), every magnitude
+// code 0 when A = 0.  Both divisions are correctly rounded float32.  Eight
+// elements (one 16-byte load, one 8-byte store) per thread per iteration.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+k_fp8_quantize(const uint16_t* __restrict__ x, int64_t n8, int64_t tensor_stride,
+               const uint32_t* __restrict__ amax, uint8_t* __restrict__ codes,
+               float* __restrict__ g) {
+  const int t = blockIdx.y;
+  const float A = bf16_bits_to_f32(amax[t]);
+  const float gt = A / kE4M3Max;
+  if (blockIdx.x == 0 && threadIdx.x == 0) g[t] = gt;
+  const uint4* xt = reinterpret_cast<const uint4*>(x + (int64_t)t * tensor_stride);
+  uint2* ct = reinterpret_cast<uint2*>(codes + (int64_t)t * tensor_stride);
+  for (int64_t i = blockIdx.x * 256LL + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    const uint4 v = xt[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t out[2] = {0u, 0u};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t h = (w[q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
+      const uint32_t mag = A > 0.f ? e4m3_encode_nonneg(bf16_bits_to_f32(h & 0x7FFFu) / gt) : 0u;
+      out[q >> 2] |= (mag | ((h >> 8) & 0x80u)) << (8 * (q & 3));
+    }
+    ct[i] = make_uint2(out[0], out[1]);
+  }
+}
+
 static unsigned grid_rows(int64_t rows, int rows_per_iter, int64_t cap) {
   int64_t need = (rows + rows_per_iter - 1) / rows_per_iter;
   if (need < 1) need = 1;
@@ -543,6 +574,36 @@ int nvfp4_qdq_weights(const void* w, int64_t E, int64_t N, int64_t K, uint8_t* c
       static_cast<const uint16_t*>(w), N, K, (int)E, amax, codes, scales, g_w,
       static_cast<uint16_t*>(w_qdq));
   return check_launch("nvfp4_qdq_weights");
+}
+
+size_t fp8_quantize_workspace_size(int64_t E) {
+  return round_up((size_t)(E > 0 ? E : 1) * sizeof(uint32_t), 256);
+}
+
+int fp8_quantize(const void* x, int64_t E, int64_t M, int64_t K, uint8_t* codes, float* g,
+                 void* ws, size_t ws_bytes, void* stream) {
+  NV_REQUIRE(g && ws, NVFP4_ERR_NULL, "fp8_quantize: g and ws are required");
+  NV_REQUIRE(E >= 1 && E <= 65535 && M >= 0 && K >= 8 && K % 8 == 0, NVFP4_ERR_SHAPE,
+             "fp8_quantize: need 1 <= E <= 65535, M >= 0, K %% 8 == 0 (E=%lld M=%lld K=%lld)",
+             (long long)E, (long long)M, (long long)K);
+  NV_REQUIRE(M == 0 || (x && codes), NVFP4_ERR_NULL, "fp8_quantize: x and codes are required");
+  NV_REQUIRE(aligned(x, 16) && aligned(codes, 8) && aligned(ws, 16), NVFP4_ERR_ALIGN,
+             "fp8_quantize: misaligned pointer");
+  NV_REQUIRE(ws_bytes >= fp8_quantize_workspace_size(E), NVFP4_ERR_WORKSPACE,
+             "fp8_quantize: workspace too small");
+  hipStream_t s = as_stream(stream);
+  uint32_t* amax = static_cast<uint32_t*>(ws);
+  fill_u32(amax, E, 0u, s);
+  const int64_t n8 = M * K / 8;
+  const int64_t per_e = (8LL * num_cus() + E - 1) / E;
+  int64_t nb = (n8 + 1023) / 1024;
+  nb = nb > per_e ? per_e : (nb < 1 ? 1 : nb);
+  if (n8 > 0)
+    k_amax_flat<<<dim3((unsigned)nb, (unsigned)E, 1), 256, 0, s>>>(
+        static_cast<const uint16_t*>(x), n8, M * K, amax);
+  k_fp8_quantize<<<dim3((unsigned)nb, (unsigned)E, 1), 256, 0, s>>>(
+      static_cast<const uint16_t*>(x), n8, M * K, amax, codes, g);
+  return check_launch("fp8_quantize");
 }
 
 }  // extern "C"

@@ -308,6 +308,39 @@ int grouped_w4a4_gemm_rac(const uint8_t* a_codes, const uint8_t* a_scales, const
 int moe_unpermute_combine(const void* y, const int32_t* inv_perm, const float* topk_w,
                           int64_t T, int64_t tk, int64_t N, void* out, void* stream);
 
+/* ------------------------------------------------------------------------
+ * FP8 (E4M3) W8A8 baseline: the low-precision rollout format the pages
+ * compare NVFP4 against (arXiv abstract; gist.science summary §1 and §3,
+ * throughput).  The pages give no FP8 recipe; this is OCP E4M3 for both
+ * operands with one float32 scale per tensor (per expert for weights).
+ *
+ * fp8_quantize: x bf16 [E][M][K] contiguous, E tensors of [M][K] each with
+ * its own scale (E = 1 for an activation, E experts for weights).  Per
+ * tensor, A = max |x|, g[e] = float32(A / 448), and codes [E][M][K] (u8)
+ * hold sign(x) << 7 | E4M3(float32(|x| / g[e])) (round to nearest, ties to
+ * the even code, saturating at 448; magnitude 0 for every element when
+ * A = 0, then g[e] = 0).  Requires 1 <= E <= 65535, M >= 0, K % 8 == 0;
+ * x 16-byte and codes 8-byte aligned.  Workspace: E 32-bit amax slots.
+ *
+ * grouped_fp8_gemm: a [M_src][K] E4M3 codes with scale *g_x (device),
+ * w [E][N][K] E4M3 codes with scales g_w [E], expert_offsets [E+1]
+ * (device), a_rows [M_total] or NULL (identity).  For output row p of
+ * expert e, t = a_rows ? a_rows[p] : p:
+ *   y[p][n] = bf16( g_x * g_w[e] * sum_k a[t][k] * w[e][n][k] )
+ * (exact products, float32 accumulation, one rounding to bf16).  Requires
+ * 1 <= E <= 1024, N % 16 == 0, K % 128 == 0, M_src * K < 2^32,
+ * N * K < 2^32; a, w and y 16-byte aligned.  Workspace: the per-expert
+ * tile prefix.
+ * ---------------------------------------------------------------------- */
+size_t fp8_quantize_workspace_size(int64_t E);
+int fp8_quantize(const void* x, int64_t E, int64_t M, int64_t K, uint8_t* codes, float* g,
+                 void* ws, size_t ws_bytes, void* stream);
+size_t grouped_fp8_gemm_workspace_size(int64_t E);
+int grouped_fp8_gemm(const uint8_t* a, const float* g_x, const int32_t* a_rows, int64_t M_src,
+                     const uint8_t* w, const float* g_w, const int32_t* expert_offsets, int64_t E,
+                     int64_t M_total, int64_t N, int64_t K, void* y, void* ws, size_t ws_bytes,
+                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

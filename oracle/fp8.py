@@ -36,11 +36,18 @@ def tensor_scale(A) -> np.float32:
     return np.float32(np.float32(A) / np.float32(E4M3_MAX))
 
 
-def quantize(x):
-    """x: bf16 values as float64, any shape, one tensor.  Returns
-    (codes uint8 of x's shape, g float32, A float32)."""
+def quantize(x, A=None):
+    """x: bf16 values as float64, any shape, one tensor.  A: the tensor's
+    absolute maximum when x is a slice (rows) of a larger tensor; by
+    default max |x|.  Returns (codes uint8 of x's shape, g float32,
+    A float32)."""
     x = np.asarray(x, dtype=np.float64)
-    A = np.float32(np.max(np.abs(x))) if x.size else np.float32(0.0)
+    amax = np.float32(np.max(np.abs(x))) if x.size else np.float32(0.0)
+    if A is None:
+        A = amax
+    A = np.float32(A)
+    if amax > A:
+        raise ValueError("A is below max |x|")
     g = tensor_scale(A)
     xf = x.astype(np.float32)                       # exact (bf16 values)
     if A > 0:

@@ -116,6 +116,27 @@ def test_gemm_validation():
     assert L.grouped_w4a4_gemm_rac(*args(ws=0)) == ERR_WS
 
 
+def test_fp8_validation():
+    L = F.lib()
+    ws = L.fp8_quantize_workspace_size(2)
+    assert L.fp8_quantize(FAKE, 0, 16, 64, FAKE, FAKE, FAKE, ws, None) == ERR_SHAPE     # E >= 1
+    assert L.fp8_quantize(FAKE, 2, 16, 60, FAKE, FAKE, FAKE, ws, None) == ERR_SHAPE     # K % 8
+    assert L.fp8_quantize(None, 2, 16, 64, FAKE, FAKE, FAKE, ws, None) == ERR_NULL
+    assert L.fp8_quantize(FAKE_MIS, 2, 16, 64, FAKE, FAKE, FAKE, ws, None) == ERR_ALIGN
+    assert L.fp8_quantize(FAKE, 2, 16, 64, FAKE, FAKE, FAKE, 0, None) == ERR_WS
+    gws = L.grouped_fp8_gemm_workspace_size(4)
+    args = lambda **kw: [kw.get("a", FAKE), FAKE, kw.get("rows", None), kw.get("msrc", 64), FAKE,
+                         FAKE, FAKE, kw.get("E", 4), 64, kw.get("N", 128), kw.get("K", 256), FAKE,
+                         FAKE, kw.get("ws", gws), None]
+    assert L.grouped_fp8_gemm(*args(K=192)) == ERR_SHAPE      # K % 128
+    assert L.grouped_fp8_gemm(*args(N=120)) == ERR_SHAPE      # N % 16
+    assert L.grouped_fp8_gemm(*args(E=0)) == ERR_SHAPE
+    assert L.grouped_fp8_gemm(*args(msrc=10)) == ERR_SHAPE    # no gather, M_src < M_total
+    assert L.grouped_fp8_gemm(*args(a=None)) == ERR_NULL
+    assert L.grouped_fp8_gemm(*args(a=FAKE_MIS)) == ERR_ALIGN
+    assert L.grouped_fp8_gemm(*args(ws=0)) == ERR_WS
+
+
 def test_combine_validation():
     L = F.lib()
     assert L.moe_unpermute_combine(FAKE, FAKE, FAKE, 4, 2, 12, FAKE, None) == ERR_SHAPE

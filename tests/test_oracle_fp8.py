@@ -141,3 +141,13 @@ def test_grouped_gemm_gather_equals_dense_per_expert(seed):
         assert np.array_equal(y[p], ref)
     sub = Q8.grouped_gemm_fp8(ac, gx, a_rows, wc, gw, offs, rows=np.array([3, 16]))
     assert np.array_equal(sub[[3, 16]], y[[3, 16]]) and np.isnan(sub[0]).all()
+
+
+def test_slice_with_the_tensor_amax_equals_slice_of_the_whole():
+    rng = np.random.default_rng(9)
+    x = _bf16(rng.standard_t(3, size=(40, 64)))
+    codes, g, A = Q8.quantize(x)
+    c2, g2, _ = Q8.quantize(x[10:17], A=A)
+    assert g2 == g and np.array_equal(c2, codes[10:17])
+    with pytest.raises(ValueError):
+        Q8.quantize(x, A=A / 2)
