@@ -1253,7 +1253,7 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
 
 // ---------------------------------------------------------------------------
 // FP8 (E4M3) W8A8 grouped GEMM: the low-precision baseline the pages compare
-// NVFP4 against (arXiv abstract; gist.science technical summary §1 and §3).
+// NVFP4 against (arXiv abstract; gist.science technical summary §1 and §4).
 // Both operands are E4M3 bytes with one float32 scale per tensor (per expert
 // for the weights): y[p, n] = bf16(g_x g_w[e] sum_k a[t, k] w_e[n, k]).
 //

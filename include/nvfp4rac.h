@@ -310,7 +310,7 @@ int moe_unpermute_combine(const void* y, const int32_t* inv_perm, const float* t
 
 /* ------------------------------------------------------------------------
  * FP8 (E4M3) W8A8 baseline: the low-precision rollout format the pages
- * compare NVFP4 against (arXiv abstract; gist.science summary §1 and §3,
+ * compare NVFP4 against (arXiv abstract; gist.science summary §1 and §4,
  * throughput).  The pages give no FP8 recipe; this is OCP E4M3 for both
  * operands with one float32 scale per tensor (per expert for weights).
  *

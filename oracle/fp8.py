@@ -4,7 +4,7 @@ that QUADS compares NVFP4 against.
 TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
 
 The pages name FP8 rollout as the stable baseline that NVFP4 is measured
-against (arXiv abstract; gist.science technical summary §1, and §3 on
+against (arXiv abstract; gist.science technical summary §1, and §4 on
 throughput, where QUADS is ~16% faster than FP8) but give no FP8 recipe.
 The reading taken here is the plainest one: OCP FP8 E4M3 for both operands,
 one float32 scale per tensor (per activation tensor, and per expert for the
