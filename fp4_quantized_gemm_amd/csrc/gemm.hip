@@ -397,7 +397,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;                      // 0..7
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // 0..7, wave-uniform (SGPR)
   const int wm = wave >> 2, wn = wave & 3;
   const int kg = lane >> 5, r32 = lane & 31;
 
@@ -513,15 +513,18 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   // A row)
   const int64_t vt = e_hi - p0;
   const int v_tile = vt > BM ? BM : (int)vt;
+  // (offsets summed in 32 bits, which cannot wrap: the image and one
+  // expert's codes are below 4 GiB; each load then takes a scalar base and
+  // one VGPR instead of a 64-bit per-lane address hoisted out of the loop)
   auto issue_loads = [&](uint8_t* st, uint32_t k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if ((i * 8 + wave) * 8 < v_tile)
-        __builtin_amdgcn_global_load_lds(a_img + off_a[i] + k0 * 2, st + (i * 8 + wave) * 1024, 16,
+        __builtin_amdgcn_global_load_lds(a_img + (off_a[i] + k0 * 2), st + (i * 8 + wave) * 1024, 16,
                                          0, 0);
-    __builtin_amdgcn_global_load_lds(wc + off_b + k0 / 2, st + A_BYTES + wave * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(wc + (off_b + k0 / 2), st + A_BYTES + wave * 1024, 16, 0, 0);
     if (wave < 4)
-      __builtin_amdgcn_global_load_lds(wsc + off_s + k0, st + A_BYTES + B_CODES + wave * 256, 4,
+      __builtin_amdgcn_global_load_lds(wsc + (off_s + k0), st + A_BYTES + B_CODES + wave * 256, 4,
                                        0, 0);
   };
 
