@@ -445,8 +445,7 @@ def w4a16_bench(cfg, wl, reps):
         c, s, gw, _ = F.nvfp4_qdq_weights(w, want_qdq=False)
         del w
         q = F.nvfp4_quantize_act(a, False, False)
-        E, N, Kh = c.shape
-        K = 2 * Kh
+        E, N, K = c.shape[0], c.shape[1] * 16, c.shape[2] * 64
         t16 = median_ms(lambda: F.grouped_w4a16_gemm(a, a_rows, c, s, gw, offs, M_total=rows))
         t4 = median_ms(lambda: F.grouped_w4a4_gemm_rac(q["codes"], q["scales"], q["g"], a_rows,
                                                        None, None, c, s, gw, offs, M_total=rows))

@@ -138,6 +138,14 @@ def _check(status, name):
                         f"{L.nvfp4_last_error().decode()}")
 
 
+def _wshape(w_codes):
+    """(E, N) of weight codes in the library's tiles [E][N/16][K/64][16][32]."""
+    if w_codes.dim() != 5 or tuple(w_codes.shape[3:]) != (16, 32):
+        raise NvfpError("weight codes must be tiled [E][N/16][K/64][16][32] "
+                        "(as nvfp4_qdq_weights returns them)")
+    return int(w_codes.shape[0]), int(w_codes.shape[1]) * 16
+
+
 def _ws(nbytes, device):
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
@@ -152,14 +160,15 @@ def _need(t, dtype, name):
 
 
 def nvfp4_qdq_weights(w, want_qdq=True):
-    """w [E][N][K] bf16 -> (codes [E][N][K/2] u8, scales [E][N/16][K/64][16][4]
-    u8 (block scales in 64-byte tiles of 16 rows x 64 columns), g_w [E] f32,
-    w_qdq [E][N][K] bf16 or None)."""
+    """w [E][N][K] bf16 -> (codes [E][N/16][K/64][16][32] u8 (two E2M1 codes
+    per byte in 512-byte tiles of 16 rows x 64 columns), scales
+    [E][N/16][K/64][16][4] u8 (block scales in 64-byte tiles of the same
+    16 rows x 64 columns), g_w [E] f32, w_qdq [E][N][K] bf16 or None)."""
     L = _load()
     _need(w, torch.bfloat16, "w")
     E, N, K = w.shape
     dev = w.device
-    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=dev)
+    codes = torch.empty((E, N // 16, K // 64, 16, 32), dtype=torch.uint8, device=dev)
     scales = torch.empty((E, N // 16, K // 64, 16, 4), dtype=torch.uint8, device=dev)
     g_w = torch.empty(E, dtype=torch.float32, device=dev)
     w_qdq = torch.empty_like(w) if want_qdq else None
@@ -270,7 +279,7 @@ def _gemm_rac(fn_name, a_codes, a_scales, g_x, a_rows, R, S, w_codes, w_scales, 
     L = _load()
     M_src, Kh = a_codes.shape
     K = Kh * 2
-    E, N, _ = w_codes.shape
+    E, N = _wshape(w_codes)
     k = 0 if S is None else int(S.shape[-1])
     if M_total is None:
         M_total = int(a_rows.numel()) if a_rows is not None else M_src
@@ -342,7 +351,7 @@ def grouped_w4a16_gemm(x, a_rows, w_codes, w_scales, g_w, expert_offsets, M_tota
     L = _load()
     _need(x, torch.bfloat16, "x")
     M_src, K = x.shape
-    E, N, _ = w_codes.shape
+    E, N = _wshape(w_codes)
     if M_total is None:
         M_total = int(a_rows.numel()) if a_rows is not None else M_src
     dev = x.device

@@ -152,7 +152,7 @@ k_gemm_generic(GemmArgs p) {
       ga[i] = *reinterpret_cast<const uint4*>(p.a_codes + (int64_t)rows_src[r] * Kh + k0 / 2 + part * 16);
       int64_t n = n0 + r;
       if (n >= p.N) n = p.N - 1;
-      gb[i] = *reinterpret_cast<const uint4*>(wc + n * Kh + k0 / 2 + part * 16);
+      gb[i] = *reinterpret_cast<const uint4*>(wc + wcode_offset(n, k0 + 32 * part, p.K));
     }
     if (tid < kBM) {
       gsa = *reinterpret_cast<const uint2*>(p.a_scales + (int64_t)rows_src[tid] * Ks + k0 / 16);
@@ -238,7 +238,7 @@ k_gemm_generic(GemmArgs p) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         if (ch[q] < 0) { v[q] = 0u; continue; }
-        const uint32_t byte = wc[n * Kh + (ch[q] >> 1)];
+        const uint32_t byte = wc[wcode_offset(n, ch[q], p.K)];
         const float wq = e2m1_unpack2<0>((byte >> (4 * (ch[q] & 1))) & 0xFu).x;
         const float ws = e4m3_decode(wsc[wscale_offset(n, ch[q] >> 4, p.K)]);
         v[q] = __float_as_uint(wq * ws) >> 16;
@@ -499,7 +499,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
     const int r = q >> 1, c = (q & 1) ^ ((r >> 3) & 1);
     int64_t n = wrow(r);
     if (n >= p.N) n = p.N - 1;
-    off_b = (uint32_t)n * Kh + 16u * c;
+    off_b = (uint32_t)wcode_offset(n, 0, p.K) + 16u * c;   // + 8 k0: the step's tile
   }
   if (wave < 4) {
     int64_t n = wrow(wave * 64 + lane);
@@ -522,7 +522,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
       if ((i * 8 + wave) * 8 < v_tile)
         __builtin_amdgcn_global_load_lds(a_img + (off_a[i] + k0 * 2), st + (i * 8 + wave) * 1024, 16,
                                          0, 0);
-    __builtin_amdgcn_global_load_lds(wc + (off_b + k0 / 2), st + A_BYTES + wave * 1024, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(wc + (off_b + k0 * 8), st + A_BYTES + wave * 1024, 16, 0, 0);
     if (wave < 4)
       __builtin_amdgcn_global_load_lds(wsc + (off_s + k0), st + A_BYTES + B_CODES + wave * 256, 4,
                                        0, 0);
@@ -852,12 +852,12 @@ k_extract_ws(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scal
   const int64_t row = blockIdx.x;                // e * N + n
   const int64_t e = row / N, n = row - e * N;
   S += e * s_stride;
-  const uint8_t* cr = codes + row * (K / 2);
+  const uint8_t* cr = codes + e * N * (K / 2);
   const uint8_t* sc = scales + e * N * (K / 16);
   for (int j = threadIdx.x; j < k; j += 256) {
     int c = S[j];
     c = c < 0 ? 0 : (c >= K ? (int)K - 1 : c);
-    const uint32_t code = (cr[c >> 1] >> (4 * (c & 1))) & 0xFu;
+    const uint32_t code = (cr[wcode_offset(n, c, K)] >> (4 * (c & 1))) & 0xFu;
     const float q = e2m1_unpack2<0>(code).x;
     const float sv = e4m3_decode(sc[wscale_offset(n, c >> 4, K)]);
     wsel[row * k + j] = (uint16_t)(__float_as_uint(q * sv) >> 16);
@@ -1002,11 +1002,13 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
   const uint8_t* wc = p.w_codes + (int64_t)e * p.N * Kh;
   const uint8_t* wsc = p.w_scales + (int64_t)e * p.N * Ks;
   // load addresses = a uniform offset (row block, chunk) + a per-lane
-  // offset fixed over the stream: code byte 32 kq of row r16, scale byte
-  // 4 r16 + 64 kq of the row block's tile (weight scales are tiled per 16
-  // rows x 64 columns, so row block rb starts at byte rb / 16 * K)
+  // offset fixed over the stream: row r16 of the chunk's code tile kq
+  // (512-byte tiles of 16 rows x 64 columns: a row block's chunk is one
+  // contiguous 2 KB run starting at byte rb / 16 * 8 K + 2048 c) and scale
+  // byte 4 r16 + 64 kq of its scale tile (row block rb starts at byte
+  // rb / 16 * K)
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const uint32_t lane_c0 = (uint32_t)(r16 * Kh + 32 * kq);
+  const uint32_t lane_c0 = (uint32_t)(512 * kq + 32 * r16);
   const uint32_t lane_s0 = (uint32_t)(4 * r16 + 64 * kq);
   const bool half_last = (p.K % KC) != 0;    // the last chunk holds 128 columns
   const float gx = *p.g_x;
@@ -1063,9 +1065,9 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
           // a row block past N (N % 16 == 0) reads the last one instead
           int64_t rb = (int64_t)(blk_lo + q.blk) * ROWS + 64 * wave_u + 16 * part;
           if (rb >= p.N) rb = p.N - 16;
-          const uint8_t* cb = wc + (uint32_t)(rb * Kh) + (uint32_t)q.c * (KC / 2);
+          const uint8_t* cb = wc + (uint32_t)((rb >> 4) * p.K * 8) + (uint32_t)q.c * (KC / 64) * 512;
           const uint8_t* sb = wsc + (uint32_t)((rb >> 4) * p.K) + (uint32_t)q.c * (KC / 64) * 64;
-          const uint4* src4 = reinterpret_cast<const uint4*>(cb + (lane_c - (tl ? 64u : 0u)));
+          const uint4* src4 = reinterpret_cast<const uint4*>(cb + (lane_c - (tl ? 1024u : 0u)));
           d.wc[part][0] = src4[0];
           d.wc[part][1] = src4[1];
           d.ws[part] = *reinterpret_cast<const uint32_t*>(sb + (lane_s - (tl ? 128u : 0u)));

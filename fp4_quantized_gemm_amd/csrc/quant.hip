@@ -348,7 +348,8 @@ k_qdq_slices(const uint16_t* __restrict__ w, int64_t N, int64_t K, int E,
       uint32_t sbyte, pk[2];
       quant_block16(c0[u], c1[u], A, xf, sbyte, s, pk);
       const int64_t orow = (int64_t)e * N + row0 + r;
-      *reinterpret_cast<uint2*>(codes + orow * (K / 2) + c * 8) = make_uint2(pk[0], pk[1]);
+      *reinterpret_cast<uint2*>(codes + (int64_t)e * N * (K / 2) + wcode_offset(row0 + r, 16 * c, K)) =
+          make_uint2(pk[0], pk[1]);
       const uint32_t s4 = sbyte | (__shfl_down(sbyte, 1) << 8) | (__shfl_down(sbyte, 2) << 16) |
                           (__shfl_down(sbyte, 3) << 24);
       if ((c & 3) == 0) *reinterpret_cast<uint32_t*>(sc_e + wscale_offset(row0 + r, c, K)) = s4;

@@ -22,7 +22,7 @@ from . import (grouped_w4a4_gemm_rac, grouped_w4a4_gemm_rac_per_expert,
 
 @dataclass
 class QuantWeights:
-    codes: torch.Tensor      # [E][N][K/2] u8
+    codes: torch.Tensor      # [E][N/16][K/64][16][32] u8 (tiled codes)
     scales: torch.Tensor     # [E][N/16][K/64][16][4] u8 (tiled block scales)
     g: torch.Tensor          # [E] f32
     qdq: torch.Tensor        # [E][N][K] bf16 or None

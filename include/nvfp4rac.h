@@ -73,7 +73,12 @@ const char* nvfp4_last_error(void);
  * §2.2 A, asymmetric W4A16 QAT).
  *
  * w      [E][N][K] bf16, K contiguous (each expert's weight, out x in).
- * codes  [E][N][K/2] packed E2M1, row-major.
+ * codes  [E][N/16][K/64][16][32] packed E2M1 (E * N * K/2 bytes), two codes
+ *        per byte (the even column in bits 3:0), in 512-byte tiles, one per
+ *        16 rows x 64 columns: the byte holding columns k, k+1 (k even) of
+ *        row n of expert e is at e*N*K/2 + ((n/16) * (K/64) + k/64) * 512 +
+ *        (n%16) * 32 + (k%64)/2.  A GEMM k-step of a row block is then one
+ *        contiguous run of whole cache lines.
  * scales [E][N/16][K/64][16][4] E4M3 (E * N * K/16 bytes): the block scales
  *        in 64-byte tiles, one per 16 rows x 64 columns; the scale of block
  *        kb (columns 16 kb .. 16 kb + 15) of row n of expert e is at byte
@@ -281,8 +286,8 @@ int moe_permute(const float* logits, const float* bias, int64_t T, int64_t E, in
  * in the bf16/fp16 operands of the matrix cores), float32 accumulation.
  * a_codes [M_src][K/2], a_scales [M_src][K/16], g_x [1]; a_rows [M_total] or
  * NULL (then M_src >= M_total); R_S [M_src][k] bf16 (NULL iff k == 0);
- * S [k] int32 ascending; w_codes [E][N][K/2], w_scales [E][N/16][K/64][16][4]
- * (the tiles nvfp4_qdq_weights writes), g_w [E];
+ * S [k] int32 ascending; w_codes [E][N/16][K/64][16][32],
+ * w_scales [E][N/16][K/64][16][4] (the tiles nvfp4_qdq_weights writes), g_w [E];
  * expert_offsets [E+1] (device; off[0] = 0, off[E] = M_total); y [M_total][N]
  * bf16.  Requires K % 128 == 0, N % 16 == 0, 0 <= k <= K.
  * The workspace holds the per-expert tile prefix and, for large problems,

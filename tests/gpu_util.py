@@ -31,6 +31,19 @@ def untile_wscales(t: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(t.transpose(0, 1, 3, 2, 4)).reshape(E, NB * 16, KG * 4)
 
 
+def tile_wcodes(c: np.ndarray) -> np.ndarray:
+    """Packed row-major weight codes [E][N][K/2] -> the library's tiles
+    [E][N/16][K/64][16][32] (a layout change only)."""
+    E, N, KH = c.shape
+    return np.ascontiguousarray(c.reshape(E, N // 16, 16, KH // 32, 32).transpose(0, 1, 3, 2, 4))
+
+
+def untile_wcodes(t: np.ndarray) -> np.ndarray:
+    """The library's weight-code tiles [E][N/16][K/64][16][32] -> [E][N][K/2]."""
+    E, NB, KG, _, _ = t.shape
+    return np.ascontiguousarray(t.transpose(0, 1, 3, 2, 4)).reshape(E, NB * 16, KG * 32)
+
+
 def bits_of(vals: np.ndarray) -> np.ndarray:
     return OF.f64_to_bf16_bits(vals)
 

@@ -31,7 +31,7 @@ from oracle import gemm as OG
 from oracle import moe as OM
 from oracle import nvfp4 as OQ
 from tests.gpu_util import (assert_gemm_close, f32_bits, host_bits, host_vals, to_dev_bf16,
-                             untile_wscales)
+                             untile_wcodes, untile_wscales)
 
 pytestmark = pytest.mark.gpu
 
@@ -59,7 +59,8 @@ def check_weights(w_bits, wq, experts, rng, n_rows=256):
         N = w.shape[0]
         r = np.arange(N) if N <= n_rows else np.sort(rng.choice(N, n_rows, replace=False))
         c, s, _, _ = OQ.quantize(w[r], A=OQ.tensor_amax(w))
-        assert np.array_equal(OQ.unpack_codes(wq.codes[e][r].cpu().numpy()), c), f"expert {e} codes"
+        c_gpu = untile_wcodes(wq.codes[e:e + 1].cpu().numpy())[0]
+        assert np.array_equal(OQ.unpack_codes(c_gpu[r]), c), f"expert {e} codes"
         s_gpu = untile_wscales(wq.scales[e:e + 1].cpu().numpy())[0]
         assert np.array_equal(s_gpu[r], s), f"expert {e} scales"
 

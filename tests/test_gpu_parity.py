@@ -17,7 +17,8 @@ from oracle import gemm as OG
 from oracle import moe as OM
 from oracle import nvfp4 as OQ
 from tests.gpu_util import (assert_gemm_close, f32_bits, heavy_bf16, host_bits, host_vals,
-                            tile_wscales, to_dev_bf16, untile_wscales)
+                            tile_wcodes, tile_wscales, to_dev_bf16, untile_wcodes,
+                            untile_wscales)
 
 pytestmark = pytest.mark.gpu
 
@@ -111,7 +112,8 @@ def test_qdq_weights_bitexact(dev, E, N, K):
     codes, scales, g_w, w_qdq = F.nvfp4_qdq_weights(wd, want_qdq=True)
     torch.cuda.synchronize()
     rc, rs, rg, rq = OQ.qdq_weights(w)
-    assert np.array_equal(OQ.unpack_codes(codes.cpu().numpy()), rc)
+    assert codes.shape == (E, N // 16, K // 64, 16, 32)
+    assert np.array_equal(OQ.unpack_codes(untile_wcodes(codes.cpu().numpy())), rc)
     assert scales.shape == (E, N // 16, K // 64, 16, 4)
     assert np.array_equal(untile_wscales(scales.cpu().numpy()), rs)
     assert np.array_equal(f32_bits(g_w.cpu().numpy()), f32_bits(rg))
@@ -189,7 +191,7 @@ def _gemm_case(rng, M_src, counts, N, K, k, gather):
         cu(a_rows) if gather else None,
         to_dev_bf16(OF.f64_to_bf16_bits(qa["R_S"])) if k else None,
         cu(qa["S"]) if k else None,
-        cu(OQ.pack_codes(wc)), cu(tile_wscales(ws)), cu(gw), cu(offs), M_total=M_total)
+        cu(tile_wcodes(OQ.pack_codes(wc))), cu(tile_wscales(ws)), cu(gw), cu(offs), M_total=M_total)
     torch.cuda.synchronize()
     return host_vals(y), ref
 
