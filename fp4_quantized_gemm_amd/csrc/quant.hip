@@ -323,8 +323,12 @@ k_qdq_slices(const uint16_t* __restrict__ w, int64_t N, int64_t K, int E,
   const float A = bf16_bits_to_f32(amax[e]);
   const float g = A / kScaleDen;
   if (blockIdx.x == 0 && tid == 0) g_w[e] = g;
-  // 16 * KB is a multiple of 64 (K % 64 == 0), so a wave's blocks are all in
-  // range or all out, and lanes 4j..4j+3 hold blocks 4i..4i+3 of one row
+  // block b of the slice is block c = 4 t + (b % 4) of row (b / 4) % 16,
+  // t = b / 64: a wave covers one 16-row x 64-column tile, so its code
+  // stores are one contiguous 512-byte tile, its scale stores one 64-byte
+  // tile, and its loads whole 128-byte row pieces.  16 * KB = K is a
+  // multiple of 64 (K % 64 == 0), so a wave's blocks are all in range or all
+  // out, and lanes 4j..4j+3 hold blocks 4t..4t+3 of one row
   const int64_t nblk = 16 * KB;
   uint8_t* sc_e = scales + (int64_t)e * N * KB;
   for (int64_t b0 = 0; b0 < nblk; b0 += 256 * kQdqRound) {
@@ -333,7 +337,7 @@ k_qdq_slices(const uint16_t* __restrict__ w, int64_t N, int64_t K, int E,
     for (int u = 0; u < kQdqRound; ++u) {
       const int64_t b = b0 + u * 256 + tid;
       if (b < nblk) {
-        const int64_t r = b / KB, c = b - r * KB;
+        const int64_t r = (b >> 2) & 15, c = ((b >> 6) << 2) + (b & 3);
         const uint16_t* xr = src + r * K + c * 16;
         c0[u] = *reinterpret_cast<const uint4*>(xr);
         c1[u] = *reinterpret_cast<const uint4*>(xr + 8);
@@ -343,7 +347,7 @@ k_qdq_slices(const uint16_t* __restrict__ w, int64_t N, int64_t K, int E,
     for (int u = 0; u < kQdqRound; ++u) {
       const int64_t b = b0 + u * 256 + tid;
       if (b >= nblk) break;                  // wave-uniform
-      const int64_t r = b / KB, c = b - r * KB;
+      const int64_t r = (b >> 2) & 15, c = ((b >> 6) << 2) + (b & 3);
       float xf[16], s;
       uint32_t sbyte, pk[2];
       quant_block16(c0[u], c1[u], A, xf, sbyte, s, pk);
