@@ -291,7 +291,7 @@ def gemm_kernel_name(cfg, m, n, k, E):
     MI355X (the library's own dispatch rule, restated for the report)."""
     if m <= 48 * E and k <= 128:
         return "k_gemm_decode"
-    if (k <= 128 or k % 128 == 0) and (m // 256) * ((n + 255) // 256) >= 512:
+    if (k <= 128 or k % 128 == 0) and cfg.H <= 16384 and cfg.inter <= 16384:
         return "k_gemm_big" if k <= 128 else "k_extract_ws + k_gemm_big"
     return "k_gemm_generic"
 
@@ -584,9 +584,9 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "frac_of_fp4_peak": round(achieved / PEAK_FP4_TFLOPS, 4)}
-        # the library's choice for large workloads (on a 256-CU MI355X)
-        _, m, n, _, _ = shapes[0]
-        big = (m // 256) * ((n + 255) // 256) >= 512
+        # the library's choice (the large-tile kernel for every shape it takes)
+        _, m, n, _, kk = shapes[0]
+        big = gemm_kernel_name(cfg, m, n, kk, cfg.E).endswith("k_gemm_big")
         name = "grouped_w4a4_gemm_rac_swiglu + grouped_w4a4_gemm_rac" if fuse else \
             "grouped_w4a4_gemm_rac"
         kernel = (f"{name}: k_decode_a + k_tile_prefix + k_gemm_big" if big

@@ -1573,9 +1573,12 @@ static int gemm_rac(bool per_expert, bool glu, uint32_t* h_amax, const uint8_t* 
   // small shapes).  The large-tile path holds at most KMAX residual channels,
   // needs the f16 image of A in the workspace and 32-bit image offsets.
   const char* force = getenv("NVFP4RAC_GEMM");
-  // few rows per expert (decode): stream each expert's weights once
+  // few rows per expert (decode): stream each expert's weights once; else
+  // the large-tile kernel wherever it takes the shape (it is also the faster
+  // one on small problems that fill only part of the chip: 64x512x512 and
+  // 2048x1024x2048 measured 20-25% faster than the generic kernel)
   bool use_dec = M_total <= 48 * E;
-  bool use_big = (M_total / big::BM) * n_tiles_big >= 2LL * num_cus();
+  bool use_big = true;
   if (force && strcmp(force, "big") == 0) use_big = true, use_dec = false;
   if (force && strcmp(force, "generic") == 0) use_big = false, use_dec = false;
   if (force && strcmp(force, "decode") == 0) use_dec = true;
