@@ -60,6 +60,10 @@ struct GemmArgs {
   // h_amax (nullable) receives max |h| as bf16 bits (atomic max)
   int64_t glu_i;
   uint32_t* h_amax;
+  // split of K over blockIdx.y (large-tile kernel, SPLIT instantiation):
+  // slice s writes its float32 partial to part[s][M_total][N]
+  int ksplit;
+  float* part;
 };
 
 // tile_prefix[e] = number of 128-row tiles of experts before e; [E] = total
@@ -376,7 +380,7 @@ k_decode_a(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales
 // way (the 8-element chunk the image would hold in slot c is chunk
 // 4 (c & 1) + (c >> 1) of the row's 64-wide block), the weights are decoded to
 // bf16 (q * s, exact), the MFMA is bf16, and there is no correction.
-template <bool W16>
+template <bool W16, bool SPLIT = false>
 __global__ void __launch_bounds__(512, 1)
 k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_tiles) {
   using namespace big;
@@ -460,11 +464,19 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
       int c = p.S[(int64_t)e * p.s_stride + tid];
       s_local[tid] = c < 0 ? 0 : (c >= p.K ? (int)p.K - 1 : c);
     }
-    const int kpad = (kl + 15) & ~15;          // zero slots k .. next multiple of 16
-    for (int j = kl; j < kpad; ++j) *reinterpret_cast<uint16_t*>(wsl + tid * WSROW + 2 * j) = 0;
+    // zero slots k .. next multiple of 16 (a K slice: every slot, since it
+    // copies only the selected columns of its own k-steps)
+    const int kpad = (kl + 15) & ~15;
+    for (int j = SPLIT ? 0 : kl; j < kpad; ++j)
+      *reinterpret_cast<uint16_t*>(wsl + tid * WSROW + 2 * j) = 0;
   }
   __syncthreads();
   const int nk = (int)(p.K / BK);
+  // this workgroup's k-steps: all of them, or slice blockIdx.y of ksplit
+  // (an even number of steps each)
+  const int nks = SPLIT ? nk / p.ksplit : nk;
+  const int kt_lo = SPLIT ? (int)blockIdx.y * nks : 0;
+  const int kt_hi = kt_lo + nks;
   if (kl > 0) {
     // (S is strictly ascending, so bit ranks are the indices j)
     for (int w = tid; w < 2 * nk; w += 512) sel_bm[w] = 0u;
@@ -560,7 +572,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   // expert's last row)
   auto kstep = [&](const uint8_t* ab, uint8_t* nxt, int kt, auto nv_c) {
     constexpr int NV = decltype(nv_c)::value;
-    if (kt + 1 < nk) issue_loads(nxt, (uint32_t)(kt + 1) * BK);
+    if (kt + 1 < kt_hi) issue_loads(nxt, (uint32_t)(kt + 1) * BK);
     else if (rdma) issue_r(nxt, 0);
     const uint8_t* bb = ab + A_BYTES;
     const uint8_t* sb = bb + B_CODES;
@@ -644,7 +656,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
     __syncthreads();
   };
 
-  issue_loads(st0, 0);
+  issue_loads(st0, (uint32_t)kt_lo * BK);
   wait_vmem0();
   __syncthreads();
   // this wave's valid rows: expert tail tiles run fewer MFMAs (every wave
@@ -654,17 +666,17 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   using nv1 = std::integral_constant<int, 1>;
   using nv0 = std::integral_constant<int, 0>;
   if (W16 || v_wave > 32) {      // (the W4A16 kernel keeps one loop: fewer registers)
-    for (int kt = 0; kt < nk; kt += 2) {
+    for (int kt = kt_lo; kt < kt_hi; kt += 2) {
       kstep(st0, st1, kt, nv4{});
       kstep(st1, st0, kt + 1, nv4{});
     }
   } else if (v_wave > 0) {
-    for (int kt = 0; kt < nk; kt += 2) {
+    for (int kt = kt_lo; kt < kt_hi; kt += 2) {
       kstep(st0, st1, kt, nv1{});
       kstep(st1, st0, kt + 1, nv1{});
     }
   } else {
-    for (int kt = 0; kt < nk; kt += 2) {
+    for (int kt = kt_lo; kt < kt_hi; kt += 2) {
       kstep(st0, st1, kt, nv0{});
       kstep(st1, st0, kt + 1, nv0{});
     }
@@ -772,6 +784,43 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
     }
   }
 
+  if constexpr (SPLIT) {
+    // this slice's float32 partial, with g_x and the correction of the
+    // selected channels among its own k-steps (the other W_S slots are zero);
+    // g_w and the rounding come in the fixed-order reduction.  Staged
+    // through LDS a 64-row quarter of the tile at a time (by the four waves
+    // that own it) for 16-byte row stores.
+    float* dst = p.part + (int64_t)blockIdx.y * p.M_total * p.N;
+    constexpr int FROW = BN * 4 + 16;            // float32 staging row (+pad)
+    static_assert(64 * FROW <= WS_BYTES, "quarter staging fits the W_S tile");
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+      __syncthreads();
+      if (wm == (qd >> 1)) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = 32 * ii + 8 * (r >> 2) + 4 * kg + (r & 3);
+              const int col = wn * 64 + 32 * j + r32;
+              *reinterpret_cast<float*>(wsl + row * FROW + 4 * col) = acc[2 * (qd & 1) + ii][j][r];
+            }
+      }
+      __syncthreads();
+      for (int q = tid; q < 64 * (BN / 4); q += 512) {
+        const int row = q / (BN / 4), ch = q % (BN / 4);
+        const int64_t prow = p0 + 64 * qd + row;
+        const int64_t n = n0 + ch * 4;
+        if (prow < e_hi && n < p.N)
+          *reinterpret_cast<float4*>(dst + prow * p.N + n) =
+              *reinterpret_cast<const float4*>(wsl + row * FROW + ch * 16);
+      }
+    }
+    return;
+  }
+
   // y = bf16(g_w * acc), staged through LDS (one 128-row half at a time, by
   // the four waves that own it) for 16-byte row stores
   const float gw = p.g_w[e];
@@ -821,6 +870,38 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
     }
   }
   if (p.glu_i > 0 && p.h_amax != nullptr) block_atomic_max<512>(hmax, p.h_amax);
+}
+
+// y[p] = bf16(g_w[e] * sum_s part[s][p]) over the K slices in order s = 0, 1,
+// ..., for row p of expert e; 8 columns per thread
+__global__ void __launch_bounds__(256)
+k_split_reduce(const float* __restrict__ part, int ksplit, int64_t M_total, int64_t N,
+               const int32_t* __restrict__ offsets, int E, const float* __restrict__ g_w,
+               uint16_t* __restrict__ y) {
+  const int64_t n8 = N / 8;
+  for (int64_t q = blockIdx.x * 256LL + threadIdx.x; q < M_total * n8;
+       q += (int64_t)gridDim.x * 256) {
+    const int64_t row = q / n8, c = (q - row * n8) * 8;
+    int lo = 0, hi = E;                          // last e with offsets[e] <= row
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (offsets[mid] <= row) lo = mid; else hi = mid;
+    }
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < ksplit; ++sp) {
+      const float4* src = reinterpret_cast<const float4*>(part + ((int64_t)sp * M_total + row) * N + c);
+      const float4 a = src[0], b = src[1];
+      v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+      v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+    }
+    const float gw = g_w[lo];
+    uint4 o;
+    o.x = f32_to_bf16_rne(v[0] * gw) | (f32_to_bf16_rne(v[1] * gw) << 16);
+    o.y = f32_to_bf16_rne(v[2] * gw) | (f32_to_bf16_rne(v[3] * gw) << 16);
+    o.z = f32_to_bf16_rne(v[4] * gw) | (f32_to_bf16_rne(v[5] * gw) << 16);
+    o.w = f32_to_bf16_rne(v[6] * gw) | (f32_to_bf16_rne(v[7] * gw) << 16);
+    *reinterpret_cast<uint4*>(y + row * N + c) = o;
+  }
 }
 
 // h [M][I] = bf16(silu(gate) * up) of y [M][2I] = [gate | up], 8 columns per
@@ -1493,12 +1574,35 @@ static size_t img_offset(int64_t E) { return round_up((size_t)(E + 1) * sizeof(i
 // the selected weight columns, bf16 [E][N][k], after the image
 static bool big_streams_ws(int64_t k) { return k > big::KMAX && k % big::KMAX == 0; }
 
+// K slices of the large-tile kernel for a problem whose tiles fill less than
+// the chip (sized for 256 CUs from the fewest tiles M_total can make; each
+// slice an even number of 64-k steps, at most 4 slices), or 1.
+// NVFP4RAC_SPLIT overrides it (tests).  Not with the fused SwiGLU or the
+// streamed correction.
+static int big_ksplit(int64_t M_total, int64_t N, int64_t K, int64_t k) {
+  if (big_streams_ws(k) || M_total <= 0) return 1;
+  const int64_t nk = K / big::BK;
+  const int64_t tiles = ((M_total + big::BM - 1) / big::BM) * ((N + big::BN - 1) / big::BN);
+  int s = 1;
+  if (const char* o = getenv("NVFP4RAC_SPLIT")) {
+    const int want = atoi(o);
+    while (s * 2 <= want && nk % (4 * s) == 0) s *= 2;
+    return s;
+  }
+  while (s < 4 && tiles * 2 * s <= 256 && nk % (4 * s) == 0) s *= 2;
+  return s;
+}
+static size_t split_bytes(int64_t M_total, int64_t N, int64_t K, int64_t k) {
+  const int s = big_ksplit(M_total, N, K, k);
+  return s > 1 ? round_up((size_t)s * (size_t)M_total * (size_t)N * 4, 256) : 0;
+}
+
 size_t grouped_w4a4_gemm_rac_workspace_size(int64_t E, int64_t M_src, int64_t M_total, int64_t N,
                                             int64_t K, int64_t k) {
-  (void)M_total;
-  if (E < 1 || M_src < 0 || K < 0 || N < 0) return 256;
+  if (E < 1 || M_src < 0 || M_total < 0 || K < 0 || N < 0) return 256;
   size_t n = img_offset(E) + round_up((size_t)M_src * (size_t)K * 2, 256);
   if (big_streams_ws(k)) n += round_up((size_t)E * (size_t)N * (size_t)k * 2, 256);
+  n += split_bytes(M_total, N, K, k);
   return n;
 }
 
@@ -1633,8 +1737,23 @@ static int gemm_rac(bool per_expert, bool glu, uint32_t* h_amax, const uint8_t* 
     k_tile_prefix<<<1, 1024, 0, s>>>(expert_offsets, (int)E, M_total, big::BM, prefix);
     const int64_t nblk = (((m_tiles_big + 3) / 4) * 4 * n_tiles_big + 7) / 8 * 8;
     if (glu) a.glu_i = N / 2, a.h_amax = h_amax;
-    k_gemm_big<false><<<(unsigned)nblk, 512, 0, s>>>(a, reinterpret_cast<const uint8_t*>(img),
-                                                    (int)n_tiles_big, (int)m_tiles_big);
+    // a problem that fills less than the chip: K slices, reduced in order
+    const int ksplit = glu ? 1 : big_ksplit(M_total, N, K, k);
+    const size_t part_off = img_offset(E) + round_up((size_t)M_src * (size_t)K * 2, 256);
+    if (ksplit > 1 && ws_bytes >= part_off + split_bytes(M_total, N, K, k)) {
+      a.ksplit = ksplit;
+      a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + part_off);
+      k_gemm_big<false, true><<<dim3((unsigned)nblk, (unsigned)ksplit), 512, 0, s>>>(
+          a, reinterpret_cast<const uint8_t*>(img), (int)n_tiles_big, (int)m_tiles_big);
+      const int64_t n8 = M_total * (N / 8);
+      int64_t nb = (n8 + 255) / 256;
+      if (nb > 8LL * num_cus()) nb = 8LL * num_cus();
+      k_split_reduce<<<(unsigned)nb, 256, 0, s>>>(a.part, ksplit, M_total, N, expert_offsets,
+                                                 (int)E, g_w, static_cast<uint16_t*>(y));
+    } else {
+      k_gemm_big<false><<<(unsigned)nblk, 512, 0, s>>>(a, reinterpret_cast<const uint8_t*>(img),
+                                                      (int)n_tiles_big, (int)m_tiles_big);
+    }
   } else {
     if (glu) a.y = glu_stage;
     k_tile_prefix<<<1, 1024, 0, s>>>(expert_offsets, (int)E, M_total, kBM, prefix);
