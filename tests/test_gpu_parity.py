@@ -196,6 +196,28 @@ def _gemm_case(rng, M_src, counts, N, K, k, gather):
     return host_vals(y), ref
 
 
+@pytest.mark.parametrize("split", [1, 2, 4])
+@pytest.mark.parametrize("M_src,counts,N,K,k,gather", [
+    (300, [100, 200], 256, 1024, 128, True),           # correction staged like A (k % 64 == 0)
+    (500, [17, 0, 0, 400, 83], 272, 1024, 32, True),  # correction from R rows directly
+    (96, [50, 46], 128, 2048, 0, False),
+])
+def test_gemm_k_split(dev, monkeypatch, split, M_src, counts, N, K, k, gather):
+    # the large-tile kernel with K split over 1, 2 or 4 workgroups (float32
+    # partials reduced in a fixed order): every split is within the GEMM
+    # tolerance of the oracle, and a repeated call is bit-identical
+    monkeypatch.setenv("NVFP4RAC_GEMM", "big")
+    monkeypatch.setenv("NVFP4RAC_SPLIT", str(split))
+    say(f"gemm k-split {split} counts={counts} N={N} K={K} k={k}")
+    rng = np.random.default_rng(sum(counts) + N + K + k)
+    y, ref = _gemm_case(rng, M_src, counts, N, K, k, gather)
+    e1, e2, ex = assert_gemm_close(y, ref)
+    rng = np.random.default_rng(sum(counts) + N + K + k)
+    y2, _ = _gemm_case(rng, M_src, counts, N, K, k, gather)
+    assert np.array_equal(y, y2)
+    say(f"   rownorm {e1:.2e} maxabs {e2:.2e} exact {ex:.5f}")
+
+
 @pytest.fixture(params=["generic", "big", "decode"])
 def gemm_kernel(request, monkeypatch):
     monkeypatch.setenv("NVFP4RAC_GEMM", request.param)
