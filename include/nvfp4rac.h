@@ -290,10 +290,13 @@ int moe_permute(const float* logits, const float* bias, int64_t T, int64_t E, in
  * w_scales [E][N/16][K/64][16][4] (the tiles nvfp4_qdq_weights writes), g_w [E];
  * expert_offsets [E+1] (device; off[0] = 0, off[E] = M_total); y [M_total][N]
  * bf16.  Requires K % 128 == 0, N % 16 == 0, 0 <= k <= K.
- * The workspace holds the per-expert tile prefix and, for large problems,
- * an exact f16 image of the activation (2 bytes per element) and, when k
- * exceeds 128 and is a multiple of 128, the selected weight columns as bf16
- * (E * N * k * 2 bytes).
+ * The workspace holds the per-expert tile prefix, an exact f16 image of the
+ * activation (2 bytes per element), when k exceeds 128 and is a multiple of
+ * 128 the selected weight columns as bf16 (E * N * k * 2 bytes), and, for a
+ * problem too small to fill the chip, float32 partial products of up to 4
+ * slices of K (slices * M_total * N * 4 bytes), summed in slice order, so
+ * results do not depend on timing.  A workspace smaller than the query
+ * returns selects the generic kernel (same results within the tolerance).
  * ---------------------------------------------------------------------- */
 size_t grouped_w4a4_gemm_rac_workspace_size(int64_t E, int64_t M_src, int64_t M_total,
                                             int64_t N, int64_t K, int64_t k);
