@@ -116,6 +116,23 @@ def test_gemm_validation():
     assert L.grouped_w4a4_gemm_rac(*args(ws=0)) == ERR_WS
 
 
+def test_gemm_workspace_covers_the_k_split(monkeypatch):
+    # a problem too small to fill the chip gets float32 partials for up to 4
+    # slices of K on top of the prefix and the f16 image; a large one none
+    L = F.lib()
+    monkeypatch.delenv("NVFP4RAC_SPLIT", raising=False)
+    E, M_src, M_total, N, K, k = 8, 1024, 2048, 1024, 2048, 32
+    base = 256 + ((M_src * K * 2 + 255) // 256) * 256
+    small = L.grouped_w4a4_gemm_rac_workspace_size(E, M_src, M_total, N, K, k)
+    assert small == base + 4 * M_total * N * 4
+    big = L.grouped_w4a4_gemm_rac_workspace_size(128, 16384, 131072, 3072, 4096, 128)
+    assert big == 768 + ((16384 * 4096 * 2 + 255) // 256) * 256
+    monkeypatch.setenv("NVFP4RAC_SPLIT", "1")
+    assert L.grouped_w4a4_gemm_rac_workspace_size(E, M_src, M_total, N, K, k) == base
+    monkeypatch.setenv("NVFP4RAC_SPLIT", "2")
+    assert L.grouped_w4a4_gemm_rac_workspace_size(E, M_src, M_total, N, K, k) == base + 2 * M_total * N * 4
+
+
 def test_fp8_validation():
     L = F.lib()
     ws = L.fp8_quantize_workspace_size(2)
