@@ -162,7 +162,7 @@ k_scatter(const int32_t* __restrict__ ids, int64_t T, int E, int tk,
 
 // out[t][n..n+8) = bf16(sum_j w[t][j] * y[inv_perm[t][j]][n..n+8)), float32
 // in slot order.  One block per token; its routing is read once.
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(512)
 k_combine(const uint16_t* __restrict__ y, const int32_t* __restrict__ inv_perm,
           const float* __restrict__ tw, int64_t T, int tk, int64_t N, uint16_t* __restrict__ out) {
   __shared__ int64_t rows[kMaxTopk];
@@ -183,7 +183,7 @@ k_combine(const uint16_t* __restrict__ y, const int32_t* __restrict__ inv_perm,
       acc[2 * i + 1] = __builtin_fmaf(wj, bf16_bits_to_f32(u[i] >> 16), acc[2 * i + 1]);
     }
   };
-  for (int64_t n = threadIdx.x * 8LL; n < N; n += 256 * 8) {
+  for (int64_t n = threadIdx.x * 8LL; n < N; n += (int64_t)blockDim.x * 8) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     int j0 = 0;
     for (; j0 + 8 <= tk; j0 += 8) {
@@ -263,7 +263,7 @@ int moe_unpermute_combine(const void* y, const int32_t* inv_perm, const float* t
   hipStream_t s = as_stream(stream);
   NV_REQUIRE(T < (1LL << 31) && tk <= kMaxTopk, NVFP4_ERR_SHAPE,
              "moe_unpermute_combine: need T < 2^31 and tk <= %d", kMaxTopk);
-  k_combine<<<(unsigned)T, 256, 0, s>>>(
+  k_combine<<<(unsigned)T, N >= 4096 ? 512 : 256, 0, s>>>(
       static_cast<const uint16_t*>(y), inv_perm, topk_w, T, (int)tk, N,
       static_cast<uint16_t*>(out));
   return check_launch("moe_unpermute_combine");
