@@ -359,8 +359,7 @@ def rac_sweep(cfg, wl, reps, n_experts=8):
         return F.grouped_w4a4_gemm_rac(q["codes"], q["scales"], q["g"], perm, R, S, c1, s1, g1,
                                        offs, M_total=rows)
 
-    E, N, Kh = c1.shape
-    K = 2 * Kh
+    E, N, K = c1.shape[0], c1.shape[1] * 16, c1.shape[2] * 64      # tiled codes
     ks = [k for k in (0, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096) if k <= K // 2]
     points = []
     t0 = None
