@@ -2,20 +2,28 @@
 MI355X.
 
     python bench.py [--steps K] [--warmup W] [--config 1..5] [--no-cpu-baseline]
+                    [--no-decode] [--no-ceilings]
 
-One step = one pass of the whole path over one batch, inputs resident in HBM:
-weight QDQ of both expert weight tensors (nvfp4_qdq_weights), route and
-permute (moe_permute), online activation quantization with channel scores,
-channel selection and residual gather, the gate+up grouped GEMM with the
-residual correction with SwiGLU fused into its output (--no-fuse-swiglu:
-into the second quantizer instead), the second quantizer, selection, the
-down grouped GEMM with correction, and the combine.
+A step is one forward of the MoE block over one batch, inputs resident in
+HBM: route and permute (moe_permute), online activation quantization with
+channel scores, channel selection and residual gather, the gate+up grouped
+GEMM with the residual correction (SwiGLU fused into its output where the
+large-tile kernel takes the shape; --no-fuse-swiglu: into the second
+quantizer instead), the second quantizer, selection, the down grouped GEMM
+with correction, and the combine.  The weight QDQ of both expert tensors
+(nvfp4_qdq_weights) runs once per weight sync, not per forward: it is timed
+on its own (weight_qdq_ms_per_sync; ms_per_step_incl_weight_qdq adds it).
 
-Prints ONE JSON line.  `value` = algorithmic GEMM flops of a step (2 * rows *
-N * (K + k) summed over both GEMMs) / wall time per step, in TFLOP/s.
-`roofline` covers the grouped GEMM call (grouped_w4a4_gemm_rac: its small
-operand-preparation kernels plus the main GEMM kernel), timed with HIP events
-on the launch stream over the timed steps:
+Prints ONE JSON line for the large-prefill workload (default --config 5).
+`value` = algorithmic GEMM flops of a step (2 * rows * N * (K + k) summed
+over both GEMMs) / wall time per step, in TFLOP/s; step_ms_events gives the
+p10 / p50 / p90 of per-step HIP-event times.  The step is timed as one HIP
+graph replay (captured once; the library allocates nothing and sizes every
+grid from shapes, so the whole forward replays without a host launch per
+kernel); ms_per_step_eager is the same step launched call by call
+(--eager: eager only).  `roofline` covers the grouped
+GEMM calls (their small operand-preparation kernels plus the main GEMM
+kernel), timed with HIP events on the launch stream over the timed steps:
   * many rows per expert (prefill): algorithmic flops / duration against the
     dense f16/bf16 MFMA peak (the exact NVFP4 product runs on that path);
   * few rows per expert (decode): algorithmic bytes -- weights of experts
@@ -23,10 +31,14 @@ on the launch stream over the timed steps:
     HBM bandwidth.
 `traffic` is the HBM byte count of the same calls from rocprofv3 counters
 (profiles/hbm_traffic.json), or null when the GEMM source has changed since
-they were taken.  `cpu_baseline` times the CPU oracle on a bounded sample of
-the same block.
+they were taken.  `decode` is the same report for the decode-sized block
+(256 tokens), `rac_overhead` the correction's cost on each GEMM call
+(t(k) / t(k = 0) - 1), `ceilings` the MFMA and HBM rates measured on the
+chip, `gates` each target against its measurement, and `cpu_baseline` the
+CPU oracle on a bounded sample of the same block.
 
     python bench.py --calibrate-copy     # 1 GiB device copy, for counter scaling
+    python bench.py --ceilings           # MFMA and HBM ceilings only
     python bench.py --rac-sweep [--config C]   # compensation strength against cost
     python bench.py --w4a16 [--config C]       # trainer-side W4A16 product, same shapes
     python bench.py --fp8 [--config C]         # FP8 (E4M3) W8A8 baseline, same shapes
@@ -69,6 +81,14 @@ def parse():
                     help="only time the trainer-side W4A16 product on the block's GEMM shapes")
     ap.add_argument("--fp8", action="store_true",
                     help="only time the FP8 (E4M3) W8A8 baseline on the block's GEMM shapes")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure the MFMA and HBM ceilings of this chip")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="leave out the decode-sized block's sub-report")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="leave out the ceiling microbenchmarks")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches only (no HIP graph replay of the step)")
     return ap.parse_args()
 
 
@@ -112,8 +132,8 @@ def to_dev(bits, dev):
 
 
 class Timer:
-    """Average duration of a bracketed region, from HIP events recorded on
-    the current (launch) stream."""
+    """Durations of bracketed regions, from HIP events recorded on the
+    current (launch) stream."""
 
     def __init__(self):
         self.pairs = []
@@ -130,13 +150,61 @@ class Timer:
         b.record()
         self.pairs.append((a, b))
 
+    def times(self):
+        return [a.elapsed_time(b) for a, b in self.pairs]
+
     def mean_ms(self):
-        if not self.pairs:
-            return float("nan")
-        return sum(a.elapsed_time(b) for a, b in self.pairs) / len(self.pairs)
+        t = self.times()
+        return sum(t) / len(t) if t else float("nan")
 
 
-def run_gpu(cfg, wl, steps, warmup, fuse_swiglu=True):
+def percentiles(ts):
+    import numpy as np
+    return {"p10": round(float(np.percentile(ts, 10)), 4),
+            "p50": round(float(np.percentile(ts, 50)), 4),
+            "p90": round(float(np.percentile(ts, 90)), 4)}
+
+
+def median_ms(fn, reps):
+    """Median of `reps` HIP-event timings of fn() (after two untimed calls)."""
+    import numpy as np
+    import torch
+    ts = []
+    for _ in range(reps + 2):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        ts.append((a, b))
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ts[2:]]))
+
+
+def interleaved_ms(fns, reps):
+    """Medians of HIP-event timings of several calls, run in turn (so that
+    clock drift affects them alike)."""
+    import numpy as np
+    import torch
+    ts = [[] for _ in fns]
+    for i in range(reps + 2):
+        for j, fn in enumerate(fns):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            if i >= 2:
+                ts[j].append((a, b))
+    torch.cuda.synchronize()
+    return [float(np.median([a.elapsed_time(b) for a, b in t])) for t in ts]
+
+
+def run_block(cfg, wl, steps, warmup, fuse_swiglu=True, use_graph=True):
+    """The block on one GPU.  Weight QDQ runs once per weight sync, so it is
+    timed on its own; a step is one forward: route and permute, quantize,
+    select, gate+up GEMM (SwiGLU fused where the large-tile kernel forms it),
+    quantize h, select, down GEMM, combine."""
     import torch
 
     import fp4_quantized_gemm_amd as F
@@ -145,14 +213,25 @@ def run_gpu(cfg, wl, steps, warmup, fuse_swiglu=True):
     x = to_dev(wl.x, dev)
     w1 = to_dev(wl.w_first, dev)
     w2 = to_dev(wl.w_down, dev) if wl.w_down is not None else None
+    logits = bias = None
     if wl.logits is not None:
         logits = torch.from_numpy(wl.logits).to(dev)
         bias = torch.from_numpy(wl.bias).to(dev) if wl.bias is not None else None
     torch.cuda.synchronize()
 
-    timers = {n: Timer() for n in ("qdq", "permute", "quant1", "select1", "gemm1", "quant2",
+    def qdq():
+        return (F.nvfp4_qdq_weights(w1, want_qdq=False),
+                F.nvfp4_qdq_weights(w2, want_qdq=False) if w2 is not None else None)
+
+    qdq_ms = median_ms(qdq, max(3, steps // 4))
+    W1, W2 = qdq()
+    del w1, w2
+    torch.cuda.empty_cache()
+
+    timers = {n: Timer() for n in ("permute", "quant1", "select1", "gemm1", "quant2",
                                    "select2", "gemm2", "combine")}
     record = [False]
+    fuse = fuse_swiglu and W2 is not None
 
     def timed(name, fn, *a, **kw):
         if not record[0]:
@@ -162,13 +241,23 @@ def run_gpu(cfg, wl, steps, warmup, fuse_swiglu=True):
         timers[name].stop(t0)
         return r
 
-    def step():
-        q1w = timed("qdq", lambda: (F.nvfp4_qdq_weights(w1, want_qdq=False),
-                                    F.nvfp4_qdq_weights(w2, want_qdq=False) if w2 is not None else None))
-        (c1, s1, g1, _), wd = q1w
+    def gemm1(q, perm, R, S, offs, rows):
+        gargs = (q["codes"], q["scales"], q["g"], perm, R, S, W1.packed_codes, W1.packed_scales,
+                 W1.g, offs)
+        if fuse:
+            return F.grouped_w4a4_gemm_rac_swiglu(*gargs, M_total=rows, with_amax=True)
+        return F.grouped_w4a4_gemm_rac(*gargs, M_total=rows), None
+
+    def gemm2(q2, R2, S2, offs, rows):
+        return F.grouped_w4a4_gemm_rac(q2["codes"], q2["scales"], q2["g"], None, R2, S2,
+                                       W2.packed_codes, W2.packed_scales, W2.g, offs, M_total=rows)
+
+    dense_offs = torch.tensor([0, cfg.T], dtype=torch.int32, device=dev)
+
+    def step(keep=False):
         if cfg.kind == "dense":
-            offs = torch.tensor([0, cfg.T], dtype=torch.int32, device=dev)
-            perm = None
+            offs = dense_offs
+            perm, inv, tw = None, None, None
             rows = cfg.T
         else:
             ids, tw, offs, perm, inv = timed("permute", F.moe_permute, logits, cfg.topk, bias)
@@ -178,16 +267,10 @@ def run_gpu(cfg, wl, steps, warmup, fuse_swiglu=True):
         if cfg.k_first:
             S, R = timed("select1", F.select_residual_channels, q["x_used"], q["codes"],
                          q["scales"], q["g"], q["score"], cfg.k_first)
-        fuse = fuse_swiglu and wd is not None
-        gargs = (q["codes"], q["scales"], q["g"], perm, R, S, c1, s1, g1, offs)
-        if fuse:
-            y1, h_amax = timed("gemm1", F.grouped_w4a4_gemm_rac_swiglu, *gargs, M_total=rows,
-                               with_amax=True)
-        else:
-            y1 = timed("gemm1", F.grouped_w4a4_gemm_rac, *gargs, M_total=rows)
-        if wd is None:
-            return y1
-        c2, s2, g2, _ = wd
+        y1, h_amax = timed("gemm1", gemm1, q, perm, R, S, offs, rows)
+        st = dict(q=q, S=S, R=R, perm=perm, offs=offs, rows=rows) if keep else None
+        if W2 is None:
+            return y1, st
         if fuse:
             q2 = timed("quant2", F.nvfp4_quantize_act_amax, y1, h_amax, cfg.k_down > 0)
         else:
@@ -196,9 +279,10 @@ def run_gpu(cfg, wl, steps, warmup, fuse_swiglu=True):
         if cfg.k_down:
             S2, R2 = timed("select2", F.select_residual_channels, q2["x_used"], q2["codes"],
                            q2["scales"], q2["g"], q2["score"], cfg.k_down)
-        y2 = timed("gemm2", F.grouped_w4a4_gemm_rac, q2["codes"], q2["scales"], q2["g"], None, R2,
-                   S2, c2, s2, g2, offs, M_total=rows)
-        return timed("combine", F.moe_unpermute_combine, y2, inv, tw)
+        y2 = timed("gemm2", gemm2, q2, R2, S2, offs, rows)
+        if keep:
+            st.update(q2=q2, S2=S2, R2=R2)
+        return timed("combine", F.moe_unpermute_combine, y2, inv, tw), st
 
     for _ in range(warmup):
         step()
@@ -208,51 +292,99 @@ def run_gpu(cfg, wl, steps, warmup, fuse_swiglu=True):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # a second pass with per-call events (kept out of the wall-clock region)
+    # per-step HIP events (their spread), then per-call events (the stage
+    # breakdown); both kept out of the wall-clock region
+    st_timer = Timer()
+    for _ in range(steps):
+        a = st_timer.start()
+        step()
+        st_timer.stop(a)
+    torch.cuda.synchronize()
     record[0] = True
     for _ in range(steps):
         step()
     torch.cuda.synchronize()
+    record[0] = False
     stage_ms = {n: t.mean_ms() for n, t in timers.items() if t.pairs}
 
-    # residual-compensation overhead: the same GEMMs with k = 0
+    # the same forward step captured once as a HIP graph and replayed: the
+    # library allocates nothing, never synchronizes and sizes every grid from
+    # shapes alone, so a serving loop can replay the whole step without a
+    # host launch per kernel
+    graph_ms = graph_pct = None
+    if use_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(2):
+                step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) / steps * 1e3
+        gt = Timer()
+        for _ in range(steps):
+            a = gt.start()
+            g.replay()
+            gt.stop(a)
+        torch.cuda.synchronize()
+        graph_pct = percentiles(gt.times())
+        del g
+
+    # residual-compensation overhead of each GEMM call as the step makes it:
+    # t(k) / t(k = 0) - 1, the two timed in turn
+    _, st = step(keep=True)
+    reps = max(steps, 10)
     rac = {}
     if cfg.k_first:
-        q = F.nvfp4_quantize_act(x, False, True)
-        S, R = F.select_residual_channels(q["x_used"], q["codes"], q["scales"], q["g"], q["score"],
-                                          cfg.k_first)
-        c1, s1, g1, _ = F.nvfp4_qdq_weights(w1, want_qdq=False)
-        if cfg.kind == "dense":
-            offs = torch.tensor([0, cfg.T], dtype=torch.int32, device=dev)
-            perm, rows = None, cfg.T
-        else:
-            _, _, offs, perm, _ = F.moe_permute(logits, cfg.topk, bias)
-            rows = perm.numel()
-        for kk, (RR, SS) in (("k", (R, S)), ("0", (None, None))):
-            tm = Timer()
-            for i in range(steps + 2):
-                a = tm.start()
-                F.grouped_w4a4_gemm_rac(q["codes"], q["scales"], q["g"], perm, RR, SS, c1, s1, g1,
-                                        offs, M_total=rows)
-                tm.stop(a)
-            torch.cuda.synchronize()
-            tm.pairs = tm.pairs[2:]
-            rac[kk] = tm.mean_ms()
-        rac = {"gemm1_ms_k": rac["k"], "gemm1_ms_k0": rac["0"],
-               "overhead": rac["k"] / rac["0"] - 1.0}
+        tk, t0k = interleaved_ms(
+            [lambda: gemm1(st["q"], st["perm"], st["R"], st["S"], st["offs"], st["rows"]),
+             lambda: gemm1(st["q"], st["perm"], None, None, st["offs"], st["rows"])], reps)
+        rac["gemm1"] = {"ms_k": round(tk, 4), "ms_k0": round(t0k, 4),
+                        "overhead": round(tk / t0k - 1.0, 4)}
+    if W2 is not None and cfg.k_down:
+        tk, t0k = interleaved_ms(
+            [lambda: gemm2(st["q2"], st["R2"], st["S2"], st["offs"], st["rows"]),
+             lambda: gemm2(st["q2"], None, None, st["offs"], st["rows"])], reps)
+        rac["gemm2"] = {"ms_k": round(tk, 4), "ms_k0": round(t0k, 4),
+                        "overhead": round(tk / t0k - 1.0, 4)}
     if cfg.kind == "dense":
         counts = [cfg.T]
     else:
-        o = F.moe_permute(logits, cfg.topk, bias)[2].cpu().numpy()
+        o = st["offs"].cpu().numpy()
         counts = list(o[1:] - o[:-1])
-    return wall / steps * 1e3, stage_ms, rac, counts
+    eager_ms = wall / steps * 1e3
+    return dict(ms=graph_ms if graph_ms is not None else eager_ms,
+                step_ms=graph_pct if graph_pct is not None else percentiles(st_timer.times()),
+                eager_ms=eager_ms, eager_step_ms=percentiles(st_timer.times()),
+                graph=graph_ms is not None, stage_ms=stage_ms, qdq_ms=qdq_ms, rac=rac,
+                counts=counts, fuse=fuse)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(cfg, wl, tokens, experts):
     """The oracle, as it stands, on a bounded sample of the same block: the
     first `tokens` tokens routed over the first `experts` experts (top-k
     capped at experts / 2), every stage of the block."""
-    import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import formats as OF
@@ -278,12 +410,59 @@ def cpu_baseline(cfg, wl, tokens, experts):
         flops = 2 * rows * w1.shape[1] * (cfg.H + cfg.k_first)
         if w2 is not None:
             flops += 2 * rows * cfg.H * (cfg.inter + cfg.k_down)
-        desc = (f"{T} tokens x top-{tk} of the first {E} experts, every stage incl. weight QDQ "
-                f"of those experts")
+        desc = (f"{T} tokens x top-{tk} of the first {E} experts of {cfg.name} (hidden "
+                f"{cfg.H}, intermediate {cfg.inter}), every stage incl. weight QDQ of those "
+                f"experts")
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": desc, "seconds": round(dt, 2)}
+            "sample": desc, "seconds": round(dt, 2), "cpu_model": cpu_model(),
+            "cores_available": cores, "blas_threads": threads}
+
+
+def ceilings(reps=5):
+    """Sustained rates measured on this chip: each matrix-core instruction
+    family the exact NVFP4 product (f16/bf16) and its FP8 baseline can use,
+    and HBM streaming read and copy."""
+    import ctypes
+
+    import torch
+
+    import fp4_quantized_gemm_amd as F
+
+    L = F.lib()
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(2 * cus * 256, dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    res = {"cus": cus}
+    for kind, name in ((0, "mfma_f16"), (1, "mfma_bf16"), (2, "mfma_fp8"), (3, "mfma_fp4")):
+        iters = 4000 if kind < 2 else 2000
+        fn = lambda: L.nvfp4_ceiling_mfma(kind, iters, 2 * cus, ctypes.c_void_p(out.data_ptr()),
+                                          stream)
+        assert fn() == 0
+        ms = median_ms(fn, reps)
+        flops = 2 * cus * 4 * iters * 4 * L.nvfp4_ceiling_mfma_flops(kind)
+        res[name + "_tflops"] = round(flops / ms / 1e9, 1)
+    nbytes = 2 << 30                                   # 2 GiB, past the 256 MB cache
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    o32 = torch.empty(1, dtype=torch.int32, device=dev)
+    rd = lambda: L.nvfp4_ceiling_read(ctypes.c_void_p(buf.data_ptr()), nbytes,
+                                      ctypes.c_void_p(o32.data_ptr()), stream)
+    assert rd() == 0
+    res["hbm_read_GBps"] = round(nbytes / median_ms(rd, reps) / 1e6, 1)
+    half = buf[: nbytes // 2]
+    dst = torch.empty_like(half)
+    res["hbm_copy_GBps"] = round(2 * half.numel() / median_ms(lambda: dst.copy_(half), reps) / 1e6,
+                                 1)
+    del buf, dst
+    torch.cuda.empty_cache()
+    return res
 
 
 def gemm_kernel_name(cfg, m, n, k, E):
@@ -314,7 +493,8 @@ def rac_sweep(cfg, wl, reps, n_experts=8):
     dev = torch.device("cuda:0")
     x = to_dev(wl.x, dev)
     w1 = to_dev(wl.w_first, dev)
-    c1, s1, g1, wq = F.nvfp4_qdq_weights(w1, want_qdq=True)
+    Wq = F.nvfp4_qdq_weights(w1, want_qdq=True)
+    c1, s1, g1, wq = Wq.packed_codes, Wq.packed_scales, Wq.g, Wq.qdq
     del w1
     if cfg.kind == "dense":
         offs = torch.tensor([0, cfg.T], dtype=torch.int32, device=dev)
@@ -441,7 +621,9 @@ def w4a16_bench(cfg, wl, reps):
 
     out = []
     for name, a, a_rows, w in gemms:
-        c, s, gw, _ = F.nvfp4_qdq_weights(w, want_qdq=False)
+        Wq = F.nvfp4_qdq_weights(w, want_qdq=False)
+        c, s, gw = Wq.packed_codes, Wq.packed_scales, Wq.g
+        del Wq
         del w
         q = F.nvfp4_quantize_act(a, False, False)
         E, N, K = c.shape[0], c.shape[1] * 16, c.shape[2] * 64
@@ -504,7 +686,9 @@ def fp8_bench(cfg, wl, reps):
     for name, a, a_rows, w, k in gemms:
         E, N, K = w.shape
         wc8, gw8 = F.fp8_quantize(w, stacked=True)
-        c, s, gw, _ = F.nvfp4_qdq_weights(w, want_qdq=False)
+        Wq = F.nvfp4_qdq_weights(w, want_qdq=False)
+        c, s, gw = Wq.packed_codes, Wq.packed_scales, Wq.g
+        del Wq
         del w
         ac8, gx8 = F.fp8_quantize(a)
         q = F.nvfp4_quantize_act(a, False, k > 0)
@@ -541,14 +725,77 @@ def gemm_algorithmic_bytes(cfg, counts):
     return total
 
 
+def roofline_of(cfg, res, decode):
+    """The grouped GEMM calls of a step against their bound: MFMA (f16/bf16
+    dense peak) for prefill, HBM for decode-sized blocks."""
+    shapes = cfg.gemm_shapes()
+    flops_step = cfg.gemm_flops()
+    gemm_ms = res["stage_ms"].get("gemm1", 0.0) + res["stage_ms"].get("gemm2", 0.0)
+    alg_bytes = gemm_algorithmic_bytes(cfg, res["counts"])
+    if decode:
+        achieved = alg_bytes / (gemm_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4)}
+        kernel = "grouped_w4a4_gemm_rac: k_gemm_decode"
+    else:
+        achieved = flops_step / (gemm_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "frac_of_fp4_peak": round(achieved / PEAK_FP4_TFLOPS, 4)}
+        _, m, n, _, kk = shapes[0]
+        big = gemm_kernel_name(cfg, m, n, kk, cfg.E).endswith("k_gemm_big")
+        name = ("grouped_w4a4_gemm_rac_swiglu + grouped_w4a4_gemm_rac" if res["fuse"]
+                else "grouped_w4a4_gemm_rac")
+        kernel = (f"{name}: k_decode_a + k_tile_prefix + k_gemm_big" if big
+                  else f"{name}: k_tile_prefix + k_gemm_generic")
+    roof["traffic"] = recorded_traffic(cfg.name)
+    roof["kernel"] = kernel
+    roof["algorithmic_bytes"] = round(alg_bytes)
+    roof["algorithmic_flops"] = round(flops_step)
+    roof["gemm_ms_per_step"] = round(gemm_ms, 4)
+    return roof
+
+
+def quantizer_rates(cfg, res):
+    q_bytes = 2.5625 * cfg.T * cfg.H
+    out = {"quant1_GBps": round(q_bytes / (res["stage_ms"]["quant1"] * 1e-3) / 1e9, 1)}
+    if "quant2" in res["stage_ms"]:
+        # h's quantizer: reads h once (amax from the fused GEMM), or reads
+        # [gate | up] and forms h
+        q2_bytes = (2.5625 if res["fuse"] else 4.5625) * cfg.rows * cfg.inter
+        out["quant2_GBps"] = round(q2_bytes / (res["stage_ms"]["quant2"] * 1e-3) / 1e9, 1)
+    out["frac_of_hbm"] = {k: round(v / PEAK_HBM_GBPS, 4) for k, v in list(out.items())}
+    return out
+
+
+def block_summary(cfg, res, decode):
+    return {
+        "workload": cfg.name,
+        "ms_per_step": round(res["ms"], 4),
+        "step_ms_events": res["step_ms"],
+        "step_launch": "one HIP graph replay per step" if res["graph"] else "eager launches",
+        "ms_per_step_eager": round(res["eager_ms"], 4),
+        "step_ms_events_eager": res["eager_step_ms"],
+        "value": round(cfg.gemm_flops() / (res["ms"] * 1e-3) / 1e12, 2),
+        "weight_qdq_ms_per_sync": round(res["qdq_ms"], 4),
+        "roofline": roofline_of(cfg, res, decode),
+        "stages_ms": {k: round(v, 4) for k, v in res["stage_ms"].items()},
+        "quantizer": quantizer_rates(cfg, res),
+        "rac_overhead": res["rac"],
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
-              f"multi-GPU path", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); every box here has "
+              f"one GPU and this build has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.ceilings:
+        print(json.dumps({"mode": "ceilings", **ceilings()}), flush=True)
         return
     import synth
 
@@ -567,48 +814,20 @@ def main():
     # on decode-sized blocks the decode kernel's output goes to the quantizer
     decode = cfg.rows <= 48 * cfg.E and cfg.kind != "dense"
     fuse = not args.no_fuse_swiglu and wl.w_down is not None and not decode
-    ms, stage_ms, rac, counts = run_gpu(cfg, wl, args.steps, args.warmup, fuse)
+    res = run_block(cfg, wl, args.steps, args.warmup, fuse, not args.eager)
+    main_block = block_summary(cfg, res, decode)
     shapes = cfg.gemm_shapes()
-    flops_step = cfg.gemm_flops()
-    value = flops_step / (ms * 1e-3) / 1e12
-    gemm_ms = stage_ms.get("gemm1", 0.0) + stage_ms.get("gemm2", 0.0)
-    alg_bytes = gemm_algorithmic_bytes(cfg, counts)
-    if decode:
-        achieved = alg_bytes / (gemm_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4)}
-        kernel = "grouped_w4a4_gemm_rac: k_gemm_decode"
-    else:
-        achieved = flops_step / (gemm_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "frac_of_fp4_peak": round(achieved / PEAK_FP4_TFLOPS, 4)}
-        # the library's choice (the large-tile kernel for every shape it takes)
-        _, m, n, _, kk = shapes[0]
-        big = gemm_kernel_name(cfg, m, n, kk, cfg.E).endswith("k_gemm_big")
-        name = "grouped_w4a4_gemm_rac_swiglu + grouped_w4a4_gemm_rac" if fuse else \
-            "grouped_w4a4_gemm_rac"
-        kernel = (f"{name}: k_decode_a + k_tile_prefix + k_gemm_big" if big
-                  else f"{name}: k_tile_prefix + k_gemm_generic")
-    roof["traffic"] = recorded_traffic(cfg.name)
-    roof["kernel"] = kernel
-    roof["algorithmic_bytes"] = round(alg_bytes)
-    roof["gemm_ms_per_step"] = round(gemm_ms, 4)
-    q_bytes = 2.5625 * cfg.T * cfg.H
-    quant = {"quant1_GBps": q_bytes / (stage_ms["quant1"] * 1e-3) / 1e9}
-    if "quant2" in stage_ms:
-        # h's quantizer: reads [gate | up] and forms h, or reads h once (fused,
-        # amax from the GEMM)
-        q2_bytes = (2.5625 if fuse else 4.5625) * cfg.rows * cfg.inter
-        quant["quant2_GBps"] = q2_bytes / (stage_ms["quant2"] * 1e-3) / 1e9
     line = {
         "metric": "grouped W4A4+RAC GEMM TFLOP/s and % of MI355X FP4 MFMA peak; quantizer GB/s",
-        "value": round(value, 2),
+        "value": main_block["value"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": main_block["ms_per_step"],
+        "step_ms_events": main_block["step_ms_events"],
+        "step_launch": main_block["step_launch"],
+        "ms_per_step_eager": main_block["ms_per_step_eager"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -616,18 +835,51 @@ def main():
         "storage": "nvfp4 (E2M1 + E4M3/16 + f32) decoded exactly to f16 MFMA operands, bf16 "
                    "residual term, f32 accumulate",
         "data": "synthetic",
+        "step": "one forward of the MoE block (route, quantize, select, gate+up GEMM+RAC, "
+                "SwiGLU, quantize, select, down GEMM+RAC, combine); the weight QDQ runs once "
+                "per weight sync and is reported as weight_qdq_ms_per_sync",
+        "weight_qdq_ms_per_sync": main_block["weight_qdq_ms_per_sync"],
+        "ms_per_step_incl_weight_qdq": round(res["ms"] + res["qdq_ms"], 4),
         "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.H, "experts": cfg.E,
                    "topk": cfg.topk, "inter": cfg.inter, "rac_k": [s[4] for s in shapes],
                    "gemms": [f"{n} {m}x{nn}x{k}" for n, m, nn, k, _ in shapes],
                    "swiglu": ("fused into the gate+up GEMM" if fuse else
                               "fused into the second quantizer") if wl.w_down is not None
                    else None},
-        "roofline": roof,
-        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-        "quantizer": {k: round(v, 1) for k, v in quant.items()},
-        "rac_overhead": {k: round(v, 4) for k, v in rac.items()},
+        "roofline": main_block["roofline"],
+        "stages_ms": main_block["stages_ms"],
+        "quantizer": main_block["quantizer"],
+        "rac_overhead": main_block["rac_overhead"],
     }
+    del res, wl
+    if not args.no_decode and args.config != 4:
+        dcfg = synth.get(4)
+        dwl = synth.make(dcfg)
+        dres = run_block(dcfg, dwl, args.steps, args.warmup, False, not args.eager)
+        line["decode"] = block_summary(dcfg, dres, True)
+        del dres
+    if not args.no_ceilings:
+        line["ceilings"] = ceilings()
+    gates = {}
+    r = line["roofline"]
+    if r["bound"] == "mfma":
+        gates["prefill_gemm_frac_bf16_peak"] = {"value": r["frac"], "target": 0.5,
+                                                "met": r["frac"] >= 0.5}
+        gates["prefill_gemm_frac_fp4_peak"] = {"value": r["frac_of_fp4_peak"], "target": 0.5,
+                                               "met": r["frac_of_fp4_peak"] >= 0.5,
+                                               "ceiling_of_exact_mapping": 0.25}
+    dec = line.get("decode", {}).get("roofline") or (r if r["bound"] == "hbm" else None)
+    if dec is not None:
+        gates["decode_gemm_frac_hbm"] = {"value": dec["frac"], "target": 0.6,
+                                         "met": dec["frac"] >= 0.6}
+    for blk, tag in ((line, "main"), (line.get("decode"), "decode")):
+        if blk:
+            for g, v in blk["rac_overhead"].items():
+                gates[f"rac_overhead_{tag}_{g}"] = {"value": v["overhead"], "target": 0.10,
+                                                    "met": v["overhead"] <= 0.10}
+    line["gates"] = gates
     if not args.no_cpu_baseline:
+        wl = synth.make(cfg)
         line["cpu_baseline"] = cpu_baseline(cfg, wl, args.cpu_tokens, args.cpu_experts)
     print(json.dumps(line), flush=True)
 

@@ -10,6 +10,8 @@ there is no fallback: importing the library fails loudly if it is missing.
 Calls (same names as the C ABI):
     nvfp4_qdq_weights, nvfp4_quantize_act, select_residual_channels,
     moe_permute, grouped_w4a4_gemm_rac, moe_unpermute_combine
+the GEMMs' weight pre-pack for row-major codes quantized elsewhere,
+    nvfp4_pack_weights
 and, for the variants of the correction, the fused SwiGLU and the
 trainer-side W4A16 product,
     nvfp4_qdq_residual, select_residual_channels_per_expert,
@@ -22,12 +24,14 @@ from __future__ import annotations
 
 import ctypes
 import os
+from typing import NamedTuple, Optional
 
 import torch
 
 from .build import LIB as LIB_PATH
 
-__all__ = ["lib", "nvfp4_qdq_weights", "nvfp4_quantize_act", "select_residual_channels",
+__all__ = ["lib", "nvfp4_qdq_weights", "nvfp4_pack_weights", "QdqWeights",
+           "nvfp4_e2m1_encode_f32", "nvfp4_quantize_act", "select_residual_channels",
            "moe_permute", "grouped_w4a4_gemm_rac", "moe_unpermute_combine", "nvfp4_qdq_residual",
            "grouped_w4a16_gemm", "select_residual_channels_per_expert",
            "grouped_w4a4_gemm_rac_per_expert", "grouped_w4a4_gemm_rac_swiglu",
@@ -36,7 +40,8 @@ __all__ = ["lib", "nvfp4_qdq_weights", "nvfp4_quantize_act", "select_residual_ch
 
 EXPORTED_SYMBOLS = [
     "nvfp4_version", "nvfp4_status_str", "nvfp4_last_error",
-    "nvfp4_qdq_weights_workspace_size", "nvfp4_qdq_weights",
+    "nvfp4_qdq_weights_workspace_size", "nvfp4_qdq_weights", "nvfp4_pack_weights",
+    "nvfp4_e2m1_encode_f32",
     "nvfp4_quantize_act_workspace_size", "nvfp4_quantize_act",
     "select_residual_channels_workspace_size", "select_residual_channels",
     "moe_permute_workspace_size", "moe_permute",
@@ -51,6 +56,10 @@ EXPORTED_SYMBOLS = [
     "fp8_quantize_workspace_size", "fp8_quantize",
     "grouped_fp8_gemm_workspace_size", "grouped_fp8_gemm",
 ]
+
+
+# measurement-only exports (include/nvfp4rac_bench.h)
+BENCH_SYMBOLS = ["nvfp4_ceiling_mfma_flops", "nvfp4_ceiling_mfma", "nvfp4_ceiling_read"]
 
 
 class NvfpError(RuntimeError):
@@ -91,7 +100,9 @@ def _load():
         f.restype = _SZ
         f.argtypes = args
     sigs = {
-        "nvfp4_qdq_weights": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P],
+        "nvfp4_qdq_weights": [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _SZ, _P],
+        "nvfp4_pack_weights": [_P, _P, _I64, _I64, _I64, _P, _P, _P],
+        "nvfp4_e2m1_encode_f32": [_P, _I64, _P, _P],
         "nvfp4_quantize_act": [_P, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P, _P, _P, _P, _SZ, _P],
         "select_residual_channels": [_P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _SZ, _P],
         "moe_permute": [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P],
@@ -115,6 +126,12 @@ def _load():
         f = getattr(L, name)
         f.restype = ctypes.c_int
         f.argtypes = args
+    L.nvfp4_ceiling_mfma_flops.restype = ctypes.c_double
+    L.nvfp4_ceiling_mfma_flops.argtypes = [ctypes.c_int]
+    L.nvfp4_ceiling_mfma.restype = ctypes.c_int
+    L.nvfp4_ceiling_mfma.argtypes = [ctypes.c_int, _I64, _I64, _P, _P]
+    L.nvfp4_ceiling_read.restype = ctypes.c_int
+    L.nvfp4_ceiling_read.argtypes = [_P, _I64, _P, _P]
     _lib = L
     return L
 
@@ -139,10 +156,11 @@ def _check(status, name):
 
 
 def _wshape(w_codes):
-    """(E, N) of weight codes in the library's tiles [E][N/16][K/64][16][32]."""
+    """(E, N) of packed weight codes [E][N/16][K/64][16][32] (the shape the
+    packed outputs of nvfp4_qdq_weights and nvfp4_pack_weights carry)."""
     if w_codes.dim() != 5 or tuple(w_codes.shape[3:]) != (16, 32):
-        raise NvfpError("weight codes must be tiled [E][N/16][K/64][16][32] "
-                        "(as nvfp4_qdq_weights returns them)")
+        raise NvfpError("weight codes must be the packed copy [E][N/16][K/64][16][32] "
+                        "(nvfp4_qdq_weights' packed outputs or nvfp4_pack_weights)")
     return int(w_codes.shape[0]), int(w_codes.shape[1]) * 16
 
 
@@ -159,24 +177,67 @@ def _need(t, dtype, name):
         raise NvfpError(f"{name} must be contiguous")
 
 
-def nvfp4_qdq_weights(w, want_qdq=True):
-    """w [E][N][K] bf16 -> (codes [E][N/16][K/64][16][32] u8 (two E2M1 codes
-    per byte in 512-byte tiles of 16 rows x 64 columns), scales
-    [E][N/16][K/64][16][4] u8 (block scales in 64-byte tiles of the same
-    16 rows x 64 columns), g_w [E] f32, w_qdq [E][N][K] bf16 or None)."""
+class QdqWeights(NamedTuple):
+    """Outputs of nvfp4_qdq_weights."""
+    codes: torch.Tensor                    # [E][N][K/2] u8, row-major E2M1 pairs
+    scales: torch.Tensor                   # [E][N][K/16] u8, row-major E4M3 block scales
+    g: torch.Tensor                        # [E] f32 tensor scales
+    qdq: Optional[torch.Tensor]            # [E][N][K] bf16 fake-quantized weight, or None
+    packed_codes: Optional[torch.Tensor]   # the GEMMs' packed copy, [E][N/16][K/64][16][32]
+    packed_scales: Optional[torch.Tensor]  # [E][N/16][K/64][16][4]
+
+
+def _packed_like(E, N, K, dev):
+    return (torch.empty((E, N // 16, K // 64, 16, 32), dtype=torch.uint8, device=dev),
+            torch.empty((E, N // 16, K // 64, 16, 4), dtype=torch.uint8, device=dev))
+
+
+def nvfp4_qdq_weights(w, want_qdq=True, want_packed=True) -> QdqWeights:
+    """w [E][N][K] bf16 -> QdqWeights: row-major codes [E][N][K/2] and block
+    scales [E][N][K/16], g [E], the bf16 fake-quantized weight (want_qdq),
+    and the packed copy the grouped GEMMs take (want_packed)."""
     L = _load()
     _need(w, torch.bfloat16, "w")
     E, N, K = w.shape
     dev = w.device
-    codes = torch.empty((E, N // 16, K // 64, 16, 32), dtype=torch.uint8, device=dev)
-    scales = torch.empty((E, N // 16, K // 64, 16, 4), dtype=torch.uint8, device=dev)
+    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((E, N, K // 16), dtype=torch.uint8, device=dev)
     g_w = torch.empty(E, dtype=torch.float32, device=dev)
     w_qdq = torch.empty_like(w) if want_qdq else None
+    pc, ps = _packed_like(E, N, K, dev) if want_packed else (None, None)
     ws = _ws(L.nvfp4_qdq_weights_workspace_size(E), dev)
     _check(L.nvfp4_qdq_weights(_ptr(w), E, N, K, _ptr(codes), _ptr(scales), _ptr(g_w),
-                               _ptr(w_qdq), _ptr(ws), ws.numel(), _stream(dev)),
+                               _ptr(w_qdq), _ptr(pc), _ptr(ps), _ptr(ws), ws.numel(),
+                               _stream(dev)),
            "nvfp4_qdq_weights")
-    return codes, scales, g_w, w_qdq
+    return QdqWeights(codes, scales, g_w, w_qdq, pc, ps)
+
+
+def nvfp4_e2m1_encode_f32(v):
+    """E2M1 codes (one per byte) of float32 values v with unit scale: the
+    element conversion of every quantizer in the library."""
+    L = _load()
+    _need(v, torch.float32, "v")
+    codes = torch.empty(v.shape, dtype=torch.uint8, device=v.device)
+    _check(L.nvfp4_e2m1_encode_f32(_ptr(v), v.numel(), _ptr(codes), _stream(v.device)),
+           "nvfp4_e2m1_encode_f32")
+    return codes
+
+
+def nvfp4_pack_weights(codes, scales):
+    """Row-major codes [E][N][K/2] and scales [E][N][K/16] (u8) -> the
+    grouped GEMMs' packed copy (packed_codes, packed_scales)."""
+    L = _load()
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.uint8, "scales")
+    E, N, Kh = codes.shape
+    K = 2 * Kh
+    if tuple(scales.shape) != (E, N, K // 16):
+        raise NvfpError("scales must be [E][N][K/16]")
+    pc, ps = _packed_like(E, N, K, codes.device)
+    _check(L.nvfp4_pack_weights(_ptr(codes), _ptr(scales), E, N, K, _ptr(pc), _ptr(ps),
+                                _stream(codes.device)), "nvfp4_pack_weights")
+    return pc, ps
 
 
 def nvfp4_quantize_act(x, glu=False, want_score=True):

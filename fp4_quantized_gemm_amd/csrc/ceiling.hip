@@ -1,0 +1,134 @@
+// Ceiling microbenchmarks for the measurement harness: the sustained rate of
+// the matrix-core instruction families the NVFP4 path and its FP8 baseline
+// can run on, and the sustained HBM read rate, measured on the chip itself
+// rather than taken from the data sheet.  Not part of the method.
+#include "device.h"
+#include "runtime.h"
+#include "nvfp4rac_bench.h"
+
+namespace nvfp4 {
+
+typedef _Float16 f16x8c_t __attribute__((ext_vector_type(8)));
+typedef float f32x16c_t __attribute__((ext_vector_type(16)));
+typedef int i32x8c_t __attribute__((ext_vector_type(8)));
+
+// Each wave runs `iters` rounds of four independent 32x32 MFMAs (so the
+// matrix pipe never waits on its own result) and writes one float per lane,
+// which keeps the chain live.  Operands are small constants: the
+// accumulators grow linearly and stay finite.
+template <int KIND>
+__global__ void __launch_bounds__(256)
+k_ceiling_mfma(int64_t iters, float* __restrict__ out) {
+  f32x16c_t acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+  const uint32_t lane = threadIdx.x & 63;
+  if constexpr (KIND == 0 || KIND == 1) {
+    // f16 / bf16 values near 1/64 (f16 0x2400, bf16 0x3C80), varied by lane
+    const uint32_t h = KIND == 0 ? 0x2400u + (lane & 7) : 0x3C80u + (lane & 7);
+    const u32x4 a = u32x4{h | (h << 16), h | (h << 16), h | (h << 16), h | (h << 16)};
+    for (int64_t i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (KIND == 0)
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8c_t, a),
+                                                          __builtin_bit_cast(f16x8c_t, a), acc[j],
+                                                          0, 0, 0);
+        else
+          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                           __builtin_bit_cast(bf16x8, a), acc[j],
+                                                           0, 0, 0);
+      }
+    }
+  } else {
+    // E4M3 0x20 (2^-4) for FP8, E2M1 0x2 (1.0) nibbles for FP4; unit E8M0
+    // block scales (127)
+    const int v = KIND == 2 ? (int)(0x20202020u + (lane & 3)) : (int)(0x22222222u);
+    i32x8c_t a;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a[q] = v;
+    for (int64_t i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, a, acc[j], KIND == 2 ? 0 : 4,
+                                                                 KIND == 2 ? 0 : 4, 0, 127, 0, 127);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[j][r];
+  out[blockIdx.x * 256LL + threadIdx.x] = s;
+}
+
+// Streaming read of `n16` 16-byte chunks, four loads in flight per thread;
+// the xor of everything read is written only if it equals a value no input
+// here produces, so the loads stay live and nothing is written.
+__global__ void __launch_bounds__(256)
+k_ceiling_read(const uint4* __restrict__ src, int64_t n16, uint32_t* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = blockIdx.x * 256LL + threadIdx.x;
+  uint32_t x = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = src[i];
+    x ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (x == 0x9E3779B9u) out[0] = x;
+}
+
+}  // namespace nvfp4
+
+using namespace nvfp4;
+
+extern "C" {
+
+double nvfp4_ceiling_mfma_flops(int kind) {
+  switch (kind) {
+    case NVFP4_CEIL_F16:
+    case NVFP4_CEIL_BF16: return 2.0 * 32 * 32 * 16;
+    case NVFP4_CEIL_FP8:
+    case NVFP4_CEIL_FP4: return 2.0 * 32 * 32 * 64;
+    default: return 0.0;
+  }
+}
+
+int nvfp4_ceiling_mfma(int kind, int64_t iters, int64_t workgroups, float* out, void* stream) {
+  NV_REQUIRE(kind >= NVFP4_CEIL_F16 && kind <= NVFP4_CEIL_FP4, NVFP4_ERR_SHAPE,
+             "nvfp4_ceiling_mfma: unknown kind %d", kind);
+  NV_REQUIRE(iters >= 1 && workgroups >= 1 && workgroups <= (1LL << 20), NVFP4_ERR_SHAPE,
+             "nvfp4_ceiling_mfma: need iters >= 1, 1 <= workgroups <= 2^20");
+  NV_REQUIRE(out != nullptr, NVFP4_ERR_NULL, "nvfp4_ceiling_mfma: out is required");
+  NV_REQUIRE(aligned(out, 4), NVFP4_ERR_ALIGN, "nvfp4_ceiling_mfma: misaligned out");
+  hipStream_t s = as_stream(stream);
+  const unsigned g = (unsigned)workgroups;
+  switch (kind) {
+    case NVFP4_CEIL_F16: k_ceiling_mfma<0><<<g, 256, 0, s>>>(iters, out); break;
+    case NVFP4_CEIL_BF16: k_ceiling_mfma<1><<<g, 256, 0, s>>>(iters, out); break;
+    case NVFP4_CEIL_FP8: k_ceiling_mfma<2><<<g, 256, 0, s>>>(iters, out); break;
+    default: k_ceiling_mfma<3><<<g, 256, 0, s>>>(iters, out); break;
+  }
+  return check_launch("nvfp4_ceiling_mfma");
+}
+
+int nvfp4_ceiling_read(const void* src, int64_t bytes, uint32_t* out, void* stream) {
+  NV_REQUIRE(bytes >= 16 && bytes % 16 == 0, NVFP4_ERR_SHAPE,
+             "nvfp4_ceiling_read: bytes must be a positive multiple of 16");
+  NV_REQUIRE(src && out, NVFP4_ERR_NULL, "nvfp4_ceiling_read: missing pointer");
+  NV_REQUIRE(aligned(src, 16) && aligned(out, 4), NVFP4_ERR_ALIGN,
+             "nvfp4_ceiling_read: misaligned pointer");
+  const int64_t n16 = bytes / 16;
+  int64_t nb = (n16 + 1023) / 1024;
+  if (nb > 8LL * num_cus()) nb = 8LL * num_cus();
+  k_ceiling_read<<<(unsigned)nb, 256, 0, as_stream(stream)>>>(
+      static_cast<const uint4*>(src), n16, out);
+  return check_launch("nvfp4_ceiling_read");
+}
+
+}  // extern "C"

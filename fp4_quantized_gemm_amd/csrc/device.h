@@ -160,6 +160,45 @@ __device__ __forceinline__ uint32_t swiglu_pair(uint32_t g2, uint32_t u2) {
   return f32_to_bf16_rne(silu_mul(g0, u0)) | (f32_to_bf16_rne(silu_mul(g1, u1)) << 16);
 }
 
+// One 16-element block (two 16-byte halves of bf16 bits) against tensor amax
+// A: the elements as float32, the E4M3 scale byte and value, and the 16
+// codes packed two per byte (element 2j in bits 3:0 of byte j).
+__device__ __forceinline__ void quant_block16(const uint4& v0, const uint4& v1, float A,
+                                              float xf[16], uint32_t& sbyte, float& s,
+                                              uint32_t pk[2]) {
+  const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  uint32_t bmax = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    xf[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+    xf[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+    bmax = max(bmax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  }
+  sbyte = 0;
+  s = 0.0f;
+  pk[0] = pk[1] = 0u;
+  if (A > 0.0f) {
+    float u = (bf16_bits_to_f32(bmax) * kE4M3Max) / A;
+    sbyte = e4m3_encode_nonneg(u);
+    s = e4m3_decode(sbyte);
+  }
+  if (s > 0.0f) {
+    const float rho = kScaleDen / (s * A);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t b = e2m1_pack2(xf[2 * i] * rho, xf[2 * i + 1] * rho);
+      pk[i >> 2] |= b << (8 * (i & 3));
+    }
+  } else {
+    // magnitude 0 everywhere; keep the signs
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t b = ((w[i] >> 12) & 0x8u) | ((w[i] >> 24) & 0x80u);
+      pk[i >> 2] |= b << (8 * (i & 3));
+    }
+  }
+}
+
 __device__ __forceinline__ int frexp_exponent(float a) {
   return (int)((__float_as_uint(a) >> 23) & 0xFFu) - 126;   // a normal and > 0
 }

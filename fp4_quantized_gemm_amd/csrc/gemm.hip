@@ -21,6 +21,7 @@
 // the dot products unchanged.
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "device.h"
@@ -1630,10 +1631,10 @@ static int gemm_rac(bool per_expert, bool glu, uint32_t* h_amax, const uint8_t* 
                  (M_total == 0 || (a_codes && a_scales && y)) && (k == 0 || (R_S && S)),
              NVFP4_ERR_NULL, "grouped_w4a4_gemm_rac: missing pointer");
   NV_REQUIRE(aligned(a_codes, 16) && aligned(w_codes, 16) && aligned(a_scales, 8) &&
-                 aligned(w_scales, 8) && aligned(ws, 16) && aligned(y, 2) && aligned(R_S, 2),
+                 aligned(w_scales, 8) && aligned(ws, 16) && aligned(y, 16) && aligned(R_S, 16),
              NVFP4_ERR_ALIGN, "grouped_w4a4_gemm_rac: misaligned pointer");
-  NV_REQUIRE(ws_bytes >= img_offset(E), NVFP4_ERR_WORKSPACE,
-             "grouped_w4a4_gemm_rac: workspace too small");
+  NV_REQUIRE(ws_bytes >= grouped_w4a4_gemm_rac_workspace_size(E, M_src, M_total, N, K, k),
+             NVFP4_ERR_WORKSPACE, "grouped_w4a4_gemm_rac: workspace too small");
   if (M_total == 0) return ok();
   hipStream_t s = as_stream(stream);
   int32_t* prefix = static_cast<int32_t*>(ws);
@@ -1694,17 +1695,22 @@ static int gemm_rac(bool per_expert, bool glu, uint32_t* h_amax, const uint8_t* 
     const int64_t n_blocks = (N + dec::ROWS - 1) / dec::ROWS;
     const int wsrow = k > 0 ? (int)(((k + 31) & ~31) * 2 + 16) : 0;
     const size_t lds = (size_t)kDecTokBytes + (size_t)dec::ROWS * wsrow;
-    // dynamic LDS above 64 KB needs the kernel's limit raised (once per device)
+    // dynamic LDS above 64 KB needs the kernel's limit raised (once per
+    // device; the cache is shared by all calling threads)
+    static std::mutex dec_mu;
     static int dec_lds_limit[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
       return fail(NVFP4_ERR_HIP, "grouped_w4a4_gemm_rac: hipGetDevice failed");
-    if ((size_t)dec_lds_limit[dev] < lds) {
-      const int want = (int)kDecTokBytes + dec::ROWS * (dec::KMAX * 2 + 16);
-      if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_decode),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, want) != hipSuccess)
-        return fail(NVFP4_ERR_HIP, "grouped_w4a4_gemm_rac: cannot raise the LDS limit");
-      dec_lds_limit[dev] = want;
+    {
+      std::lock_guard<std::mutex> lock(dec_mu);
+      if ((size_t)dec_lds_limit[dev] < lds) {
+        const int want = (int)kDecTokBytes + dec::ROWS * (dec::KMAX * 2 + 16);
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_decode),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, want) != hipSuccess)
+          return fail(NVFP4_ERR_HIP, "grouped_w4a4_gemm_rac: cannot raise the LDS limit");
+        dec_lds_limit[dev] = want;
+      }
     }
     // one round of workgroups: each takes bpw consecutive row blocks of its
     // expert (two workgroups per CU when the LDS allows it)

@@ -1,19 +1,13 @@
-// NVFP4 quantizers: online activation quantization (with the per-channel
-// residual statistic used to pick compensation channels) and the weight QDQ
-// path shared by trainer and rollout.
+// NVFP4 quantize-dequantize paths: the weight QDQ shared by trainer and
+// rollout (weights go through one quantize-dequantize path on both sides:
+// arXiv abstract; gist.science technical summary §2.1, §2.2 A), its packed
+// copy for the grouped GEMMs, the second-pass QDQ of the compensated residual
+// (summary §2.2 B), the E2M1 conversion itself, and the FP8 (E4M3) baseline's
+// quantizer.  The online activation quantizer is in actquant.hip.
 //
-// QUADS (arXiv abstract; gist.science technical summary §2.1, §2.2 A-B):
-// activations are recomputed and quantized to E2M1 every forward; weights go
-// through one quantize-dequantize path on both sides; the channels with the
-// largest activation residual get compensated.
-//
-// Pass structure (both HBM-bound):
-//   1. amax: per-tensor max |x| (integer max over bf16 bit patterns, so the
-//      result is exact and order-free); for the SwiGLU input it also forms
-//      h = bf16(silu(gate) * up) and writes h once.
-//   2. quantize: one thread per 16-element block; block max -> E4M3 scale,
-//      codes via the hardware E2M1 conversion, residual and fixed-point
-//      channel score in the same pass.
+// Pass structure (HBM-bound): an amax pass (integer max over bf16 bit
+// patterns, exact and order-free), then a block quantizer: block max -> E4M3
+// scale, codes via the hardware E2M1 conversion.
 #include <cstdlib>
 
 #include "device.h"
@@ -43,28 +37,6 @@ static RowTiling row_tiling(int64_t chunks) {
   return t;
 }
 
-// ---------------------------------------------------------------------------
-// Pass 1a: amax over one or more [rows][K] bf16 tensors stacked by row
-// (tensor id = blockIdx.z).  Chunks of 8 elements (one 16-byte load).
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256)
-k_amax(const uint16_t* __restrict__ x, int64_t rows, int64_t ldx, int64_t tensor_stride,
-       int chunks, int rows_per_iter, uint32_t* __restrict__ amax) {
-  const int tid = threadIdx.x;
-  const int cw = chunks < 256 ? chunks : 256;
-  const int rsub = tid / cw;
-  const int c = blockIdx.y * 256 + tid % cw;
-  const uint16_t* xt = x + (int64_t)blockIdx.z * tensor_stride;
-  uint32_t m = 0;
-  if (rsub < rows_per_iter && c < chunks) {
-    for (int64_t r = (int64_t)blockIdx.x * rows_per_iter + rsub; r < rows;
-         r += (int64_t)gridDim.x * rows_per_iter) {
-      m = max(m, absmax_bf16x8(*reinterpret_cast<const uint4*>(xt + r * ldx + (int64_t)c * 8)));
-    }
-  }
-  block_atomic_max<256>(m, amax + blockIdx.z);
-}
-
 // Contiguous tensors: flat loop, four independent 16-byte loads in flight
 // per thread (tensor t = blockIdx.y, n8 chunks of 8 elements each).
 
@@ -83,76 +55,6 @@ k_amax_flat(const uint16_t* __restrict__ x, int64_t n8, int64_t tensor_stride,
   block_atomic_max<256>(m, amax + blockIdx.y);
 }
 
-// ---------------------------------------------------------------------------
-// Pass 1b: h = bf16(silu(gate) * up) from y = [gate | up] ([M][2I], row stride
-// ldy); writes h [M][I] and its amax.  silu(g) = g / (1 + exp(-g)), float32.
-// ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256)
-k_swiglu_amax(const uint16_t* __restrict__ y, int64_t rows, int64_t ldy, int64_t inter,
-              int chunks, int rows_per_iter, uint16_t* __restrict__ h,
-              uint32_t* __restrict__ amax) {
-  const int tid = threadIdx.x;
-  const int cw = chunks < 256 ? chunks : 256;
-  const int rsub = tid / cw;
-  const int c = blockIdx.y * 256 + tid % cw;
-  uint32_t m = 0;
-  if (rsub < rows_per_iter && c < chunks) {
-    for (int64_t r = (int64_t)blockIdx.x * rows_per_iter + rsub; r < rows;
-         r += (int64_t)gridDim.x * rows_per_iter) {
-      const uint16_t* yr = y + r * ldy + (int64_t)c * 8;
-      uint4 g = *reinterpret_cast<const uint4*>(yr);
-      uint4 u = *reinterpret_cast<const uint4*>(yr + inter);
-      uint4 o;
-      o.x = swiglu_pair(g.x, u.x);
-      o.y = swiglu_pair(g.y, u.y);
-      o.z = swiglu_pair(g.z, u.z);
-      o.w = swiglu_pair(g.w, u.w);
-      *reinterpret_cast<uint4*>(h + r * inter + (int64_t)c * 8) = o;
-      m = max(m, absmax_bf16x8(o));
-    }
-  }
-  block_atomic_max<256>(m, amax);
-}
-
-// One 16-element block (two 16-byte halves of bf16 bits) against tensor amax
-// A: the elements as float32, the E4M3 scale byte and value, and the 16
-// codes packed two per byte (element 2j in bits 3:0 of byte j).
-__device__ __forceinline__ void quant_block16(const uint4& v0, const uint4& v1, float A,
-                                              float xf[16], uint32_t& sbyte, float& s,
-                                              uint32_t pk[2]) {
-  const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-  uint32_t bmax = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    xf[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
-    xf[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
-    bmax = max(bmax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
-  }
-  sbyte = 0;
-  s = 0.0f;
-  pk[0] = pk[1] = 0u;
-  if (A > 0.0f) {
-    float u = (bf16_bits_to_f32(bmax) * kE4M3Max) / A;
-    sbyte = e4m3_encode_nonneg(u);
-    s = e4m3_decode(sbyte);
-  }
-  if (s > 0.0f) {
-    const float rho = kScaleDen / (s * A);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t b = e2m1_pack2(xf[2 * i] * rho, xf[2 * i + 1] * rho);
-      pk[i >> 2] |= b << (8 * (i & 3));
-    }
-  } else {
-    // magnitude 0 everywhere; keep the signs
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t b = ((w[i] >> 12) & 0x8u) | ((w[i] >> 24) & 0x80u);
-      pk[i >> 2] |= b << (8 * (i & 3));
-    }
-  }
-}
-
 // The fake-quantized value of a block's 16 codes, bf16(fp32(q * s) * g), sign
 // from the code bit, as 8 dwords of bf16 pairs.
 __device__ __forceinline__ void fake_quant16(const uint32_t pk[2], float s, float g,
@@ -169,135 +71,44 @@ __device__ __forceinline__ void fake_quant16(const uint32_t pk[2], float s, floa
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2: block quantizer.  One thread per 16-element block; tensors stacked
-// by row (blockIdx.z), each with its own amax (bf16 bits) and tensor scale.
+// Block quantizer of the second-pass residual QDQ: one thread per 16-element
+// block of a [rows][K] tensor with amax given as bf16 bits.
 //
 //   A = amax, g = fp32(A / 2688)
 //   s = e4m3( fp32(blockmax * 448) / A )            (fp32 divide, RNE)
 //   rho = fp32(2688 / fp32(s * A)),  v = fp32(x * rho),  code = e2m1(v)
 //   s == 0: every magnitude 0.   Sign of a code = sign of x.
-//   residual r = bf16(fma(-(q*s), g, x))            (one rounding to fp32)
-//   score[j] += floor(|r| * 2^(31 - E_A))           (exact, <= 2^31)
-//   w_qdq = bf16(fp32(q*s) * g)                     (trainer fake-quant)
+//   out_qdq = bf16(fp32(q*s) * g)                   (the fake-quantized value)
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
-k_quantize(const uint16_t* __restrict__ x, int64_t rows, int64_t ldx, int64_t K,
-           int64_t tensor_stride, int ntensors, int blocks, int rows_per_iter,
-           const uint32_t* __restrict__ amax, uint8_t* __restrict__ codes,
+k_quantize(const uint16_t* __restrict__ x, int64_t rows, int64_t ldx, int64_t K, int blocks,
+           int rows_per_iter, const uint32_t* __restrict__ amax, uint8_t* __restrict__ codes,
            uint8_t* __restrict__ scales, float* __restrict__ g_out,
-           uint64_t* __restrict__ partial, uint16_t* __restrict__ w_qdq) {
-  // partial: [gridDim.x][K] per-workgroup channel sums (or NULL: no scores)
-  extern __shared__ uint64_t red[];               // 256 * 16 entries when rows_per_iter > 1
-  uint64_t* score = partial;
+           uint16_t* __restrict__ out_qdq) {
   const int tid = threadIdx.x;
-  const int t = blockIdx.z;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0)
-    g_out[t] = bf16_bits_to_f32(amax[t]) / kScaleDen;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *g_out = bf16_bits_to_f32(*amax) / kScaleDen;
   const int cw = blocks < 256 ? blocks : 256;
   const int rsub = tid / cw;
   const int c = blockIdx.y * 256 + tid % cw;
-  const bool active = rsub < rows_per_iter && c < blocks;
-
-  const float A = bf16_bits_to_f32(amax[t]);
+  if (rsub >= rows_per_iter || c >= blocks) return;
+  const float A = bf16_bits_to_f32(*amax);
   const float g = A / kScaleDen;
-  const int ea = A > 0.0f ? frexp_exponent(A) : 0;
-  const uint16_t* xt = x + (int64_t)t * tensor_stride;
-  const int64_t row0 = (int64_t)t * rows;     // output row offset of this tensor
-  uint64_t acc[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0;
-
-  const int64_t rstep = (int64_t)gridDim.x * rows_per_iter;
-  uint4 n0 = make_uint4(0, 0, 0, 0), n1 = n0;
-  int64_t r = (int64_t)blockIdx.x * rows_per_iter + rsub;
-  if (active && r < rows) {
-    const uint16_t* xr = xt + r * ldx + (int64_t)c * 16;
-    n0 = *reinterpret_cast<const uint4*>(xr);
-    n1 = *reinterpret_cast<const uint4*>(xr + 8);
-  }
-  for (; active && r < rows; r += rstep) {
-    // the next row's loads are issued before this row's arithmetic
-    const uint4 v0 = n0, v1 = n1;
-    if (r + rstep < rows) {
-      const uint16_t* xn = xt + (r + rstep) * ldx + (int64_t)c * 16;
-      n0 = *reinterpret_cast<const uint4*>(xn);
-      n1 = *reinterpret_cast<const uint4*>(xn + 8);
-    }
+  for (int64_t r = (int64_t)blockIdx.x * rows_per_iter + rsub; r < rows;
+       r += (int64_t)gridDim.x * rows_per_iter) {
+    const uint16_t* xr = x + r * ldx + (int64_t)c * 16;
+    const uint4 v0 = *reinterpret_cast<const uint4*>(xr);
+    const uint4 v1 = *reinterpret_cast<const uint4*>(xr + 8);
     float xf[16];
     uint32_t sbyte, pk[2];
     float s;
     quant_block16(v0, v1, A, xf, sbyte, s, pk);
-    const int64_t orow = row0 + r;
-    *reinterpret_cast<uint2*>(codes + orow * (K / 2) + (int64_t)c * 8) = make_uint2(pk[0], pk[1]);
-    scales[orow * (K / 16) + c] = (uint8_t)sbyte;
-
-    if (score != nullptr || w_qdq != nullptr) {
-      float qs[16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x2 a0 = e2m1_unpack2<0>(pk[i >> 1] >> (16 * (i & 1)));
-        f32x2 a1 = e2m1_unpack2<1>(pk[i >> 1] >> (16 * (i & 1)));
-        qs[4 * i + 0] = a0.x * s;
-        qs[4 * i + 1] = a0.y * s;
-        qs[4 * i + 2] = a1.x * s;
-        qs[4 * i + 3] = a1.y * s;
-      }
-      if (score != nullptr && A > 0.0f) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float rr = __builtin_fmaf(-qs[i], g, xf[i]);
-          float rb = bf16_bits_to_f32(f32_to_bf16_rne(rr));
-          acc[i] += (uint64_t)(uint32_t)__builtin_ldexpf(__builtin_fabsf(rb), 31 - ea);
-        }
-      }
-      if (w_qdq != nullptr) {
-        uint32_t o[8];
-        fake_quant16(pk, s, g, o);
-        uint16_t* wo = w_qdq + orow * K + (int64_t)c * 16;
-        *reinterpret_cast<uint4*>(wo) = make_uint4(o[0], o[1], o[2], o[3]);
-        *reinterpret_cast<uint4*>(wo + 8) = make_uint4(o[4], o[5], o[6], o[7]);
-      }
-    }
-  }
-  if (partial == nullptr) return;
-  // sum the rows_per_iter row groups of this workgroup, then one write per
-  // channel: exact integer sums, so any grouping gives the same bits
-  if (rows_per_iter > 1) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) red[tid * 16 + i] = acc[i];
-    __syncthreads();
-    if (rsub == 0 && active) {
-      for (int q = 1; q < rows_per_iter; ++q)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i] += red[(q * cw + tid) * 16 + i];
-    }
-  }
-  if (rsub == 0 && active) {
-    uint64_t* dst = partial + (int64_t)blockIdx.x * K + (int64_t)c * 16;
-#pragma unroll
-    for (int i = 0; i < 16; i += 2)
-      *reinterpret_cast<ulonglong2*>(dst + i) = make_ulonglong2(acc[i], acc[i + 1]);
-  }
-}
-
-// score[j] += sum over workgroups of partial[w][j]: a block sums a tile of
-// 64 channels x 64 partial rows (four row groups, LDS combine), then one
-// 64-bit integer atomic per channel.  Integer sums: any order, same bits.
-__global__ void __launch_bounds__(256)
-k_score_reduce(const uint64_t* __restrict__ partial, int nparts, int64_t K,
-               uint64_t* __restrict__ score) {
-  __shared__ uint64_t red4[4][64];
-  const int ch = threadIdx.x & 63, pg = threadIdx.x >> 6;
-  const int64_t j = blockIdx.x * 64LL + ch;
-  const int p0 = blockIdx.y * 64;
-  uint64_t s = 0;
-  if (j < K)
-    for (int q = pg; q < 64 && p0 + q < nparts; q += 4) s += partial[(int64_t)(p0 + q) * K + j];
-  red4[pg][ch] = s;
-  __syncthreads();
-  if (pg == 0 && j < K) {
-    s = red4[0][ch] + red4[1][ch] + red4[2][ch] + red4[3][ch];
-    if (s) atomicAdd(reinterpret_cast<unsigned long long*>(score + j), (unsigned long long)s);
+    *reinterpret_cast<uint2*>(codes + r * (K / 2) + (int64_t)c * 8) = make_uint2(pk[0], pk[1]);
+    scales[r * (K / 16) + c] = (uint8_t)sbyte;
+    uint32_t o[8];
+    fake_quant16(pk, s, g, o);
+    uint16_t* wo = out_qdq + r * K + (int64_t)c * 16;
+    *reinterpret_cast<uint4*>(wo) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4*>(wo + 8) = make_uint4(o[4], o[5], o[6], o[7]);
   }
 }
 
@@ -316,7 +127,8 @@ constexpr int kQdqRound = 4;
 __global__ void __launch_bounds__(256)
 k_qdq_slices(const uint16_t* __restrict__ w, int64_t N, int64_t K, int E,
              const uint32_t* __restrict__ amax, uint8_t* __restrict__ codes,
-             uint8_t* __restrict__ scales, float* __restrict__ g_w, uint16_t* __restrict__ w_qdq) {
+             uint8_t* __restrict__ scales, float* __restrict__ g_w, uint16_t* __restrict__ w_qdq,
+             uint8_t* __restrict__ pcodes, uint8_t* __restrict__ pscales) {
   const int tid = threadIdx.x;
   const int e = E - 1 - (int)blockIdx.y;
   const int64_t row0 = (int64_t)blockIdx.x * 16;
@@ -326,13 +138,14 @@ k_qdq_slices(const uint16_t* __restrict__ w, int64_t N, int64_t K, int E,
   const float g = A / kScaleDen;
   if (blockIdx.x == 0 && tid == 0) g_w[e] = g;
   // block b of the slice is block c = 4 t + (b % 4) of row (b / 4) % 16,
-  // t = b / 64: a wave covers one 16-row x 64-column tile, so its code
-  // stores are one contiguous 512-byte tile, its scale stores one 64-byte
-  // tile, and its loads whole 128-byte row pieces.  16 * KB = K is a
-  // multiple of 64 (K % 64 == 0), so a wave's blocks are all in range or all
-  // out, and lanes 4j..4j+3 hold blocks 4t..4t+3 of one row
+  // t = b / 64: a wave covers one 16-row x 64-column tile, so its loads are
+  // whole 128-byte row pieces, its row-major code stores 32 bytes per row,
+  // and (packed copy) its code stores one contiguous 512-byte tile and its
+  // scale stores one 64-byte tile.  16 * KB = K is a multiple of 64
+  // (K % 64 == 0), so a wave's blocks are all in range or all out, and lanes
+  // 4j..4j+3 hold blocks 4t..4t+3 of one row
   const int64_t nblk = 16 * KB;
-  uint8_t* sc_e = scales + (int64_t)e * N * KB;
+  uint8_t* psc_e = pscales ? pscales + (int64_t)e * N * KB : nullptr;
   for (int64_t b0 = 0; b0 < nblk; b0 += 256 * kQdqRound) {
     uint4 c0[kQdqRound], c1[kQdqRound];
 #pragma unroll
@@ -354,11 +167,15 @@ k_qdq_slices(const uint16_t* __restrict__ w, int64_t N, int64_t K, int E,
       uint32_t sbyte, pk[2];
       quant_block16(c0[u], c1[u], A, xf, sbyte, s, pk);
       const int64_t orow = (int64_t)e * N + row0 + r;
-      *reinterpret_cast<uint2*>(codes + (int64_t)e * N * (K / 2) + wcode_offset(row0 + r, 16 * c, K)) =
-          make_uint2(pk[0], pk[1]);
+      *reinterpret_cast<uint2*>(codes + orow * (K / 2) + c * 8) = make_uint2(pk[0], pk[1]);
       const uint32_t s4 = sbyte | (__shfl_down(sbyte, 1) << 8) | (__shfl_down(sbyte, 2) << 16) |
                           (__shfl_down(sbyte, 3) << 24);
-      if ((c & 3) == 0) *reinterpret_cast<uint32_t*>(sc_e + wscale_offset(row0 + r, c, K)) = s4;
+      if ((c & 3) == 0) *reinterpret_cast<uint32_t*>(scales + orow * KB + c) = s4;
+      if (pcodes != nullptr) {
+        *reinterpret_cast<uint2*>(pcodes + (int64_t)e * N * (K / 2) + wcode_offset(row0 + r, 16 * c, K)) =
+            make_uint2(pk[0], pk[1]);
+        if ((c & 3) == 0) *reinterpret_cast<uint32_t*>(psc_e + wscale_offset(row0 + r, c, K)) = s4;
+      }
       if (w_qdq != nullptr) {
         uint32_t o[8];
         fake_quant16(pk, s, g, o);
@@ -370,6 +187,35 @@ k_qdq_slices(const uint16_t* __restrict__ w, int64_t N, int64_t K, int E,
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Row-major NVFP4 weights -> the grouped GEMMs' packed copy: codes in
+// 512-byte tiles of 16 rows x 64 columns ([E][N/16][K/64][16][32]) and block
+// scales in 64-byte tiles of the same rows and columns ([..][16][4]).  A
+// permutation of bytes: thread q moves the 16-byte code chunk q of the packed
+// codes, and (q < the number of scale dwords) the scale dword q.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+k_pack_weights(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t E,
+               int64_t N, int64_t K, uint8_t* __restrict__ pcodes, uint8_t* __restrict__ pscales) {
+  const int64_t kt = K / 64, nt = N / 16;
+  const int64_t n_chunks = E * N * K / 32;        // 16-byte code chunks
+  const int64_t n_words = E * N * K / 64;         // scale dwords
+  for (int64_t q = blockIdx.x * 256LL + threadIdx.x; q < n_chunks; q += (int64_t)gridDim.x * 256) {
+    const int64_t tile = q >> 5, within = q & 31;
+    const int64_t kb = tile % kt, nb = (tile / kt) % nt, e = tile / (kt * nt);
+    const int64_t row = e * N + nb * 16 + (within >> 1);
+    const uint4 v = *reinterpret_cast<const uint4*>(codes + row * (K / 2) + kb * 32 + (within & 1) * 16);
+    *reinterpret_cast<uint4*>(pcodes + q * 16) = v;
+    if (q < n_words) {
+      const int64_t st = q >> 4, r = q & 15;
+      const int64_t skb = st % kt, snb = (st / kt) % nt, se = st / (kt * nt);
+      const int64_t srow = se * N + snb * 16 + r;
+      reinterpret_cast<uint32_t*>(pscales)[q] =
+          *reinterpret_cast<const uint32_t*>(scales + srow * (K / 16) + skb * 4);
+    }
+  }
+}
 
 // ---------------------------------------------------------------------------
 // FP8 (E4M3) quantization with one float32 scale per tensor (tensor t =
@@ -401,6 +247,19 @@ k_fp8_quantize(const uint16_t* __restrict__ x, int64_t n8, int64_t tensor_stride
   }
 }
 
+// E2M1 codes of float32 values with unit scale, one code per output byte:
+// the conversion every quantizer here applies to x * rho (e2m1_pack2).
+__global__ void __launch_bounds__(256)
+k_e2m1_encode(const float* __restrict__ v, int64_t n, uint8_t* __restrict__ codes) {
+  for (int64_t i = blockIdx.x * 256LL + threadIdx.x; 2 * i < n; i += (int64_t)gridDim.x * 256) {
+    const float a = v[2 * i];
+    const float b = 2 * i + 1 < n ? v[2 * i + 1] : 0.0f;
+    const uint32_t pk = e2m1_pack2(a, b);
+    codes[2 * i] = (uint8_t)(pk & 0xFu);
+    if (2 * i + 1 < n) codes[2 * i + 1] = (uint8_t)(pk >> 4);
+  }
+}
+
 static unsigned grid_rows(int64_t rows, int rows_per_iter, int64_t cap) {
   int64_t need = (rows + rows_per_iter - 1) / rows_per_iter;
   if (need < 1) need = 1;
@@ -413,107 +272,8 @@ using namespace nvfp4;
 
 extern "C" {
 
-// at most 4 workgroups per CU: each writes one row of channel-score
-// partials ([grid][K] u64), and at 8 per CU those partials were half the
-// bytes of the activation itself (4 per CU measured 6-7% faster; 2 per CU
-// slower on the h of the large-prefill block)
-static int quant_grid(int64_t M, int64_t K) {
-  RowTiling t16 = row_tiling(K / 16);
-  return (int)grid_rows(M, t16.rows_per_iter, 4LL * num_cus());
-}
-
-size_t nvfp4_quantize_act_workspace_size(int64_t M, int64_t K) {
-  if (M < 0 || K < 32) return 256;
-  return 256 + round_up((size_t)quant_grid(M, K) * (size_t)K * sizeof(uint64_t), 256);
-}
-
 size_t nvfp4_qdq_weights_workspace_size(int64_t E) {
   return round_up((size_t)(E > 0 ? E : 1) * sizeof(uint32_t), 256);
-}
-
-// the quantize pass (and the channel-score reduction) once the amax is known
-static void quantize_pass(const uint16_t* src, int64_t M, int64_t K, int64_t ld,
-                          const uint32_t* amax, uint8_t* codes, uint8_t* scales, float* g_x,
-                          uint64_t* score, uint64_t* partial, hipStream_t s) {
-  RowTiling t16 = row_tiling(K / 16);
-  const int nq = quant_grid(M, K);
-  dim3 grid(nq, t16.col_groups, 1);
-  const size_t red_bytes = (score && t16.rows_per_iter > 1) ? 256 * 16 * sizeof(uint64_t) : 0;
-  k_quantize<<<grid, 256, red_bytes, s>>>(src, M, ld, K, 0, 1, t16.chunks, t16.rows_per_iter,
-                                          amax, codes, scales, g_x, score ? partial : nullptr,
-                                          nullptr);
-  if (score) {
-    fill_u64(score, K, 0ull, s);
-    k_score_reduce<<<dim3((unsigned)((K + 63) / 64), (unsigned)((nq + 63) / 64)), 256, 0, s>>>(
-        partial, nq, K, score);
-  }
-}
-
-int nvfp4_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, int glu,
-                       uint8_t* codes, uint8_t* scales, float* g_x, uint64_t* score,
-                       void* x_used, void* ws, size_t ws_bytes, void* stream) {
-  NV_REQUIRE(g_x && ws, NVFP4_ERR_NULL, "nvfp4_quantize_act: g_x and ws are required");
-  NV_REQUIRE(M >= 0 && K >= 32 && K % 32 == 0, NVFP4_ERR_SHAPE,
-             "nvfp4_quantize_act: need M >= 0, K >= 32, K %% 32 == 0 (M=%lld K=%lld)",
-             (long long)M, (long long)K);
-  NV_REQUIRE(glu == 0 || glu == 1, NVFP4_ERR_SHAPE, "nvfp4_quantize_act: glu must be 0 or 1");
-  NV_REQUIRE(ldx >= (glu ? 2 * K : K) && ldx % 8 == 0, NVFP4_ERR_SHAPE,
-             "nvfp4_quantize_act: bad ldx %lld", (long long)ldx);
-  NV_REQUIRE(M == 0 || (x && codes && scales), NVFP4_ERR_NULL,
-             "nvfp4_quantize_act: x, codes and scales are required");
-  NV_REQUIRE(!glu || x_used, NVFP4_ERR_NULL, "nvfp4_quantize_act: glu=1 needs x_used for h");
-  NV_REQUIRE(aligned(x, 16) && aligned(codes, 8) && aligned(x_used, 16) && aligned(score, 8) &&
-                 aligned(ws, 16),
-             NVFP4_ERR_ALIGN, "nvfp4_quantize_act: misaligned pointer");
-  NV_REQUIRE(ws_bytes >= nvfp4_quantize_act_workspace_size(M, K), NVFP4_ERR_WORKSPACE,
-             "nvfp4_quantize_act: workspace too small");
-  hipStream_t s = as_stream(stream);
-  uint32_t* amax = static_cast<uint32_t*>(ws);
-  uint64_t* partial = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + 256);
-  fill_u32(amax, 1, 0u, s);
-  const int cus = num_cus();
-  const uint16_t* src = static_cast<const uint16_t*>(x);
-  int64_t ld = ldx;
-  if (M > 0) {
-    RowTiling t8 = row_tiling(K / 8);
-    dim3 grid(grid_rows(M, t8.rows_per_iter, 8LL * cus), t8.col_groups, 1);
-    if (glu) {
-      k_swiglu_amax<<<grid, 256, 0, s>>>(src, M, ldx, K, t8.chunks, t8.rows_per_iter,
-                                         static_cast<uint16_t*>(x_used), amax);
-      src = static_cast<const uint16_t*>(x_used);
-      ld = K;
-    } else if (ldx == K) {
-      const int64_t n8 = M * K / 8;
-      int64_t nb = (n8 + 1023) / 1024;
-      if (nb > 8LL * cus) nb = 8LL * cus;
-      k_amax_flat<<<dim3((unsigned)(nb > 0 ? nb : 1), 1, 1), 256, 0, s>>>(src, n8, 0, amax);
-    } else {
-      k_amax<<<grid, 256, 0, s>>>(src, M, ldx, 0, t8.chunks, t8.rows_per_iter, amax);
-    }
-  }
-  quantize_pass(src, M, K, ld, amax, codes, scales, g_x, score, partial, s);
-  return check_launch("nvfp4_quantize_act");
-}
-
-int nvfp4_quantize_act_amax(const void* x, int64_t M, int64_t K, int64_t ldx,
-                            const uint32_t* amax, uint8_t* codes, uint8_t* scales, float* g_x,
-                            uint64_t* score, void* ws, size_t ws_bytes, void* stream) {
-  NV_REQUIRE(g_x && ws && amax, NVFP4_ERR_NULL,
-             "nvfp4_quantize_act_amax: g_x, amax and ws are required");
-  NV_REQUIRE(M >= 0 && K >= 32 && K % 32 == 0 && ldx >= K && ldx % 8 == 0, NVFP4_ERR_SHAPE,
-             "nvfp4_quantize_act_amax: need M >= 0, K >= 32, K %% 32 == 0, ldx >= K, "
-             "ldx %% 8 == 0 (M=%lld K=%lld)", (long long)M, (long long)K);
-  NV_REQUIRE(M == 0 || (x && codes && scales), NVFP4_ERR_NULL,
-             "nvfp4_quantize_act_amax: x, codes and scales are required");
-  NV_REQUIRE(aligned(x, 16) && aligned(codes, 8) && aligned(score, 8) && aligned(ws, 16) &&
-                 aligned(amax, 4),
-             NVFP4_ERR_ALIGN, "nvfp4_quantize_act_amax: misaligned pointer");
-  NV_REQUIRE(ws_bytes >= nvfp4_quantize_act_workspace_size(M, K), NVFP4_ERR_WORKSPACE,
-             "nvfp4_quantize_act_amax: workspace too small");
-  uint64_t* partial = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + 256);
-  quantize_pass(static_cast<const uint16_t*>(x), M, K, ldx, amax, codes, scales, g_x, score,
-                partial, as_stream(stream));
-  return check_launch("nvfp4_quantize_act_amax");
 }
 
 size_t nvfp4_qdq_residual_workspace_size(int64_t M, int64_t k) {
@@ -551,21 +311,24 @@ int nvfp4_qdq_residual(const void* r, int64_t M, int64_t k, uint8_t* codes, uint
   }
   RowTiling t16 = row_tiling(k / 16);
   dim3 grid(grid_rows(M, t16.rows_per_iter, 8LL * cus), t16.col_groups, 1);
-  k_quantize<<<grid, 256, 0, s>>>(src, M, k, k, 0, 1, t16.chunks, t16.rows_per_iter, amax, codes,
-                                  scales, g_r, nullptr, static_cast<uint16_t*>(r_qdq));
+  k_quantize<<<grid, 256, 0, s>>>(src, M, k, k, t16.chunks, t16.rows_per_iter, amax, codes, scales,
+                                  g_r, static_cast<uint16_t*>(r_qdq));
   return check_launch("nvfp4_qdq_residual");
 }
 
 int nvfp4_qdq_weights(const void* w, int64_t E, int64_t N, int64_t K, uint8_t* codes,
-                      uint8_t* scales, float* g_w, void* w_qdq, void* ws, size_t ws_bytes,
-                      void* stream) {
+                      uint8_t* scales, float* g_w, void* w_qdq, uint8_t* packed_codes,
+                      uint8_t* packed_scales, void* ws, size_t ws_bytes, void* stream) {
   NV_REQUIRE(w && codes && scales && g_w && ws, NVFP4_ERR_NULL,
              "nvfp4_qdq_weights: w, codes, scales, g_w and ws are required");
+  NV_REQUIRE((packed_codes == nullptr) == (packed_scales == nullptr), NVFP4_ERR_NULL,
+             "nvfp4_qdq_weights: give both packed outputs or neither");
   NV_REQUIRE(E >= 1 && E <= 65535 && N >= 16 && N % 16 == 0 && K >= 64 && K % 64 == 0,
              NVFP4_ERR_SHAPE,
              "nvfp4_qdq_weights: need 1 <= E <= 65535, N %% 16 == 0, K %% 64 == 0 "
              "(N=%lld K=%lld)", (long long)N, (long long)K);
-  NV_REQUIRE(aligned(w, 16) && aligned(codes, 8) && aligned(w_qdq, 16) && aligned(ws, 16),
+  NV_REQUIRE(aligned(w, 16) && aligned(codes, 8) && aligned(scales, 4) && aligned(w_qdq, 16) &&
+                 aligned(packed_codes, 16) && aligned(packed_scales, 4) && aligned(ws, 16),
              NVFP4_ERR_ALIGN, "nvfp4_qdq_weights: misaligned pointer");
   NV_REQUIRE(ws_bytes >= nvfp4_qdq_weights_workspace_size(E), NVFP4_ERR_WORKSPACE,
              "nvfp4_qdq_weights: workspace too small");
@@ -583,8 +346,38 @@ int nvfp4_qdq_weights(const void* w, int64_t E, int64_t N, int64_t K, uint8_t* c
   }
   k_qdq_slices<<<dim3((unsigned)(N / 16), (unsigned)E, 1), 256, 0, s>>>(
       static_cast<const uint16_t*>(w), N, K, (int)E, amax, codes, scales, g_w,
-      static_cast<uint16_t*>(w_qdq));
+      static_cast<uint16_t*>(w_qdq), packed_codes, packed_scales);
   return check_launch("nvfp4_qdq_weights");
+}
+
+int nvfp4_pack_weights(const uint8_t* codes, const uint8_t* scales, int64_t E, int64_t N,
+                       int64_t K, uint8_t* packed_codes, uint8_t* packed_scales, void* stream) {
+  NV_REQUIRE(codes && scales && packed_codes && packed_scales, NVFP4_ERR_NULL,
+             "nvfp4_pack_weights: missing pointer");
+  NV_REQUIRE(E >= 1 && E <= 65535 && N >= 16 && N % 16 == 0 && K >= 64 && K % 64 == 0,
+             NVFP4_ERR_SHAPE,
+             "nvfp4_pack_weights: need 1 <= E <= 65535, N %% 16 == 0, K %% 64 == 0 "
+             "(N=%lld K=%lld)", (long long)N, (long long)K);
+  NV_REQUIRE(aligned(codes, 16) && aligned(scales, 4) && aligned(packed_codes, 16) &&
+                 aligned(packed_scales, 4),
+             NVFP4_ERR_ALIGN, "nvfp4_pack_weights: misaligned pointer");
+  const int64_t n_chunks = E * N * K / 32;
+  int64_t nb = (n_chunks + 255) / 256;
+  if (nb > 16LL * num_cus()) nb = 16LL * num_cus();
+  k_pack_weights<<<(unsigned)nb, 256, 0, as_stream(stream)>>>(codes, scales, E, N, K,
+                                                             packed_codes, packed_scales);
+  return check_launch("nvfp4_pack_weights");
+}
+
+int nvfp4_e2m1_encode_f32(const float* v, int64_t n, uint8_t* codes, void* stream) {
+  NV_REQUIRE(n >= 0, NVFP4_ERR_SHAPE, "nvfp4_e2m1_encode_f32: n < 0");
+  if (n == 0) return ok();
+  NV_REQUIRE(v && codes, NVFP4_ERR_NULL, "nvfp4_e2m1_encode_f32: missing pointer");
+  NV_REQUIRE(aligned(v, 4), NVFP4_ERR_ALIGN, "nvfp4_e2m1_encode_f32: misaligned v");
+  int64_t nb = (n / 2 + 256) / 256;
+  if (nb > 16LL * num_cus()) nb = 16LL * num_cus();
+  k_e2m1_encode<<<(unsigned)nb, 256, 0, as_stream(stream)>>>(v, n, codes);
+  return check_launch("nvfp4_e2m1_encode_f32");
 }
 
 size_t fp8_quantize_workspace_size(int64_t E) {

@@ -2,9 +2,9 @@
 // (QUADS, gist.science technical summary §2.2 B: a binary mask picks the
 // channels of largest residual magnitude; their residual is added back).
 //
-//   1. k_select_topk (one workgroup): bitonic sort of (score desc, index asc)
-//      over all K channels in LDS; flag the first k; compact the flags in
-//      index order, which writes S ascending.
+//   1. k_select_topk (one workgroup): an MSB-first radix select of the k-th
+//      largest score over all K channels, then the channels above it and the
+//      lowest-index ties, compacted in index order, which writes S ascending.
 //   2. k_gather_residual: R_S[m][j] = bf16(fma(-(q*s), g, x[m][S[j]])), the
 //      same rounding as the residual behind the scores.
 //
@@ -17,7 +17,7 @@
 
 namespace nvfp4 {
 
-constexpr int kSelectMaxK = 4096;
+constexpr int kSelectMaxK = 16384;
 constexpr int kSelectThreads = 1024;
 
 __device__ __forceinline__ uint64_t wave_or_u64(uint64_t v) {
@@ -45,17 +45,17 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum) {
   return base + incl - v;
 }
 
-// Top-k of up to 4096 (score desc, index asc) keys by one workgroup (one
-// score vector per workgroup: several for the per-expert selection).
-// Thread t holds channels 4t .. 4t+3.  An MSB-first radix select finds the
+// Top-k of up to 1024 * CPT (score desc, index asc) keys by one workgroup
+// (one score vector per workgroup: several for the per-expert selection).
+// Thread t holds channels CPT t .. CPT t + CPT - 1.  An MSB-first radix select finds the
 // k-th largest score T one byte at a time (a 256-bin LDS histogram of the
 // remaining candidates, then one wave scans the bins from the top); the
 // channels above T are taken, and of the channels equal to T the ones of
 // lowest index, as many as k still needs.  The selected channels are then
 // written in index order, so S is ascending.
+template <int CPT>
 __global__ void __launch_bounds__(kSelectThreads)
-k_select_topk(const uint64_t* __restrict__ score, int K, int Kpad, int k, int32_t* __restrict__ S) {
-  (void)Kpad;
+k_select_topk(const uint64_t* __restrict__ score, int K, int k, int32_t* __restrict__ S) {
   score += (int64_t)blockIdx.x * K;
   S += (int64_t)blockIdx.x * k;
   __shared__ uint32_t hist[256];
@@ -64,16 +64,18 @@ k_select_topk(const uint64_t* __restrict__ score, int K, int Kpad, int k, int32_
   __shared__ uint64_t s_prefix;
   __shared__ int s_need;
   const int tid = threadIdx.x;
-  uint64_t key[4];
-  bool valid[4];
+  uint64_t key[CPT];
+  bool valid[CPT];
+  uint64_t any = 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = 4 * tid + q;
+  for (int q = 0; q < CPT; ++q) {
+    const int e = CPT * tid + q;
     valid[q] = e < K;
     key[q] = valid[q] ? score[e] : 0ull;
+    any |= key[q];
   }
   // the highest byte any key uses
-  uint64_t orv = wave_or_u64(key[0] | key[1] | key[2] | key[3]);
+  uint64_t orv = wave_or_u64(any);
   if ((tid & 63) == 0) orw[tid >> 6] = orv;
   __syncthreads();
   orv = 0;
@@ -86,7 +88,7 @@ k_select_topk(const uint64_t* __restrict__ score, int K, int Kpad, int k, int32_
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < CPT; ++q)
       if (valid[q] && (key[q] & mask) == prefix) atomicAdd(&hist[(key[q] >> (8 * b)) & 0xFFu], 1u);
     __syncthreads();
     if (tid < 64) {
@@ -121,12 +123,12 @@ k_select_topk(const uint64_t* __restrict__ score, int K, int Kpad, int k, int32_
   // the first `need` channels equal to it
   int ties = 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) ties += (valid[q] && key[q] == prefix) ? 1 : 0;
+  for (int q = 0; q < CPT; ++q) ties += (valid[q] && key[q] == prefix) ? 1 : 0;
   int tie_rank = block_exclusive_scan(ties, wsum);
-  bool sel[4];
+  bool sel[CPT];
   int nsel = 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < CPT; ++q) {
     sel[q] = false;
     if (valid[q] && key[q] > prefix) sel[q] = true;
     if (valid[q] && key[q] == prefix) sel[q] = tie_rank++ < need;
@@ -134,8 +136,19 @@ k_select_topk(const uint64_t* __restrict__ score, int K, int Kpad, int k, int32_
   }
   int pos = block_exclusive_scan(nsel, wsum);
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    if (sel[q]) S[pos++] = 4 * tid + q;
+  for (int q = 0; q < CPT; ++q)
+    if (sel[q]) S[pos++] = CPT * tid + q;
+}
+
+// one workgroup per score vector (grid = number of vectors)
+static void launch_select_topk(const uint64_t* score, int64_t K, int64_t k, int32_t* S,
+                               unsigned vectors, hipStream_t s) {
+  if (K <= 4 * kSelectThreads)
+    k_select_topk<4><<<vectors, kSelectThreads, 0, s>>>(score, (int)K, (int)k, S);
+  else if (K <= 8 * kSelectThreads)
+    k_select_topk<8><<<vectors, kSelectThreads, 0, s>>>(score, (int)K, (int)k, S);
+  else
+    k_select_topk<16><<<vectors, kSelectThreads, 0, s>>>(score, (int)K, (int)k, S);
 }
 
 // R[m][j] = bf16(fma(-(q*s), g, x[m][S[j]])): a block owns 64 rows; its 256
@@ -196,8 +209,9 @@ __device__ __forceinline__ int expert_of(const int32_t* __restrict__ offsets, in
 constexpr int kExpertRows = 64;      // permuted rows per workgroup
 
 // score[e][j] += floor(|r[t][j]| * 2^(31 - E_A)) over the permuted rows p of
-// expert e (t = a_rows[p]).  Thread b owns channels 16 b .. 16 b + 15 (K <=
-// 4096); a workgroup walks 64 consecutive permuted rows, which belong to one
+// expert e (t = a_rows[p]).  Thread b owns channels 16 b .. 16 b + 15 of the
+// workgroup's 4096-channel slice (blockIdx.y); a workgroup walks 64
+// consecutive permuted rows, which belong to one
 // expert or a few, and adds its integer sums per expert with 64-bit atomics
 // (any order gives the same bits).  The residual is the quantizer's: r =
 // bf16(fma(-(q * s), g, x)).  A, whose binary exponent scales the terms, is
@@ -212,7 +226,7 @@ k_expert_scores(const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __re
   if (!(g > 0.0f)) return;                     // A == 0: every score is 0
   const float A = bf16_bits_to_f32(f32_to_bf16_rne(g * kScaleDen));
   const int ea = frexp_exponent(A);
-  const int b = threadIdx.x;
+  const int b = (int)blockIdx.y * 256 + threadIdx.x;
   const bool active = b < K / 16;
   const int64_t p_lo = (int64_t)blockIdx.x * kExpertRows;
   const int64_t p_hi = p_lo + kExpertRows < M_total ? p_lo + kExpertRows : M_total;
@@ -334,9 +348,7 @@ int select_residual_channels(const void* x_used, int64_t ldx, const uint8_t* cod
   NV_REQUIRE(aligned(score, 8) && aligned(S, 4) && aligned(R_S, 2) && aligned(x_used, 2),
              NVFP4_ERR_ALIGN, "select_residual_channels: misaligned pointer");
   hipStream_t s = as_stream(stream);
-  int Kpad = 4;
-  while (Kpad < K) Kpad <<= 1;
-  k_select_topk<<<1, kSelectThreads, 0, s>>>(score, (int)K, Kpad, (int)k, S);
+  launch_select_topk(score, K, k, S, 1, s);
   if (M > 0) {
     const int64_t blocks = (M + kGatherRows - 1) / kGatherRows;
     k_gather_residual<<<(unsigned)blocks, 256, 0, s>>>(
@@ -383,12 +395,10 @@ int select_residual_channels_per_expert(const void* x_used, int64_t ldx, const u
   fill_u64(score, E * K, 0ull, s);
   const int64_t blocks = (M_total + kExpertRows - 1) / kExpertRows;
   if (M_total > 0)
-    k_expert_scores<<<(unsigned)blocks, 256, 0, s>>>(
+    k_expert_scores<<<dim3((unsigned)blocks, (unsigned)((K + 4095) / 4096)), 256, 0, s>>>(
         static_cast<const uint16_t*>(x_used), ldx, codes, scales, g_x, a_rows, expert_offsets,
         (int)E, M_src, M_total, K, score);
-  int Kpad = 4;
-  while (Kpad < K) Kpad <<= 1;
-  k_select_topk<<<(unsigned)E, kSelectThreads, 0, s>>>(score, (int)K, Kpad, (int)k, S);
+  launch_select_topk(score, K, k, S, (unsigned)E, s);
   if (M_total > 0)
     k_gather_residual_rows<<<(unsigned)blocks, 256, 0, s>>>(
         static_cast<const uint16_t*>(x_used), ldx, codes, scales, g_x, a_rows, expert_offsets,

@@ -22,14 +22,16 @@ from . import (grouped_w4a4_gemm_rac, grouped_w4a4_gemm_rac_per_expert,
 
 @dataclass
 class QuantWeights:
-    codes: torch.Tensor      # [E][N/16][K/64][16][32] u8 (tiled codes)
-    scales: torch.Tensor     # [E][N/16][K/64][16][4] u8 (tiled block scales)
+    codes: torch.Tensor      # [E][N][K/2] u8, row-major E2M1 pairs
+    scales: torch.Tensor     # [E][N][K/16] u8, row-major E4M3 block scales
     g: torch.Tensor          # [E] f32
     qdq: torch.Tensor        # [E][N][K] bf16 or None
+    packed_codes: torch.Tensor    # the grouped GEMMs' packed copy of codes ...
+    packed_scales: torch.Tensor   # ... and block scales
 
 
 def prepare_weights(w, want_qdq=False) -> QuantWeights:
-    return QuantWeights(*nvfp4_qdq_weights(w, want_qdq=want_qdq))
+    return QuantWeights(*nvfp4_qdq_weights(w, want_qdq=want_qdq, want_packed=True))
 
 
 def quantized_linear_rac(x, wq: QuantWeights, k, a_rows=None, offsets=None, M_total=None,
@@ -67,7 +69,8 @@ def quantized_linear_rac(x, wq: QuantWeights, k, a_rows=None, offsets=None, M_to
             R = nvfp4_qdq_residual(R)[3]
     if swiglu_out and per_expert:
         raise ValueError("the fused SwiGLU output takes the shared channel selection")
-    args = (q["codes"], q["scales"], q["g"], a_rows, R, S, wq.codes, wq.scales, wq.g, offsets)
+    args = (q["codes"], q["scales"], q["g"], a_rows, R, S, wq.packed_codes, wq.packed_scales, wq.g,
+            offsets)
     if swiglu_out:
         y, amax = grouped_w4a4_gemm_rac_swiglu(*args, M_total=M_total, with_amax=True)
         return y, dict(q=q, S=S, R=R, h_amax=amax)

@@ -73,29 +73,47 @@ const char* nvfp4_last_error(void);
  * §2.2 A, asymmetric W4A16 QAT).
  *
  * w      [E][N][K] bf16, K contiguous (each expert's weight, out x in).
- * codes  [E][N/16][K/64][16][32] packed E2M1 (E * N * K/2 bytes), two codes
- *        per byte (the even column in bits 3:0), in 512-byte tiles, one per
- *        16 rows x 64 columns: the byte holding columns k, k+1 (k even) of
- *        row n of expert e is at e*N*K/2 + ((n/16) * (K/64) + k/64) * 512 +
- *        (n%16) * 32 + (k%64)/2.  A GEMM k-step of a row block is then one
- *        contiguous run of whole cache lines.
- * scales [E][N/16][K/64][16][4] E4M3 (E * N * K/16 bytes): the block scales
- *        in 64-byte tiles, one per 16 rows x 64 columns; the scale of block
- *        kb (columns 16 kb .. 16 kb + 15) of row n of expert e is at byte
- *        e*N*K/16 + ((n/16) * (K/64) + kb/4) * 64 + (n%16) * 4 + kb%4.
- *        The grouped GEMM reads whole tiles for a stretch of K.
+ * codes  [E][N][K/2] packed E2M1, row-major: byte j of row n holds columns
+ *        2j (bits 3:0) and 2j+1 (bits 7:4).
+ * scales [E][N][K/16] E4M3, row-major: the scale of columns 16b .. 16b+15.
  * g_w    [E] float32: per-expert tensor scale g = fp32(amax_e / 2688).
  * w_qdq  [E][N][K] bf16 or NULL: bf16(fp32(e2m1 * e4m3) * g), the weight the
  *        trainer's forward sees.
+ * packed_codes, packed_scales (both or neither; NULL: not written): the same
+ *        codes and scales in the grouped GEMMs' packed layout (E*N*K/2 and
+ *        E*N*K/16 bytes), the w_codes and w_scales the GEMM calls take.  An
+ *        opaque pre-pack: a permutation of the row-major bytes that lets a
+ *        GEMM k-step of a row block read whole cache lines
+ *        (nvfp4_pack_weights makes it from row-major codes and scales).
  * Scale recipe per 16-block (all float32, round to nearest even):
  *   s = e4m3((blockmax * 448) / amax);  code = e2m1(x * (2688 / (s * amax)))
  *   (s == 0 gives magnitude 0); the sign bit of a code is the sign of x.
- * Requires 1 <= E <= 65535, N % 16 == 0, K % 64 == 0.
+ * Requires 1 <= E <= 65535, N % 16 == 0, K % 64 == 0; codes 8-byte, scales
+ * and packed_scales 4-byte, packed_codes 16-byte aligned.
  * ---------------------------------------------------------------------- */
 size_t nvfp4_qdq_weights_workspace_size(int64_t E);
 int nvfp4_qdq_weights(const void* w, int64_t E, int64_t N, int64_t K,
                       uint8_t* codes, uint8_t* scales, float* g_w, void* w_qdq,
+                      uint8_t* packed_codes, uint8_t* packed_scales,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* The grouped GEMMs' packed copy of row-major NVFP4 weights (codes
+ * [E][N][K/2], scales [E][N][K/16], as nvfp4_qdq_weights writes them), for
+ * weights quantized elsewhere: packed_codes (E*N*K/2 bytes) and packed_scales
+ * (E*N*K/16 bytes) as described under nvfp4_qdq_weights.  A byte permutation,
+ * no arithmetic.  Requires 1 <= E <= 65535, N % 16 == 0, K % 64 == 0; codes
+ * and packed_codes 16-byte, scales and packed_scales 4-byte aligned.  No
+ * workspace. */
+int nvfp4_pack_weights(const uint8_t* codes, const uint8_t* scales, int64_t E, int64_t N,
+                       int64_t K, uint8_t* packed_codes, uint8_t* packed_scales, void* stream);
+
+/* E2M1 encoding of float32 values with unit scale, the element conversion
+ * every quantizer here applies to x * (2688 / (s * amax)) (the E2M1 grid of
+ * gist.science summary §1): codes[i] (one code per byte, bits 3:0) = sign of
+ * v[i] | index of the nearest of {0, .5, 1, 1.5, 2, 3, 4, 6} to |v[i]|, ties
+ * to the even index, saturating at 6.  v [n] float32 (finite), codes [n]
+ * bytes; v 4-byte aligned, codes unaligned.  No workspace. */
+int nvfp4_e2m1_encode_f32(const float* v, int64_t n, uint8_t* codes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Online activation quantization (activations are recomputed and quantized
@@ -130,7 +148,7 @@ int nvfp4_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, int glu
  * them ascending in S [k] int32, and gathers the residual of those channels,
  * R_S [M][k] bf16 = bf16(fp32(x - dequant(x))), from x_used (row stride ldx),
  * codes, scales and g_x as produced by nvfp4_quantize_act.
- * k == 0 enqueues nothing.  Requires 0 <= k <= K <= 4096, K % 32 == 0.
+ * k == 0 enqueues nothing.  Requires 0 <= k <= K <= 16384, K % 32 == 0.
  * ---------------------------------------------------------------------- */
 size_t select_residual_channels_workspace_size(int64_t M, int64_t K, int64_t k);
 int select_residual_channels(const void* x_used, int64_t ldx, const uint8_t* codes,
@@ -185,7 +203,7 @@ int nvfp4_quantize_act_amax(const void* x, int64_t M, int64_t K, int64_t ldx,
  * and R [M_total][k] bf16, R[p][j] = bf16(fp32(x - dequant(x))) of row t on
  * channel S[e][j].  An expert with no rows gets channels 0 .. k-1.
  * x_used (row stride ldx), codes, scales, g_x as from nvfp4_quantize_act.
- * Requires 1 <= E <= 1024, 0 <= k <= K <= 4096, K % 32 == 0, ldx % 8 == 0;
+ * Requires 1 <= E <= 1024, 0 <= k <= K <= 16384, K % 32 == 0, ldx % 8 == 0;
  * k == 0 enqueues nothing.  ws: the per-expert scores, E * K * 8 bytes.
  *
  * grouped_w4a4_gemm_rac_per_expert: grouped_w4a4_gemm_rac with S_E [E][k]
@@ -286,8 +304,8 @@ int moe_permute(const float* logits, const float* bias, int64_t T, int64_t E, in
  * in the bf16/fp16 operands of the matrix cores), float32 accumulation.
  * a_codes [M_src][K/2], a_scales [M_src][K/16], g_x [1]; a_rows [M_total] or
  * NULL (then M_src >= M_total); R_S [M_src][k] bf16 (NULL iff k == 0);
- * S [k] int32 ascending; w_codes [E][N/16][K/64][16][32],
- * w_scales [E][N/16][K/64][16][4] (the tiles nvfp4_qdq_weights writes), g_w [E];
+ * S [k] int32 ascending; w_codes, w_scales: the packed copy of the weight
+ * codes and scales (nvfp4_qdq_weights' packed outputs, or nvfp4_pack_weights), g_w [E];
  * expert_offsets [E+1] (device; off[0] = 0, off[E] = M_total); y [M_total][N]
  * bf16.  Requires K % 128 == 0, N % 16 == 0, 0 <= k <= K.
  * The workspace holds the per-expert tile prefix, an exact f16 image of the
@@ -296,7 +314,7 @@ int moe_permute(const float* logits, const float* bias, int64_t T, int64_t E, in
  * problem too small to fill the chip, float32 partial products of up to 4
  * slices of K (slices * M_total * N * 4 bytes), summed in slice order, so
  * results do not depend on timing.  A workspace smaller than the query
- * returns selects the generic kernel (same results within the tolerance).
+ * returns NVFP4_ERR_WORKSPACE.
  * ---------------------------------------------------------------------- */
 size_t grouped_w4a4_gemm_rac_workspace_size(int64_t E, int64_t M_src, int64_t M_total,
                                             int64_t N, int64_t K, int64_t k);

@@ -37,6 +37,21 @@ def test_library_exports_every_declared_symbol():
     assert sorted(F.EXPORTED_SYMBOLS) == names
 
 
+def test_measurement_header_symbols_exported():
+    L = F.lib()
+    text = open(os.path.join(ROOT, "include", "nvfp4rac_bench.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+    assert names == sorted(F.BENCH_SYMBOLS)
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.nvfp4_ceiling_mfma_flops(0) == 2 * 32 * 32 * 16
+    assert L.nvfp4_ceiling_mfma_flops(3) == 2 * 32 * 32 * 64
+    assert L.nvfp4_ceiling_mfma(7, 1, 1, FAKE, None) == ERR_SHAPE
+    assert L.nvfp4_ceiling_mfma(0, 1, 1, None, None) == ERR_NULL
+    assert L.nvfp4_ceiling_read(FAKE, 24, FAKE, None) == ERR_SHAPE
+
+
 def test_version_and_status_strings():
     L = F.lib()
     assert L.nvfp4_version() >= 100
@@ -69,20 +84,41 @@ def test_quantize_act_validation():
 
 def test_qdq_weights_validation():
     L = F.lib()
-    assert L.nvfp4_qdq_weights(FAKE, 0, 16, 64, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == ERR_SHAPE
-    # scales are tiled per 16 rows x 64 columns: N % 16 and K % 64
-    assert L.nvfp4_qdq_weights(FAKE, 2, 24, 64, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == ERR_SHAPE
-    assert L.nvfp4_qdq_weights(FAKE, 2, 16, 96, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == ERR_SHAPE
-    assert L.nvfp4_qdq_weights(None, 2, 16, 64, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None) == ERR_NULL
-    assert L.nvfp4_qdq_weights(FAKE, 2, 16, 64, FAKE, FAKE, FAKE, None, FAKE, 4, None) == ERR_WS
+    q = lambda w, E, N, K, pc=None, ps=None, sc=FAKE, ws=1 << 20: L.nvfp4_qdq_weights(
+        w, E, N, K, FAKE, sc, FAKE, None, pc, ps, FAKE, ws, None)
+    assert q(FAKE, 0, 16, 64) == ERR_SHAPE
+    # the packed copy is tiled per 16 rows x 64 columns: N % 16 and K % 64
+    assert q(FAKE, 2, 24, 64) == ERR_SHAPE
+    assert q(FAKE, 2, 16, 96) == ERR_SHAPE
+    assert q(None, 2, 16, 64) == ERR_NULL
+    assert q(FAKE, 2, 16, 64, pc=FAKE) == ERR_NULL          # both packed outputs or neither
+    assert q(FAKE, 2, 16, 64, pc=FAKE_MIS, ps=FAKE) == ERR_ALIGN
+    assert q(FAKE, 2, 16, 64, sc=FAKE_MIS) == ERR_ALIGN
+    assert q(FAKE, 2, 16, 64, ws=4) == ERR_WS
+
+
+def test_pack_weights_validation():
+    L = F.lib()
+    assert L.nvfp4_pack_weights(FAKE, FAKE, 2, 24, 64, FAKE, FAKE, None) == ERR_SHAPE
+    assert L.nvfp4_pack_weights(FAKE, FAKE, 2, 16, 96, FAKE, FAKE, None) == ERR_SHAPE
+    assert L.nvfp4_pack_weights(FAKE, None, 2, 16, 64, FAKE, FAKE, None) == ERR_NULL
+    assert L.nvfp4_pack_weights(FAKE_MIS, FAKE, 2, 16, 64, FAKE, FAKE, None) == ERR_ALIGN
+
+
+def test_e2m1_encode_validation():
+    L = F.lib()
+    assert L.nvfp4_e2m1_encode_f32(None, 0, None, None) == OK          # nothing to do
+    assert L.nvfp4_e2m1_encode_f32(FAKE, -1, FAKE, None) == ERR_SHAPE
+    assert L.nvfp4_e2m1_encode_f32(None, 4, FAKE, None) == ERR_NULL
+    assert L.nvfp4_e2m1_encode_f32(FAKE_MIS, 4, FAKE, None) == ERR_ALIGN
 
 
 def test_select_validation():
     L = F.lib()
     assert L.select_residual_channels(FAKE, 64, FAKE, FAKE, FAKE, FAKE, 4, 64, 65, FAKE, FAKE,
                                       None, 0, None) == ERR_SHAPE
-    assert L.select_residual_channels(FAKE, 8192, FAKE, FAKE, FAKE, FAKE, 4, 8192, 8, FAKE, FAKE,
-                                      None, 0, None) == ERR_SHAPE
+    assert L.select_residual_channels(FAKE, 32768, FAKE, FAKE, FAKE, FAKE, 4, 32768, 8, FAKE,
+                                      FAKE, None, 0, None) == ERR_SHAPE
     # k == 0 is a no-op and needs no pointers at all
     assert L.select_residual_channels(None, 64, None, None, None, None, 4, 64, 0, None, None,
                                       None, 0, None) == OK
@@ -113,7 +149,13 @@ def test_gemm_validation():
     assert L.grouped_w4a4_gemm_rac(*args(msrc=10)) == ERR_SHAPE         # no gather, M_src < M_total
     assert L.grouped_w4a4_gemm_rac(*args(k=4)) == ERR_NULL              # k > 0 needs R_S and S
     assert L.grouped_w4a4_gemm_rac(*args(ac=FAKE_MIS)) == ERR_ALIGN
+    # y and R_S take 16-byte vector accesses
+    y_mis = args()
+    y_mis[16] = ctypes.c_void_p(0x10008)
+    assert L.grouped_w4a4_gemm_rac(*y_mis) == ERR_ALIGN
+    assert L.grouped_w4a4_gemm_rac(*args(k=4, R=ctypes.c_void_p(0x10008), S=FAKE)) == ERR_ALIGN
     assert L.grouped_w4a4_gemm_rac(*args(ws=0)) == ERR_WS
+    assert L.grouped_w4a4_gemm_rac(*args(ws=ws - 256)) == ERR_WS        # below the query
 
 
 def test_gemm_workspace_covers_the_k_split(monkeypatch):
@@ -203,7 +245,7 @@ def test_per_expert_validation():
                         FAKE, FAKE, kw.get("ws", ws), None]
     assert L.select_residual_channels_per_expert(*sel(k=65)) == ERR_SHAPE
     assert L.select_residual_channels_per_expert(*sel(E=0)) == ERR_SHAPE
-    assert L.select_residual_channels_per_expert(*sel(K=8192, ldx=8192)) == ERR_SHAPE
+    assert L.select_residual_channels_per_expert(*sel(K=32768, ldx=32768)) == ERR_SHAPE
     assert L.select_residual_channels_per_expert(*sel(S=None)) == ERR_NULL
     assert L.select_residual_channels_per_expert(*sel(ws=8)) == ERR_WS
     assert L.select_residual_channels_per_expert(*sel(k=0, S=None, ws=0)) == OK   # no-op

@@ -59,10 +59,15 @@ def check_weights(w_bits, wq, experts, rng, n_rows=256):
         N = w.shape[0]
         r = np.arange(N) if N <= n_rows else np.sort(rng.choice(N, n_rows, replace=False))
         c, s, _, _ = OQ.quantize(w[r], A=OQ.tensor_amax(w))
-        c_gpu = untile_wcodes(wq.codes[e:e + 1].cpu().numpy())[0]
+        c_gpu = wq.codes[e].cpu().numpy()
         assert np.array_equal(OQ.unpack_codes(c_gpu[r]), c), f"expert {e} codes"
-        s_gpu = untile_wscales(wq.scales[e:e + 1].cpu().numpy())[0]
+        s_gpu = wq.scales[e].cpu().numpy()
         assert np.array_equal(s_gpu[r], s), f"expert {e} scales"
+        # the packed copy holds the same bytes
+        assert np.array_equal(untile_wcodes(wq.packed_codes[e:e + 1].cpu().numpy())[0][r],
+                              c_gpu[r]), f"expert {e} packed codes"
+        assert np.array_equal(untile_wscales(wq.packed_scales[e:e + 1].cpu().numpy())[0][r],
+                              s_gpu[r]), f"expert {e} packed scales"
 
 
 def check_activation(x, st, k, rows, blocks):

@@ -47,6 +47,30 @@ def check_quant_against_oracle(q, x_vals):
     return codes, scales, g, A, r, score
 
 
+# ---------------------------------------------------------- E2M1 conversion
+
+def test_e2m1_device_encoder_sweep(dev):
+    # the hardware conversion every quantizer uses, over a fixed strided sweep
+    # of all finite float32 bit patterns (every binade, normals, subnormals,
+    # both signs) and the +-64-ulp neighbourhood of every grid point, every
+    # midpoint between grid points and the saturation region, against the
+    # oracle's nearest-point rule (ties to the even code, saturating, sign kept)
+    say("e2m1 encoder sweep")
+    pats = np.arange(0, 2 ** 32, 1021, dtype=np.uint64).astype(np.uint32)
+    marks = np.array([0, 0.25, 0.5, 0.75, 1, 1.25, 1.5, 1.75, 2, 2.5, 3, 3.5, 4, 5, 6, 7, 8, 1e30],
+                     dtype=np.float32).view(np.uint32)
+    near = (marks[:, None].astype(np.int64) + np.arange(-64, 65)[None, :]).reshape(-1)
+    near = near[near >= 0].astype(np.uint32)
+    pats = np.concatenate([pats, near, near | np.uint32(0x80000000)])
+    pats = pats[((pats >> 23) & 0xFF) != 0xFF]                    # finite values only
+    v = pats.view(np.float32)
+    got = F.nvfp4_e2m1_encode_f32(torch.from_numpy(v).cuda()).cpu().numpy()
+    want = OF.e2m1_encode(v)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{bad.size} codes differ, first {v[bad[:5]]} -> {got[bad[:5]]} want {want[bad[:5]]}"
+    say(f"   {v.size} values bit-exact")
+
+
 # ------------------------------------------------------------------ quantizer
 
 @pytest.mark.parametrize("M,K", [(1, 32), (5, 96), (37, 512), (130, 768), (64, 4096), (3, 8192)])
@@ -109,20 +133,32 @@ def test_qdq_weights_bitexact(dev, E, N, K):
     if E > 3:
         w[2] = 0.0                                   # an all-zero expert: g = 0, codes 0
     wd = to_dev_bf16(OF.f64_to_bf16_bits(w))
-    codes, scales, g_w, w_qdq = F.nvfp4_qdq_weights(wd, want_qdq=True)
+    codes, scales, g_w, w_qdq, pc, ps = F.nvfp4_qdq_weights(wd, want_qdq=True)
     torch.cuda.synchronize()
     rc, rs, rg, rq = OQ.qdq_weights(w)
-    assert codes.shape == (E, N // 16, K // 64, 16, 32)
-    assert np.array_equal(OQ.unpack_codes(untile_wcodes(codes.cpu().numpy())), rc)
-    assert scales.shape == (E, N // 16, K // 64, 16, 4)
-    assert np.array_equal(untile_wscales(scales.cpu().numpy()), rs)
+    # row-major codes and scales, compared with the oracle directly
+    assert codes.shape == (E, N, K // 2) and scales.shape == (E, N, K // 16)
+    assert np.array_equal(codes.cpu().numpy(), OQ.pack_codes(rc))
+    assert np.array_equal(scales.cpu().numpy(), rs)
     assert np.array_equal(f32_bits(g_w.cpu().numpy()), f32_bits(rg))
     assert np.array_equal(host_bits(w_qdq), OF.f64_to_bf16_bits(rq))
+    # the GEMMs' packed copy: the same bytes, permuted into tiles
+    assert pc.shape == (E, N // 16, K // 64, 16, 32)
+    assert np.array_equal(untile_wcodes(pc.cpu().numpy()), OQ.pack_codes(rc))
+    assert ps.shape == (E, N // 16, K // 64, 16, 4)
+    assert np.array_equal(untile_wscales(ps.cpu().numpy()), rs)
+    # nvfp4_pack_weights of the row-major outputs gives the same packed copy
+    pc2, ps2 = F.nvfp4_pack_weights(codes, scales)
+    assert torch.equal(pc2, pc) and torch.equal(ps2, ps)
+    # without the packed copy, the row-major outputs are unchanged
+    q2 = F.nvfp4_qdq_weights(wd, want_qdq=False, want_packed=False)
+    assert q2.packed_codes is None and torch.equal(q2.codes, codes) and torch.equal(q2.scales, scales)
 
 
 # ------------------------------------------------------------------ selection
 
-@pytest.mark.parametrize("M,K,k", [(9, 64, 1), (50, 512, 16), (20, 768, 64), (4, 96, 96), (300, 4096, 128)])
+@pytest.mark.parametrize("M,K,k", [(9, 64, 1), (50, 512, 16), (20, 768, 64), (4, 96, 96), (300, 4096, 128),
+                                   (6, 8192, 100), (3, 16384, 300)])
 def test_select_residual_bitexact(dev, M, K, k):
     say(f"select M={M} K={K} k={k}")
     rng = np.random.default_rng(M + K + k)
@@ -232,6 +268,8 @@ def gemm_kernel(request, monkeypatch):
     (500, [17, 0, 0, 400, 83], 272, 1024, 128, True),
     (700, [300, 1, 511, 0, 255], 528, 768, 64, True),  # several 256-row tiles, N tail
     (64, [3, 0, 17, 33, 1, 0, 16, 40], 512, 1024, 64, True),  # decode-sized: 0-40 rows each
+    (64, [3, 0, 17, 33, 1, 0, 16, 40], 512, 384, 64, True),   # decode: last chunk of 128 columns
+    (48, [20, 9, 0, 19], 256, 640, 64, True),                  # ... with two full chunks before it
     (300, [100, 200], 256, 1024, 256, True),           # large k: two 128-channel chunks
     (500, [17, 0, 0, 400, 83], 272, 1024, 384, True),  # three chunks, N tail
     (96, [50, 46], 128, 512, 512, False),              # large k = K: every channel

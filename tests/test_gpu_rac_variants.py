@@ -91,7 +91,8 @@ def test_gemm_with_quantized_residual(dev, gemm_kernel, M_src, counts, N, K, k):
     q = F.nvfp4_quantize_act(to_dev_bf16(OF.f64_to_bf16_bits(x)))
     S, R = F.select_residual_channels(q["x_used"], q["codes"], q["scales"], q["g"], q["score"], k)
     rq = F.nvfp4_qdq_residual(R)
-    wc_d, ws_d, gw_d, _ = F.nvfp4_qdq_weights(to_dev_bf16(OF.f64_to_bf16_bits(w)), want_qdq=False)
+    wqd = F.nvfp4_qdq_weights(to_dev_bf16(OF.f64_to_bf16_bits(w)), want_qdq=False)
+    wc_d, ws_d, gw_d = wqd.packed_codes, wqd.packed_scales, wqd.g
     y = F.grouped_w4a4_gemm_rac(q["codes"], q["scales"], q["g"], cu(a_rows), rq[3], S, wc_d, ws_d,
                                 gw_d, cu(offs), M_total=M_total)
     torch.cuda.synchronize()
@@ -125,8 +126,8 @@ def test_full_size_first_gemm_with_quantized_residual(dev, idx):
     S, R = F.select_residual_channels(q["x_used"], q["codes"], q["scales"], q["g"], q["score"],
                                       cfg.k_first)
     rq = F.nvfp4_qdq_residual(R)
-    y = F.grouped_w4a4_gemm_rac(q["codes"], q["scales"], q["g"], perm, rq[3], S, w1.codes,
-                                w1.scales, w1.g, offs, M_total=perm.numel())
+    y = F.grouped_w4a4_gemm_rac(q["codes"], q["scales"], q["g"], perm, rq[3], S, w1.packed_codes,
+                                w1.packed_scales, w1.g, offs, M_total=perm.numel())
     torch.cuda.synchronize()
     # the quantized residual, in full, teacher-forced on the GPU's R_S (which
     # the full-size pipeline test checks against the oracle)
@@ -174,6 +175,7 @@ def _routing(rng, M_src, counts, gather):
     (100, [3, 0, 17, 33, 1, 0, 16, 40], 1024, 64, True),
     (40, [20, 20], 96, 96, True),                        # every channel
     (300, [120, 200, 80], 4096, 128, True),
+    (60, [25, 0, 35], 8192, 64, True),                   # two 4096-channel score slices
 ])
 def test_select_per_expert_bitexact(dev, M_src, counts, K, k, gather):
     say(f"select per expert counts={counts} K={K} k={k}")

@@ -60,9 +60,9 @@ def test_w4a16_empty(dev):
     say("w4a16 empty")
     x = torch.zeros((4, 256), dtype=torch.bfloat16, device="cuda")
     w = torch.zeros((2, 32, 256), dtype=torch.bfloat16, device="cuda")
-    c, s, g, _ = F.nvfp4_qdq_weights(w, want_qdq=False)
+    wq = F.nvfp4_qdq_weights(w, want_qdq=False)
     offs = torch.zeros(3, dtype=torch.int32, device="cuda")
-    y = F.grouped_w4a16_gemm(x, None, c, s, g, offs, M_total=0)
+    y = F.grouped_w4a16_gemm(x, None, wq.packed_codes, wq.packed_scales, wq.g, offs, M_total=0)
     torch.cuda.synchronize()
     assert y.shape == (0, 32)
 
@@ -79,7 +79,8 @@ def test_full_size_first_gemm_w4a16(dev, idx):
     bias = torch.from_numpy(wl.bias).cuda() if wl.bias is not None else None
     say(f"workload {cfg.name}: running the library")
     ids, tw, offs, perm, inv = F.moe_permute(logits, cfg.topk, bias)
-    y = F.grouped_w4a16_gemm(x_dev, perm, w1.codes, w1.scales, w1.g, offs, M_total=perm.numel())
+    y = F.grouped_w4a16_gemm(x_dev, perm, w1.packed_codes, w1.packed_scales, w1.g, offs,
+                             M_total=perm.numel())
     torch.cuda.synchronize()
     x = OF.bf16_bits_to_f64(wl.x)
     offs_np, perm_np = offs.cpu().numpy(), perm.cpu().numpy()
