@@ -31,7 +31,7 @@ import torch
 from .build import LIB as LIB_PATH
 
 __all__ = ["lib", "nvfp4_qdq_weights", "nvfp4_pack_weights", "QdqWeights",
-           "nvfp4_e2m1_encode_f32", "nvfp4_quantize_act", "select_residual_channels",
+           "nvfp4_e2m1_encode_f32", "nvfp4_quantize_act", "nvfp4_quantize_act_noalloc", "select_residual_channels",
            "moe_permute", "grouped_w4a4_gemm_rac", "moe_unpermute_combine", "nvfp4_qdq_residual",
            "grouped_w4a16_gemm", "select_residual_channels_per_expert",
            "grouped_w4a4_gemm_rac_per_expert", "grouped_w4a4_gemm_rac_swiglu",
@@ -42,7 +42,7 @@ EXPORTED_SYMBOLS = [
     "nvfp4_version", "nvfp4_status_str", "nvfp4_last_error",
     "nvfp4_qdq_weights_workspace_size", "nvfp4_qdq_weights", "nvfp4_pack_weights",
     "nvfp4_e2m1_encode_f32",
-    "nvfp4_quantize_act_workspace_size", "nvfp4_quantize_act",
+    "nvfp4_quantize_act_workspace_size", "nvfp4_quantize_act", "nvfp4_quantize_act_noalloc",
     "select_residual_channels_workspace_size", "select_residual_channels",
     "moe_permute_workspace_size", "moe_permute",
     "grouped_w4a4_gemm_rac_workspace_size", "grouped_w4a4_gemm_rac",
@@ -104,6 +104,7 @@ def _load():
         "nvfp4_pack_weights": [_P, _P, _I64, _I64, _I64, _P, _P, _P],
         "nvfp4_e2m1_encode_f32": [_P, _I64, _P, _P],
         "nvfp4_quantize_act": [_P, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P, _P, _P, _P, _SZ, _P],
+        "nvfp4_quantize_act_noalloc": [_P, _I64, _I64, _I64, ctypes.c_int, _P, _P, _P, _P, _P, _P],
         "select_residual_channels": [_P, _I64, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _SZ, _P],
         "moe_permute": [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P],
         "grouped_w4a4_gemm_rac": [_P, _P, _P, _P, _I64, _P, _P, _I64, _P, _P, _P, _P, _I64, _I64,
@@ -257,6 +258,36 @@ def nvfp4_quantize_act(x, glu=False, want_score=True):
     _check(L.nvfp4_quantize_act(_ptr(x), M, K, C, int(bool(glu)), _ptr(codes), _ptr(scales),
                                 _ptr(g), _ptr(score), _ptr(h), _ptr(ws), ws.numel(), _stream(dev)),
            "nvfp4_quantize_act")
+    return dict(codes=codes, scales=scales, g=g, score=score, x_used=h if glu else x)
+
+
+def nvfp4_quantize_act_noalloc(x, glu=False, want_score=True, out=None):
+    """nvfp4_quantize_act on the library's fixed device scratch (no
+    workspace).  out: optional dict of preallocated codes, scales, g, score
+    (and h for glu) tensors to write into, so the call allocates nothing."""
+    L = _load()
+    _need(x, torch.bfloat16, "x")
+    M, C = x.shape
+    K = C // 2 if glu else C
+    dev = x.device
+    o = out or {}
+    codes = o.get("codes", None)
+    codes = codes if codes is not None else torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    scales = o.get("scales", None)
+    scales = scales if scales is not None else torch.empty((M, K // 16), dtype=torch.uint8,
+                                                           device=dev)
+    g = o.get("g", None)
+    g = g if g is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    score = o.get("score", None)
+    if score is None and want_score:
+        score = torch.empty(K, dtype=torch.uint64, device=dev)
+    h = o.get("x_used", None) if glu else None
+    if glu and h is None:
+        h = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    _check(L.nvfp4_quantize_act_noalloc(_ptr(x), M, K, C, int(bool(glu)), _ptr(codes),
+                                        _ptr(scales), _ptr(g), _ptr(score), _ptr(h),
+                                        _stream(dev)),
+           "nvfp4_quantize_act_noalloc")
     return dict(codes=codes, scales=scales, g=g, score=score, x_used=h if glu else x)
 
 

@@ -238,7 +238,8 @@ struct ActPlan {
 };
 
 // max_part_bytes: a cap on the partial sums (the fixed scratch of the
-// allocation-free entry point), or 0 for none
+// allocation-free entry point), or 0 for none; fewer row groups then share
+// the rows
 static ActPlan act_plan(int64_t M, int64_t K, int cus, size_t max_part_bytes) {
   ActPlan p;
   p.tiles = (int)((K / 16 + kTileBlocks - 1) / kTileBlocks);
@@ -294,6 +295,41 @@ static int act_quantize(const char* who, const void* x, int64_t M, int64_t K, in
   return check_launch(who);
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free entry point: the same two kernels on a fixed scratch array
+// in device memory (one copy per device, kept until the process ends), for
+// callers that cannot allocate.  Every call on a device shares its copy:
+// the amax slots and partial sums are written before they are read in each
+// call, so nothing carries over from one call to the next; calls that
+// overlap in time on one device race.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+constexpr int64_t kNoAllocMaxK = 65536;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_addr[64];
+
+// The device address of this device's copy of `scratch`, looked up once per
+// device with that device current.  (In host code the array's name is a
+// host-side stand-in, not a device address.)
+static int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return fail(NVFP4_ERR_HIP, "nvfp4_quantize_act_noalloc: hipGetDevice failed");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(NVFP4_ERR_HIP, "nvfp4_quantize_act_noalloc: hipGetSymbolAddress: %s",
+                  hipGetErrorString(e));
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return NVFP4_OK;
+}
+
 }  // namespace nvfp4
 
 using namespace nvfp4;
@@ -325,6 +361,39 @@ int nvfp4_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, int glu
   NV_REQUIRE(ws_bytes >= pl.bytes, NVFP4_ERR_WORKSPACE, "nvfp4_quantize_act: workspace too small");
   return act_quantize("nvfp4_quantize_act", x, M, K, ldx, glu, nullptr, codes, scales, g_x, score,
                       x_used, ws, pl, as_stream(stream));
+}
+
+int nvfp4_quantize_act_noalloc(const void* x, int64_t M, int64_t K, int64_t ldx, int glu,
+                               uint8_t* codes, uint8_t* scales, float* g_x, uint64_t* score,
+                               void* x_used, void* stream) {
+  NV_REQUIRE(g_x, NVFP4_ERR_NULL, "nvfp4_quantize_act_noalloc: g_x is required");
+  NV_REQUIRE(M >= 0 && K >= 32 && K % 32 == 0 && M < (1LL << 40), NVFP4_ERR_SHAPE,
+             "nvfp4_quantize_act_noalloc: need M >= 0, K >= 32, K %% 32 == 0 (M=%lld K=%lld)",
+             (long long)M, (long long)K);
+  NV_REQUIRE(K <= kNoAllocMaxK, NVFP4_ERR_UNSUPPORTED,
+             "nvfp4_quantize_act_noalloc: K=%lld exceeds %lld, the largest the fixed scratch "
+             "takes; use nvfp4_quantize_act with a workspace",
+             (long long)K, (long long)kNoAllocMaxK);
+  NV_REQUIRE(glu == 0 || glu == 1, NVFP4_ERR_SHAPE,
+             "nvfp4_quantize_act_noalloc: glu must be 0 or 1");
+  NV_REQUIRE(ldx >= (glu ? 2 * K : K) && ldx % 8 == 0, NVFP4_ERR_SHAPE,
+             "nvfp4_quantize_act_noalloc: bad ldx %lld", (long long)ldx);
+  NV_REQUIRE(M == 0 || (x && codes && scales), NVFP4_ERR_NULL,
+             "nvfp4_quantize_act_noalloc: x, codes and scales are required");
+  NV_REQUIRE(!glu || x_used, NVFP4_ERR_NULL,
+             "nvfp4_quantize_act_noalloc: glu=1 needs x_used for h");
+  NV_REQUIRE(aligned(x, 16) && aligned(codes, 8) && aligned(scales, 4) && aligned(x_used, 16) &&
+                 aligned(score, 8),
+             NVFP4_ERR_ALIGN, "nvfp4_quantize_act_noalloc: misaligned pointer");
+  const ActPlan pl = act_plan(M, K, num_cus(), kNoAllocScratchBytes - kAmaxSlots * 4);
+  NV_REQUIRE(pl.bytes <= kNoAllocScratchBytes, NVFP4_ERR_UNSUPPORTED,
+             "nvfp4_quantize_act_noalloc: needs %zu bytes of scratch, the fixed array holds %zu",
+             pl.bytes, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st != NVFP4_OK) return st;
+  return act_quantize("nvfp4_quantize_act_noalloc", x, M, K, ldx, glu, nullptr, codes, scales,
+                      g_x, score, x_used, ws, pl, as_stream(stream));
 }
 
 int nvfp4_quantize_act_amax(const void* x, int64_t M, int64_t K, int64_t ldx,

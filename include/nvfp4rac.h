@@ -140,6 +140,20 @@ int nvfp4_quantize_act(const void* x, int64_t M, int64_t K, int64_t ldx, int glu
                        uint64_t* score, void* x_used,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* nvfp4_quantize_act without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, outputs and requirements as
+ * nvfp4_quantize_act minus ws/ws_bytes.  Scratch is a fixed 4 MiB array in
+ * device memory, one copy per device, held until the process ends; its
+ * address is looked up on the first call on each device.  The call allocates
+ * and frees nothing.  K above 65536 returns NVFP4_ERR_UNSUPPORTED; any M is
+ * taken (fewer row groups share the work when the scratch would overflow).
+ * Calls on one device share the array: calls that overlap in time there
+ * (other streams, other threads) race; calls in stream order do not. */
+int nvfp4_quantize_act_noalloc(const void* x, int64_t M, int64_t K, int64_t ldx, int glu,
+                               uint8_t* codes, uint8_t* scales, float* g_x,
+                               uint64_t* score, void* x_used, void* stream);
+
 /* ------------------------------------------------------------------------
  * High-residual channel selection (the binary channel mask of Residual
  * Activation Compensation, gist.science summary §2.2 B, both languages).

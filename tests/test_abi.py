@@ -82,6 +82,16 @@ def test_quantize_act_validation():
     assert st == ERR_WS
 
 
+def test_quantize_act_noalloc_validation():
+    L = F.lib()
+    f = L.nvfp4_quantize_act_noalloc
+    assert f(FAKE, 4, 48, 48, 0, FAKE, FAKE, FAKE, None, None, None) == ERR_SHAPE
+    assert f(FAKE, 4, 65536 + 32, 65536 + 32, 0, FAKE, FAKE, FAKE, None, None, None) == 5
+    assert b"65536" in L.nvfp4_last_error()
+    assert f(FAKE, 4, 64, 64, 0, FAKE, FAKE, None, None, None, None) == ERR_NULL
+    assert f(FAKE_MIS, 4, 64, 64, 0, FAKE, FAKE, FAKE, None, None, None) == ERR_ALIGN
+
+
 def test_qdq_weights_validation():
     L = F.lib()
     q = lambda w, E, N, K, pc=None, ps=None, sc=FAKE, ws=1 << 20: L.nvfp4_qdq_weights(
