@@ -1009,6 +1009,13 @@ constexpr int kDecTokBytes = 2 * dec::TMAX * 8 * 64 * 16;
 constexpr int kDecStaticLds = 4 * dec::KMAX + 32 * dec::CHUNKS_MAX + 2 * (4 * dec::CHUNKS_MAX + 1);
 constexpr int kLdsPerCu = 160 * 1024;
 
+// W16 = true is the trainer-side W4A16 product on decode-sized problems: the
+// tokens are bf16 activations x [M_src][K] (p.a_codes holds their address),
+// copied by global->LDS loads straight into the token-fragment slots instead
+// of being decoded (so they take no registers), the weights are decoded to
+// bf16 (q * s, exact), the MFMA is bf16, and there is no g_x and no
+// correction.
+template <bool W16>
 __global__ void __launch_bounds__(256, 2)
 k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
   using namespace dec;
@@ -1058,7 +1065,7 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
   if (Me == 0 || nbw <= 0) return;           // uniform over the workgroup
   const int64_t Kh = p.K / 2, Ks = p.K / 16;
   const int nc = (int)((p.K + KC - 1) / KC);
-  const int kk = p.k;
+  const int kk = W16 ? 0 : p.k;
 
   if (kk > 0) {
     for (int j = tid; j < kk; j += 256) {
@@ -1094,7 +1101,7 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
   const uint32_t lane_c0 = (uint32_t)(512 * kq + 32 * r16);
   const uint32_t lane_s0 = (uint32_t)(4 * r16 + 64 * kq);
   const bool half_last = (p.K % KC) != 0;    // the last chunk holds 128 columns
-  const float gx = *p.g_x;
+  const float gx = W16 ? 1.0f : *p.g_x;
   const float gw = p.g_w[e];
 
   // position in the workgroup's chunk stream: local row block, chunk
@@ -1104,6 +1111,9 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
   auto advance = [&](Pos q) { return q.c + 1 == nc ? Pos{q.blk + 1, 0} : Pos{q.blk, q.c + 1}; };
 
   for (int64_t t0 = 0; t0 < Me; t0 += 16 * TMAX) {
+    // a pass's first chunk refills fragment buffer 0, which the previous
+    // pass's last chunk may still be reading when its chunk count is odd
+    if (t0 > 0) __syncthreads();
     const int ntile_rt = (int)((Me - t0 + 15) / 16 < TMAX ? (Me - t0 + 15) / 16 : TMAX);
     int64_t src[TMAX], rrow[TMAX];
 #pragma unroll
@@ -1134,14 +1144,16 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
     uint32_t lane_tc[TMAX], lane_ts[TMAX];
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
-      lane_tc[t] = (uint32_t)(src[t] * Kh) + 8 * wave + 32 * kq;
+      // W4A16: byte offset of the lane's 16 bf16 tokens (2 * (64 kq + 16 wave))
+      lane_tc[t] = W16 ? (uint32_t)(src[t] * p.K * 2) + 32 * wave + 128 * kq
+                       : (uint32_t)(src[t] * Kh) + 8 * wave + 32 * kq;
       lane_ts[t] = (uint32_t)(src[t] * Ks) + 4 * kq;
     }
     // the chunk stream for ntile token tiles (a constant, so the unrolled
     // MFMA steps hold no branches)
     auto run = [&](auto ntc) __attribute__((always_inline)) {
       constexpr int ntile = decltype(ntc)::value;
-      auto load_part = [&](DecChunk& d, Pos q, int part) __attribute__((always_inline)) {
+      auto load_part = [&](DecChunk& d, Pos q, int part, int buf) __attribute__((always_inline)) {
         // lanes kq >= 2 of a last half chunk re-read the chunk's first half
         const bool tl = half_last && q.c == nc - 1 && kq >= 2;
         if (part < 4) {
@@ -1156,15 +1168,29 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
           d.ws[part] = *reinterpret_cast<const uint32_t*>(sb + (lane_s - (tl ? 128u : 0u)));
         } else if (part - 4 < TMAX) {
           const int t = part - 4;
-          d.tc[t] = *reinterpret_cast<const uint2*>(p.a_codes + (uint32_t)q.c * (KC / 2) +
-                                                    (lane_tc[t] - (tl ? 64u : 0u)));
-          d.ts[t] = *reinterpret_cast<const uint32_t*>(p.a_scales + (uint32_t)q.c * (KC / 16) +
-                                                       (lane_ts[t] - (tl ? 8u : 0u)));
+          if constexpr (W16) {
+            // this wave's two steps of token tile t, into the fragment slots
+            // of buffer `buf` (lane i's 16 bytes land at slot base + 16 i);
+            // lanes past K load nothing and are zeroed before use
+            if (!tl) {
+              const uint8_t* xs = p.a_codes + (uint32_t)q.c * (KC * 2) + lane_tc[t];
+              __builtin_amdgcn_global_load_lds(xs, tok + (((buf * TMAX + t) * 8 + 2 * wave_u) << 10),
+                                               16, 0, 0);
+              __builtin_amdgcn_global_load_lds(xs + 16,
+                                               tok + (((buf * TMAX + t) * 8 + 2 * wave_u + 1) << 10),
+                                               16, 0, 0);
+            }
+          } else {
+            d.tc[t] = *reinterpret_cast<const uint2*>(p.a_codes + (uint32_t)q.c * (KC / 2) +
+                                                      (lane_tc[t] - (tl ? 64u : 0u)));
+            d.ts[t] = *reinterpret_cast<const uint32_t*>(p.a_scales + (uint32_t)q.c * (KC / 16) +
+                                                         (lane_ts[t] - (tl ? 8u : 0u)));
+          }
         }
       };
-      auto load = [&](DecChunk& d, Pos q) __attribute__((always_inline)) {
+      auto load = [&](DecChunk& d, Pos q, int buf) __attribute__((always_inline)) {
   #pragma unroll
-        for (int part = 0; part < 4 + TMAX; ++part) load_part(d, q, part);
+        for (int part = 0; part < 4 + TMAX; ++part) load_part(d, q, part, buf);
       };
 
       f32x4_t acc[4][TMAX];
@@ -1186,7 +1212,7 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
         for (int b = 0; b < 4; ++b)
   #pragma unroll
           for (int t = 0; t < TMAX; ++t) acc[b][t] *= gx;
-        if (kk > 0) {
+        if (!W16 && kk > 0) {
           __syncthreads();                     // W_S complete
           for (int cb = 0; cb < kk; cb += 32) {
             const int slot = cb + 8 * kq;
@@ -1244,14 +1270,23 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
         const int c = q.c;
         // decode this wave's two steps of every token tile for the workgroup;
         // the barrier also ends every wave's reads of this buffer two chunks ago
+        if constexpr (W16) wait_vmem0();         // this chunk's token slots have landed
   #pragma unroll
         for (int t = 0; t < TMAX; ++t) {
           if (t >= ntile) continue;
+          const bool past_k = (int64_t)c * KC + 64 * kq >= p.K;
+          if constexpr (W16) {
+            if (past_k) {
+              *reinterpret_cast<u32x4*>(frag(buf, t, 2 * wave)) = u32x4{0u, 0u, 0u, 0u};
+              *reinterpret_cast<u32x4*>(frag(buf, t, 2 * wave + 1)) = u32x4{0u, 0u, 0u, 0u};
+            }
+            continue;
+          }
           float sc;
           h2_t mu;
           scale_prep((d.ts[t] >> (8 * wave)) & 0xFFu, sc, mu);
           u32x4 f0 = decode8_f16(d.tc[t].x, sc, mu), f1 = decode8_f16(d.tc[t].y, sc, mu);
-          if ((int64_t)c * KC + 64 * kq >= p.K) f0 = f1 = u32x4{0u, 0u, 0u, 0u};
+          if (past_k) f0 = f1 = u32x4{0u, 0u, 0u, 0u};
           *reinterpret_cast<u32x4*>(frag(buf, t, 2 * wave)) = f0;
           *reinterpret_cast<u32x4*>(frag(buf, t, 2 * wave + 1)) = f1;
         }
@@ -1259,23 +1294,31 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
   #pragma unroll
         for (int s = 0; s < 8; ++s) {
           // token tiles first: their fragments are decoded first next chunk
-          if (NEXT && s < 4 + TMAX) load_part(dn, qn, (s + 4) % (4 + TMAX));
+          if (NEXT && s < 4 + TMAX) load_part(dn, qn, (s + 4) % (4 + TMAX), buf ^ 1);
           u32x4 tf[TMAX];
   #pragma unroll
           for (int t = 0; t < TMAX; ++t)
             if (t < ntile) tf[t] = *reinterpret_cast<const u32x4*>(frag(buf, t, s));
   #pragma unroll
           for (int b = 0; b < 4; ++b) {
-            float sc;
-            h2_t mu;
-            scale_prep((d.ws[b] >> (8 * (s >> 1))) & 0xFFu, sc, mu);
-            const u32x4 wf = decode8_f16(dword_of(d.wc[b], s), sc, mu);
+            if constexpr (W16) {
+              const u32x4 wf = decode8_bf16(dword_of(d.wc[b], s),
+                                            e4m3_decode((d.ws[b] >> (8 * (s >> 1))) & 0xFFu));
   #pragma unroll
-            for (int t = 0; t < TMAX; ++t)
-              if (t < ntile) acc[b][t] = mfma16_f16(wf, tf[t], acc[b][t]);
+              for (int t = 0; t < TMAX; ++t)
+                if (t < ntile) acc[b][t] = mfma16_bf16(wf, tf[t], acc[b][t]);
+            } else {
+              float sc;
+              h2_t mu;
+              scale_prep((d.ws[b] >> (8 * (s >> 1))) & 0xFFu, sc, mu);
+              const u32x4 wf = decode8_f16(dword_of(d.wc[b], s), sc, mu);
+  #pragma unroll
+              for (int t = 0; t < TMAX; ++t)
+                if (t < ntile) acc[b][t] = mfma16_f16(wf, tf[t], acc[b][t]);
+            }
           }
         }
-        if (kk > 0) {
+        if (!W16 && kk > 0) {
           // weights of the selected channels in this chunk -> W_S rows (each
           // wave writes, and later reads, only its own 64 rows): each lane
           // walks the selected columns of its own 64, code dword by code
@@ -1315,7 +1358,7 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
       const int total = nbw * nc;
       DecChunk b0, b1;
       Pos qa{0, 0};
-      load(b0, qa);
+      load(b0, qa, 0);
       int i = 0;
       for (; i + 2 < total; i += 2) {
         const Pos qb = advance(qa), qc = advance(qb);
@@ -1706,7 +1749,7 @@ static int gemm_rac(bool per_expert, bool glu, uint32_t* h_amax, const uint8_t* 
       std::lock_guard<std::mutex> lock(dec_mu);
       if ((size_t)dec_lds_limit[dev] < lds) {
         const int want = (int)kDecTokBytes + dec::ROWS * (dec::KMAX * 2 + 16);
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_decode),
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_decode<false>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, want) != hipSuccess)
           return fail(NVFP4_ERR_HIP, "grouped_w4a4_gemm_rac: cannot raise the LDS limit");
         dec_lds_limit[dev] = want;
@@ -1720,7 +1763,7 @@ static int gemm_rac(bool per_expert, bool glu, uint32_t* h_amax, const uint8_t* 
     bpw = bpw < 1 ? 1 : (bpw > n_blocks ? n_blocks : bpw);
     const int64_t groups = (n_blocks + bpw - 1) / bpw;
     if (glu) a.y = glu_stage;
-    k_gemm_decode<<<(unsigned)(E * groups), 256, lds, s>>>(a, (int)n_blocks, (int)bpw, wsrow);
+    k_gemm_decode<false><<<(unsigned)(E * groups), 256, lds, s>>>(a, (int)n_blocks, (int)bpw, wsrow);
     if (glu) launch_swiglu();
     return check_launch("grouped_w4a4_gemm_rac");
   }
@@ -1860,6 +1903,24 @@ int grouped_w4a16_gemm(const void* x, const int32_t* a_rows, int64_t M_src,
   a.K = K;
   a.E = (int)E;
   a.k = 0;
+  // few rows per expert (decode): stream each expert's weights once with
+  // bf16 tokens (NVFP4RAC_GEMM=decode|big forces a kernel)
+  const char* force = getenv("NVFP4RAC_GEMM");
+  bool use_dec = M_total <= 48 * E;
+  if (force && strcmp(force, "decode") == 0) use_dec = true;
+  if (force && (strcmp(force, "big") == 0 || strcmp(force, "generic") == 0)) use_dec = false;
+  use_dec = use_dec && K / dec::KC <= dec::CHUNKS_MAX;
+  if (use_dec) {
+    a.a_codes = static_cast<const uint8_t*>(x);
+    const int64_t n_blocks = (N + dec::ROWS - 1) / dec::ROWS;
+    const size_t lds = (size_t)kDecTokBytes;
+    const int64_t slots = (int64_t)num_cus() * (2 * (lds + kDecStaticLds) <= kLdsPerCu ? 2 : 1);
+    int64_t bpw = (E * n_blocks + slots - 1) / slots;
+    bpw = bpw < 1 ? 1 : (bpw > n_blocks ? n_blocks : bpw);
+    const int64_t groups = (n_blocks + bpw - 1) / bpw;
+    k_gemm_decode<true><<<(unsigned)(E * groups), 256, lds, s>>>(a, (int)n_blocks, (int)bpw, 0);
+    return check_launch("grouped_w4a16_gemm");
+  }
   const int64_t n_tiles = (N + big::BN - 1) / big::BN;
   const int64_t m_tiles = (M_total + big::BM - 1) / big::BM + E;
   k_tile_prefix<<<1, 1024, 0, s>>>(expert_offsets, (int)E, M_total, big::BM, prefix);

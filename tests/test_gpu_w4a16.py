@@ -27,15 +27,28 @@ def say(msg):
     sys.stdout.flush()
 
 
+@pytest.fixture(params=["auto", "big", "decode"])
+def w16_kernel(request, monkeypatch):
+    # "auto": the library's own choice; "big" / "decode" force the large-tile
+    # or the weight-streaming kernel
+    if request.param == "auto":
+        monkeypatch.delenv("NVFP4RAC_GEMM", raising=False)
+    else:
+        monkeypatch.setenv("NVFP4RAC_GEMM", request.param)
+    return request.param
+
+
 @pytest.mark.parametrize("M_src,counts,N,K,gather", [
     (64, [64], 512, 512, False),
     (200, [0, 130, 1, 257], 144, 256, True),          # empty / single-row experts, N tail
     (700, [300, 1, 511, 0, 255], 528, 768, True),      # several 256-row tiles, N tail
-    (64, [3, 0, 17, 33, 1, 0, 16, 40], 512, 1024, True),
+    (64, [3, 0, 17, 33, 1, 0, 16, 40], 512, 1024, True),   # decode-sized: 0-40 rows each
+    (64, [3, 0, 17, 33, 1, 0, 16, 40], 272, 384, True),    # last chunk of 128 columns, N tail
+    (48, [20, 9, 0, 19], 256, 640, True),               # two full chunks, then a half one
     (300, [300], 256, 4096, False),
 ])
-def test_w4a16_gemm(dev, M_src, counts, N, K, gather):
-    say(f"w4a16 counts={counts} N={N} K={K} gather={gather}")
+def test_w4a16_gemm(dev, w16_kernel, M_src, counts, N, K, gather):
+    say(f"w4a16[{w16_kernel}] counts={counts} N={N} K={K} gather={gather}")
     rng = np.random.default_rng(sum(counts) + N + K)
     E = len(counts)
     x = heavy_bf16(rng, (M_src, K))
