@@ -539,7 +539,7 @@ def rac_sweep(cfg, wl, reps, n_experts=8):
         return F.grouped_w4a4_gemm_rac(q["codes"], q["scales"], q["g"], perm, R, S, c1, s1, g1,
                                        offs, M_total=rows)
 
-    E, N, K = c1.shape[0], c1.shape[1] * 16, c1.shape[2] * 64      # tiled codes
+    E, N, K = c1.shape[0], c1.shape[2] * 16, c1.shape[3] * 64      # packed codes
     ks = [k for k in (0, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096) if k <= K // 2]
     points = []
     t0 = None
@@ -626,7 +626,7 @@ def w4a16_bench(cfg, wl, reps):
         del Wq
         del w
         q = F.nvfp4_quantize_act(a, False, False)
-        E, N, K = c.shape[0], c.shape[1] * 16, c.shape[2] * 64
+        E, N, K = c.shape[0], c.shape[2] * 16, c.shape[3] * 64
         t16 = median_ms(lambda: F.grouped_w4a16_gemm(a, a_rows, c, s, gw, offs, M_total=rows))
         t4 = median_ms(lambda: F.grouped_w4a4_gemm_rac(q["codes"], q["scales"], q["g"], a_rows,
                                                        None, None, c, s, gw, offs, M_total=rows))

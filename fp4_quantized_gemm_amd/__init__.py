@@ -157,12 +157,14 @@ def _check(status, name):
 
 
 def _wshape(w_codes):
-    """(E, N) of packed weight codes [E][N/16][K/64][16][32] (the shape the
-    packed outputs of nvfp4_qdq_weights and nvfp4_pack_weights carry)."""
-    if w_codes.dim() != 5 or tuple(w_codes.shape[3:]) != (16, 32):
-        raise NvfpError("weight codes must be the packed copy [E][N/16][K/64][16][32] "
+    """(E, N) of packed weight codes [E][2][N/16][K/64][16][32] (the shape the
+    packed outputs of nvfp4_qdq_weights and nvfp4_pack_weights carry: per
+    expert the code tiles, then the same bytes' worth of channel-major
+    codes)."""
+    if w_codes.dim() != 6 or w_codes.shape[1] != 2 or tuple(w_codes.shape[4:]) != (16, 32):
+        raise NvfpError("weight codes must be the packed copy [E][2][N/16][K/64][16][32] "
                         "(nvfp4_qdq_weights' packed outputs or nvfp4_pack_weights)")
-    return int(w_codes.shape[0]), int(w_codes.shape[1]) * 16
+    return int(w_codes.shape[0]), int(w_codes.shape[2]) * 16
 
 
 def _ws(nbytes, device):
@@ -184,13 +186,16 @@ class QdqWeights(NamedTuple):
     scales: torch.Tensor                   # [E][N][K/16] u8, row-major E4M3 block scales
     g: torch.Tensor                        # [E] f32 tensor scales
     qdq: Optional[torch.Tensor]            # [E][N][K] bf16 fake-quantized weight, or None
-    packed_codes: Optional[torch.Tensor]   # the GEMMs' packed copy, [E][N/16][K/64][16][32]
-    packed_scales: Optional[torch.Tensor]  # [E][N/16][K/64][16][4]
+    # the GEMMs' packed copy: per expert [0] the tiles [N/16][K/64][16][32]
+    # (codes) and [..][16][4] (scales), [1] the same sizes holding the
+    # channel-major codes [K][N/2] and scales [K/16][N]
+    packed_codes: Optional[torch.Tensor]   # [E][2][N/16][K/64][16][32]
+    packed_scales: Optional[torch.Tensor]  # [E][2][N/16][K/64][16][4]
 
 
 def _packed_like(E, N, K, dev):
-    return (torch.empty((E, N // 16, K // 64, 16, 32), dtype=torch.uint8, device=dev),
-            torch.empty((E, N // 16, K // 64, 16, 4), dtype=torch.uint8, device=dev))
+    return (torch.empty((E, 2, N // 16, K // 64, 16, 32), dtype=torch.uint8, device=dev),
+            torch.empty((E, 2, N // 16, K // 64, 16, 4), dtype=torch.uint8, device=dev))
 
 
 def nvfp4_qdq_weights(w, want_qdq=True, want_packed=True) -> QdqWeights:

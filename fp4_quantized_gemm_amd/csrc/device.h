@@ -142,6 +142,20 @@ __device__ __forceinline__ int64_t wcode_offset(int64_t n, int64_t k, int64_t K)
   return (((n >> 4) * (K >> 6) + (k >> 6)) << 9) + ((n & 15) << 5) + ((k & 63) >> 1);
 }
 
+// The grouped GEMMs' packed copy of one expert's weights is the code tiles
+// above (N * K / 2 bytes) followed by a channel-major copy of the codes,
+// [K][N / 2] (byte n / 2 of column k: rows n, n + 1, the lower row in bits
+// 3:0); its scales are the scale tiles (N * K / 16 bytes) followed by a
+// channel-major copy [K / 16][N].  The channel-major copies let the
+// residual correction gather the weight columns of a few selected channels
+// without reading the whole matrix.
+__host__ __device__ __forceinline__ int64_t packed_codes_per_expert(int64_t N, int64_t K) {
+  return N * K;
+}
+__host__ __device__ __forceinline__ int64_t packed_scales_per_expert(int64_t N, int64_t K) {
+  return N * K / 8;
+}
+
 // SwiGLU of bf16 gate and up values: silu(g) * u in float32 with the
 // hardware exp2 and reciprocal (a few float32 ulps), then one rounding to
 // bf16: the correctly rounded bf16 value except when the float32 value lies

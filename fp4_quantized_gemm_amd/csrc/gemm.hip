@@ -44,7 +44,7 @@ struct GemmArgs {
   const uint8_t* w_codes;
   const uint8_t* w_scales;
   const float* g_w;
-  const uint16_t* wsel;        // [E][N][k] bf16 q * s of the selected columns (large k only)
+  const uint16_t* wsel;        // [E][N][kp] bf16 q * s of the selected columns (large-tile kernel)
   const int32_t* offsets;
   const int32_t* tile_prefix;
   uint16_t* y;
@@ -137,8 +137,8 @@ k_gemm_generic(GemmArgs p) {
   }
   __syncthreads();
 
-  const uint8_t* wc = p.w_codes + (int64_t)e * p.N * Kh;
-  const uint8_t* wsc = p.w_scales + (int64_t)e * p.N * Ks;
+  const uint8_t* wc = p.w_codes + e * packed_codes_per_expert(p.N, p.K);
+  const uint8_t* wsc = p.w_scales + e * packed_scales_per_expert(p.N, p.K);
 
   f32x4_t acc[4][4];
 #pragma unroll
@@ -394,11 +394,6 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t wsl[WS_BYTES];   // W_S tile, then output staging
   __shared__ int32_t rows_src[BM];
-  __shared__ int32_t s_local[KMAX];
-  // selected columns as a bitmap over K, and rank32[g] = number of selected
-  // columns below column 32 g
-  __shared__ uint32_t sel_bm[2 * KSTEPS_MAX];
-  __shared__ uint16_t rank32[2 * KSTEPS_MAX + 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -450,26 +445,22 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
     return r < 128 ? c : p.glu_i + c;
   };
   const uint32_t Kh = (uint32_t)(p.K / 2), Ks = (uint32_t)(p.K / 16), K2 = (uint32_t)(p.K * 2);
-  const int kk = W16 ? 0 : p.k;
-  // more than KMAX channels (a multiple of KMAX): the selected weight columns
-  // come from p.wsel after the loop instead of being copied as it passes
-  const bool sws = kk > KMAX;
-  const int kl = sws ? 0 : kk;                 // channels copied in the loop
+  // channels of the correction (K slices: all on slice 0, none on the others)
+  const int kk = (W16 || (SPLIT && blockIdx.y != 0)) ? 0 : p.k;
+  // The selected channels' weight columns come from p.wsel (bf16
+  // [E][N][kp], kp = k rounded up to 16, zero past k), KMAX channels (one
+  // W_S tile) at a time; the first tile is loaded as the main loop runs.
+  const int64_t kp = (p.k + 15) & ~15;
+  const int ws_ch = kk > KMAX ? KMAX : (int)((kk + 15) & ~15);   // channels per W_S tile
+  // the residual rows by direct loads in 64-channel halves (k % 64 == 0);
+  // otherwise each lane loads its own
+  const bool rdma = kk > 0 && (kk & 63) == 0;
 
   if (tid < BM) {
     int64_t pr = p0 + tid;
     if (pr >= e_hi) pr = e_hi - 1;
     int64_t t = p.a_rows ? (int64_t)p.a_rows[pr] : pr;
     rows_src[tid] = (int32_t)(t < 0 ? 0 : (t >= p.M_src ? p.M_src - 1 : t));
-    if (tid < kl) {
-      int c = p.S[(int64_t)e * p.s_stride + tid];
-      s_local[tid] = c < 0 ? 0 : (c >= p.K ? (int)p.K - 1 : c);
-    }
-    // zero slots k .. next multiple of 16 (a K slice: every slot, since it
-    // copies only the selected columns of its own k-steps)
-    const int kpad = (kl + 15) & ~15;
-    for (int j = SPLIT ? 0 : kl; j < kpad; ++j)
-      *reinterpret_cast<uint16_t*>(wsl + tid * WSROW + 2 * j) = 0;
   }
   __syncthreads();
   const int nk = (int)(p.K / BK);
@@ -478,24 +469,9 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   const int nks = SPLIT ? nk / p.ksplit : nk;
   const int kt_lo = SPLIT ? (int)blockIdx.y * nks : 0;
   const int kt_hi = kt_lo + nks;
-  if (kl > 0) {
-    // (S is strictly ascending, so bit ranks are the indices j)
-    for (int w = tid; w < 2 * nk; w += 512) sel_bm[w] = 0u;
-    __syncthreads();
-    for (int j = tid; j < kl; j += 512) atomicOr(&sel_bm[s_local[j] >> 5], 1u << (s_local[j] & 31));
-    for (int g = tid; g <= 2 * nk; g += 512) {
-      int a = 0, b = kl;
-      while (a < b) {
-        const int m = (a + b) >> 1;
-        if (s_local[m] < g * 32) a = m + 1; else b = m;
-      }
-      rank32[g] = (uint16_t)a;
-    }
-    __syncthreads();
-  }
 
-  const uint8_t* wc = p.w_codes + (int64_t)e * p.N * Kh;
-  const uint8_t* wsc = p.w_scales + (int64_t)e * p.N * Ks;
+  const uint8_t* wc = p.w_codes + e * packed_codes_per_expert(p.N, p.K);
+  const uint8_t* wsc = p.w_scales + e * packed_scales_per_expert(p.N, p.K);
 
   // byte offsets of this lane's staging loads (fixed over K): A 2048 chunks
   // (4 per thread), B codes 512 chunks (1 per thread), B scales 256 dwords
@@ -541,10 +517,26 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
                                        0, 0);
   };
 
+  // W_S tile of channels c0 .. c0 + ws_ch into wsl: instruction b (of
+  // WS_INSTS, b % 8 = wave) fills LDS bytes 1024 b ..; lanes in a row's pad
+  // or past the tile's channels load nothing (those slots are never read)
+  constexpr int WS_INSTS = (BN * WSROW + 1023) / 1024;
+  const uint16_t* wse = p.wsel + (int64_t)e * p.N * kp;
+  auto issue_ws = [&](int c0, int b) __attribute__((always_inline)) {
+    const int o = b * 1024 + lane * 16;
+    const int row = o / WSROW, cb = o - row * WSROW;
+    if (b < WS_INSTS && row < BN && cb < ws_ch * 2) {
+      int64_t n = wrow(row);
+      if (n >= p.N) n = p.N - 1;
+      __builtin_amdgcn_global_load_lds(wse + n * kp + c0 + cb / 2, wsl + b * 1024, 16, 0, 0);
+    }
+  };
+  // the first W_S tile goes out with the first ws_steps k-steps' loads
+  const int ws_steps = kk > 0 ? (nks < (WS_INSTS + 7) / 8 ? nks : (WS_INSTS + 7) / 8) : 0;
+
   // residual rows for the correction, staged like the A image: 64 channels
   // of the tile's 256 rows per stage, 8-channel chunks swizzled as A's
   // (whole 64-channel halves, so only when k % 64 == 0)
-  const bool rdma = kl > 0 && (kl & 63) == 0;
   auto issue_r = [&](uint8_t* st, int cb0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -552,7 +544,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
       const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
       const int64_t rr = p.r_perm ? (p0 + r < e_hi ? p0 + r : e_hi - 1) : rows_src[r];
       const uint8_t* src = reinterpret_cast<const uint8_t*>(p.R) +
-                           (uint32_t)rr * (uint32_t)(2 * kk) + 2u * (uint32_t)(cb0 + 8 * c);
+                           (uint32_t)rr * (uint32_t)(2 * p.k) + 2u * (uint32_t)(cb0 + 8 * c);
       __builtin_amdgcn_global_load_lds(src, st + (i * 8 + wave) * 1024, 16, 0, 0);
     }
   };
@@ -571,10 +563,11 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   // one k-step on stage `ab` while stage `nxt` fills with step kt + 1; the
   // wave computes its first NV 32-row blocks (the others lie past the
   // expert's last row)
-  auto kstep = [&](const uint8_t* ab, uint8_t* nxt, int kt, auto nv_c) {
+  auto kstep = [&](const uint8_t* ab, uint8_t* nxt, int kt, auto nv_c) __attribute__((always_inline)) {
     constexpr int NV = decltype(nv_c)::value;
     if (kt + 1 < kt_hi) issue_loads(nxt, (uint32_t)(kt + 1) * BK);
     else if (rdma) issue_r(nxt, 0);
+    if (kt - kt_lo < ws_steps) issue_ws(0, 8 * (kt - kt_lo) + wave);
     const uint8_t* bb = ab + A_BYTES;
     const uint8_t* sb = bb + B_CODES;
 
@@ -586,39 +579,6 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
       br[j] = *reinterpret_cast<const uint4*>(bb + rb * 32 + physb * 16);
       bs[j] = *reinterpret_cast<const uint16_t*>(sb + rb * 4 + 2 * kg);
     }
-    // the selected columns among this lane's 32 (k0 + 32 kg ..), and the
-    // index j of the first of them
-    uint32_t selm = 0u;
-    int jb = 0;
-    if (kl > 0) {
-      selm = sel_bm[2 * kt + kg];
-      jb = rank32[2 * kt + kg];
-    }
-    // copy the selected columns' weights (exact in bf16) into the W_S rows,
-    // from the codes this lane holds, before this step's MFMAs (measured
-    // 1.5-2% faster than after them, also at k = 0): the waves of row half
-    // wm take code dwords 2 wm, 2 wm + 1
-    if (!W16 && selm != 0u) {
-#pragma unroll
-      for (int tq = 0; tq < 2; ++tq) {
-        const int t = 2 * wm + tq;               // wave-uniform
-        uint32_t mb = (selm >> (8 * t)) & 0xFFu;
-        while (mb) {
-          const int ii = __builtin_ctz(mb);
-          mb &= mb - 1;
-          const int j = jb + __builtin_popcount(selm & ((1u << (8 * t + ii)) - 1u));
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const uint32_t w = t == 0 ? br[jj].x : t == 1 ? br[jj].y : t == 2 ? br[jj].z : br[jj].w;
-            const float qv = e2m1_unpack2<0>((w >> (4 * ii)) & 0xFu).x;
-            const float sv = e4m3_decode((bs[jj] >> (8 * (t >> 1))) & 0xFFu);
-            *reinterpret_cast<uint16_t*>(wsl + (wn * 64 + 32 * jj + r32) * WSROW + 2 * j) =
-                (uint16_t)(__float_as_uint(qv * sv) >> 16);
-          }
-        }
-      }
-    }
-
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       float sbv[2];
@@ -695,7 +655,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   }
 
   // (the loop ends on stage st1: the first residual half is in st0)
-  auto rac_half = [&](const uint8_t* rb, int cb0) {
+  auto rac_half = [&](const uint8_t* rb, int cb0) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       u32x4 A[4];
@@ -715,41 +675,39 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
       }
     }
   };
+  // the rest of the first W_S tile (fewer k-steps than its loads)
+  if (kk > 0 && 8 * ws_steps < WS_INSTS) {
+#pragma unroll 1
+    for (int b = 8 * ws_steps + wave; b < WS_INSTS; b += 8) issue_ws(0, b);
+    wait_vmem0();
+    __syncthreads();
+  }
   if (rdma) {
-    if (kk > 64) issue_r(st1, 64);
-    rac_half(st0, 0);
-    if (kk > 64) {
-      wait_vmem0();
-      __syncthreads();
-      rac_half(st1, 64);
-    }
-  }
-  if (sws) {
-    // the correction in chunks of KMAX channels: the chunk's weight columns
-    // (bf16 q * s from k_extract_ws) go to the W_S tile by global->LDS loads
-    // (1 KB per wave instruction; the 16-byte row pads are skipped), its
-    // residual rows to the two stages, then the same bf16 MFMAs
-    const uint16_t* wse = p.wsel + (int64_t)e * p.N * kk;
+    // W_S tiles of KMAX channels; a tile's residual rows in two 64-channel
+    // halves (the first tile's first half arrived with the last k-step)
+#pragma unroll 1
     for (int c0 = 0; c0 < kk; c0 += KMAX) {
-      __syncthreads();                         // the last reads of wsl and the stages are done
-      for (int b = wave; b * 1024 < BN * WSROW; b += 8) {
-        const int o = b * 1024 + lane * 16;
-        const int row = o / WSROW, cb = o - row * WSROW;
-        if (row < BN && cb < KMAX * 2) {
-          int64_t n = wrow(row);
-          if (n >= p.N) n = p.N - 1;
-          __builtin_amdgcn_global_load_lds(wse + n * kk + c0 + cb / 2, wsl + b * 1024, 16, 0, 0);
-        }
+      const bool two = kk - c0 > 64;
+      if (c0 > 0) {
+        __syncthreads();                       // the last reads of wsl and the stages are done
+#pragma unroll 1
+        for (int b = wave; b < WS_INSTS; b += 8) issue_ws(c0, b);
+        issue_r(st0, c0);
       }
-      issue_r(st0, c0);
-      issue_r(st1, c0 + 64);
-      wait_vmem0();
-      __syncthreads();
+      if (two) issue_r(st1, c0 + 64);
+      if (c0 > 0) {
+        wait_vmem0();
+        __syncthreads();
+      }
       rac_half(st0, 0);
-      rac_half(st1, 64);
+      if (two) {
+        wait_vmem0();
+        __syncthreads();
+        rac_half(st1, 64);
+      }
     }
   }
-  for (int cb0 = 0; !rdma && !sws && cb0 < kk; cb0 += 64) {
+  for (int cb0 = 0; !rdma && cb0 < kk; cb0 += 64) {
     u32x4 A[4][4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -925,25 +883,56 @@ k_swiglu_rows(const uint16_t* __restrict__ y, int64_t M, int64_t I, uint16_t* __
   if (h_amax != nullptr) block_atomic_max<256>(m8, h_amax);
 }
 
-// Weight columns of the selected channels for the large-k correction: bf16
-// q * s (exact; no tensor scale) of column S[j] of each expert row,
-// wsel[e][n][j].  One workgroup per weight row.
+// Weight columns of the selected channels for the large-tile kernel's
+// correction: wsel[e][n][j] = bf16(q * s) (exact; no tensor scale) of column
+// S[j] of expert e's row n, j < k, and 0 for k <= j < kp (kp: k rounded up to
+// 16, the correction's MFMA depth).  From the channel-major part of the
+// packed copy: a selected column is N / 2 contiguous code bytes and N scale
+// bytes.  Workgroup (row block of 256, expert); its 256 threads take one row
+// each, the channels in chunks of 32 through an LDS transpose so that a
+// row's values go out as 16-byte stores.
 __global__ void __launch_bounds__(256)
-k_extract_ws(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-             const int32_t* __restrict__ S, int64_t s_stride, int64_t N, int64_t K, int k,
-             uint16_t* __restrict__ wsel) {
-  const int64_t row = blockIdx.x;                // e * N + n
-  const int64_t e = row / N, n = row - e * N;
+k_gather_ws(const uint8_t* __restrict__ pcodes, const uint8_t* __restrict__ pscales,
+            const int32_t* __restrict__ S, int64_t s_stride, int64_t N, int64_t K, int k, int kp,
+            uint16_t* __restrict__ wsel) {
+  __shared__ uint16_t tile[256][34];
+  const int t = threadIdx.x;
+  const int64_t e = blockIdx.y, n = (int64_t)blockIdx.x * 256 + t;
   S += e * s_stride;
-  const uint8_t* cr = codes + e * N * (K / 2);
-  const uint8_t* sc = scales + e * N * (K / 16);
-  for (int j = threadIdx.x; j < k; j += 256) {
-    int c = S[j];
-    c = c < 0 ? 0 : (c >= K ? (int)K - 1 : c);
-    const uint32_t code = (cr[wcode_offset(n, c, K)] >> (4 * (c & 1))) & 0xFu;
-    const float q = e2m1_unpack2<0>(code).x;
-    const float sv = e4m3_decode(sc[wscale_offset(n, c >> 4, K)]);
-    wsel[row * k + j] = (uint16_t)(__float_as_uint(q * sv) >> 16);
+  const uint8_t* cc = pcodes + e * packed_codes_per_expert(N, K) + N * K / 2;
+  const uint8_t* cs = pscales + e * packed_scales_per_expert(N, K) + N * K / 16;
+  uint16_t* out = wsel + (e * N + (int64_t)blockIdx.x * 256) * kp;
+  for (int j0 = 0; j0 < kp; j0 += 32) {
+    if (n < N) {
+      for (int jj = 0; jj < 32; ++jj) {
+        const int j = j0 + jj;
+        uint16_t v = 0;
+        if (j < k) {
+          int c = S[j];
+          c = c < 0 ? 0 : (c >= K ? (int)K - 1 : c);
+          const uint32_t code = (cc[(int64_t)c * (N / 2) + (n >> 1)] >> (4 * (n & 1))) & 0xFu;
+          const float sv = e4m3_decode(cs[(int64_t)(c >> 4) * N + n]);
+          v = (uint16_t)(__float_as_uint(e2m1_unpack2<0>(code).x * sv) >> 16);
+        }
+        tile[t][jj] = v;
+      }
+    }
+    __syncthreads();
+    // row r of the block: channels j0 .. j0 + 31 (or up to kp), 8 per store
+    const int per_row = (kp - j0 < 32 ? kp - j0 : 32) / 8;
+    for (int q = t; q < 256 * per_row; q += 256) {
+      const int r = q / per_row, c8 = q - r * per_row;
+      if ((int64_t)blockIdx.x * 256 + r < N) {
+        const uint16_t* src = &tile[r][8 * c8];
+        uint4 o;
+        o.x = src[0] | ((uint32_t)src[1] << 16);
+        o.y = src[2] | ((uint32_t)src[3] << 16);
+        o.z = src[4] | ((uint32_t)src[5] << 16);
+        o.w = src[6] | ((uint32_t)src[7] << 16);
+        *reinterpret_cast<uint4*>(out + (int64_t)r * kp + j0 + 8 * c8) = o;
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -1089,8 +1078,8 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
     __syncthreads();
   }
 
-  const uint8_t* wc = p.w_codes + (int64_t)e * p.N * Kh;
-  const uint8_t* wsc = p.w_scales + (int64_t)e * p.N * Ks;
+  const uint8_t* wc = p.w_codes + e * packed_codes_per_expert(p.N, p.K);
+  const uint8_t* wsc = p.w_scales + e * packed_scales_per_expert(p.N, p.K);
   // load addresses = a uniform offset (row block, chunk) + a per-lane
   // offset fixed over the stream: row r16 of the chunk's code tile kq
   // (512-byte tiles of 16 rows x 64 columns: a row block's chunk is one
@@ -1615,9 +1604,14 @@ extern "C" {
 // prefix [E+1] int32, then (large-tile path) the f16 image of A [M_src][K]
 static size_t img_offset(int64_t E) { return round_up((size_t)(E + 1) * sizeof(int32_t), 256); }
 
-// large k (more than the large-tile kernel's W_S tile, a multiple of it):
-// the selected weight columns, bf16 [E][N][k], after the image
+// large k (more than the large-tile kernel's W_S tile): the kernel takes a
+// multiple of it
 static bool big_streams_ws(int64_t k) { return k > big::KMAX && k % big::KMAX == 0; }
+// the selected weight columns for the large-tile kernel's correction, bf16
+// [E][N][kp] (kp: k rounded up to 16), after the image
+static size_t wsel_bytes(int64_t E, int64_t N, int64_t k) {
+  return k > 0 ? round_up((size_t)E * (size_t)N * (size_t)((k + 15) & ~15) * 2, 256) : 0;
+}
 
 // K slices of the large-tile kernel for a problem whose tiles fill less than
 // the chip (sized for 256 CUs from the fewest tiles M_total can make; each
@@ -1646,7 +1640,7 @@ size_t grouped_w4a4_gemm_rac_workspace_size(int64_t E, int64_t M_src, int64_t M_
                                             int64_t K, int64_t k) {
   if (E < 1 || M_src < 0 || M_total < 0 || K < 0 || N < 0) return 256;
   size_t n = img_offset(E) + round_up((size_t)M_src * (size_t)K * 2, 256);
-  if (big_streams_ws(k)) n += round_up((size_t)E * (size_t)N * (size_t)k * 2, 256);
+  n += wsel_bytes(E, N, k);
   n += split_bytes(M_total, N, K, k);
   return n;
 }
@@ -1773,11 +1767,11 @@ static int gemm_rac(bool per_expert, bool glu, uint32_t* h_amax, const uint8_t* 
             (uint64_t)(per_expert ? M_total : M_src) * k * 2 < (1ULL << 32);
   if (use_big) {
     uint16_t* img = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + img_offset(E));
-    if (big_streams_ws(k)) {
-      uint16_t* wsel = reinterpret_cast<uint16_t*>(
-          static_cast<char*>(ws) + img_offset(E) + round_up((size_t)M_src * (size_t)K * 2, 256));
-      k_extract_ws<<<(unsigned)(E * N), 256, 0, s>>>(w_codes, w_scales, S, a.s_stride, N, K,
-                                                     (int)k, wsel);
+    const size_t wsel_off = img_offset(E) + round_up((size_t)M_src * (size_t)K * 2, 256);
+    if (k > 0) {
+      uint16_t* wsel = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + wsel_off);
+      k_gather_ws<<<dim3((unsigned)((N + 255) / 256), (unsigned)E), 256, 0, s>>>(
+          w_codes, w_scales, S, a.s_stride, N, K, (int)k, (int)((k + 15) & ~15), wsel);
       a.wsel = wsel;
     }
     const int64_t chunks = M_src * (K / 8);
@@ -1789,7 +1783,7 @@ static int gemm_rac(bool per_expert, bool glu, uint32_t* h_amax, const uint8_t* 
     if (glu) a.glu_i = N / 2, a.h_amax = h_amax;
     // a problem that fills less than the chip: K slices, reduced in order
     const int ksplit = glu ? 1 : big_ksplit(M_total, N, K, k);
-    const size_t part_off = img_offset(E) + round_up((size_t)M_src * (size_t)K * 2, 256);
+    const size_t part_off = wsel_off + wsel_bytes(E, N, k);
     if (ksplit > 1 && ws_bytes >= part_off + split_bytes(M_total, N, K, k)) {
       a.ksplit = ksplit;
       a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + part_off);

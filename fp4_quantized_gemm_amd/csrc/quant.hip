@@ -145,7 +145,7 @@ k_qdq_slices(const uint16_t* __restrict__ w, int64_t N, int64_t K, int E,
   // (K % 64 == 0), so a wave's blocks are all in range or all out, and lanes
   // 4j..4j+3 hold blocks 4t..4t+3 of one row
   const int64_t nblk = 16 * KB;
-  uint8_t* psc_e = pscales ? pscales + (int64_t)e * N * KB : nullptr;
+  uint8_t* psc_e = pscales ? pscales + e * packed_scales_per_expert(N, K) : nullptr;
   for (int64_t b0 = 0; b0 < nblk; b0 += 256 * kQdqRound) {
     uint4 c0[kQdqRound], c1[kQdqRound];
 #pragma unroll
@@ -172,8 +172,8 @@ k_qdq_slices(const uint16_t* __restrict__ w, int64_t N, int64_t K, int E,
                           (__shfl_down(sbyte, 3) << 24);
       if ((c & 3) == 0) *reinterpret_cast<uint32_t*>(scales + orow * KB + c) = s4;
       if (pcodes != nullptr) {
-        *reinterpret_cast<uint2*>(pcodes + (int64_t)e * N * (K / 2) + wcode_offset(row0 + r, 16 * c, K)) =
-            make_uint2(pk[0], pk[1]);
+        *reinterpret_cast<uint2*>(pcodes + e * packed_codes_per_expert(N, K) +
+                                  wcode_offset(row0 + r, 16 * c, K)) = make_uint2(pk[0], pk[1]);
         if ((c & 3) == 0) *reinterpret_cast<uint32_t*>(psc_e + wscale_offset(row0 + r, c, K)) = s4;
       }
       if (w_qdq != nullptr) {
@@ -189,11 +189,12 @@ k_qdq_slices(const uint16_t* __restrict__ w, int64_t N, int64_t K, int E,
 
 
 // ---------------------------------------------------------------------------
-// Row-major NVFP4 weights -> the grouped GEMMs' packed copy: codes in
-// 512-byte tiles of 16 rows x 64 columns ([E][N/16][K/64][16][32]) and block
-// scales in 64-byte tiles of the same rows and columns ([..][16][4]).  A
-// permutation of bytes: thread q moves the 16-byte code chunk q of the packed
-// codes, and (q < the number of scale dwords) the scale dword q.
+// Row-major NVFP4 weights -> the tiles of the grouped GEMMs' packed copy:
+// codes in 512-byte tiles of 16 rows x 64 columns ([N/16][K/64][16][32] per
+// expert) and block scales in 64-byte tiles of the same rows and columns
+// ([..][16][4]).  A permutation of bytes: thread q moves the 16-byte code
+// chunk q of the tiles, and (q < the number of scale dwords) the scale
+// dword q.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
 k_pack_weights(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t E,
@@ -201,20 +202,95 @@ k_pack_weights(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ sc
   const int64_t kt = K / 64, nt = N / 16;
   const int64_t n_chunks = E * N * K / 32;        // 16-byte code chunks
   const int64_t n_words = E * N * K / 64;         // scale dwords
+  const int64_t chunks_e = N * K / 32, words_e = N * K / 64;
   for (int64_t q = blockIdx.x * 256LL + threadIdx.x; q < n_chunks; q += (int64_t)gridDim.x * 256) {
     const int64_t tile = q >> 5, within = q & 31;
     const int64_t kb = tile % kt, nb = (tile / kt) % nt, e = tile / (kt * nt);
     const int64_t row = e * N + nb * 16 + (within >> 1);
     const uint4 v = *reinterpret_cast<const uint4*>(codes + row * (K / 2) + kb * 32 + (within & 1) * 16);
-    *reinterpret_cast<uint4*>(pcodes + q * 16) = v;
+    *reinterpret_cast<uint4*>(pcodes + e * packed_codes_per_expert(N, K) + (q - e * chunks_e) * 16) = v;
     if (q < n_words) {
       const int64_t st = q >> 4, r = q & 15;
       const int64_t skb = st % kt, snb = (st / kt) % nt, se = st / (kt * nt);
       const int64_t srow = se * N + snb * 16 + r;
-      reinterpret_cast<uint32_t*>(pscales)[q] =
+      *reinterpret_cast<uint32_t*>(pscales + se * packed_scales_per_expert(N, K) +
+                                   (q - se * words_e) * 4) =
           *reinterpret_cast<const uint32_t*>(scales + srow * (K / 16) + skb * 4);
     }
   }
+}
+
+// Row-major NVFP4 weights -> the channel-major part of the packed copy.
+// One wave per tile of 64 rows x 64 columns of one expert (rows past N
+// skipped; N % 16 == 0): it stages the tile's codes (32 bytes per row) and
+// scales (4 bytes per row) in LDS, then lane l writes column k0 + l's
+// nibbles of the tile's rows (8 bytes per 16 rows) and lanes 0..15 the 16
+// scale bytes of block k0 / 16 + l / 4, rows 16 (l % 4) ..
+__global__ void __launch_bounds__(256)
+k_pack_channel_major(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                     int64_t E, int64_t N, int64_t K, uint8_t* __restrict__ pcodes,
+                     uint8_t* __restrict__ pscales) {
+  __shared__ uint8_t ct[4][64][33];               // (+1: column reads spread over banks)
+  __shared__ uint8_t st[4][64][4];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t rt = (N + 63) / 64, kt = K / 64;
+  const int64_t tiles = E * rt * kt;
+  // every wave runs the same number of iterations (the barriers)
+  for (int64_t t0 = (int64_t)blockIdx.x * 4; t0 < tiles; t0 += (int64_t)gridDim.x * 4) {
+    const int64_t t = t0 + w;
+    const bool live = t < tiles;
+    const int64_t kb = live ? t % kt : 0, nb = live ? (t / kt) % rt : 0, e = live ? t / (kt * rt) : 0;
+    const int64_t n0 = nb * 64, k0 = kb * 64;
+    const int64_t rows = N - n0 < 64 ? N - n0 : 64;
+    if (live && lane < rows) {
+      const int64_t row = e * N + n0 + lane;
+      // (8-byte loads: the codes need only 8-byte alignment)
+      const uint2* src = reinterpret_cast<const uint2*>(codes + row * (K / 2) + k0 / 2);
+      const uint2 a = src[0], b = src[1], c = src[2], d = src[3];
+      const uint32_t v[8] = {a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+#pragma unroll
+      for (int j = 0; j < 32; ++j) ct[w][lane][j] = (uint8_t)(v[j >> 2] >> (8 * (j & 3)));
+      const uint32_t s4 = *reinterpret_cast<const uint32_t*>(scales + row * (K / 16) + k0 / 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st[w][lane][j] = (uint8_t)(s4 >> (8 * j));
+    }
+    __syncthreads();
+    if (live) {
+      uint8_t* pc = pcodes + e * packed_codes_per_expert(N, K) + N * K / 2;
+      for (int g = 0; g < rows / 16; ++g) {
+        uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t a = (ct[w][16 * g + 2 * j][lane >> 1] >> (4 * (lane & 1))) & 0xFu;
+          const uint32_t b = (ct[w][16 * g + 2 * j + 1][lane >> 1] >> (4 * (lane & 1))) & 0xFu;
+          const uint32_t byte = a | (b << 4);
+          if (j < 4) lo |= byte << (8 * j);
+          else hi |= byte << (8 * (j - 4));
+        }
+        *reinterpret_cast<uint2*>(pc + (k0 + lane) * (N / 2) + (n0 + 16 * g) / 2) = make_uint2(lo, hi);
+      }
+      if (lane < 16 && 16 * (lane & 3) < rows) {
+        const int kk = lane >> 2, r0 = 16 * (lane & 3);
+        uint32_t o[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[j >> 2] |= (uint32_t)st[w][r0 + j][kk] << (8 * (j & 3));
+        uint32_t* ps = reinterpret_cast<uint32_t*>(pscales + e * packed_scales_per_expert(N, K) +
+                                                   N * K / 16 + (k0 / 16 + kk) * N + n0 + r0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ps[j] = o[j];   // (the scales need only 4-byte alignment)
+      }
+    }
+    __syncthreads();
+  }
+}
+
+static void launch_pack_channel_major(const uint8_t* codes, const uint8_t* scales, int64_t E,
+                                      int64_t N, int64_t K, uint8_t* pcodes, uint8_t* pscales,
+                                      hipStream_t s) {
+  const int64_t tiles = E * ((N + 63) / 64) * (K / 64);
+  int64_t nb = (tiles + 3) / 4;
+  if (nb > 16LL * num_cus()) nb = 16LL * num_cus();
+  k_pack_channel_major<<<(unsigned)nb, 256, 0, s>>>(codes, scales, E, N, K, pcodes, pscales);
 }
 
 // ---------------------------------------------------------------------------
@@ -347,6 +423,8 @@ int nvfp4_qdq_weights(const void* w, int64_t E, int64_t N, int64_t K, uint8_t* c
   k_qdq_slices<<<dim3((unsigned)(N / 16), (unsigned)E, 1), 256, 0, s>>>(
       static_cast<const uint16_t*>(w), N, K, (int)E, amax, codes, scales, g_w,
       static_cast<uint16_t*>(w_qdq), packed_codes, packed_scales);
+  if (packed_codes != nullptr)
+    launch_pack_channel_major(codes, scales, E, N, K, packed_codes, packed_scales, s);
   return check_launch("nvfp4_qdq_weights");
 }
 
@@ -366,6 +444,8 @@ int nvfp4_pack_weights(const uint8_t* codes, const uint8_t* scales, int64_t E, i
   if (nb > 16LL * num_cus()) nb = 16LL * num_cus();
   k_pack_weights<<<(unsigned)nb, 256, 0, as_stream(stream)>>>(codes, scales, E, N, K,
                                                              packed_codes, packed_scales);
+  launch_pack_channel_major(codes, scales, E, N, K, packed_codes, packed_scales,
+                            as_stream(stream));
   return check_launch("nvfp4_pack_weights");
 }
 

@@ -80,10 +80,12 @@ const char* nvfp4_last_error(void);
  * w_qdq  [E][N][K] bf16 or NULL: bf16(fp32(e2m1 * e4m3) * g), the weight the
  *        trainer's forward sees.
  * packed_codes, packed_scales (both or neither; NULL: not written): the same
- *        codes and scales in the grouped GEMMs' packed layout (E*N*K/2 and
- *        E*N*K/16 bytes), the w_codes and w_scales the GEMM calls take.  An
- *        opaque pre-pack: a permutation of the row-major bytes that lets a
- *        GEMM k-step of a row block read whole cache lines
+ *        codes and scales in the grouped GEMMs' packed layout (E*N*K and
+ *        E*N*K/8 bytes), the w_codes and w_scales the GEMM calls take.  An
+ *        opaque pre-pack, two copies of the row-major bytes per expert: a
+ *        permutation that lets a GEMM k-step of a row block read whole cache
+ *        lines, then a channel-major copy from which the residual correction
+ *        gathers the weight columns of its selected channels
  *        (nvfp4_pack_weights makes it from row-major codes and scales).
  * Scale recipe per 16-block (all float32, round to nearest even):
  *   s = e4m3((blockmax * 448) / amax);  code = e2m1(x * (2688 / (s * amax)))
@@ -99,9 +101,9 @@ int nvfp4_qdq_weights(const void* w, int64_t E, int64_t N, int64_t K,
 
 /* The grouped GEMMs' packed copy of row-major NVFP4 weights (codes
  * [E][N][K/2], scales [E][N][K/16], as nvfp4_qdq_weights writes them), for
- * weights quantized elsewhere: packed_codes (E*N*K/2 bytes) and packed_scales
- * (E*N*K/16 bytes) as described under nvfp4_qdq_weights.  A byte permutation,
- * no arithmetic.  Requires 1 <= E <= 65535, N % 16 == 0, K % 64 == 0; codes
+ * weights quantized elsewhere: packed_codes (E*N*K bytes) and packed_scales
+ * (E*N*K/8 bytes) as described under nvfp4_qdq_weights.  Byte moves, no
+ * arithmetic.  Requires 1 <= E <= 65535, N % 16 == 0, K % 64 == 0; codes
  * and packed_codes 16-byte, scales and packed_scales 4-byte aligned.  No
  * workspace. */
 int nvfp4_pack_weights(const uint8_t* codes, const uint8_t* scales, int64_t E, int64_t N,
@@ -323,8 +325,8 @@ int moe_permute(const float* logits, const float* bias, int64_t T, int64_t E, in
  * expert_offsets [E+1] (device; off[0] = 0, off[E] = M_total); y [M_total][N]
  * bf16.  Requires K % 128 == 0, N % 16 == 0, 0 <= k <= K.
  * The workspace holds the per-expert tile prefix, an exact f16 image of the
- * activation (2 bytes per element), when k exceeds 128 and is a multiple of
- * 128 the selected weight columns as bf16 (E * N * k * 2 bytes), and, for a
+ * activation (2 bytes per element), when k > 0 the selected weight columns
+ * as bf16 (E * N * kp * 2 bytes, kp = k rounded up to 16), and, for a
  * problem too small to fill the chip, float32 partial products of up to 4
  * slices of K (slices * M_total * N * 4 bytes), summed in slice order, so
  * results do not depend on timing.  A workspace smaller than the query

@@ -44,6 +44,35 @@ def untile_wcodes(t: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(t.transpose(0, 1, 3, 2, 4)).reshape(E, NB * 16, KG * 32)
 
 
+def channel_major_codes(c: np.ndarray) -> np.ndarray:
+    """Packed row-major weight codes [E][N][K/2] -> [E][K][N/2]: byte n/2 of
+    column k holds rows n (bits 3:0) and n+1 (bits 7:4) (a layout change
+    only)."""
+    lo, hi = c & 0xF, c >> 4
+    E, N, KH = c.shape
+    cols = np.empty((E, N, 2 * KH), dtype=np.uint8)
+    cols[:, :, 0::2], cols[:, :, 1::2] = lo, hi
+    t = np.ascontiguousarray(cols.transpose(0, 2, 1))           # [E][K][N] nibbles
+    return (t[:, :, 0::2] | (t[:, :, 1::2] << 4)).astype(np.uint8)
+
+
+def gemm_wcodes(c: np.ndarray) -> np.ndarray:
+    """Packed row-major weight codes [E][N][K/2] -> the GEMMs' packed copy
+    [E][2][N/16][K/64][16][32]: the tiles, then the channel-major codes."""
+    E, N, KH = c.shape
+    cm = channel_major_codes(c).reshape(E, N // 16, KH // 32, 16, 32)
+    return np.ascontiguousarray(np.stack([tile_wcodes(c), cm], axis=1))
+
+
+def gemm_wscales(s: np.ndarray) -> np.ndarray:
+    """Row-major weight block scales [E][N][K/16] -> the GEMMs' packed copy
+    [E][2][N/16][K/64][16][4]: the tiles, then the channel-major scales
+    [K/16][N]."""
+    E, N, KB = s.shape
+    cm = np.ascontiguousarray(s.transpose(0, 2, 1)).reshape(E, N // 16, KB // 4, 16, 4)
+    return np.ascontiguousarray(np.stack([tile_wscales(s), cm], axis=1))
+
+
 def bits_of(vals: np.ndarray) -> np.ndarray:
     return OF.f64_to_bf16_bits(vals)
 

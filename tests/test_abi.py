@@ -148,7 +148,7 @@ def test_permute_validation():
 
 def test_gemm_validation():
     L = F.lib()
-    ws = L.grouped_w4a4_gemm_rac_workspace_size(4, 64, 64, 128, 256, 8)
+    ws = L.grouped_w4a4_gemm_rac_workspace_size(4, 64, 64, 128, 256, 0)
     args = lambda **kw: [kw.get("ac", FAKE), FAKE, FAKE, kw.get("rows", None), kw.get("msrc", 64),
                          kw.get("R", None), kw.get("S", None), kw.get("k", 0), FAKE, FAKE, FAKE,
                          FAKE, kw.get("E", 4), 64, kw.get("N", 128), kw.get("K", 256), FAKE, FAKE,
@@ -169,16 +169,22 @@ def test_gemm_validation():
 
 
 def test_gemm_workspace_covers_the_k_split(monkeypatch):
-    # a problem too small to fill the chip gets float32 partials for up to 4
-    # slices of K on top of the prefix and the f16 image; a large one none
+    # the prefix, the f16 image, the selected weight columns (bf16 [E][N][kp],
+    # kp = k rounded up to 16) and, for a problem too small to fill the chip,
+    # float32 partials for up to 4 slices of K; a large problem none
     L = F.lib()
     monkeypatch.delenv("NVFP4RAC_SPLIT", raising=False)
     E, M_src, M_total, N, K, k = 8, 1024, 2048, 1024, 2048, 32
-    base = 256 + ((M_src * K * 2 + 255) // 256) * 256
+    base = 256 + ((M_src * K * 2 + 255) // 256) * 256 + E * N * 32 * 2
     small = L.grouped_w4a4_gemm_rac_workspace_size(E, M_src, M_total, N, K, k)
     assert small == base + 4 * M_total * N * 4
     big = L.grouped_w4a4_gemm_rac_workspace_size(128, 16384, 131072, 3072, 4096, 128)
-    assert big == 768 + ((16384 * 4096 * 2 + 255) // 256) * 256
+    assert big == 768 + ((16384 * 4096 * 2 + 255) // 256) * 256 + 128 * 3072 * 128 * 2
+    assert L.grouped_w4a4_gemm_rac_workspace_size(128, 16384, 131072, 3072, 4096, 0) == \
+        768 + ((16384 * 4096 * 2 + 255) // 256) * 256
+    # k = 37 rounds up to 48 channels
+    assert L.grouped_w4a4_gemm_rac_workspace_size(128, 16384, 131072, 3072, 4096, 37) == \
+        768 + ((16384 * 4096 * 2 + 255) // 256) * 256 + 128 * 3072 * 48 * 2
     monkeypatch.setenv("NVFP4RAC_SPLIT", "1")
     assert L.grouped_w4a4_gemm_rac_workspace_size(E, M_src, M_total, N, K, k) == base
     monkeypatch.setenv("NVFP4RAC_SPLIT", "2")

@@ -64,9 +64,9 @@ def check_weights(w_bits, wq, experts, rng, n_rows=256):
         s_gpu = wq.scales[e].cpu().numpy()
         assert np.array_equal(s_gpu[r], s), f"expert {e} scales"
         # the packed copy holds the same bytes
-        assert np.array_equal(untile_wcodes(wq.packed_codes[e:e + 1].cpu().numpy())[0][r],
+        assert np.array_equal(untile_wcodes(wq.packed_codes[e:e + 1, 0].cpu().numpy())[0][r],
                               c_gpu[r]), f"expert {e} packed codes"
-        assert np.array_equal(untile_wscales(wq.packed_scales[e:e + 1].cpu().numpy())[0][r],
+        assert np.array_equal(untile_wscales(wq.packed_scales[e:e + 1, 0].cpu().numpy())[0][r],
                               s_gpu[r]), f"expert {e} packed scales"
 
 

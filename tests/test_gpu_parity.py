@@ -17,7 +17,7 @@ from oracle import gemm as OG
 from oracle import moe as OM
 from oracle import nvfp4 as OQ
 from tests.gpu_util import (assert_gemm_close, f32_bits, heavy_bf16, host_bits, host_vals,
-                            tile_wcodes, tile_wscales, to_dev_bf16, untile_wcodes,
+                            channel_major_codes, gemm_wcodes, gemm_wscales, to_dev_bf16, untile_wcodes,
                             untile_wscales)
 
 pytestmark = pytest.mark.gpu
@@ -142,11 +142,15 @@ def test_qdq_weights_bitexact(dev, E, N, K):
     assert np.array_equal(scales.cpu().numpy(), rs)
     assert np.array_equal(f32_bits(g_w.cpu().numpy()), f32_bits(rg))
     assert np.array_equal(host_bits(w_qdq), OF.f64_to_bf16_bits(rq))
-    # the GEMMs' packed copy: the same bytes, permuted into tiles
-    assert pc.shape == (E, N // 16, K // 64, 16, 32)
-    assert np.array_equal(untile_wcodes(pc.cpu().numpy()), OQ.pack_codes(rc))
-    assert ps.shape == (E, N // 16, K // 64, 16, 4)
-    assert np.array_equal(untile_wscales(ps.cpu().numpy()), rs)
+    # the GEMMs' packed copy: the same bytes, permuted into tiles, then the
+    # channel-major copy
+    assert pc.shape == (E, 2, N // 16, K // 64, 16, 32)
+    assert np.array_equal(untile_wcodes(pc[:, 0].cpu().numpy()), OQ.pack_codes(rc))
+    assert ps.shape == (E, 2, N // 16, K // 64, 16, 4)
+    assert np.array_equal(untile_wscales(ps[:, 0].cpu().numpy()), rs)
+    assert np.array_equal(pc[:, 1].cpu().numpy().reshape(E, K, N // 2),
+                          channel_major_codes(OQ.pack_codes(rc)))
+    assert np.array_equal(ps[:, 1].cpu().numpy().reshape(E, K // 16, N), rs.transpose(0, 2, 1))
     # nvfp4_pack_weights of the row-major outputs gives the same packed copy
     pc2, ps2 = F.nvfp4_pack_weights(codes, scales)
     assert torch.equal(pc2, pc) and torch.equal(ps2, ps)
@@ -227,7 +231,7 @@ def _gemm_case(rng, M_src, counts, N, K, k, gather):
         cu(a_rows) if gather else None,
         to_dev_bf16(OF.f64_to_bf16_bits(qa["R_S"])) if k else None,
         cu(qa["S"]) if k else None,
-        cu(tile_wcodes(OQ.pack_codes(wc))), cu(tile_wscales(ws)), cu(gw), cu(offs), M_total=M_total)
+        cu(gemm_wcodes(OQ.pack_codes(wc))), cu(gemm_wscales(ws)), cu(gw), cu(offs), M_total=M_total)
     torch.cuda.synchronize()
     return host_vals(y), ref
 

@@ -18,7 +18,7 @@ from oracle import gemm as OG
 from oracle import moe as OM
 from oracle import nvfp4 as OQ
 from tests.gpu_util import (assert_gemm_close, f32_bits, heavy_bf16, host_bits, host_vals,
-                            tile_wcodes, tile_wscales, to_dev_bf16)
+                            gemm_wcodes, gemm_wscales, to_dev_bf16)
 from tests.test_gpu_full import sample_rows, weight_host
 
 pytestmark = pytest.mark.gpu
@@ -213,7 +213,7 @@ def test_gemm_per_expert(dev, gemm_kernel, M_src, counts, N, K, k):
                                                  k, cu(a_rows), cu(offs), M_total=M_total)
     wc, ws, gw, _ = OQ.qdq_weights(w)
     y = F.grouped_w4a4_gemm_rac_per_expert(q["codes"], q["scales"], q["g"], cu(a_rows), R, S,
-                                           cu(tile_wcodes(OQ.pack_codes(wc))), cu(tile_wscales(ws)), cu(gw),
+                                           cu(gemm_wcodes(OQ.pack_codes(wc))), cu(gemm_wscales(ws)), cu(gw),
                                            cu(offs), M_total=M_total)
     torch.cuda.synchronize()
     codes, scales, g, A = OQ.quantize(x)
@@ -291,8 +291,8 @@ def test_gemm_swiglu_fused(dev, gemm_kernel, monkeypatch, M_src, counts, I, K, k
     q = F.nvfp4_quantize_act(to_dev_bf16(OF.f64_to_bf16_bits(x)))
     S, R = F.select_residual_channels(q["x_used"], q["codes"], q["scales"], q["g"], q["score"], k)
     wc, ws, gw, _ = OQ.qdq_weights(w)
-    args = (q["codes"], q["scales"], q["g"], cu(a_rows), R, S, cu(tile_wcodes(OQ.pack_codes(wc))),
-            cu(tile_wscales(ws)), cu(gw), cu(offs))
+    args = (q["codes"], q["scales"], q["g"], cu(a_rows), R, S, cu(gemm_wcodes(OQ.pack_codes(wc))),
+            cu(gemm_wscales(ws)), cu(gw), cu(offs))
     h, amax = F.grouped_w4a4_gemm_rac_swiglu(*args, M_total=M_total, with_amax=True)
     y = F.grouped_w4a4_gemm_rac(*args, M_total=M_total)
     hq = F.nvfp4_quantize_act(y, glu=True)

@@ -15,7 +15,7 @@ from fp4_quantized_gemm_amd import pipeline
 from oracle import formats as OF
 from oracle import gemm as OG
 from oracle import nvfp4 as OQ
-from tests.gpu_util import (assert_gemm_close, heavy_bf16, host_vals, tile_wcodes, tile_wscales,
+from tests.gpu_util import (assert_gemm_close, gemm_wcodes, gemm_wscales, heavy_bf16, host_vals,
                             to_dev_bf16)
 from tests.test_gpu_full import sample_rows, weight_host
 
@@ -62,7 +62,7 @@ def test_w4a16_gemm(dev, w16_kernel, M_src, counts, N, K, gather):
     ref = OG.grouped_gemm_w4a16(x, a_rows, wc, ws, gw, offs)
     cu = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     y = F.grouped_w4a16_gemm(to_dev_bf16(OF.f64_to_bf16_bits(x)), cu(a_rows) if gather else None,
-                             cu(tile_wcodes(OQ.pack_codes(wc))), cu(tile_wscales(ws)), cu(gw), cu(offs),
+                             cu(gemm_wcodes(OQ.pack_codes(wc))), cu(gemm_wscales(ws)), cu(gw), cu(offs),
                              M_total=M_total)
     torch.cuda.synchronize()
     e1, e2, ex = assert_gemm_close(host_vals(y), ref)
