@@ -186,7 +186,8 @@ class QdqWeights(NamedTuple):
     scales: torch.Tensor                   # [E][N][K/16] u8, row-major E4M3 block scales
     g: torch.Tensor                        # [E] f32 tensor scales
     qdq: Optional[torch.Tensor]            # [E][N][K] bf16 fake-quantized weight, or None
-    # the GEMMs' packed copy: per expert [0] the tiles [N/16][K/64][16][32]
+    # the GEMMs' packed copy: per expert [0] the 512-byte code tiles [N/16][K/64]
+    # (bytes ordered [2 column halves][16 rows][16]; viewed as [16][32])
     # (codes) and [..][16][4] (scales), [1] the same sizes holding the
     # channel-major codes [K][N/2] and scales [K/16][N]
     packed_codes: Optional[torch.Tensor]   # [E][2][N/16][K/64][16][32]

@@ -64,20 +64,27 @@ k_ceiling_mfma(int64_t iters, float* __restrict__ out) {
   out[blockIdx.x * 256LL + threadIdx.x] = s;
 }
 
-// Streaming read of `n16` 16-byte chunks, four loads in flight per thread;
+// Streaming read of `n16` 16-byte chunks, eight loads in flight per thread;
 // the xor of everything read is written only if it equals a value no input
 // here produces, so the loads stay live and nothing is written.
 __global__ void __launch_bounds__(256)
 k_ceiling_read(const uint4* __restrict__ src, int64_t n16, uint32_t* __restrict__ out) {
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  const v4u* s4 = reinterpret_cast<const v4u*>(src);
   const int64_t stride = (int64_t)gridDim.x * 256;
   int64_t i = blockIdx.x * 256LL + threadIdx.x;
   uint32_t x = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  // eight 16-byte streaming (nontemporal) loads in flight per lane: the
+  // fastest read pattern measured on this chip (plain loads ~10% slower)
+  for (; i + 7 * stride < n16; i += 8 * stride) {
+    v4u a[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u] = __builtin_nontemporal_load(s4 + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x ^= a[u].x ^ a[u].y ^ a[u].z ^ a[u].w;
   }
   for (; i < n16; i += stride) {
-    const uint4 a = src[i];
+    const v4u a = __builtin_nontemporal_load(s4 + i);
     x ^= a.x ^ a.y ^ a.z ^ a.w;
   }
   if (x == 0x9E3779B9u) out[0] = x;
@@ -124,8 +131,8 @@ int nvfp4_ceiling_read(const void* src, int64_t bytes, uint32_t* out, void* stre
   NV_REQUIRE(aligned(src, 16) && aligned(out, 4), NVFP4_ERR_ALIGN,
              "nvfp4_ceiling_read: misaligned pointer");
   const int64_t n16 = bytes / 16;
-  int64_t nb = (n16 + 1023) / 1024;
-  if (nb > 8LL * num_cus()) nb = 8LL * num_cus();
+  int64_t nb = (n16 + 2047) / 2048;
+  if (nb > 32LL * num_cus()) nb = 32LL * num_cus();
   k_ceiling_read<<<(unsigned)nb, 256, 0, as_stream(stream)>>>(
       static_cast<const uint4*>(src), n16, out);
   return check_launch("nvfp4_ceiling_read");

@@ -133,13 +133,16 @@ __device__ __forceinline__ int64_t wscale_offset(int64_t n, int64_t kb, int64_t 
   return (((n >> 4) * (K >> 6) + (kb >> 2)) << 6) + ((n & 15) << 2) + (kb & 3);
 }
 
-// Weight codes are tiled the same way, 512 bytes per 16 rows x 64 k:
-// [N/16][K/64][16 rows][32 bytes], so a 64-k step of a row block is one
-// contiguous run of whole cache lines (row-major [N][K/2] gives each step
-// 32 bytes of every row, half of a 64-byte request).  Byte offset of the
-// code byte holding columns k, k + 1 (k even) of row n, for K columns:
+// Weight codes are tiled the same way, 512 bytes per 16 rows x 64 k, in two
+// halves of 32 columns: [N/16][K/64][2 halves][16 rows][16 bytes].  A 64-k
+// step of a row block is then one contiguous run of whole cache lines
+// (row-major [N][K/2] gives each step 32 bytes of every row, half of a
+// 64-byte request), and a load instruction whose lanes take 16 bytes of 16
+// rows of one half reads whole 128-byte lines.  Byte offset of the code
+// byte holding columns k, k + 1 (k even) of row n, for K columns:
 __device__ __forceinline__ int64_t wcode_offset(int64_t n, int64_t k, int64_t K) {
-  return (((n >> 4) * (K >> 6) + (k >> 6)) << 9) + ((n & 15) << 5) + ((k & 63) >> 1);
+  return (((n >> 4) * (K >> 6) + (k >> 6)) << 9) + (((k & 63) >> 5) << 8) + ((n & 15) << 4) +
+         ((k & 31) >> 1);
 }
 
 // The grouped GEMMs' packed copy of one expert's weights is the code tiles

@@ -488,7 +488,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
     const int r = q >> 1, c = (q & 1) ^ ((r >> 3) & 1);
     int64_t n = wrow(r);
     if (n >= p.N) n = p.N - 1;
-    off_b = (uint32_t)wcode_offset(n, 0, p.K) + 16u * c;   // + 8 k0: the step's tile
+    off_b = (uint32_t)wcode_offset(n, 32 * c, p.K);   // + 8 k0: the step's tile
   }
   if (wave < 4) {
     int64_t n = wrow(wave * 64 + lane);
@@ -1006,7 +1006,7 @@ constexpr int kLdsPerCu = 160 * 1024;
 // correction.
 template <bool W16>
 __global__ void __launch_bounds__(256, 2)
-k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
+k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow, int rsrow) {
   using namespace dec;
   extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
   __shared__ int32_t s_local[KMAX];
@@ -1016,6 +1016,9 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
   __shared__ uint16_t rank64[4 * CHUNKS_MAX + 1];
   uint8_t* const tok = dsm;
   uint8_t* const wsl = dsm + kDecTokBytes;
+  // the pass's residual rows (16 TMAX rows x the selected channels rounded
+  // up to 32, zero past k, row stride rsrow bytes), for every block's epilogue
+  uint8_t* const rsl = wsl + ROWS * wsrow;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, kq = lane >> 4;
@@ -1081,13 +1084,14 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
   const uint8_t* wc = p.w_codes + e * packed_codes_per_expert(p.N, p.K);
   const uint8_t* wsc = p.w_scales + e * packed_scales_per_expert(p.N, p.K);
   // load addresses = a uniform offset (row block, chunk) + a per-lane
-  // offset fixed over the stream: row r16 of the chunk's code tile kq
-  // (512-byte tiles of 16 rows x 64 columns: a row block's chunk is one
-  // contiguous 2 KB run starting at byte rb / 16 * 8 K + 2048 c) and scale
+  // offset fixed over the stream: row r16 of the chunk's code tile kq, whose
+  // two 16-byte halves lie 256 bytes apart (512-byte tiles of 16 rows x 64
+  // columns: a row block's chunk is one contiguous 2 KB run starting at byte
+  // rb / 16 * 8 K + 2048 c) and scale
   // byte 4 r16 + 64 kq of its scale tile (row block rb starts at byte
   // rb / 16 * K)
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const uint32_t lane_c0 = (uint32_t)(512 * kq + 32 * r16);
+  const uint32_t lane_c0 = (uint32_t)(512 * kq + 16 * r16);
   const uint32_t lane_s0 = (uint32_t)(4 * r16 + 64 * kq);
   const bool half_last = (p.K % KC) != 0;    // the last chunk holds 128 columns
   const float gx = W16 ? 1.0f : *p.g_x;
@@ -1104,7 +1108,7 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
     // pass's last chunk may still be reading when its chunk count is odd
     if (t0 > 0) __syncthreads();
     const int ntile_rt = (int)((Me - t0 + 15) / 16 < TMAX ? (Me - t0 + 15) / 16 : TMAX);
-    int64_t src[TMAX], rrow[TMAX];
+    int64_t src[TMAX];
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
       int64_t q = t0 + 16 * t + r16;
@@ -1112,7 +1116,6 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
       const int64_t pr = e_lo + q;
       int64_t sr = p.a_rows ? (int64_t)p.a_rows[pr] : pr;
       src[t] = sr < 0 ? 0 : (sr >= p.M_src ? p.M_src - 1 : sr);
-      rrow[t] = p.r_perm ? pr : src[t];
     }
 
     // K is a multiple of 128: the lanes of a half chunk past the end (kq >= 2
@@ -1151,10 +1154,16 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
           if (rb >= p.N) rb = p.N - 16;
           const uint8_t* cb = wc + (uint32_t)((rb >> 4) * p.K * 8) + (uint32_t)q.c * (KC / 64) * 512;
           const uint8_t* sb = wsc + (uint32_t)((rb >> 4) * p.K) + (uint32_t)q.c * (KC / 64) * 64;
-          const uint4* src4 = reinterpret_cast<const uint4*>(cb + (lane_c - (tl ? 1024u : 0u)));
-          d.wc[part][0] = src4[0];
-          d.wc[part][1] = src4[1];
-          d.ws[part] = *reinterpret_cast<const uint32_t*>(sb + (lane_s - (tl ? 128u : 0u)));
+          // (nontemporal: each weight byte is read once per call, and the
+          // streaming hint measured ~10% more read bandwidth on this chip)
+          // (the row's two 16-byte halves of the tile, 256 bytes apart: each
+          // load instruction reads whole cache lines)
+          const u32x4* src4 = reinterpret_cast<const u32x4*>(cb + (lane_c - (tl ? 1024u : 0u)));
+          const u32x4 c0 = __builtin_nontemporal_load(src4), c1 = __builtin_nontemporal_load(src4 + 16);
+          d.wc[part][0] = make_uint4(c0.x, c0.y, c0.z, c0.w);
+          d.wc[part][1] = make_uint4(c1.x, c1.y, c1.z, c1.w);
+          d.ws[part] = __builtin_nontemporal_load(
+              reinterpret_cast<const uint32_t*>(sb + (lane_s - (tl ? 128u : 0u))));
         } else if (part - 4 < TMAX) {
           const int t = part - 4;
           if constexpr (W16) {
@@ -1208,17 +1217,8 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
             u32x4 rf[TMAX];
   #pragma unroll
             for (int t = 0; t < TMAX; ++t) {
-              const uint16_t* rr = p.R + rrow[t] * kk + slot;
-              if ((kk & 7) == 0 && slot + 8 <= kk) {
-                const uint4 v = *reinterpret_cast<const uint4*>(rr);
-                rf[t] = u32x4{v.x, v.y, v.z, v.w};
-              } else {
-                uint32_t v[8];
-  #pragma unroll
-                for (int q = 0; q < 8; ++q) v[q] = (slot + q < kk) ? rr[q] : 0u;
-                rf[t] = u32x4{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
-                              v[6] | (v[7] << 16)};
-              }
+              const uint4 v = *reinterpret_cast<const uint4*>(rsl + (16 * t + r16) * rsrow + 2 * slot);
+              rf[t] = u32x4{v.x, v.y, v.z, v.w};
             }
   #pragma unroll
             for (int b = 0; b < 4; ++b) {
@@ -1348,6 +1348,32 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow) {
       DecChunk b0, b1;
       Pos qa{0, 0};
       load(b0, qa, 0);
+      if (!W16 && kk > 0) {
+        // residual rows of this pass into LDS (their loads overlap the first
+        // chunk's; the first epilogue's barrier orders them before any read)
+        const int kp32 = (kk + 31) & ~31, per_row = kp32 / 8;
+        for (int q = tid; q < 16 * TMAX * per_row; q += 256) {
+          const int row = q / per_row, c8 = q - row * per_row;
+          int64_t tq = t0 + row;
+          if (tq >= Me) tq = Me - 1;
+          const int64_t pr = e_lo + tq;
+          int64_t sr = p.a_rows ? (int64_t)p.a_rows[pr] : pr;
+          sr = sr < 0 ? 0 : (sr >= p.M_src ? p.M_src - 1 : sr);
+          const int64_t rr = p.r_perm ? pr : sr;
+          const uint16_t* src = p.R + rr * kk + 8 * c8;
+          uint4 o;
+          if ((kk & 7) == 0 && 8 * c8 + 8 <= kk) {
+            o = *reinterpret_cast<const uint4*>(src);
+          } else {
+            uint32_t v[8];
+  #pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = (8 * c8 + j < kk) ? src[j] : 0u;
+            o = make_uint4(v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16),
+                           v[6] | (v[7] << 16));
+          }
+          *reinterpret_cast<uint4*>(rsl + row * rsrow + 16 * c8) = o;
+        }
+      }
       int i = 0;
       for (; i + 2 < total; i += 2) {
         const Pos qb = advance(qa), qc = advance(qb);
@@ -1731,7 +1757,9 @@ static int gemm_rac(bool per_expert, bool glu, uint32_t* h_amax, const uint8_t* 
   if (use_dec) {
     const int64_t n_blocks = (N + dec::ROWS - 1) / dec::ROWS;
     const int wsrow = k > 0 ? (int)(((k + 31) & ~31) * 2 + 16) : 0;
-    const size_t lds = (size_t)kDecTokBytes + (size_t)dec::ROWS * wsrow;
+    const int rsrow = wsrow;                    // (the residual rows: the same channel span)
+    const size_t lds = (size_t)kDecTokBytes + (size_t)dec::ROWS * wsrow +
+                       (size_t)(16 * dec::TMAX) * rsrow;
     // dynamic LDS above 64 KB needs the kernel's limit raised (once per
     // device; the cache is shared by all calling threads)
     static std::mutex dec_mu;
@@ -1742,7 +1770,7 @@ static int gemm_rac(bool per_expert, bool glu, uint32_t* h_amax, const uint8_t* 
     {
       std::lock_guard<std::mutex> lock(dec_mu);
       if ((size_t)dec_lds_limit[dev] < lds) {
-        const int want = (int)kDecTokBytes + dec::ROWS * (dec::KMAX * 2 + 16);
+        const int want = (int)kDecTokBytes + (dec::ROWS + 16 * dec::TMAX) * (dec::KMAX * 2 + 16);
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_decode<false>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, want) != hipSuccess)
           return fail(NVFP4_ERR_HIP, "grouped_w4a4_gemm_rac: cannot raise the LDS limit");
@@ -1757,7 +1785,8 @@ static int gemm_rac(bool per_expert, bool glu, uint32_t* h_amax, const uint8_t* 
     bpw = bpw < 1 ? 1 : (bpw > n_blocks ? n_blocks : bpw);
     const int64_t groups = (n_blocks + bpw - 1) / bpw;
     if (glu) a.y = glu_stage;
-    k_gemm_decode<false><<<(unsigned)(E * groups), 256, lds, s>>>(a, (int)n_blocks, (int)bpw, wsrow);
+    k_gemm_decode<false><<<(unsigned)(E * groups), 256, lds, s>>>(a, (int)n_blocks, (int)bpw, wsrow,
+                                                                 rsrow);
     if (glu) launch_swiglu();
     return check_launch("grouped_w4a4_gemm_rac");
   }
@@ -1912,7 +1941,7 @@ int grouped_w4a16_gemm(const void* x, const int32_t* a_rows, int64_t M_src,
     int64_t bpw = (E * n_blocks + slots - 1) / slots;
     bpw = bpw < 1 ? 1 : (bpw > n_blocks ? n_blocks : bpw);
     const int64_t groups = (n_blocks + bpw - 1) / bpw;
-    k_gemm_decode<true><<<(unsigned)(E * groups), 256, lds, s>>>(a, (int)n_blocks, (int)bpw, 0);
+    k_gemm_decode<true><<<(unsigned)(E * groups), 256, lds, s>>>(a, (int)n_blocks, (int)bpw, 0, 0);
     return check_launch("grouped_w4a16_gemm");
   }
   const int64_t n_tiles = (N + big::BN - 1) / big::BN;

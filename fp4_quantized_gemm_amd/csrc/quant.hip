@@ -190,11 +190,11 @@ k_qdq_slices(const uint16_t* __restrict__ w, int64_t N, int64_t K, int E,
 
 // ---------------------------------------------------------------------------
 // Row-major NVFP4 weights -> the tiles of the grouped GEMMs' packed copy:
-// codes in 512-byte tiles of 16 rows x 64 columns ([N/16][K/64][16][32] per
-// expert) and block scales in 64-byte tiles of the same rows and columns
-// ([..][16][4]).  A permutation of bytes: thread q moves the 16-byte code
-// chunk q of the tiles, and (q < the number of scale dwords) the scale
-// dword q.
+// codes in 512-byte tiles of 16 rows x 64 columns ([N/16][K/64][2][16][16]
+// per expert: column halves, rows, bytes) and block scales in 64-byte tiles
+// of the same rows and columns ([..][16][4]).  A permutation of bytes:
+// thread q moves the 16-byte code chunk q of the tiles, and (q < the number
+// of scale dwords) the scale dword q.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
 k_pack_weights(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t E,
@@ -206,8 +206,8 @@ k_pack_weights(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ sc
   for (int64_t q = blockIdx.x * 256LL + threadIdx.x; q < n_chunks; q += (int64_t)gridDim.x * 256) {
     const int64_t tile = q >> 5, within = q & 31;
     const int64_t kb = tile % kt, nb = (tile / kt) % nt, e = tile / (kt * nt);
-    const int64_t row = e * N + nb * 16 + (within >> 1);
-    const uint4 v = *reinterpret_cast<const uint4*>(codes + row * (K / 2) + kb * 32 + (within & 1) * 16);
+    const int64_t row = e * N + nb * 16 + (within & 15);
+    const uint4 v = *reinterpret_cast<const uint4*>(codes + row * (K / 2) + kb * 32 + (within >> 4) * 16);
     *reinterpret_cast<uint4*>(pcodes + e * packed_codes_per_expert(N, K) + (q - e * chunks_e) * 16) = v;
     if (q < n_words) {
       const int64_t st = q >> 4, r = q & 15;

@@ -36,7 +36,7 @@ double nvfp4_ceiling_mfma_flops(int kind);
 int nvfp4_ceiling_mfma(int kind, int64_t iters, int64_t workgroups, float* out, void* stream);
 
 /* Streaming read of `bytes` (a multiple of 16) from src, 16 bytes per lane
- * per load, four loads in flight per lane; out [1] uint32 is never written
+ * per nontemporal load, eight loads in flight per lane; out [1] uint32 is never written
  * for real data (it keeps the loads live). */
 int nvfp4_ceiling_read(const void* src, int64_t bytes, uint32_t* out, void* stream);
 

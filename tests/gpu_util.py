@@ -32,16 +32,20 @@ def untile_wscales(t: np.ndarray) -> np.ndarray:
 
 
 def tile_wcodes(c: np.ndarray) -> np.ndarray:
-    """Packed row-major weight codes [E][N][K/2] -> the library's tiles
-    [E][N/16][K/64][16][32] (a layout change only)."""
+    """Packed row-major weight codes [E][N][K/2] -> the library's tiles: per
+    16 rows x 64 columns, the 32-column halves, each [16 rows][16 bytes]
+    ([E][N/16][K/64][2][16][16], returned as [E][N/16][K/64][16][32]; a
+    layout change only)."""
     E, N, KH = c.shape
-    return np.ascontiguousarray(c.reshape(E, N // 16, 16, KH // 32, 32).transpose(0, 1, 3, 2, 4))
+    t = c.reshape(E, N // 16, 16, KH // 32, 2, 16).transpose(0, 1, 3, 4, 2, 5)
+    return np.ascontiguousarray(t).reshape(E, N // 16, KH // 32, 16, 32)
 
 
 def untile_wcodes(t: np.ndarray) -> np.ndarray:
-    """The library's weight-code tiles [E][N/16][K/64][16][32] -> [E][N][K/2]."""
+    """The library's weight-code tiles -> [E][N][K/2]."""
     E, NB, KG, _, _ = t.shape
-    return np.ascontiguousarray(t.transpose(0, 1, 3, 2, 4)).reshape(E, NB * 16, KG * 32)
+    u = t.reshape(E, NB, KG, 2, 16, 16).transpose(0, 1, 4, 2, 3, 5)
+    return np.ascontiguousarray(u).reshape(E, NB * 16, KG * 32)
 
 
 def channel_major_codes(c: np.ndarray) -> np.ndarray:
