@@ -995,7 +995,7 @@ struct DecChunk {
 // Dynamic LDS: token fragments [2][TMAX][8 steps][64 lanes][16 B], then the
 // W_S tile [256][wsrow] (wsrow = 2 * k rounded up to 32, + 16; none for k = 0).
 constexpr int kDecTokBytes = 2 * dec::TMAX * 8 * 64 * 16;
-constexpr int kDecStaticLds = 4 * dec::KMAX + 32 * dec::CHUNKS_MAX + 2 * (4 * dec::CHUNKS_MAX + 1);
+constexpr int kDecStaticLds = 4 * dec::KMAX + 16;
 constexpr int kLdsPerCu = 160 * 1024;
 
 // W16 = true is the trainer-side W4A16 product on decode-sized problems: the
@@ -1010,10 +1010,6 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow, int rsrow) {
   using namespace dec;
   extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
   __shared__ int32_t s_local[KMAX];
-  // selected columns as a bitmap over K (rounded up to whole chunks), and
-  // rank64[g] = number of selected columns below column 64 g
-  __shared__ uint32_t sel_bm[8 * CHUNKS_MAX];
-  __shared__ uint16_t rank64[4 * CHUNKS_MAX + 1];
   uint8_t* const tok = dsm;
   uint8_t* const wsl = dsm + kDecTokBytes;
   // the pass's residual rows (16 TMAX rows x the selected channels rounded
@@ -1066,23 +1062,14 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow, int rsrow) {
     }
     const int kpad = (kk + 31) & ~31;        // zero channels k .. next multiple of 32
     for (int j = kk; j < kpad; ++j) *reinterpret_cast<uint16_t*>(wsl + tid * wsrow + 2 * j) = 0;
-    for (int w = tid; w < 8 * nc; w += 256) sel_bm[w] = 0u;
-    __syncthreads();
-    // (S is strictly ascending, so bit ranks are the indices j)
-    for (int j = tid; j < kk; j += 256) atomicOr(&sel_bm[s_local[j] >> 5], 1u << (s_local[j] & 31));
-    for (int g = tid; g <= 4 * nc; g += 256) {
-      int a = 0, b = kk;
-      while (a < b) {
-        const int m = (a + b) >> 1;
-        if (s_local[m] < g * 64) a = m + 1; else b = m;
-      }
-      rank64[g] = (uint16_t)a;
-    }
     __syncthreads();
   }
 
   const uint8_t* wc = p.w_codes + e * packed_codes_per_expert(p.N, p.K);
   const uint8_t* wsc = p.w_scales + e * packed_scales_per_expert(p.N, p.K);
+  // the channel-major copies (the residual correction's weight columns)
+  const uint8_t* wcm = wc + p.N * p.K / 2;
+  const uint8_t* wscm = wsc + p.N * p.K / 16;
   // load addresses = a uniform offset (row block, chunk) + a per-lane
   // offset fixed over the stream: row r16 of the chunk's code tile kq, whose
   // two 16-byte halves lie 256 bytes apart (512-byte tiles of 16 rows x 64
@@ -1197,6 +1184,55 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow, int rsrow) {
   #pragma unroll
         for (int t = 0; t < TMAX; ++t) acc[b][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+      // The block's W_S tile (bf16 q * s of the selected channels' weight
+      // columns), gathered from the channel-major copy of the weights in
+      // parts of 32 channels: each wave its own 64 rows (it alone writes and
+      // later reads them); lane task i of part h covers channel
+      // 32 h + (lane + 64 i) / 8 and rows 8 ((lane + 64 i) % 8) .. + 8 of the
+      // wave's rows (4 code bytes, 8 scale bytes).  With enough chunks a
+      // part's loads go out at the end of chunk c_first + h and are stored
+      // at the start of the next chunk.  (32-bit offsets: one expert's
+      // codes are below 4 GiB.)
+      const int nh = (kk + 31) >> 5;
+      const int c_first = nc - 1 - nh < 0 ? 0 : nc - 1 - nh;
+      uint32_t gq[4];
+      uint2 gs[4];
+      auto gather_issue = [&](int blk, int h) __attribute__((always_inline)) {
+        const uint32_t nb = (uint32_t)((blk_lo + blk) * ROWS + 64 * wave);
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int task = lane + 64 * i, ch = 32 * h + (task >> 3), rg = task & 7;
+          uint32_t n = nb + 8 * rg;
+          if (n + 8 > (uint32_t)p.N) n = (uint32_t)p.N - 8;   // rows past N: never stored
+          const uint32_t col = (uint32_t)s_local[ch < kk ? ch : kk - 1];
+          gq[i] = *reinterpret_cast<const uint32_t*>(wcm + (col * (uint32_t)(p.N / 2) + n / 2));
+          gs[i] = *reinterpret_cast<const uint2*>(wscm + ((col >> 4) * (uint32_t)p.N + n));
+        }
+      };
+      auto gather_store = [&](int h) __attribute__((always_inline)) {
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int task = lane + 64 * i, ch = 32 * h + (task >> 3), rg = task & 7;
+          if (ch >= kk) continue;
+          uint8_t* dst = wsl + (64 * wave + 8 * rg) * wsrow + 2 * ch;
+          const uint32_t sc[2] = {gs[i].x, gs[i].y};
+  #pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            f32x2 q2;
+            if (m == 0) q2 = e2m1_unpack2<0>(gq[i]);
+            else if (m == 1) q2 = e2m1_unpack2<1>(gq[i]);
+            else if (m == 2) q2 = e2m1_unpack2<2>(gq[i]);
+            else q2 = e2m1_unpack2<3>(gq[i]);
+            const float s0 = e4m3_decode((sc[m >> 1] >> (16 * (m & 1))) & 0xFFu);
+            const float s1 = e4m3_decode((sc[m >> 1] >> (16 * (m & 1) + 8)) & 0xFFu);
+            *reinterpret_cast<uint16_t*>(dst + (2 * m) * wsrow) =
+                (uint16_t)(__float_as_uint(q2.x * s0) >> 16);
+            *reinterpret_cast<uint16_t*>(dst + (2 * m + 1) * wsrow) =
+                (uint16_t)(__float_as_uint(q2.y * s1) >> 16);
+          }
+        }
+      };
+
       // token fragment of tile t, step s, this lane, in buffer `buf`
       auto frag = [&](int buf, int t, int s) {
         return tok + ((((buf * TMAX + t) * 8 + s) * 64 + lane) << 4);
@@ -1211,6 +1247,13 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow, int rsrow) {
   #pragma unroll
           for (int t = 0; t < TMAX; ++t) acc[b][t] *= gx;
         if (!W16 && kk > 0) {
+          // (short K: parts whose loads could not go out a chunk early)
+  #pragma unroll
+          for (int h = 0; h < 4; ++h)
+            if (h < nh && c_first + h > nc - 2) {
+              gather_issue(blk, h);
+              gather_store(h);
+            }
           __syncthreads();                     // W_S complete
           for (int cb = 0; cb < kk; cb += 32) {
             const int slot = cb + 8 * kq;
@@ -1279,6 +1322,9 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow, int rsrow) {
           *reinterpret_cast<u32x4*>(frag(buf, t, 2 * wave)) = f0;
           *reinterpret_cast<u32x4*>(frag(buf, t, 2 * wave + 1)) = f1;
         }
+  #pragma unroll
+        for (int h = 0; h < 4; ++h)
+          if (!W16 && h < nh && c_first + h <= nc - 2 && c == c_first + h + 1) gather_store(h);
         __syncthreads();
   #pragma unroll
         for (int s = 0; s < 8; ++s) {
@@ -1307,34 +1353,10 @@ k_gemm_decode(GemmArgs p, int n_blocks, int bpw, int wsrow, int rsrow) {
             }
           }
         }
-        if (!W16 && kk > 0) {
-          // weights of the selected channels in this chunk -> W_S rows (each
-          // wave writes, and later reads, only its own 64 rows): each lane
-          // walks the selected columns of its own 64, code dword by code
-          // dword (static, so no register selects), the four row blocks at once
-          const int g64 = 4 * c + kq;
-          const uint32_t m0 = sel_bm[2 * g64], m1 = sel_bm[2 * g64 + 1];
-          const int jb = rank64[g64];
+        // the block's W_S parts: loads out one chunk before their stores
   #pragma unroll
-          for (int sd = 0; sd < 8; ++sd) {
-            uint32_t mb = ((sd < 4 ? m0 : m1) >> (8 * (sd & 3))) & 0xFFu;
-            while (mb) {
-              const int ii = __builtin_ctz(mb);
-              mb &= mb - 1;
-              const uint32_t below = (1u << (8 * (sd & 3) + ii)) - 1u;
-              const int j = jb + (sd < 4 ? __builtin_popcount(m0 & below)
-                                         : __builtin_popcount(m0) + __builtin_popcount(m1 & below));
-  #pragma unroll
-              for (int b = 0; b < 4; ++b) {
-                const uint32_t code = (dword_of(d.wc[b], sd) >> (4 * ii)) & 0xFu;
-                const float qv = e2m1_unpack2<0>(code).x;
-                const float sv = e4m3_decode((d.ws[b] >> (8 * (sd >> 1))) & 0xFFu);
-                *reinterpret_cast<uint16_t*>(wsl + (64 * wave + 16 * b + r16) * wsrow + 2 * j) =
-                    (uint16_t)(__float_as_uint(qv * sv) >> 16);
-              }
-            }
-          }
-        }
+        for (int h = 0; h < 4; ++h)
+          if (!W16 && h < nh && c_first + h <= nc - 2 && c == c_first + h) gather_issue(q.blk, h);
         if (c + 1 == nc) finish(q.blk);
       };
 
