@@ -887,53 +887,48 @@ k_swiglu_rows(const uint16_t* __restrict__ y, int64_t M, int64_t I, uint16_t* __
 // correction: wsel[e][n][j] = bf16(q * s) (exact; no tensor scale) of column
 // S[j] of expert e's row n, j < k, and 0 for k <= j < kp (kp: k rounded up to
 // 16, the correction's MFMA depth).  From the channel-major part of the
-// packed copy: a selected column is N / 2 contiguous code bytes and N scale
-// bytes.  Workgroup (row block of 256, expert); its 256 threads take one row
-// each, the channels in chunks of 32 through an LDS transpose so that a
-// row's values go out as 16-byte stores.
+// packed copy, where a selected column is N / 2 contiguous code bytes and N
+// scale bytes.  Workgroup (256 rows, expert, 16 channels): the 16 column
+// indices first, then every thread's 32 byte loads (row t's code and scale
+// of each channel) at once, so a workgroup waits out two load latencies in
+// all; thread t writes row t's 16 values (32 bytes).
 __global__ void __launch_bounds__(256)
 k_gather_ws(const uint8_t* __restrict__ pcodes, const uint8_t* __restrict__ pscales,
             const int32_t* __restrict__ S, int64_t s_stride, int64_t N, int64_t K, int k, int kp,
             uint16_t* __restrict__ wsel) {
-  __shared__ uint16_t tile[256][34];
   const int t = threadIdx.x;
-  const int64_t e = blockIdx.y, n = (int64_t)blockIdx.x * 256 + t;
+  const int64_t e = blockIdx.y;
+  const int j0 = (int)blockIdx.z * 16;
+  const int64_t n = (int64_t)blockIdx.x * 256 + t;
+  if (n >= N) return;
   S += e * s_stride;
   const uint8_t* cc = pcodes + e * packed_codes_per_expert(N, K) + N * K / 2;
   const uint8_t* cs = pscales + e * packed_scales_per_expert(N, K) + N * K / 16;
-  uint16_t* out = wsel + (e * N + (int64_t)blockIdx.x * 256) * kp;
-  for (int j0 = 0; j0 < kp; j0 += 32) {
-    if (n < N) {
-      for (int jj = 0; jj < 32; ++jj) {
-        const int j = j0 + jj;
-        uint16_t v = 0;
-        if (j < k) {
-          int c = S[j];
-          c = c < 0 ? 0 : (c >= K ? (int)K - 1 : c);
-          const uint32_t code = (cc[(int64_t)c * (N / 2) + (n >> 1)] >> (4 * (n & 1))) & 0xFu;
-          const float sv = e4m3_decode(cs[(int64_t)(c >> 4) * N + n]);
-          v = (uint16_t)(__float_as_uint(e2m1_unpack2<0>(code).x * sv) >> 16);
-        }
-        tile[t][jj] = v;
-      }
-    }
-    __syncthreads();
-    // row r of the block: channels j0 .. j0 + 31 (or up to kp), 8 per store
-    const int per_row = (kp - j0 < 32 ? kp - j0 : 32) / 8;
-    for (int q = t; q < 256 * per_row; q += 256) {
-      const int r = q / per_row, c8 = q - r * per_row;
-      if ((int64_t)blockIdx.x * 256 + r < N) {
-        const uint16_t* src = &tile[r][8 * c8];
-        uint4 o;
-        o.x = src[0] | ((uint32_t)src[1] << 16);
-        o.y = src[2] | ((uint32_t)src[3] << 16);
-        o.z = src[4] | ((uint32_t)src[5] << 16);
-        o.w = src[6] | ((uint32_t)src[7] << 16);
-        *reinterpret_cast<uint4*>(out + (int64_t)r * kp + j0 + 8 * c8) = o;
-      }
-    }
-    __syncthreads();
+  int col[16];
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    const int j = j0 + jj < k ? j0 + jj : k - 1;
+    const int c = S[j];                            // (uniform over the workgroup)
+    col[jj] = c < 0 ? 0 : (c >= K ? (int)K - 1 : c);
   }
+  uint32_t code[16], sc[16];
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    code[jj] = cc[(int64_t)col[jj] * (N / 2) + (n >> 1)];
+    sc[jj] = cs[(int64_t)(col[jj] >> 4) * N + n];
+  }
+  uint32_t v[8];
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    const uint32_t q4 = (code[jj] >> (4 * (n & 1))) & 0xFu;
+    const float f = e2m1_unpack2<0>(q4).x * e4m3_decode(sc[jj]);
+    const uint32_t b = j0 + jj < k ? __float_as_uint(f) >> 16 : 0u;
+    if (jj & 1) v[jj >> 1] |= b << 16;
+    else v[jj >> 1] = b;
+  }
+  uint4* out = reinterpret_cast<uint4*>(wsel + (e * N + n) * kp + j0);
+  out[0] = make_uint4(v[0], v[1], v[2], v[3]);
+  out[1] = make_uint4(v[4], v[5], v[6], v[7]);
 }
 
 // ---------------------------------------------------------------------------
@@ -1821,8 +1816,9 @@ static int gemm_rac(bool per_expert, bool glu, uint32_t* h_amax, const uint8_t* 
     const size_t wsel_off = img_offset(E) + round_up((size_t)M_src * (size_t)K * 2, 256);
     if (k > 0) {
       uint16_t* wsel = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + wsel_off);
-      k_gather_ws<<<dim3((unsigned)((N + 255) / 256), (unsigned)E), 256, 0, s>>>(
-          w_codes, w_scales, S, a.s_stride, N, K, (int)k, (int)((k + 15) & ~15), wsel);
+      const int kp = (int)((k + 15) & ~15);
+      k_gather_ws<<<dim3((unsigned)((N + 255) / 256), (unsigned)E, (unsigned)(kp / 16)), 256, 0,
+                    s>>>(w_codes, w_scales, S, a.s_stride, N, K, (int)k, kp, wsel);
       a.wsel = wsel;
     }
     const int64_t chunks = M_src * (K / 8);
