@@ -373,8 +373,9 @@ k_decode_a(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales
 }
 
 // Eight waves (two per SIMD, so one wave's waits are covered by the other's
-// MFMAs): wave w owns rows 128 * (w / 4) .. +128 and columns 64 * (w % 4) .. +64
-// of the 256x256 tile.
+// MFMAs): wave w owns all 256 rows and columns 32 w .. +32 of the 256x256
+// tile, so each weight fragment it decodes feeds eight MFMAs (the decode's
+// instructions are what limits a SIMD's issue).
 //
 // W16 = true is the trainer-side W4A16 product (bf16 activations times the
 // same dequantized weights): A is the bf16 activation itself, staged the same
@@ -398,7 +399,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // 0..7, wave-uniform (SGPR)
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wn = wave;
   const int kg = lane >> 5, r32 = lane & 31;
 
   // tile order: groups of 4 row tiles x all column tiles, so the workgroups
@@ -549,11 +550,11 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
     }
   };
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[8][1];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 1; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -571,35 +572,35 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
     const uint8_t* bb = ab + A_BYTES;
     const uint8_t* sb = bb + B_CODES;
 
-    uint4 br[2];
-    uint32_t bs[2];
+    uint4 br[1];
+    uint32_t bs[1];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int rb = wn * 64 + 32 * j + r32;
+    for (int j = 0; j < 1; ++j) {
+      const int rb = wn * 32 + 32 * j + r32;
       br[j] = *reinterpret_cast<const uint4*>(bb + rb * 32 + physb * 16);
       bs[j] = *reinterpret_cast<const uint16_t*>(sb + rb * 4 + 2 * kg);
     }
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      float sbv[2];
-      h2_t mb[2];
+      float sbv[1];
+      h2_t mb[1];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < 1; ++j) {
         if constexpr (W16) sbv[j] = e4m3_decode((bs[j] >> (8 * hb)) & 0xFFu);
         else scale_prep((bs[j] >> (8 * hb)) & 0xFFu, sbv[j], mb[j]);
       }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const int t = 2 * hb + s2;
-        u32x4 A[4];
+        u32x4 A[8];
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-          const int ra = wm * 128 + 32 * i + r32;
+          const int ra = 32 * i + r32;
           const uint4 v4 = *reinterpret_cast<const uint4*>(ab + ra * 128 + (((2 * t + kg) ^ swa) << 4));
           A[i] = u32x4{v4.x, v4.y, v4.z, v4.w};
         }
 #pragma unroll
-        for (int j = 0; j < (NV > 0 ? 2 : 0); ++j) {
+        for (int j = 0; j < (NV > 0 ? 1 : 0); ++j) {
           const uint32_t w = t == 0 ? br[j].x : t == 1 ? br[j].y : t == 2 ? br[j].z : br[j].w;
           if constexpr (W16) {
             const u32x4 B = decode8_bf16(w, sbv[j]);
@@ -621,57 +622,52 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   issue_loads(st0, (uint32_t)kt_lo * BK);
   wait_vmem0();
   __syncthreads();
-  // this wave's valid rows: expert tail tiles run fewer MFMAs (every wave
-  // still takes part in the loads and barriers).  nk is even (K % 128 == 0).
-  const int v_wave = v_tile - wm * 128;
-  using nv4 = std::integral_constant<int, 4>;
-  using nv1 = std::integral_constant<int, 1>;
-  using nv0 = std::integral_constant<int, 0>;
-  if (W16 || v_wave > 32) {      // (the W4A16 kernel keeps one loop: fewer registers)
+  // the tile's valid rows: expert tail tiles run fewer MFMAs (their first NV
+  // 32-row blocks; every wave still takes part in the loads and barriers).
+  // nk is even (K % 128 == 0).
+  auto run = [&](auto nv_c) __attribute__((always_inline)) {
     for (int kt = kt_lo; kt < kt_hi; kt += 2) {
-      kstep(st0, st1, kt, nv4{});
-      kstep(st1, st0, kt + 1, nv4{});
+      kstep(st0, st1, kt, nv_c);
+      kstep(st1, st0, kt + 1, nv_c);
     }
-  } else if (v_wave > 0) {
-    for (int kt = kt_lo; kt < kt_hi; kt += 2) {
-      kstep(st0, st1, kt, nv1{});
-      kstep(st1, st0, kt + 1, nv1{});
-    }
-  } else {
-    for (int kt = kt_lo; kt < kt_hi; kt += 2) {
-      kstep(st0, st1, kt, nv0{});
-      kstep(st1, st0, kt + 1, nv0{});
-    }
-  }
+  };
+  if (W16 || v_tile > 128)       // (the W4A16 kernel keeps one loop: less code)
+    run(std::integral_constant<int, 8>{});
+  else if (v_tile > 64)
+    run(std::integral_constant<int, 4>{});
+  else if (v_tile > 32)
+    run(std::integral_constant<int, 2>{});
+  else
+    run(std::integral_constant<int, 1>{});
 
   // epilogue: x g_x, residual K-extension (16 channels per MFMA), x g_w.
   // Residual operand loads are issued in batches of four chunks, then consumed.
   if constexpr (!W16) {
     const float gx = *p.g_x;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] *= gx;
+      for (int j = 0; j < 1; ++j) acc[i][j] *= gx;
   }
 
   // (the loop ends on stage st1: the first residual half is in st0)
   auto rac_half = [&](const uint8_t* rb, int cb0) __attribute__((always_inline)) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      u32x4 A[4];
+      u32x4 A[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ra = wm * 128 + 32 * i + r32;
+      for (int i = 0; i < 8; ++i) {
+        const int ra = 32 * i + r32;
         const uint4 v4 = *reinterpret_cast<const uint4*>(rb + ra * 128 + (((2 * c + kg) ^ swa) << 4));
         A[i] = u32x4{v4.x, v4.y, v4.z, v4.w};
       }
       const int slot = cb0 + 16 * c + 8 * kg;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint4 vv = *reinterpret_cast<const uint4*>(wsl + (wn * 64 + 32 * j + r32) * WSROW + 2 * slot);
+      for (int j = 0; j < 1; ++j) {
+        const uint4 vv = *reinterpret_cast<const uint4*>(wsl + (wn * 32 + 32 * j + r32) * WSROW + 2 * slot);
         const u32x4 B = u32x4{vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i][j] = mfma32_bf16(A[i], B, acc[i][j]);
+        for (int i = 0; i < 8; ++i) acc[i][j] = mfma32_bf16(A[i], B, acc[i][j]);
       }
     }
   };
@@ -707,67 +703,53 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
       }
     }
   }
-  for (int cb0 = 0; !rdma && cb0 < kk; cb0 += 64) {
-    u32x4 A[4][4];
+  // (k % 64 != 0: each lane loads its residual rows' 8-channel pieces)
+#pragma unroll 1
+  for (int cb = 0; !rdma && cb < kk; cb += 16) {
+    const int slot = cb + 8 * kg;
+    u32x4 A[8];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int slot = cb0 + 16 * c + 8 * kg;
+    for (int i = 0; i < 8; ++i) {
+      const int lr = 32 * i + r32;
+      int64_t t = rows_src[lr];
+      if (p.r_perm) t = p0 + lr < e_hi ? p0 + lr : e_hi - 1;
+      const uint16_t* rr = p.R + t * kk + slot;
+      if ((kk & 7) == 0 && slot + 8 <= kk) {
+        const uint4 vv = *reinterpret_cast<const uint4*>(rr);
+        A[i] = u32x4{vv.x, vv.y, vv.z, vv.w};
+      } else {
+        uint32_t vv[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int lr = wm * 128 + 32 * i + r32;
-        int64_t t = rows_src[lr];
-        if (p.r_perm) t = p0 + lr < e_hi ? p0 + lr : e_hi - 1;
-        const uint16_t* rr = p.R + t * kk + slot;
-        if ((kk & 7) == 0 && slot + 8 <= kk) {
-          const uint4 vv = *reinterpret_cast<const uint4*>(rr);
-          A[c][i] = u32x4{vv.x, vv.y, vv.z, vv.w};
-        } else {
-          uint32_t vv[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) vv[q] = (slot + q < kk) ? rr[q] : 0u;
-          A[c][i] = u32x4{vv[0] | (vv[1] << 16), vv[2] | (vv[3] << 16), vv[4] | (vv[5] << 16),
-                          vv[6] | (vv[7] << 16)};
-        }
+        for (int q = 0; q < 8; ++q) vv[q] = (slot + q < kk) ? rr[q] : 0u;
+        A[i] = u32x4{vv[0] | (vv[1] << 16), vv[2] | (vv[3] << 16), vv[4] | (vv[5] << 16),
+                     vv[6] | (vv[7] << 16)};
       }
     }
+    const uint4 vv = *reinterpret_cast<const uint4*>(wsl + (wn * 32 + r32) * WSROW + 2 * slot);
+    const u32x4 B = u32x4{vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if (cb0 + 16 * c >= kk) break;
-      const int slot = cb0 + 16 * c + 8 * kg;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint4 vv = *reinterpret_cast<const uint4*>(wsl + (wn * 64 + 32 * j + r32) * WSROW + 2 * slot);
-        const u32x4 B = u32x4{vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i][j] = mfma32_bf16(A[c][i], B, acc[i][j]);
-      }
-    }
+    for (int i = 0; i < 8; ++i) acc[i][0] = mfma32_bf16(A[i], B, acc[i][0]);
   }
 
   if constexpr (SPLIT) {
-    // this slice's float32 partial, with g_x and the correction of the
-    // selected channels among its own k-steps (the other W_S slots are zero);
-    // g_w and the rounding come in the fixed-order reduction.  Staged
-    // through LDS a 64-row quarter of the tile at a time (by the four waves
-    // that own it) for 16-byte row stores.
+    // this slice's float32 partial, with g_x (and on slice 0 the
+    // correction); g_w and the rounding come in the fixed-order reduction.
+    // Staged through LDS a 64-row quarter of the tile at a time for 16-byte
+    // row stores.
     float* dst = p.part + (int64_t)blockIdx.y * p.M_total * p.N;
     constexpr int FROW = BN * 4 + 16;            // float32 staging row (+pad)
     static_assert(64 * FROW <= WS_BYTES, "quarter staging fits the W_S tile");
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd) {
       __syncthreads();
-      if (wm == (qd >> 1)) {
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii)
+      for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int row = 32 * ii + 8 * (r >> 2) + 4 * kg + (r & 3);
-              const int col = wn * 64 + 32 * j + r32;
-              *reinterpret_cast<float*>(wsl + row * FROW + 4 * col) = acc[2 * (qd & 1) + ii][j][r];
-            }
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * ii + 8 * (r >> 2) + 4 * kg + (r & 3);
+          const int col = wn * 32 + r32;
+          *reinterpret_cast<float*>(wsl + row * FROW + 4 * col) = acc[2 * qd + ii][0][r];
+        }
       __syncthreads();
       for (int q = tid; q < 64 * (BN / 4); q += 512) {
         const int row = q / (BN / 4), ch = q % (BN / 4);
@@ -781,26 +763,22 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
     return;
   }
 
-  // y = bf16(g_w * acc), staged through LDS (one 128-row half at a time, by
-  // the four waves that own it) for 16-byte row stores
+  // y = bf16(g_w * acc), staged through LDS (one 128-row half at a time)
+  // for 16-byte row stores
   const float gw = p.g_w[e];
   uint32_t hmax = 0;                             // max |h| bits (fused SwiGLU)
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     __syncthreads();
-    if (wm == h) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = 32 * i + 8 * (r >> 2) + 4 * kg + (r & 3);
-            const int col = wn * 64 + 32 * j + r32;
-            *reinterpret_cast<uint16_t*>(wsl + row * OUTROW + 2 * col) =
-                (uint16_t)f32_to_bf16_rne(acc[i][j][r] * gw);
-          }
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * i + 8 * (r >> 2) + 4 * kg + (r & 3);
+        const int col = wn * 32 + r32;
+        *reinterpret_cast<uint16_t*>(wsl + row * OUTROW + 2 * col) =
+            (uint16_t)f32_to_bf16_rne(acc[4 * h + i][0][r] * gw);
+      }
     __syncthreads();
     if (p.glu_i > 0) {
       // h = bf16(silu(gate) * up) of the staged bf16 outputs: gate columns
