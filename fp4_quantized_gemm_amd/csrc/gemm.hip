@@ -44,7 +44,6 @@ struct GemmArgs {
   const uint8_t* w_codes;
   const uint8_t* w_scales;
   const float* g_w;
-  const uint16_t* wsel;        // [E][N][kp] bf16 q * s of the selected columns (large-tile kernel)
   const int32_t* offsets;
   const int32_t* tile_prefix;
   uint16_t* y;
@@ -395,6 +394,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   __shared__ __attribute__((aligned(16))) uint8_t st1[STAGE];
   __shared__ __attribute__((aligned(16))) uint8_t wsl[WS_BYTES];   // W_S tile, then output staging
   __shared__ int32_t rows_src[BM];
+  __shared__ int32_t s_sel[KMAX];                      // the first W_S tile's channels
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -448,20 +448,23 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   const uint32_t Kh = (uint32_t)(p.K / 2), Ks = (uint32_t)(p.K / 16), K2 = (uint32_t)(p.K * 2);
   // channels of the correction (K slices: all on slice 0, none on the others)
   const int kk = (W16 || (SPLIT && blockIdx.y != 0)) ? 0 : p.k;
-  // The selected channels' weight columns come from p.wsel (bf16
-  // [E][N][kp], kp = k rounded up to 16, zero past k), KMAX channels (one
-  // W_S tile) at a time; the first tile is loaded as the main loop runs.
-  const int64_t kp = (p.k + 15) & ~15;
+  // The selected channels' weight columns go through LDS KMAX channels (one
+  // W_S tile, bf16, zero past k) at a time; the first tile is loaded with
+  // the first k-step.
   const int ws_ch = kk > KMAX ? KMAX : (int)((kk + 15) & ~15);   // channels per W_S tile
   // the residual rows by direct loads in 64-channel halves (k % 64 == 0);
   // otherwise each lane loads its own
   const bool rdma = kk > 0 && (kk & 63) == 0;
 
+  auto sel_col = [&](int c) { return c < 0 ? 0 : (c >= p.K ? (int)p.K - 1 : c); };
   if (tid < BM) {
     int64_t pr = p0 + tid;
     if (pr >= e_hi) pr = e_hi - 1;
     int64_t t = p.a_rows ? (int64_t)p.a_rows[pr] : pr;
     rows_src[tid] = (int32_t)(t < 0 ? 0 : (t >= p.M_src ? p.M_src - 1 : t));
+  } else if (tid - BM < ws_ch) {
+    const int j = tid - BM;
+    s_sel[j] = sel_col(p.S[(int64_t)e * p.s_stride + (j < kk ? j : kk - 1)]);
   }
   __syncthreads();
   const int nk = (int)(p.K / BK);
@@ -518,22 +521,72 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
                                        0, 0);
   };
 
-  // W_S tile of channels c0 .. c0 + ws_ch into wsl: instruction b (of
-  // WS_INSTS, b % 8 = wave) fills LDS bytes 1024 b ..; lanes in a row's pad
-  // or past the tile's channels load nothing (those slots are never read)
-  constexpr int WS_INSTS = (BN * WSROW + 1023) / 1024;
-  const uint16_t* wse = p.wsel + (int64_t)e * p.N * kp;
-  auto issue_ws = [&](int c0, int b) __attribute__((always_inline)) {
-    const int o = b * 1024 + lane * 16;
-    const int row = o / WSROW, cb = o - row * WSROW;
-    if (b < WS_INSTS && row < BN && cb < ws_ch * 2) {
-      int64_t n = wrow(row);
-      if (n >= p.N) n = p.N - 1;
-      __builtin_amdgcn_global_load_lds(wse + n * kp + c0 + cb / 2, wsl + b * 1024, 16, 0, 0);
+  // W_S tile of channels c0 .. c0 + ws_ch into wsl, read from the channel-
+  // major part of the packed weights (a selected channel is N / 2 code bytes
+  // and, for its block of 16 channels, N scale bytes): wave u takes channels
+  // c0 + 16 u .. +16 (u < ws_ch / 16), lane l the tile rows 8 (l % 32) .. +8
+  // (eight consecutive weight rows) and channels 8 (l / 32) .. +8 of those,
+  // one code dword and two scale dwords per channel (whole 128-byte lines
+  // across the wave).  ws_issue loads them, ws_store decodes bf16 q * s
+  // (exact; zero past k) and writes each row's 8 channels as one 16-byte
+  // piece.
+  const uint8_t* wcm = wc + (int64_t)p.N * p.K / 2;     // codes [K][N / 2]
+  const uint8_t* wscm = wsc + (int64_t)p.N * p.K / 16;  // scales [K / 16][N]
+  const int ws_r8 = 8 * (lane & 31);
+  const int ws_cl = 16 * wave + 8 * (lane >> 5);         // the lane's first channel slot
+  uint32_t wq[8], wsa[8], wsb[8];
+  auto ws_issue = [&](int c0) __attribute__((always_inline)) {
+    if (16 * wave >= ws_ch) return;
+    int64_t n;                                          // first of the lane's 8 weight rows
+    if (W16 || p.glu_i == 0) {
+      n = n0 + ws_r8;
+      if (n + 8 > p.N) n = p.N - 8;
+    } else {
+      int64_t c = (int64_t)nt * 128 + (ws_r8 & 127);
+      if (c + 8 > p.glu_i) c = p.glu_i - 8;
+      n = ws_r8 < 128 ? c : p.glu_i + c;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int slot = c0 + ws_cl + j;
+      const int c = c0 == 0 ? s_sel[slot < KMAX ? slot : KMAX - 1]
+                            : sel_col(p.S[(int64_t)e * p.s_stride + (slot < kk ? slot : kk - 1)]);
+      wq[j] = *reinterpret_cast<const uint32_t*>(wcm + (uint32_t)c * (uint32_t)(p.N / 2) +
+                                                 (uint32_t)(n >> 1));
+      const uint2 sv = *reinterpret_cast<const uint2*>(wscm + (uint32_t)(c >> 4) * (uint32_t)p.N +
+                                                       (uint32_t)n);
+      wsa[j] = sv.x;
+      wsb[j] = sv.y;
     }
   };
-  // the first W_S tile goes out with the first ws_steps k-steps' loads
-  const int ws_steps = kk > 0 ? (nks < (WS_INSTS + 7) / 8 ? nks : (WS_INSTS + 7) / 8) : 0;
+  auto ws_store = [&](int c0) __attribute__((always_inline)) {
+    if (16 * wave >= ws_ch) return;
+    uint32_t q[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = c0 + ws_cl + j < kk ? wq[j] : 0u;   // +0 past k
+    // rows 2 h and 2 h + 1: code byte h of each channel, scale bytes 2 h, 2 h + 1
+    auto rows2 = [&](auto h_c) __attribute__((always_inline)) {
+      constexpr int H = decltype(h_c)::value;
+      float v0[8], v1[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const f32x2 f = e2m1_unpack2<H>(q[j]);
+        const int sw = H < 2 ? (int)wsa[j] : (int)wsb[j];
+        v0[j] = f.x * __builtin_amdgcn_cvt_f32_fp8(sw, (2 * H) & 3);
+        v1[j] = f.y * __builtin_amdgcn_cvt_f32_fp8(sw, (2 * H + 1) & 3);
+      }
+      *reinterpret_cast<uint4*>(wsl + (ws_r8 + 2 * H) * WSROW + 2 * ws_cl) =
+          make_uint4(pack_hi16(v0[0], v0[1]), pack_hi16(v0[2], v0[3]), pack_hi16(v0[4], v0[5]),
+                     pack_hi16(v0[6], v0[7]));
+      *reinterpret_cast<uint4*>(wsl + (ws_r8 + 2 * H + 1) * WSROW + 2 * ws_cl) =
+          make_uint4(pack_hi16(v1[0], v1[1]), pack_hi16(v1[2], v1[3]), pack_hi16(v1[4], v1[5]),
+                     pack_hi16(v1[6], v1[7]));
+    };
+    rows2(std::integral_constant<int, 0>{});
+    rows2(std::integral_constant<int, 1>{});
+    rows2(std::integral_constant<int, 2>{});
+    rows2(std::integral_constant<int, 3>{});
+  };
 
   // residual rows for the correction, staged like the A image: 64 channels
   // of the tile's 256 rows per stage, 8-channel chunks swizzled as A's
@@ -568,7 +621,6 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
     constexpr int NV = decltype(nv_c)::value;
     if (kt + 1 < kt_hi) issue_loads(nxt, (uint32_t)(kt + 1) * BK);
     else if (rdma) issue_r(nxt, 0);
-    if (kt - kt_lo < ws_steps) issue_ws(0, 8 * (kt - kt_lo) + wave);
     const uint8_t* bb = ab + A_BYTES;
     const uint8_t* sb = bb + B_CODES;
 
@@ -620,8 +672,10 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   };
 
   issue_loads(st0, (uint32_t)kt_lo * BK);
+  if (kk > 0) ws_issue(0);
   wait_vmem0();
   __syncthreads();
+  if (kk > 0) ws_store(0);                       // (read after the k-steps' barriers)
   // the tile's valid rows: expert tail tiles run fewer MFMAs (their first NV
   // 32-row blocks; every wave still takes part in the loads and barriers).
   // nk is even (K % 128 == 0).
@@ -671,13 +725,6 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
       }
     }
   };
-  // the rest of the first W_S tile (fewer k-steps than its loads)
-  if (kk > 0 && 8 * ws_steps < WS_INSTS) {
-#pragma unroll 1
-    for (int b = 8 * ws_steps + wave; b < WS_INSTS; b += 8) issue_ws(0, b);
-    wait_vmem0();
-    __syncthreads();
-  }
   if (rdma) {
     // W_S tiles of KMAX channels; a tile's residual rows in two 64-channel
     // halves (the first tile's first half arrived with the last k-step)
@@ -686,12 +733,12 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
       const bool two = kk - c0 > 64;
       if (c0 > 0) {
         __syncthreads();                       // the last reads of wsl and the stages are done
-#pragma unroll 1
-        for (int b = wave; b < WS_INSTS; b += 8) issue_ws(c0, b);
+        ws_issue(c0);
         issue_r(st0, c0);
       }
       if (two) issue_r(st1, c0 + 64);
       if (c0 > 0) {
+        ws_store(c0);
         wait_vmem0();
         __syncthreads();
       }
@@ -859,54 +906,6 @@ k_swiglu_rows(const uint16_t* __restrict__ y, int64_t M, int64_t I, uint16_t* __
     m8 = max(m8, absmax_bf16x8(o));
   }
   if (h_amax != nullptr) block_atomic_max<256>(m8, h_amax);
-}
-
-// Weight columns of the selected channels for the large-tile kernel's
-// correction: wsel[e][n][j] = bf16(q * s) (exact; no tensor scale) of column
-// S[j] of expert e's row n, j < k, and 0 for k <= j < kp (kp: k rounded up to
-// 16, the correction's MFMA depth).  From the channel-major part of the
-// packed copy, where a selected column is N / 2 contiguous code bytes and N
-// scale bytes.  Workgroup (256 rows, expert, 16 channels): the 16 column
-// indices first, then every thread's 32 byte loads (row t's code and scale
-// of each channel) at once, so a workgroup waits out two load latencies in
-// all; thread t writes row t's 16 values (32 bytes).
-__global__ void __launch_bounds__(256)
-k_gather_ws(const uint8_t* __restrict__ pcodes, const uint8_t* __restrict__ pscales,
-            const int32_t* __restrict__ S, int64_t s_stride, int64_t N, int64_t K, int k, int kp,
-            uint16_t* __restrict__ wsel) {
-  const int t = threadIdx.x;
-  const int64_t e = blockIdx.y;
-  const int j0 = (int)blockIdx.z * 16;
-  const int64_t n = (int64_t)blockIdx.x * 256 + t;
-  if (n >= N) return;
-  S += e * s_stride;
-  const uint8_t* cc = pcodes + e * packed_codes_per_expert(N, K) + N * K / 2;
-  const uint8_t* cs = pscales + e * packed_scales_per_expert(N, K) + N * K / 16;
-  int col[16];
-#pragma unroll
-  for (int jj = 0; jj < 16; ++jj) {
-    const int j = j0 + jj < k ? j0 + jj : k - 1;
-    const int c = S[j];                            // (uniform over the workgroup)
-    col[jj] = c < 0 ? 0 : (c >= K ? (int)K - 1 : c);
-  }
-  uint32_t code[16], sc[16];
-#pragma unroll
-  for (int jj = 0; jj < 16; ++jj) {
-    code[jj] = cc[(int64_t)col[jj] * (N / 2) + (n >> 1)];
-    sc[jj] = cs[(int64_t)(col[jj] >> 4) * N + n];
-  }
-  uint32_t v[8];
-#pragma unroll
-  for (int jj = 0; jj < 16; ++jj) {
-    const uint32_t q4 = (code[jj] >> (4 * (n & 1))) & 0xFu;
-    const float f = e2m1_unpack2<0>(q4).x * e4m3_decode(sc[jj]);
-    const uint32_t b = j0 + jj < k ? __float_as_uint(f) >> 16 : 0u;
-    if (jj & 1) v[jj >> 1] |= b << 16;
-    else v[jj >> 1] = b;
-  }
-  uint4* out = reinterpret_cast<uint4*>(wsel + (e * N + n) * kp + j0);
-  out[0] = make_uint4(v[0], v[1], v[2], v[3]);
-  out[1] = make_uint4(v[4], v[5], v[6], v[7]);
 }
 
 // ---------------------------------------------------------------------------
@@ -1628,12 +1627,6 @@ static size_t img_offset(int64_t E) { return round_up((size_t)(E + 1) * sizeof(i
 // large k (more than the large-tile kernel's W_S tile): the kernel takes a
 // multiple of it
 static bool big_streams_ws(int64_t k) { return k > big::KMAX && k % big::KMAX == 0; }
-// the selected weight columns for the large-tile kernel's correction, bf16
-// [E][N][kp] (kp: k rounded up to 16), after the image
-static size_t wsel_bytes(int64_t E, int64_t N, int64_t k) {
-  return k > 0 ? round_up((size_t)E * (size_t)N * (size_t)((k + 15) & ~15) * 2, 256) : 0;
-}
-
 // K slices of the large-tile kernel for a problem whose tiles fill less than
 // the chip (sized for 256 CUs from the fewest tiles M_total can make; each
 // slice an even number of 64-k steps, at most 4 slices), or 1.
@@ -1661,7 +1654,6 @@ size_t grouped_w4a4_gemm_rac_workspace_size(int64_t E, int64_t M_src, int64_t M_
                                             int64_t K, int64_t k) {
   if (E < 1 || M_src < 0 || M_total < 0 || K < 0 || N < 0) return 256;
   size_t n = img_offset(E) + round_up((size_t)M_src * (size_t)K * 2, 256);
-  n += wsel_bytes(E, N, k);
   n += split_bytes(M_total, N, K, k);
   return n;
 }
@@ -1791,14 +1783,6 @@ static int gemm_rac(bool per_expert, bool glu, uint32_t* h_amax, const uint8_t* 
             (uint64_t)(per_expert ? M_total : M_src) * k * 2 < (1ULL << 32);
   if (use_big) {
     uint16_t* img = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + img_offset(E));
-    const size_t wsel_off = img_offset(E) + round_up((size_t)M_src * (size_t)K * 2, 256);
-    if (k > 0) {
-      uint16_t* wsel = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + wsel_off);
-      const int kp = (int)((k + 15) & ~15);
-      k_gather_ws<<<dim3((unsigned)((N + 255) / 256), (unsigned)E, (unsigned)(kp / 16)), 256, 0,
-                    s>>>(w_codes, w_scales, S, a.s_stride, N, K, (int)k, kp, wsel);
-      a.wsel = wsel;
-    }
     const int64_t chunks = M_src * (K / 8);
     int64_t nb = (chunks + 255) / 256;
     if (nb > 16LL * num_cus()) nb = 16LL * num_cus();
@@ -1808,7 +1792,7 @@ static int gemm_rac(bool per_expert, bool glu, uint32_t* h_amax, const uint8_t* 
     if (glu) a.glu_i = N / 2, a.h_amax = h_amax;
     // a problem that fills less than the chip: K slices, reduced in order
     const int ksplit = glu ? 1 : big_ksplit(M_total, N, K, k);
-    const size_t part_off = wsel_off + wsel_bytes(E, N, k);
+    const size_t part_off = img_offset(E) + round_up((size_t)M_src * (size_t)K * 2, 256);
     if (ksplit > 1 && ws_bytes >= part_off + split_bytes(M_total, N, K, k)) {
       a.ksplit = ksplit;
       a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + part_off);

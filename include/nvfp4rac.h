@@ -325,8 +325,7 @@ int moe_permute(const float* logits, const float* bias, int64_t T, int64_t E, in
  * expert_offsets [E+1] (device; off[0] = 0, off[E] = M_total); y [M_total][N]
  * bf16.  Requires K % 128 == 0, N % 16 == 0, 0 <= k <= K.
  * The workspace holds the per-expert tile prefix, an exact f16 image of the
- * activation (2 bytes per element), when k > 0 the selected weight columns
- * as bf16 (E * N * kp * 2 bytes, kp = k rounded up to 16), and, for a
+ * activation (2 bytes per element) and, for a
  * problem too small to fill the chip, float32 partial products of up to 4
  * slices of K (slices * M_total * N * 4 bytes), summed in slice order, so
  * results do not depend on timing.  A workspace smaller than the query
