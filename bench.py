@@ -471,7 +471,7 @@ def gemm_kernel_name(cfg, m, n, k, E):
     if m <= 48 * E and k <= 128:
         return "k_gemm_decode"
     if (k <= 128 or k % 128 == 0) and cfg.H <= 16384 and cfg.inter <= 16384:
-        return "k_gemm_big" if k <= 128 else "k_extract_ws + k_gemm_big"
+        return "k_gemm_big" if k <= 128 else "k_gemm_big, 128-channel W_S tiles after the loop"
     return "k_gemm_generic"
 
 

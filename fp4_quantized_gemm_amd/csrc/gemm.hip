@@ -927,7 +927,8 @@ k_swiglu_rows(const uint16_t* __restrict__ y, int64_t M, int64_t I, uint16_t* __
 // step s (0..7) takes the lane's code dword s, i.e. k0 + 64 (l / 16) + 8 s + i
 // in the instruction's k slot 8 (l / 16) + i; both operands use this order.
 // The residual correction runs after each block (bf16 MFMAs over the
-// selected channels, whose weights are copied to LDS as the chunks pass).
+// selected channels, whose weight columns are gathered into LDS from the
+// channel-major part of the packed weights during the block's last chunks).
 // ---------------------------------------------------------------------------
 namespace dec {
 constexpr int ROWS = 256;
