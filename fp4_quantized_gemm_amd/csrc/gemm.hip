@@ -301,9 +301,10 @@ constexpr int BM = 256, BN = 256, BK = 64;
 // LDS reads of 16 bytes serve 16 lanes per pass over 64 four-byte banks, so
 // 16 consecutive rows of a fragment must land in 16 distinct 16-byte bank
 // groups: with 128-byte A rows two rows share a 256-byte bank line, hence the
-// A swizzle on row >> 1; with 32-byte B rows eight rows share one.
+// A swizzle on row >> 1.  B keeps the code tiles' own order, in which a
+// half's 16 rows are 256 consecutive bytes.
 constexpr int A_BYTES = BM * BK * 2;           // f16 [256][64]: 8 chunks/row, chunk c at c ^ ((row >> 1) & 7)
-constexpr int B_CODES = BN * 32;               // [256][32 B]: chunk c at c ^ ((row >> 3) & 1)
+constexpr int B_CODES = BN * 32;               // [16][2][16][16 B]: the packed code tiles as stored
 constexpr int B_SCALES = BN * 4;               // [256][4 B]
 constexpr int STAGE = A_BYTES + B_CODES + B_SCALES;   // 41984
 constexpr int KMAX = 128;                      // residual channels held in LDS
@@ -339,6 +340,12 @@ __device__ __forceinline__ void scale_prep(uint32_t byte, float& sc, h2_t& mu) {
 }
 
 __device__ __forceinline__ void wait_vmem0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// word 3 of a raw (untyped, stride 0) buffer resource on gfx9: 32-bit data
+// format, so dword loads return the bytes as stored
+constexpr int kBufferRsrcWord3 = 0x00020000;
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+__device__ __forceinline__ lds_void_ptr lds_ptr(void* p) { return (lds_void_ptr)p; }
 __device__ __forceinline__ f32x16_t mfma32_f16(const u32x4& a, const u32x4& b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
                                                 __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
@@ -488,15 +495,30 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
     off_a[i] = (uint32_t)rows_src[r] * K2 + 16u * (W16 ? 4 * (c & 1) + (c >> 1) : c);
   }
   {
+    // lane q of the stage's B area takes bytes 16 q .. of the tiles in their
+    // stored order (16-row block q / 32, 32-column half (q / 16) % 2, row
+    // q % 16), so a load instruction reads two whole 512-byte code tiles
     const int q = wave * 64 + lane;
-    const int r = q >> 1, c = (q & 1) ^ ((r >> 3) & 1);
+    const int r = 16 * (q >> 5) + (q & 15), c = (q >> 4) & 1;
     int64_t n = wrow(r);
     if (n >= p.N) n = p.N - 1;
     off_b = (uint32_t)wcode_offset(n, 32 * c, p.K);   // + 8 k0: the step's tile
   }
-  if (wave < 4) {
-    int64_t n = wrow(wave * 64 + lane);
-    if (n >= p.N) n = p.N - 1;
+  if (wave == 7) {
+    // the step's 256 x 4 scale bytes in one instruction: lane l takes rows
+    // 4 l .. 4 l + 3 (16 bytes of one scale tile: a 4-row group starting at
+    // a multiple of 4 never crosses a 16-row tile, as N and the gate/up
+    // split are multiples of 8)
+    const int r = 4 * lane;
+    int64_t n;
+    if (W16 || p.glu_i == 0) {
+      n = n0 + r;
+      if (n + 4 > p.N) n = p.N - 4;
+    } else {
+      int64_t c = (int64_t)nt * 128 + (r & 127);
+      if (c + 4 > p.glu_i) c = p.glu_i - 4;
+      n = r < 128 ? c : p.glu_i + c;
+    }
     off_s = (uint32_t)wscale_offset(n, 0, p.K);   // + k0: the step's tile
   }
   // rows of the tile inside the expert: a load instruction covers 8
@@ -506,19 +528,30 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
   // A row)
   const int64_t vt = e_hi - p0;
   const int v_tile = vt > BM ? BM : (int)vt;
-  // (offsets summed in 32 bits, which cannot wrap: the image and one
-  // expert's codes are below 4 GiB; each load then takes a scalar base and
-  // one VGPR instead of a 64-bit per-lane address hoisted out of the loop)
+  // Stage loads are buffer loads into LDS: the lane's byte offset (fixed
+  // over K) is the VGPR offset and the step, k0 times the bytes per column,
+  // the scalar offset, so no per-step address register exists (the image
+  // and one expert's code tiles are below 4 GiB; a buffer's range is its
+  // size, and a load past it reads zeros).
+  const __amdgpu_buffer_rsrc_t rs_a =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a_img), (short)0,
+                                        (int)(uint32_t)((uint64_t)p.M_src * (uint64_t)p.K * 2),
+                                        kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_b = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(wc), (short)0, (int)(uint32_t)(p.N * p.K / 2), kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(wsc), (short)0, (int)(uint32_t)(p.N * p.K / 16), kBufferRsrcWord3);
   auto issue_loads = [&](uint8_t* st, uint32_t k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if ((i * 8 + wave) * 8 < v_tile)
-        __builtin_amdgcn_global_load_lds(a_img + (off_a[i] + k0 * 2), st + (i * 8 + wave) * 1024, 16,
-                                         0, 0);
-    __builtin_amdgcn_global_load_lds(wc + (off_b + k0 * 8), st + A_BYTES + wave * 1024, 16, 0, 0);
-    if (wave < 4)
-      __builtin_amdgcn_global_load_lds(wsc + (off_s + k0), st + A_BYTES + B_CODES + wave * 256, 4,
-                                       0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, lds_ptr(st + (i * 8 + wave) * 1024), 16,
+                                                 off_a[i], k0 * 2, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, lds_ptr(st + A_BYTES + wave * 1024), 16, off_b,
+                                             k0 * 8, 0, 0);
+    if (wave == 7)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_s, lds_ptr(st + A_BYTES + B_CODES), 16, off_s, k0,
+                                               0, 0);
   };
 
   // W_S tile of channels c0 .. c0 + ws_ch into wsl, read from the channel-
@@ -612,7 +645,11 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int swa = (r32 >> 1) & 7;                  // A rows = 32 i + r32 (+ multiples of 32)
-  const int physb = kg ^ ((r32 >> 3) & 1);
+  // the lane's B fragment in the stage: row wn * 32 + r32, half kg, in the
+  // code tiles' order (the empty asm keeps the sum an opaque offset from the
+  // stage, so the compiler still tells the two stages apart)
+  int b_off = (2 * wn + (r32 >> 4)) * 512 + kg * 256 + (r32 & 15) * 16;
+  asm volatile("" : "+v"(b_off));
 
   // one k-step on stage `ab` while stage `nxt` fills with step kt + 1; the
   // wave computes its first NV 32-row blocks (the others lie past the
@@ -629,7 +666,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
 #pragma unroll
     for (int j = 0; j < 1; ++j) {
       const int rb = wn * 32 + 32 * j + r32;
-      br[j] = *reinterpret_cast<const uint4*>(bb + rb * 32 + physb * 16);
+      br[j] = *reinterpret_cast<const uint4*>(bb + b_off);
       bs[j] = *reinterpret_cast<const uint16_t*>(sb + rb * 4 + 2 * kg);
     }
 #pragma unroll
