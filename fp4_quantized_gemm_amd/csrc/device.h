@@ -30,6 +30,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// Two float32 values -> their bf16 bits packed (a low, b high), round to
+// nearest even: one hardware conversion on gfx950.
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Non-negative float32 -> E4M3 byte, round to nearest even, saturate at 448.
 // Subnormal range (u < 2^-6): the code is the nearest multiple of 2^-9,
 // which rintf (ties to even) gives exactly after an exact power-of-two
