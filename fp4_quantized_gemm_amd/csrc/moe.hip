@@ -3,7 +3,8 @@
 // gist.science technical summary §4; the router is not described there:
 // top-k of logit + bias, ties to the lower expert, softmax over the chosen k).
 //
-// Permutation without host synchronisation or float atomics:
+// Permutation without host synchronisation or float atomics (a few tokens:
+// steps 2-4 in one workgroup, k_permute_small):
 //   1. k_route: one wave per token -> topk_ids, topk_w (softmax in float64).
 //   2. k_route_masks: one wave per chunk of 64 tokens; per expert a 64-bit
 //      mask of the chunk's tokens that chose it (LDS atomic OR), plus counts.
@@ -20,12 +21,13 @@ namespace nvfp4 {
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopk = 32;
 
-__global__ void __launch_bounds__(256)
-k_route(const float* __restrict__ logits, const float* __restrict__ bias, int64_t T, int E,
-        int tk, int32_t* __restrict__ ids, float* __restrict__ w) {
+// Routing of token t by one wave: the top-tk experts of logit + bias (ties
+// to the lower expert) and their softmax weights.
+__device__ __forceinline__ void route_token(const float* __restrict__ logits,
+                                            const float* __restrict__ bias, int64_t t, int E,
+                                            int tk, int32_t* __restrict__ ids,
+                                            float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = blockIdx.x * 4LL + (threadIdx.x >> 6);
-  if (t >= T) return;
   constexpr int kPer = kMaxExperts / 64;
   float v[kPer];
   uint32_t taken = 0;
@@ -76,6 +78,14 @@ k_route(const float* __restrict__ logits, const float* __restrict__ bias, int64_
     ids[t * tk + lane] = my_e;
     w[t * tk + lane] = (float)(z / sum);
   }
+}
+
+__global__ void __launch_bounds__(256)
+k_route(const float* __restrict__ logits, const float* __restrict__ bias, int64_t T, int E,
+        int tk, int32_t* __restrict__ ids, float* __restrict__ w) {
+  const int64_t t = blockIdx.x * 4LL + (threadIdx.x >> 6);
+  if (t >= T) return;
+  route_token(logits, bias, t, E, tk, ids, w);
 }
 
 // masks [nchunks][E] uint64, counts [nchunks][E] int32
@@ -157,6 +167,61 @@ k_scatter(const int32_t* __restrict__ ids, int64_t T, int E, int tk,
     const int p = offsets[e] + base[c * E + e] + __popcll(masks[c * E + e] & below);
     perm_token[p] = (int32_t)t;
     inv_perm[t * tk + j] = p;
+  }
+}
+
+// Steps 2-4 in one workgroup for a few tokens (T <= 512, E <= 256), with
+// barriers between them: the chunk masks and counts live in LDS, thread e
+// scans expert e's chunks, the first E threads scan the totals, and thread t
+// scatters token t.  Identical results, one launch after k_route.
+constexpr int kSmallT = 512;
+constexpr int kSmallE = 256;
+__global__ void __launch_bounds__(1024)
+k_permute_small(const int32_t* __restrict__ ids, int T, int E, int tk,
+                int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token,
+                int32_t* __restrict__ inv_perm) {
+  __shared__ unsigned long long m[kSmallT / 64][kSmallE];
+  __shared__ int base[kSmallT / 64][kSmallE];
+  __shared__ int off[kSmallE];
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int nchunks = (T + 63) / 64;
+  for (int i = tid; i < nchunks * kSmallE; i += 1024) m[i / kSmallE][i % kSmallE] = 0ull;
+  __syncthreads();
+  if (tid < T)
+    for (int j = 0; j < tk; ++j) atomicOr(&m[tid >> 6][ids[tid * tk + j]], 1ull << (tid & 63));
+  __syncthreads();
+  int total = 0;
+  if (tid < E)
+    for (int c = 0; c < nchunks; ++c) {
+      base[c][tid] = total;
+      total += __popcll(m[c][tid]);
+    }
+  // exclusive scan of the totals over the experts
+  int incl = total;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o);
+    if ((tid & 63) >= o) incl += u;
+  }
+  if ((tid & 63) == 63) wsum[wave] = incl;
+  __syncthreads();
+  int wb = 0;
+  for (int q = 0; q < wave; ++q) wb += wsum[q];
+  if (tid < E) {
+    off[tid] = wb + incl - total;
+    offsets[tid] = wb + incl - total;
+  }
+  if (tid == E - 1) offsets[E] = wb + incl;
+  __syncthreads();
+  if (tid < T) {
+    const int c = tid >> 6, lane = tid & 63;
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    for (int j = 0; j < tk; ++j) {
+      const int e = ids[tid * tk + j];
+      const int p = off[e] + base[c][e] + __popcll(m[c][e] & below);
+      perm_token[p] = tid;
+      inv_perm[tid * tk + j] = p;
+    }
   }
 }
 
@@ -243,6 +308,11 @@ int moe_permute(const float* logits, const float* bias, int64_t T, int64_t E, in
   }
   k_route<<<(unsigned)((T + 3) / 4), 256, 0, s>>>(logits, bias, T, (int)E, (int)tk, topk_ids,
                                                   topk_w);
+  if (T <= kSmallT && E <= kSmallE) {
+    k_permute_small<<<1, 1024, 0, s>>>(topk_ids, (int)T, (int)E, (int)tk, expert_offsets,
+                                       perm_token, inv_perm);
+    return check_launch("moe_permute");
+  }
   int32_t* totals = counts + (size_t)nchunks * E;
   k_route_masks<<<(unsigned)nchunks, 64, 0, s>>>(topk_ids, T, (int)E, (int)tk, masks, counts);
   k_chunk_scan<<<(unsigned)((E + 3) / 4), 256, 0, s>>>(counts, nchunks, (int)E, totals);

@@ -191,6 +191,8 @@ def test_select_ties_prefer_lower_index(dev):
 
 @pytest.mark.parametrize("T,E,tk,bias", [(1, 8, 2, False), (63, 8, 1, False), (64, 16, 4, True),
                                          (65, 128, 8, True), (300, 128, 8, False),
+                                         (512, 256, 8, True),    # largest one-workgroup case
+                                         (513, 128, 8, False),   # smallest multi-kernel case
                                          (1000, 1024, 32, True)])
 def test_moe_permute_bitexact(dev, T, E, tk, bias):
     say(f"permute T={T} E={E} tk={tk} bias={bias}")
