@@ -162,7 +162,9 @@ def test_qdq_weights_bitexact(dev, E, N, K):
 # ------------------------------------------------------------------ selection
 
 @pytest.mark.parametrize("M,K,k", [(9, 64, 1), (50, 512, 16), (20, 768, 64), (4, 96, 96), (300, 4096, 128),
-                                   (6, 8192, 100), (3, 16384, 300)])
+                                   (6, 8192, 100), (3, 16384, 300),
+                                   (256, 4096, 64),    # the decode block's first selection
+                                   (257, 1024, 64)])
 def test_select_residual_bitexact(dev, M, K, k):
     say(f"select M={M} K={K} k={k}")
     rng = np.random.default_rng(M + K + k)
