@@ -788,8 +788,8 @@ def block_summary(cfg, res, decode):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); every box here has "
-              f"one GPU and this build has no multi-GPU path", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the library runs each "
+              f"call on one device and has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
