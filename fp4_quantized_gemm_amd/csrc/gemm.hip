@@ -1537,15 +1537,20 @@ k_gemm_fp8(Fp8Args p, int n_tiles, int m_tiles) {
   }
   const int64_t vt = e_hi - p0;
   const int v_tile = vt > BM ? BM : (int)vt;
-  // (offsets summed in 32 bits, which cannot wrap: M_src K and N K are
-  // below 2^32; the loads then take the scalar base and one VGPR each,
-  // instead of 64-bit per-lane addresses hoisted out of the loop)
+  // stage loads as buffer loads into LDS, as in k_gemm_big: the lane's
+  // offset (fixed over K) in a VGPR, the step in the scalar offset (M_src K
+  // and one expert's N K are below 2^32; a load past a buffer reads zeros)
+  const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(p.a), (short)0, (int)(uint32_t)(p.M_src * p.K), kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(wc), (short)0, (int)(uint32_t)(p.N * p.K), kBufferRsrcWord3);
   auto issue_loads = [&](uint8_t* st, uint32_t k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_global_load_lds(p.a + (off_a[i] + k0), st + (i * 8 + wave) * 1024, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(wc + (off_b[i] + k0), st + A_BYTES + (i * 8 + wave) * 1024, 16, 0,
-                                       0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, lds_ptr(st + (i * 8 + wave) * 1024), 16, off_a[i],
+                                               k0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, lds_ptr(st + A_BYTES + (i * 8 + wave) * 1024), 16,
+                                               off_b[i], k0, 0, 0);
     }
   };
 
