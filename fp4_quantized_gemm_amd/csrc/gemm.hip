@@ -280,16 +280,16 @@ k_gemm_generic(GemmArgs p) {
 //    significant bits, magnitudes 2^-10 .. 2880, so f16 holds it exactly) in
 //    the workspace.  Inside every 64-wide K block the eight 16-byte chunks
 //    are stored in the order the matrix-core lanes consume them.
-// 2. k_gemm_big: 256x256 per workgroup, four waves of 128x128, K in steps of
-//    64 through double-buffered LDS filled by direct global->LDS loads.  A
-//    tiles arrive as f16; weight tiles arrive packed and each wave decodes
-//    its 128 columns in registers: the hardware FP4 convert applies the block
-//    scale's power of two, one packed f16 multiply its significand
+// 2. k_gemm_big: 256x256 per workgroup, eight waves of 256x32, K in steps of
+//    64 through double-buffered LDS filled by buffer loads straight into
+//    LDS.  A tiles arrive as f16; weight tiles arrive packed and each wave
+//    decodes its 32 columns in registers: the hardware FP4 convert applies
+//    the block scale's power of two, one packed f16 multiply its significand
 //    (s = 2^E * mu, mu in [1, 2)).  Products run on v_mfma_f32_32x32x16_f16.
-//    The weights of the selected residual channels are copied out of each
-//    staged K tile into an LDS tile (bf16, exact) as the loop passes them;
-//    after the loop the correction runs on v_mfma_f32_32x32x16_bf16 into
-//    the same accumulators.
+//    The weights of the selected residual channels are decoded per tile from
+//    the channel-major part of the packed weights into an LDS tile (bf16,
+//    exact); after the loop the correction runs on v_mfma_f32_32x32x16_bf16
+//    into the same accumulators.
 //
 // MFMA 32x32x16 operand layout: lane l supplies row (or column) l % 32 and
 // the 8 k values of group kg = l / 32.  Within a 64-wide K step, lane group
@@ -452,7 +452,7 @@ k_gemm_big(GemmArgs p, const uint8_t* __restrict__ a_img, int n_tiles, int m_til
     c = c < p.glu_i ? c : p.glu_i - 1;
     return r < 128 ? c : p.glu_i + c;
   };
-  const uint32_t Kh = (uint32_t)(p.K / 2), Ks = (uint32_t)(p.K / 16), K2 = (uint32_t)(p.K * 2);
+  const uint32_t K2 = (uint32_t)(p.K * 2);
   // channels of the correction (K slices: all on slice 0, none on the others)
   const int kk = (W16 || (SPLIT && blockIdx.y != 0)) ? 0 : p.k;
   // The selected channels' weight columns go through LDS KMAX channels (one
