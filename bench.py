@@ -424,10 +424,42 @@ def cpu_baseline(cfg, wl, tokens, experts):
             "cores_available": cores, "blas_threads": threads}
 
 
-def ceilings(reps=5):
+def nvfp4_operands(x_bits, w_bits):
+    """MFMA operand values as the large-tile GEMM multiplies them: 64 rows of
+    activations and 64 weight rows (bf16 bits, host arrays [64][K]) quantized
+    to NVFP4 by the library and decoded to q * s, as [64 lanes][8 A + 8 B
+    registers][8] f16 and bf16 bit patterns (device tensors).  Measurement
+    only: the decode here is two table lookups."""
+    import numpy as np
+    import torch
+
+    import fp4_quantized_gemm_amd as F
+
+    dev = torch.device("cuda:0")
+    to = lambda b: torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+    q = F.nvfp4_quantize_act(to(x_bits))
+    W = F.nvfp4_qdq_weights(to(w_bits)[None], want_qdq=False, want_packed=False)
+    grid = torch.tensor([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6],
+                        dtype=torch.float32, device=dev)
+
+    def values(codes, scales):
+        c = codes.reshape(codes.shape[0], -1).to(torch.int64)
+        nib = torch.stack([c & 15, c >> 4], dim=-1).reshape(c.shape[0], -1)
+        s = scales.reshape(scales.shape[0], -1).view(torch.float8_e4m3fn).to(torch.float32)
+        return (grid[nib] * s.repeat_interleave(16, dim=1)).reshape(-1)[:4096]
+
+    a, b = values(q["codes"], q["scales"]), values(W.codes[0], W.scales[0])
+    ops = torch.cat([a.reshape(64, 8, 8), b.reshape(64, 8, 8)], dim=1)   # [lane][16][8]
+    return ops.to(torch.float16).contiguous(), ops.to(torch.bfloat16).contiguous()
+
+
+def ceilings(reps=5, operands=None):
     """Sustained rates measured on this chip: each matrix-core instruction
     family the exact NVFP4 product (f16/bf16) and its FP8 baseline can use,
-    and HBM streaming read and copy."""
+    and HBM streaming read and copy.  With `operands` (nvfp4_operands), also
+    the f16 and bf16 rates on exactly decoded NVFP4 values of the workload,
+    run long enough for the clock to settle: the matrix cores' rate depends
+    on the operand bits."""
     import ctypes
 
     import torch
@@ -437,7 +469,7 @@ def ceilings(reps=5):
     L = F.lib()
     dev = torch.device("cuda:0")
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    out = torch.empty(2 * cus * 256, dtype=torch.float32, device=dev)
+    out = torch.empty(4 * cus * 256, dtype=torch.float32, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     res = {"cus": cus}
     for kind, name in ((0, "mfma_f16"), (1, "mfma_bf16"), (2, "mfma_fp8"), (3, "mfma_fp4")):
@@ -448,6 +480,16 @@ def ceilings(reps=5):
         ms = median_ms(fn, reps)
         flops = 2 * cus * 4 * iters * 4 * L.nvfp4_ceiling_mfma_flops(kind)
         res[name + "_tflops"] = round(flops / ms / 1e9, 1)
+    if operands is not None:
+        iters = 40000                                  # ~25 ms per call
+        for bf, name, ops in ((0, "mfma_f16", operands[0]), (1, "mfma_bf16", operands[1])):
+            fn = lambda: L.nvfp4_ceiling_mfma_operands(bf, ctypes.c_void_p(ops.data_ptr()), iters,
+                                                       4 * cus, ctypes.c_void_p(out.data_ptr()),
+                                                       stream)
+            assert fn() == 0
+            ms = median_ms(fn, 3)
+            flops = 4 * cus * 4 * iters * 8 * 2 * 32 * 32 * 16
+            res[name + "_nvfp4_operands_tflops"] = round(flops / ms / 1e9, 1)
     nbytes = 2 << 30                                   # 2 GiB, past the 256 MB cache
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     buf.fill_(1)
@@ -851,6 +893,9 @@ def main():
         "quantizer": main_block["quantizer"],
         "rac_overhead": main_block["rac_overhead"],
     }
+    ops = None
+    if not args.no_ceilings and wl.w_first is not None:
+        ops = nvfp4_operands(wl.x[:64], wl.w_first[0, :64])
     del res, wl
     if not args.no_decode and args.config != 4:
         dcfg = synth.get(4)
@@ -859,7 +904,13 @@ def main():
         line["decode"] = block_summary(dcfg, dres, True)
         del dres
     if not args.no_ceilings:
-        line["ceilings"] = ceilings()
+        line["ceilings"] = ceilings(operands=ops)
+        c16 = line["ceilings"].get("mfma_f16_nvfp4_operands_tflops")
+        if c16 and line["roofline"]["bound"] == "mfma":
+            # the same achieved rate against the f16 matrix-core rate on
+            # this workload's own NVFP4 operand values
+            line["roofline"]["frac_of_f16_rate_on_these_operands"] = round(
+                line["roofline"]["achieved"] / c16, 4)
     gates = {}
     r = line["roofline"]
     if r["bound"] == "mfma":

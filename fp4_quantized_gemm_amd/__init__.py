@@ -59,7 +59,8 @@ EXPORTED_SYMBOLS = [
 
 
 # measurement-only exports (include/nvfp4rac_bench.h)
-BENCH_SYMBOLS = ["nvfp4_ceiling_mfma_flops", "nvfp4_ceiling_mfma", "nvfp4_ceiling_read"]
+BENCH_SYMBOLS = ["nvfp4_ceiling_mfma_flops", "nvfp4_ceiling_mfma", "nvfp4_ceiling_mfma_operands",
+                 "nvfp4_ceiling_read"]
 
 
 class NvfpError(RuntimeError):
@@ -131,6 +132,8 @@ def _load():
     L.nvfp4_ceiling_mfma_flops.argtypes = [ctypes.c_int]
     L.nvfp4_ceiling_mfma.restype = ctypes.c_int
     L.nvfp4_ceiling_mfma.argtypes = [ctypes.c_int, _I64, _I64, _P, _P]
+    L.nvfp4_ceiling_mfma_operands.restype = ctypes.c_int
+    L.nvfp4_ceiling_mfma_operands.argtypes = [ctypes.c_int, _P, _I64, _I64, _P, _P]
     L.nvfp4_ceiling_read.restype = ctypes.c_int
     L.nvfp4_ceiling_read.argtypes = [_P, _I64, _P, _P]
     _lib = L

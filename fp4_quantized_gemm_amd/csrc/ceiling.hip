@@ -64,6 +64,50 @@ k_ceiling_mfma(int64_t iters, float* __restrict__ out) {
   out[blockIdx.x * 256LL + threadIdx.x] = s;
 }
 
+// The same instruction fed with given operand values: lane l loads eight A
+// and eight B registers (16 bytes each) from operands[l][16], and each wave
+// runs `iters` rounds of eight MFMAs that rotate through them (so every
+// instruction sees new operand bits), on four accumulators.  The matrix
+// cores' sustained rate depends on the operands' bits (the chip holds a
+// lower clock when they toggle more), so this gives the ceiling for the
+// values a GEMM actually multiplies.
+template <bool BF>
+__global__ void __launch_bounds__(256)
+k_ceiling_operands(const uint4* __restrict__ operands, int64_t iters, float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  u32x4 a[8], b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint4 va = operands[lane * 16 + i], vb = operands[lane * 16 + 8 + i];
+    a[i] = u32x4{va.x, va.y, va.z, va.w};
+    b[i] = u32x4{vb.x, vb.y, vb.z, vb.w};
+  }
+  f32x16c_t acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (BF)
+        acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[i]),
+                                                             __builtin_bit_cast(bf16x8, b[(i + 3) & 7]),
+                                                             acc[i & 3], 0, 0, 0);
+      else
+        acc[i & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8c_t, a[i]),
+                                                            __builtin_bit_cast(f16x8c_t, b[(i + 3) & 7]),
+                                                            acc[i & 3], 0, 0, 0);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[j][r];
+  out[blockIdx.x * 256LL + threadIdx.x] = s;
+}
+
 // Streaming read of `n16` 16-byte chunks, eight loads in flight per thread;
 // the xor of everything read is written only if it equals a value no input
 // here produces, so the loads stay live and nothing is written.
@@ -122,6 +166,23 @@ int nvfp4_ceiling_mfma(int kind, int64_t iters, int64_t workgroups, float* out, 
     default: k_ceiling_mfma<3><<<g, 256, 0, s>>>(iters, out); break;
   }
   return check_launch("nvfp4_ceiling_mfma");
+}
+
+int nvfp4_ceiling_mfma_operands(int bf16, const void* operands, int64_t iters, int64_t workgroups,
+                                float* out, void* stream) {
+  NV_REQUIRE(bf16 == 0 || bf16 == 1, NVFP4_ERR_SHAPE, "nvfp4_ceiling_mfma_operands: bf16 is 0 or 1");
+  NV_REQUIRE(iters >= 1 && workgroups >= 1 && workgroups <= (1LL << 20), NVFP4_ERR_SHAPE,
+             "nvfp4_ceiling_mfma_operands: need iters >= 1, 1 <= workgroups <= 2^20");
+  NV_REQUIRE(operands != nullptr && out != nullptr, NVFP4_ERR_NULL,
+             "nvfp4_ceiling_mfma_operands: missing pointer");
+  NV_REQUIRE(aligned(operands, 16) && aligned(out, 4), NVFP4_ERR_ALIGN,
+             "nvfp4_ceiling_mfma_operands: misaligned pointer");
+  hipStream_t s = as_stream(stream);
+  const unsigned g = (unsigned)workgroups;
+  const uint4* ops = static_cast<const uint4*>(operands);
+  if (bf16) k_ceiling_operands<true><<<g, 256, 0, s>>>(ops, iters, out);
+  else k_ceiling_operands<false><<<g, 256, 0, s>>>(ops, iters, out);
+  return check_launch("nvfp4_ceiling_mfma_operands");
 }
 
 int nvfp4_ceiling_read(const void* src, int64_t bytes, uint32_t* out, void* stream) {

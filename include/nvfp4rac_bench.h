@@ -35,6 +35,18 @@ double nvfp4_ceiling_mfma_flops(int kind);
  * workgroups * 4 * iters * 4 * nvfp4_ceiling_mfma_flops(kind). */
 int nvfp4_ceiling_mfma(int kind, int64_t iters, int64_t workgroups, float* out, void* stream);
 
+/* The f16 (bf16 = 0) or bf16 (bf16 = 1) 32x32x16 MFMA fed with given
+ * operand values: operands is 64 lanes x 16 registers x 16 bytes (16 KB of
+ * 16-bit values, device memory); lane l takes registers 0..7 as its A and
+ * 8..15 as its B operands, and every wave issues iters * 8 MFMAs rotating
+ * through them, on four accumulators.  out [workgroups * 256] float32
+ * receives one value per lane.  Total flops = workgroups * 4 * iters * 8 *
+ * 2 * 32 * 32 * 16.  The matrix cores' sustained rate depends on the
+ * operand bits, so this measures the ceiling for the values a GEMM
+ * multiplies (e.g. exactly decoded NVFP4 operands). */
+int nvfp4_ceiling_mfma_operands(int bf16, const void* operands, int64_t iters, int64_t workgroups,
+                                float* out, void* stream);
+
 /* Streaming read of `bytes` (a multiple of 16) from src, 16 bytes per lane
  * per nontemporal load, eight loads in flight per lane; out [1] uint32 is never written
  * for real data (it keeps the loads live). */

@@ -48,6 +48,8 @@ def test_measurement_header_symbols_exported():
     assert L.nvfp4_ceiling_mfma_flops(0) == 2 * 32 * 32 * 16
     assert L.nvfp4_ceiling_mfma_flops(3) == 2 * 32 * 32 * 64
     assert L.nvfp4_ceiling_mfma(7, 1, 1, FAKE, None) == ERR_SHAPE
+    assert L.nvfp4_ceiling_mfma_operands(2, FAKE, 1, 1, FAKE, None) == ERR_SHAPE
+    assert L.nvfp4_ceiling_mfma_operands(0, None, 1, 1, FAKE, None) == ERR_NULL
     assert L.nvfp4_ceiling_mfma(0, 1, 1, None, None) == ERR_NULL
     assert L.nvfp4_ceiling_read(FAKE, 24, FAKE, None) == ERR_SHAPE
 
