@@ -26,6 +26,8 @@ def test_bench_mode_prints_json(dev, mode):
         assert d["roofline"]["bound"] == "mfma" and d["value"] > 0
         assert set(d["step_ms_events"]) == {"p10", "p50", "p90"}
         assert d["ceilings"]["mfma_f16_tflops"] > 0 and d["ceilings"]["hbm_read_GBps"] > 0
+        assert d["ceilings"]["mfma_f16_nvfp4_operands_tflops"] > 0
+        assert d["roofline"]["frac_of_f16_rate_on_these_operands"] > 0
         assert "gemm1" in d["rac_overhead"] and "gates" in d
     else:
         assert d["mode"] in ("rac_sweep", "w4a16", "fp8", "ceilings")
