@@ -1770,7 +1770,8 @@ static int gemm_rac(bool per_expert, bool glu, uint32_t* h_amax, const uint8_t* 
   const int64_t m_tiles_big = (M_total + big::BM - 1) / big::BM + E;
   // NVFP4RAC_GEMM=generic|big forces a kernel (tests use it to cover both on
   // small shapes).  The large-tile path holds at most KMAX residual channels,
-  // needs the f16 image of A in the workspace and 32-bit image offsets.
+  // needs the f16 image of A in the workspace, and 32-bit offsets into the
+  // image, one expert's weights and the residual rows.
   const char* force = getenv("NVFP4RAC_GEMM");
   // few rows per expert (decode): stream each expert's weights once; else
   // the large-tile kernel wherever it takes the shape (it is also the faster
@@ -1823,6 +1824,7 @@ static int gemm_rac(bool per_expert, bool glu, uint32_t* h_amax, const uint8_t* 
   const size_t need_big = grouped_w4a4_gemm_rac_workspace_size(E, M_src, M_total, N, K, k);
   use_big = use_big && (k <= big::KMAX || big_streams_ws(k)) && K / big::BK <= big::KSTEPS_MAX &&
             ws_bytes >= need_big && (uint64_t)M_src * K * 2 < (1ULL << 32) &&
+            (uint64_t)N * (uint64_t)K / 2 < (1ULL << 32) &&
             (uint64_t)(per_expert ? M_total : M_src) * k * 2 < (1ULL << 32);
   if (use_big) {
     uint16_t* img = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + img_offset(E));
