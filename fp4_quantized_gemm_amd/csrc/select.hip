@@ -177,9 +177,10 @@ k_gather_residual(const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __
         const int64_t m = m0 + q / k;
         const int j = (int)(q % k);
         const int c = S[j];
-        cb[u] = codes[m * (K / 2) + (c >> 1)];
-        sb[u] = scales[m * (K / 16) + (c >> 4)];
-        xb[u] = x[m * ldx + c];
+        // (streaming hint: the last read of these rows in a forward)
+        cb[u] = __builtin_nontemporal_load(codes + m * (K / 2) + (c >> 1));
+        sb[u] = __builtin_nontemporal_load(scales + m * (K / 16) + (c >> 4));
+        xb[u] = __builtin_nontemporal_load(x + m * ldx + c);
         sh[u] = 4 * (c & 1);
       }
     }
