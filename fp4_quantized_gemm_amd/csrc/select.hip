@@ -177,9 +177,10 @@ k_gather_residual(const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __
         const int64_t m = m0 + q / k;
         const int j = (int)(q % k);
         const int c = S[j];
-        // (streaming hint: the last read of these rows in a forward)
-        cb[u] = __builtin_nontemporal_load(codes + m * (K / 2) + (c >> 1));
-        sb[u] = __builtin_nontemporal_load(scales + m * (K / 16) + (c >> 4));
+        cb[u] = codes[m * (K / 2) + (c >> 1)];
+        sb[u] = scales[m * (K / 16) + (c >> 4)];
+        // (streaming hint: the last read of x in a forward; the codes and
+        // scales are read again to build the GEMM's operand image)
         xb[u] = __builtin_nontemporal_load(x + m * ldx + c);
         sh[u] = 4 * (c & 1);
       }
