@@ -192,13 +192,16 @@ __device__ __forceinline__ void quant_block16(const uint4& v0, const uint4& v1, 
                                               float xf[16], uint32_t& sbyte, float& s,
                                               uint32_t pk[2]) {
   const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-  uint32_t bmax = 0;
+  // largest |x| bits: a packed 16-bit max over the sign-cleared pairs
+  typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+  u16x2_t m2 = {0, 0};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     xf[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
     xf[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
-    bmax = max(bmax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+    m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, w[i] & 0x7FFF7FFFu));
   }
+  const uint32_t bmax = max((uint32_t)m2.x, (uint32_t)m2.y);
   sbyte = 0;
   s = 0.0f;
   pk[0] = pk[1] = 0u;
@@ -209,11 +212,13 @@ __device__ __forceinline__ void quant_block16(const uint4& v0, const uint4& v1, 
   }
   if (s > 0.0f) {
     const float rho = kScaleDen / (s * A);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t b = e2m1_pack2(xf[2 * i] * rho, xf[2 * i + 1] * rho);
-      pk[i >> 2] |= b << (8 * (i & 3));
-    }
+    // each conversion writes its two codes into byte i % 4 of the word
+#define NV_PK_FP4(I)                                                                    \
+  pk[(I) >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(pk[(I) >> 2], xf[2 * (I)] * rho, \
+                                                          xf[2 * (I) + 1] * rho, 1.0f, (I) & 3)
+    NV_PK_FP4(0); NV_PK_FP4(1); NV_PK_FP4(2); NV_PK_FP4(3);
+    NV_PK_FP4(4); NV_PK_FP4(5); NV_PK_FP4(6); NV_PK_FP4(7);
+#undef NV_PK_FP4
   } else {
     // magnitude 0 everywhere; keep the signs
 #pragma unroll
