@@ -182,7 +182,7 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 __device__ __forceinline__ uint32_t swiglu_pair(uint32_t g2, uint32_t u2) {
   float g0 = bf16_bits_to_f32(g2 & 0xFFFFu), g1 = bf16_bits_to_f32(g2 >> 16);
   float u0 = bf16_bits_to_f32(u2 & 0xFFFFu), u1 = bf16_bits_to_f32(u2 >> 16);
-  return f32_to_bf16_rne(silu_mul(g0, u0)) | (f32_to_bf16_rne(silu_mul(g1, u1)) << 16);
+  return bf16x2_rne(silu_mul(g0, u0), silu_mul(g1, u1));
 }
 
 // One 16-element block (two 16-byte halves of bf16 bits) against tensor amax
