@@ -4,23 +4,26 @@
 // gist.science technical summary §2.1; the channels of largest residual get
 // compensated, summary §2.2 B).
 //
-// Up to three kernels per call, HBM-bound:
+// Two kernels per call (three when the amax is given and G_r > 1):
 //   1. amax: every workgroup writes the largest |x| of its share (bf16 bits,
 //      an integer max, so exact and order-free) to its own slot; nothing is
 //      shared, so nothing needs clearing first.  For the SwiGLU input it also
-//      forms h = bf16(silu(gate) * up) and writes h once.
+//      forms h = bf16(silu(gate) * up) and writes h once.  Its first
+//      workgroup zeroes the scores for step 2.
 //   2. quantize: a workgroup owns one column tile of 256 channels (16 blocks
 //      of 16) for every G_r-th group of 16 rows: it takes the tensor amax as
 //      the largest slot, quantizes its blocks (E4M3 scale, E2M1 codes via the
 //      hardware conversion), forms the residual and the fixed-point channel
-//      score of its rows, and writes the 256 channel sums of its row groups
-//      (with G_r = 1, the scores themselves).
-//   3. score sum (G_r > 1): score[j] = the G_r partial sums of channel j.
-//      Integer sums: any grouping gives the same bits.
+//      score of its rows, and adds the 256 channel sums of its row groups to
+//      the scores with 64-bit integer atomics (with G_r = 1 it writes them).
+//      Integer sums: any order gives the same bits.
+//   3. only when the amax is given (no pass 1 to zero the scores) and
+//      G_r > 1: step 2 writes its channel sums to the scratch instead, and
+//      score[j] = the G_r partial sums of channel j, as a kernel.
 //
-// Scratch per call: the amax slots and G_r x K u64 partial sums, with G_r
-// chosen so the grid holds about four workgroups per CU: at most ~2 MB at
-// K = 4096 on 256 CUs, whatever M is.
+// Scratch per call: the amax slots and (amax given) G_r x K u64 partial
+// sums, with G_r chosen so the grid holds about four workgroups per CU: at
+// most ~2 MB at K = 4096 on 256 CUs, whatever M is.
 #include <mutex>
 
 #include "device.h"
@@ -46,7 +49,10 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
 // Pass 1, contiguous x: n8 chunks of 8 bf16, four 16-byte loads in flight per
 // thread; workgroup b writes its max to part[b].
 __global__ void __launch_bounds__(256)
-k_act_amax(const uint16_t* __restrict__ x, int64_t n8, uint32_t* __restrict__ part) {
+k_act_amax(const uint16_t* __restrict__ x, int64_t n8, uint32_t* __restrict__ part,
+           uint64_t* __restrict__ zero, int64_t n_zero) {
+  if (blockIdx.x == 0)
+    for (int64_t i = threadIdx.x; i < n_zero; i += 256) zero[i] = 0ull;
   const uint4* xv = reinterpret_cast<const uint4*>(x);
   const int64_t stride = (int64_t)gridDim.x * 256;
   int64_t i = blockIdx.x * 256LL + threadIdx.x;
@@ -63,7 +69,9 @@ k_act_amax(const uint16_t* __restrict__ x, int64_t n8, uint32_t* __restrict__ pa
 // Pass 1, rows of K bf16 at stride ldx (workgroup b takes rows b, b + G, ...).
 __global__ void __launch_bounds__(256)
 k_act_amax_rows(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
-                uint32_t* __restrict__ part) {
+                uint32_t* __restrict__ part, uint64_t* __restrict__ zero, int64_t n_zero) {
+  if (blockIdx.x == 0)
+    for (int64_t i = threadIdx.x; i < n_zero; i += 256) zero[i] = 0ull;
   uint32_t m = 0;
   for (int64_t r = blockIdx.x; r < M; r += gridDim.x)
     for (int64_t c = threadIdx.x; c < K / 8; c += 256)
@@ -76,7 +84,10 @@ k_act_amax_rows(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ld
 // y = [gate | up] ([M][2I], row stride ldy), written once, with its amax.
 __global__ void __launch_bounds__(256)
 k_act_swiglu_amax(const uint16_t* __restrict__ y, int64_t M, int64_t ldy, int64_t I,
-                  uint16_t* __restrict__ h, uint32_t* __restrict__ part) {
+                  uint16_t* __restrict__ h, uint32_t* __restrict__ part,
+                  uint64_t* __restrict__ zero, int64_t n_zero) {
+  if (blockIdx.x == 0)
+    for (int64_t i = threadIdx.x; i < n_zero; i += 256) zero[i] = 0ull;
   uint32_t m = 0;
   const int64_t n8 = M * (I / 8);
   for (int64_t q = blockIdx.x * 256LL + threadIdx.x; q < n8; q += (int64_t)gridDim.x * 256) {
@@ -108,7 +119,8 @@ __global__ void __launch_bounds__(256)
 k_act_quant(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
             const uint32_t* __restrict__ part, int n_part, const uint32_t* __restrict__ amax_given,
             uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ g_out,
-            uint64_t* __restrict__ score, uint64_t* __restrict__ score_part) {
+            uint64_t* __restrict__ score, uint64_t* __restrict__ score_part,
+            int score_zeroed) {
   __shared__ uint64_t red[kTileRows][kTileBlocks * 16];      // 32 KB: [row sub][channel]
   const int tid = threadIdx.x;
   const int rs = tid >> 4, cb = tid & 15;
@@ -212,7 +224,13 @@ k_act_quant(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
 #pragma unroll
   for (int q = 0; q < kTileRows; ++q) tot += red[q][tid];
   const int64_t ch = (int64_t)ct * (kTileBlocks * 16) + tid;
-  if (ch < K) (G_r == 1 ? score : score_part + (int64_t)gy * K)[ch] = tot;
+  if (ch >= K) return;
+  if (G_r == 1)
+    score[ch] = tot;
+  else if (score_zeroed)
+    atomicAdd(reinterpret_cast<unsigned long long*>(score + ch), (unsigned long long)tot);
+  else
+    score_part[(int64_t)gy * K + ch] = tot;
 }
 
 // Pass 3: score[j] = sum over q < G_r of part[q][j].  A workgroup takes 64
@@ -275,6 +293,13 @@ static int act_quantize(const char* who, const void* x, int64_t M, int64_t K, in
                         hipStream_t s) {
   uint32_t* part = static_cast<uint32_t*>(ws);
   uint64_t* score_part = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + pl.part_off);
+  // with the amax pass in this call, it zeroes the scores and the quantize
+  // pass adds each workgroup's channel sums with 64-bit integer atomics (no
+  // third launch, no partial sums); with the amax given, the partial sums
+  // go to the scratch and a separate pass adds them
+  const bool atomic_scores = amax_given == nullptr && score != nullptr && pl.groups > 1;
+  uint64_t* zero = atomic_scores ? score : nullptr;
+  const int64_t n_zero = atomic_scores ? K : 0;
   const uint16_t* src = static_cast<const uint16_t*>(x);
   int64_t ld = ldx;
   int n_part = 0;
@@ -286,24 +311,26 @@ static int act_quantize(const char* who, const void* x, int64_t M, int64_t K, in
       nb = nb > 4LL * cus ? 4LL * cus : nb;
       nb = nb > kAmaxSlots ? kAmaxSlots : (nb < 1 ? 1 : nb);
       k_act_swiglu_amax<<<(unsigned)nb, 256, 0, s>>>(src, M, ldx, K,
-                                                    static_cast<uint16_t*>(x_used), part);
+                                                    static_cast<uint16_t*>(x_used), part,
+                                                    zero, n_zero);
       src = static_cast<const uint16_t*>(x_used);
       ld = K;
     } else if (ldx == K) {
       nb = (M * K / 8 + 1023) / 1024;
       nb = nb > 4LL * cus ? 4LL * cus : nb;
       nb = nb > kAmaxSlots ? kAmaxSlots : (nb < 1 ? 1 : nb);
-      k_act_amax<<<(unsigned)nb, 256, 0, s>>>(src, M * K / 8, part);
+      k_act_amax<<<(unsigned)nb, 256, 0, s>>>(src, M * K / 8, part, zero, n_zero);
     } else {
       nb = M < 1 ? 1 : (M > 4LL * cus ? 4LL * cus : M);
       nb = nb > kAmaxSlots ? kAmaxSlots : nb;
-      k_act_amax_rows<<<(unsigned)nb, 256, 0, s>>>(src, M, K, ldx, part);
+      k_act_amax_rows<<<(unsigned)nb, 256, 0, s>>>(src, M, K, ldx, part, zero, n_zero);
     }
     n_part = (int)nb;
   }
   k_act_quant<<<dim3((unsigned)pl.tiles, (unsigned)pl.groups), 256, 0, s>>>(
-      src, M, K, ld, part, n_part, amax_given, codes, scales, g_x, score, score_part);
-  if (score != nullptr && pl.groups > 1)
+      src, M, K, ld, part, n_part, amax_given, codes, scales, g_x, score, score_part,
+      atomic_scores ? 1 : 0);
+  if (score != nullptr && pl.groups > 1 && !atomic_scores)
     k_act_score_sum<<<(unsigned)((K + 63) / 64), 256, 0, s>>>(score_part, pl.groups, K, score);
   return check_launch(who);
 }
