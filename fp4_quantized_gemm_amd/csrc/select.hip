@@ -151,21 +151,21 @@ static void launch_select_topk(const uint64_t* score, int64_t K, int64_t k, int3
     k_select_topk<16><<<vectors, kSelectThreads, 0, s>>>(score, (int)K, (int)k, S);
 }
 
-// R[m][j] = bf16(fma(-(q*s), g, x[m][S[j]])): a block owns 64 rows; its 256
-// threads take the (row, channel) pairs of those rows in order, eight pairs
-// in flight per thread (the gathers of one pair are three dependent-free
-// loads, so they overlap across pairs).
+// R[m][j] = bf16(fma(-(q*s), g, x[m][S[j]])): a block owns `rpb` rows (at
+// most 64); its 256 threads take the (row, channel) pairs of those rows in
+// order, eight pairs in flight per thread (the gathers of one pair are three
+// dependent-free loads, so they overlap across pairs).
 constexpr int kGatherRows = 64;
 constexpr int kGatherInFlight = 8;
 
 __global__ void __launch_bounds__(256)
 k_gather_residual(const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ codes,
                   const uint8_t* __restrict__ scales, const float* __restrict__ g_x,
-                  const int32_t* __restrict__ S, int64_t M, int64_t K, int k,
+                  const int32_t* __restrict__ S, int64_t M, int64_t K, int k, int rpb,
                   uint16_t* __restrict__ R) {
   const float g = *g_x;
-  const int64_t m0 = (int64_t)blockIdx.x * kGatherRows;
-  const int64_t rows = M - m0 < kGatherRows ? M - m0 : kGatherRows;
+  const int64_t m0 = (int64_t)blockIdx.x * rpb;
+  const int64_t rows = M - m0 < rpb ? M - m0 : rpb;
   const int64_t n = rows * k;
   for (int64_t q0 = 0; q0 < n; q0 += 256 * kGatherInFlight) {
     uint32_t cb[kGatherInFlight], sb[kGatherInFlight], xb[kGatherInFlight];
@@ -352,9 +352,14 @@ int select_residual_channels(const void* x_used, int64_t ldx, const uint8_t* cod
   hipStream_t s = as_stream(stream);
   launch_select_topk(score, K, k, S, 1, s);
   if (M > 0) {
-    const int64_t blocks = (M + kGatherRows - 1) / kGatherRows;
+    // rows per block: 64, halved while that leaves fewer than two blocks
+    // per CU and a block still has more than one pair per thread (few rows:
+    // the gather is then latency-bound, and more blocks overlap it)
+    int rpb = kGatherRows;
+    while (rpb > 1 && (M + rpb - 1) / rpb < 2LL * num_cus() && (int64_t)rpb * k > 256) rpb /= 2;
+    const int64_t blocks = (M + rpb - 1) / rpb;
     k_gather_residual<<<(unsigned)blocks, 256, 0, s>>>(
-        static_cast<const uint16_t*>(x_used), ldx, codes, scales, g_x, S, M, K, (int)k,
+        static_cast<const uint16_t*>(x_used), ldx, codes, scales, g_x, S, M, K, (int)k, rpb,
         static_cast<uint16_t*>(R_S));
   }
   return check_launch("select_residual_channels");
