@@ -58,11 +58,11 @@ __global__ void __launch_bounds__(kSelectThreads)
 k_select_topk(const uint64_t* __restrict__ score, int K, int k, int32_t* __restrict__ S) {
   score += (int64_t)blockIdx.x * K;
   S += (int64_t)blockIdx.x * k;
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[2][256];                    // passes alternate buffers
   __shared__ uint64_t orw[kSelectThreads / 64];
   __shared__ int wsum[kSelectThreads / 64];
   __shared__ uint64_t s_prefix;
-  __shared__ int s_need;
+  __shared__ int s_need, s_exact;
   const int tid = threadIdx.x;
   uint64_t key[CPT];
   bool valid[CPT];
@@ -74,6 +74,7 @@ k_select_topk(const uint64_t* __restrict__ score, int K, int k, int32_t* __restr
     key[q] = valid[q] ? score[e] : 0ull;
     any |= key[q];
   }
+  if (tid < 512) hist[tid >> 8][tid & 255] = 0u;
   // the highest byte any key uses
   uint64_t orv = wave_or_u64(any);
   if ((tid & 63) == 0) orw[tid >> 6] = orv;
@@ -82,20 +83,25 @@ k_select_topk(const uint64_t* __restrict__ score, int K, int k, int32_t* __restr
   for (int w = 0; w < kSelectThreads / 64; ++w) orv |= orw[w];
   const int top = orv == 0 ? 0 : (63 - __builtin_clzll(orv)) >> 3;
 
+  // Per pass (byte b, from the top): histogram the remaining candidates'
+  // byte b, then one wave finds the bin holding the need-th largest.  If
+  // that bin holds exactly the keys still needed, every key whose bytes
+  // from the top down to b are at least the prefix is selected, and the
+  // lower bytes need no pass.  Two barriers per pass: the next pass's
+  // histogram buffer is cleared while this one is scanned.
   uint64_t prefix = 0, mask = 0;
-  int need = k;
-  for (int b = top; b >= 0; --b) {
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
+  int need = k, exact = 0;
+  for (int b = top, i = 0; b >= 0; --b, ++i) {
+    uint32_t* h = hist[i & 1];
 #pragma unroll
     for (int q = 0; q < CPT; ++q)
-      if (valid[q] && (key[q] & mask) == prefix) atomicAdd(&hist[(key[q] >> (8 * b)) & 0xFFu], 1u);
+      if (valid[q] && (key[q] & mask) == prefix) atomicAdd(&h[(key[q] >> (8 * b)) & 0xFFu], 1u);
     __syncthreads();
     if (tid < 64) {
       // lane l owns bins 255 - 4l .. 252 - 4l (descending)
       int cnt[4], sum = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sum += (cnt[i] = (int)hist[255 - 4 * tid - i]);
+      for (int j = 0; j < 4; ++j) sum += (cnt[j] = (int)h[255 - 4 * tid - j]);
       int incl = sum;
       for (int o = 1; o < 64; o <<= 1) {
         const int w = __shfl_up(incl, o);
@@ -104,34 +110,46 @@ k_select_topk(const uint64_t* __restrict__ score, int K, int k, int32_t* __restr
       int c = incl - sum;                      // keys in higher bins
       if (c < need && need <= incl) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (c + cnt[i] >= need) {
-            s_prefix = prefix | ((uint64_t)(255 - 4 * tid - i) << (8 * b));
+        for (int j = 0; j < 4; ++j) {
+          if (c + cnt[j] >= need) {
+            s_prefix = prefix | ((uint64_t)(255 - 4 * tid - j) << (8 * b));
             s_need = need - c;
+            s_exact = c + cnt[j] == need ? 1 : 0;
             break;
           }
-          c += cnt[i];
+          c += cnt[j];
         }
       }
+    } else if (tid >= 256 && tid < 512) {
+      hist[(i + 1) & 1][tid - 256] = 0u;
     }
     __syncthreads();
     prefix = s_prefix;
     need = s_need;
+    exact = s_exact;
     mask |= 0xFFull << (8 * b);
+    if (exact) break;
   }
-  // prefix is now the k-th largest score T; take everything above it and
-  // the first `need` channels equal to it
+  // exact: the selection is every key whose masked bytes are >= prefix.
+  // Otherwise prefix is the k-th largest score T: take everything above it
+  // and the first `need` channels equal to it.
   int ties = 0;
+  if (!exact) {
 #pragma unroll
-  for (int q = 0; q < CPT; ++q) ties += (valid[q] && key[q] == prefix) ? 1 : 0;
+    for (int q = 0; q < CPT; ++q) ties += (valid[q] && key[q] == prefix) ? 1 : 0;
+  }
   int tie_rank = block_exclusive_scan(ties, wsum);
   bool sel[CPT];
   int nsel = 0;
 #pragma unroll
   for (int q = 0; q < CPT; ++q) {
     sel[q] = false;
-    if (valid[q] && key[q] > prefix) sel[q] = true;
-    if (valid[q] && key[q] == prefix) sel[q] = tie_rank++ < need;
+    if (exact) {
+      sel[q] = valid[q] && (key[q] & mask) >= prefix;
+    } else {
+      if (valid[q] && key[q] > prefix) sel[q] = true;
+      if (valid[q] && key[q] == prefix) sel[q] = tie_rank++ < need;
+    }
     nsel += sel[q] ? 1 : 0;
   }
   int pos = block_exclusive_scan(nsel, wsum);
