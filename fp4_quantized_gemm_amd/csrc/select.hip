@@ -300,10 +300,11 @@ k_gather_residual_rows(const uint16_t* __restrict__ x, int64_t ldx,
                        const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                        const float* __restrict__ g_x, const int32_t* __restrict__ a_rows,
                        const int32_t* __restrict__ offsets, int E, int64_t M_src, int64_t M_total,
-                       int64_t K, int k, const int32_t* __restrict__ S, uint16_t* __restrict__ R) {
+                       int64_t K, int k, int rpb, const int32_t* __restrict__ S,
+                       uint16_t* __restrict__ R) {
   const float g = *g_x;
-  const int64_t p_lo = (int64_t)blockIdx.x * kExpertRows;
-  const int64_t rows = M_total - p_lo < kExpertRows ? M_total - p_lo : kExpertRows;
+  const int64_t p_lo = (int64_t)blockIdx.x * rpb;
+  const int64_t rows = M_total - p_lo < rpb ? M_total - p_lo : rpb;
   const int64_t n = rows * k;
   for (int64_t q0 = 0; q0 < n; q0 += 256 * kGatherInFlight) {
     uint32_t cb[kGatherInFlight], sb[kGatherInFlight], xb[kGatherInFlight];
@@ -424,10 +425,15 @@ int select_residual_channels_per_expert(const void* x_used, int64_t ldx, const u
         static_cast<const uint16_t*>(x_used), ldx, codes, scales, g_x, a_rows, expert_offsets,
         (int)E, M_src, M_total, K, score);
   launch_select_topk(score, K, k, S, (unsigned)E, s);
-  if (M_total > 0)
-    k_gather_residual_rows<<<(unsigned)blocks, 256, 0, s>>>(
+  if (M_total > 0) {
+    // rows per block as in select_residual_channels
+    int rpb = kExpertRows;
+    while (rpb > 1 && (M_total + rpb - 1) / rpb < 2LL * num_cus() && (int64_t)rpb * k > 256)
+      rpb /= 2;
+    k_gather_residual_rows<<<(unsigned)((M_total + rpb - 1) / rpb), 256, 0, s>>>(
         static_cast<const uint16_t*>(x_used), ldx, codes, scales, g_x, a_rows, expert_offsets,
-        (int)E, M_src, M_total, K, (int)k, S, static_cast<uint16_t*>(R));
+        (int)E, M_src, M_total, K, (int)k, rpb, S, static_cast<uint16_t*>(R));
+  }
   return check_launch("select_residual_channels_per_expert");
 }
 
